@@ -1,0 +1,148 @@
+"""fp64 CPU oracle for the decode-phase linear layer y = x . W^T.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+loads it, and it loads nothing of the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, threaded over output
+rows).  This module builds it with gcc when needed and marshals numpy arrays.
+
+Definition followed (see oracle.c for the citations):
+    y_ref[m][n] = sum_k x[m][k] * w[n][k]            in fp64
+    w[n][k]     = bf16 value                         (bf16 weights)
+                = e4m3(q[n][k]) * S[n//128][k//128]  (FP8 weights)
+    A[m][n]     = sum_k |x[m][k] * w[n][k]|
+A GPU result passes when |y - y_ref| <= 2e-3 * A + 1e-6 for every output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+REL_TOL = 2e-3
+ABS_TOL = 1e-6
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (host only, no HIP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                        "-o", tmp, _SRC, "-lpthread", "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    """Load a compiled oracle and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_linear_bf16.restype = ctypes.c_int
+    lib.oracle_linear_bf16.argtypes = [p, p, i64, i64, i64, p, p, ctypes.c_int]
+    lib.oracle_linear_fp8_bs128.restype = ctypes.c_int
+    lib.oracle_linear_fp8_bs128.argtypes = [p, p, p, i64, i64, i64, p, p, ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def host_threads() -> int:
+    """Cores this process may run on (the oracle's default thread count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def bf16_value(code: int) -> float:
+    return _load().oracle_bf16_value(int(code) & 0xFFFF)
+
+
+def e4m3_value(code: int) -> float:
+    return _load().oracle_e4m3_value(int(code) & 0xFF)
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def linear_bf16(x: np.ndarray, w: np.ndarray, threads: int | None = None):
+    """x: [M][K] uint16 bf16 codes, w: [N][K] uint16 bf16 codes.
+
+    Returns (y_ref, A, threads_used): fp64 [M][N] each."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("x and w disagree on K")
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    t = _load().oracle_linear_bf16(x.ctypes.data, w.ctypes.data, M, N, K, y.ctypes.data,
+                                   a.ctypes.data, threads or host_threads())
+    if t < 0:
+        raise RuntimeError("oracle_linear_bf16 failed")
+    return y, a, t
+
+
+def linear_fp8_bs128(x: np.ndarray, q: np.ndarray, scale: np.ndarray,
+                     threads: int | None = None):
+    """x: [M][K] uint16 bf16 codes, q: [N][K] uint8 e4m3 codes,
+    scale: [ceil(N/128)][ceil(K/128)] float32.
+
+    Returns (y_ref, A, threads_used): fp64 [M][N] each."""
+    x = _c(x, np.uint16)
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    M, K = x.shape
+    N, K2 = q.shape
+    if K != K2:
+        raise ValueError("x and q disagree on K")
+    if scale.shape != ((N + 127) // 128, (K + 127) // 128):
+        raise ValueError("scale must be [ceil(N/128)][ceil(K/128)]")
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    t = _load().oracle_linear_fp8_bs128(x.ctypes.data, q.ctypes.data, scale.ctypes.data,
+                                        M, N, K, y.ctypes.data, a.ctypes.data,
+                                        threads or host_threads())
+    if t < 0:
+        raise RuntimeError("oracle_linear_fp8_bs128 failed")
+    return y, a, t
+
+
+def bound(a: np.ndarray) -> np.ndarray:
+    """Per-output tolerance 2e-3 * A + 1e-6."""
+    return REL_TOL * a + ABS_TOL
+
+
+def check(y_gpu: np.ndarray, y_ref: np.ndarray, a: np.ndarray):
+    """Compare a GPU result (any float dtype, [M][N]) with the oracle.
+
+    Returns (ok, worst ratio err/bound, index of the worst output)."""
+    err = np.abs(np.asarray(y_gpu, np.float64) - y_ref)
+    ratio = err / bound(a)
+    if ratio.size == 0:
+        return True, 0.0, None
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    worst = float(ratio[idx])
+    return bool(np.all(ratio <= 1.0)), worst, idx

@@ -1,0 +1,273 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each test fixes the oracle to something the pages or the mathematics decide:
+the pages' printed worked examples, exact rational brute force, a library
+routine (torch's fp64 matmul and its bf16 / float8_e4m3fn decoders), closed
+forms and special cases (identity, permutation, constants)."""
+import json
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemv_skinny_gemm_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+BF16_ONE = 0x3F80
+
+
+def bf16_codes_of(values):
+    """Exact bf16 codes of values that bf16 represents exactly (via torch)."""
+    t = torch.tensor(np.asarray(values, np.float64), dtype=torch.float64)
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.to(torch.float64), t), "value not exact in bf16"
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_codes_of(values):
+    t = torch.tensor(np.asarray(values, np.float64), dtype=torch.float64)
+    f = t.to(torch.float8_e4m3fn)
+    assert torch.equal(f.to(torch.float64), t), "value not exact in e4m3"
+    return f.view(torch.uint8).numpy()
+
+
+def torch_bf16_values(codes):
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint16).view(np.int16))
+    return c.view(torch.bfloat16).to(torch.float64)
+
+
+def torch_e4m3_values(codes):
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+# --- number formats ---------------------------------------------------------
+
+def test_bf16_decode_matches_torch_on_all_codes():
+    lib = oracle._load()
+    mine = np.array([lib.oracle_bf16_value(c) for c in range(65536)])
+    ref = torch_bf16_values(np.arange(65536, dtype=np.uint32).astype(np.uint16)).numpy()
+    both_nan = np.isnan(mine) & np.isnan(ref)
+    assert np.all(both_nan | (mine == ref))
+    assert np.array_equal(np.signbit(mine[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def test_e4m3_decode_matches_torch_and_spec():
+    mine = np.array([oracle.e4m3_value(c) for c in range(256)])
+    ref = torch_e4m3_values(np.arange(256, dtype=np.uint8)).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # Anchors of the OCP E4M3FN definition.
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0xFE) == -448.0
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+# --- brute force in exact rationals -----------------------------------------
+
+def _exact_linear(xv, wv):
+    """Exact rational y and A from fp64 input values (each exactly representable)."""
+    M, K = xv.shape
+    N = wv.shape[0]
+    xf = [[Fraction(float(v)) for v in row] for row in xv]
+    wf = [[Fraction(float(v)) for v in row] for row in wv]
+    y = [[sum((xf[m][k] * wf[n][k] for k in range(K)), Fraction(0)) for n in range(N)]
+         for m in range(M)]
+    a = [[sum((abs(xf[m][k] * wf[n][k]) for k in range(K)), Fraction(0)) for n in range(N)]
+         for m in range(M)]
+    return y, a
+
+
+def _assert_close_to_exact(y, a, y_ex, a_ex, K):
+    M, N = y.shape
+    for m in range(M):
+        for n in range(N):
+            ab = float(a_ex[m][n])
+            # K-term left-to-right fp64 sum: error at most K * 2^-53 * A.
+            tol = K * 2.0 ** -52 * ab
+            assert abs(Fraction(float(y[m, n])) - y_ex[m][n]) <= Fraction(tol)
+            assert abs(a[m, n] - ab) <= tol
+
+
+def test_bf16_linear_vs_exact_rationals():
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 5, 37
+    x = bf16_codes_of(torch.randn(M, K, generator=torch.Generator().manual_seed(1),
+                                  dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy())
+    w = rng.integers(0, 65536, size=(N, K)).astype(np.uint16)
+    w[((w >> 7) & 0xFF) == 0xFF] = BF16_ONE                 # no inf/NaN codes
+    y, a, _ = oracle.linear_bf16(x, w, threads=2)
+    xv = torch_bf16_values(x).numpy()
+    wv = torch_bf16_values(w).numpy()
+    y_ex, a_ex = _exact_linear(xv, wv)
+    # Wide exponent range: results differ from the exact sum only by fp64 rounding.
+    _assert_close_to_exact(y, a, y_ex, a_ex, K)
+
+
+def test_fp8_linear_vs_exact_rationals_with_partial_edge_blocks():
+    rng = np.random.default_rng(12)
+    M, N, K = 2, 130, 260                                   # 2 x 3 scale blocks, ragged edges
+    x = bf16_codes_of(np.round(rng.standard_normal((M, K)) * 64) / 64)
+    q = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38                              # no NaN codes
+    s = (rng.uniform(0.5, 4.0, size=(2, 3)) * np.array([[1, 2, 4], [8, 16, 32]])).astype(np.float32)
+    y, a, _ = oracle.linear_fp8_bs128(x, q, s, threads=3)
+    xv = torch_bf16_values(x).numpy()
+    wv = torch_e4m3_values(q).numpy() * np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:N, :K]
+    y_ex, a_ex = _exact_linear(xv, wv)
+    _assert_close_to_exact(y, a, y_ex, a_ex, K)
+
+
+# --- a library routine: torch fp64 matmul ------------------------------------
+
+def test_bf16_linear_vs_torch_matmul():
+    g = torch.Generator().manual_seed(3)
+    M, N, K = 4, 300, 520
+    xt = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    wt = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16)
+    x = xt.view(torch.int16).numpy().view(np.uint16)
+    w = wt.view(torch.int16).numpy().view(np.uint16)
+    y, a, _ = oracle.linear_bf16(x, w)
+    ref = (xt.double() @ wt.double().T).numpy()
+    ref_a = (xt.double().abs() @ wt.double().abs().T).numpy()
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * ref_a.max())
+    assert np.allclose(a, ref_a, rtol=1e-13, atol=0)
+
+
+def test_fp8_linear_vs_torch_matmul():
+    M, N, K = 6, 300, 520
+    x = synth.tensor_bf16(0, 5, M, K, 1.0)
+    w = synth.tensor_bf16(0, 6, N, K, 0.02)
+    q, s = synth.quantize_bs128(w)
+    y, a, _ = oracle.linear_fp8_bs128(x, q, s)
+    xv = torch_bf16_values(x)
+    full = torch.from_numpy(s.astype(np.float64)).repeat_interleave(128, 0).repeat_interleave(128, 1)
+    wv = torch_e4m3_values(q) * full[:N, :K]
+    ref = (xv @ wv.T).numpy()
+    ref_a = (xv.abs() @ wv.abs().T).numpy()
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * ref_a.max())
+    assert np.allclose(a, ref_a, rtol=1e-13, atol=0)
+
+
+def test_scale_index_is_row_block_then_col_block():
+    # One nonzero scale block tells a swapped (k-block, n-block) index apart.
+    M, N, K = 1, 256, 384
+    x = np.full((M, K), BF16_ONE, np.uint16)
+    q = np.full((N, K), 0x38, np.uint8)                       # every weight code = 1.0
+    s = np.zeros((2, 3), np.float32)
+    s[0, 2] = 2.0                                             # rows 0..127, cols 256..383
+    y, _, _ = oracle.linear_fp8_bs128(x, q, s)
+    assert np.array_equal(y[0, :128], np.full(128, 256.0))
+    assert np.array_equal(y[0, 128:], np.zeros(128))
+
+
+# --- special cases and closed forms -------------------------------------------
+
+def test_identity_bf16_and_fp8():
+    K = 256
+    x = synth.tensor_bf16(0, 7, 3, K, 1.0)
+    w = np.zeros((K, K), np.uint16)
+    w[np.arange(K), np.arange(K)] = BF16_ONE
+    y, _, _ = oracle.linear_bf16(x, w)
+    assert np.array_equal(y, torch_bf16_values(x).numpy())
+    q = np.zeros((K, K), np.uint8)
+    q[np.arange(K), np.arange(K)] = 0x38
+    y8, _, _ = oracle.linear_fp8_bs128(x, q, np.ones((2, 2), np.float32))
+    assert np.array_equal(y8, torch_bf16_values(x).numpy())
+
+
+def test_permutation_bf16():
+    K, N = 192, 100
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(K)[:N]
+    x = synth.tensor_bf16(0, 8, 2, K, 1.0)
+    w = np.zeros((N, K), np.uint16)
+    w[np.arange(N), perm] = BF16_ONE
+    y, _, _ = oracle.linear_bf16(x, w)
+    assert np.array_equal(y, torch_bf16_values(x).numpy()[:, perm])
+
+
+def test_constant_closed_form():
+    K = 8192
+    x = np.full((2, K), 0x3F00, np.uint16)                   # 0.5
+    w = np.full((3, K), 0x3E00, np.uint16)                   # 0.125
+    y, a, _ = oracle.linear_bf16(x, w)
+    assert np.all(y == K * 0.5 * 0.125) and np.all(a == 512.0)
+    q = np.full((3, K), 0x30, np.uint8)                      # e4m3 0.5
+    s = np.full((1, K // 128), 0.25, np.float32)             # weight 0.125
+    y8, _, _ = oracle.linear_fp8_bs128(x, q, s)
+    assert np.all(y8 == 512.0)
+    x[1] = 0xBF00                                            # -0.5: sign carried through
+    y, a, _ = oracle.linear_bf16(x, w)
+    assert np.all(y[1] == -512.0) and np.all(a[1] == 512.0)
+
+
+# --- the pages' printed worked examples --------------------------------------
+
+def test_page_example_column_split():
+    d = json.load(open(os.path.join(GOLDEN, "p2_ex2_column_split.json")))
+    x = np.array(d["x"], np.float64)
+    w_kn = np.array([[((6 * i + j) % 5) - 2 for j in range(6)] for i in range(4)], np.float64)
+    assert w_kn.tolist() == d["w_kn"]
+    w = w_kn.T                                                  # N x K
+    y, _, _ = oracle.linear_bf16(bf16_codes_of(x), bf16_codes_of(w))
+    assert y.tolist() == d["y_printed"]
+    # Each device's column block is the same product on a slice of W's rows.
+    y0, _, _ = oracle.linear_bf16(bf16_codes_of(x), bf16_codes_of(w[:3]))
+    y1, _, _ = oracle.linear_bf16(bf16_codes_of(x), bf16_codes_of(w[3:]))
+    assert y0.tolist() == d["device0_printed"] and y1.tolist() == d["device1_printed"]
+    # FP8 path: the weights -2..2 are exact e4m3 codes; scale 1.
+    y8, _, _ = oracle.linear_fp8_bs128(bf16_codes_of(x), e4m3_codes_of(w), np.ones((1, 1), np.float32))
+    assert y8.tolist() == d["y_printed"]
+
+
+def test_page_example_split_k_partials():
+    d = json.load(open(os.path.join(GOLDEN, "p2_ex3_mlp_split.json")))
+    x = np.array(d["x"], np.float64)
+    a_mat = np.array([[((8 * i + j) % 7) - 3 for j in range(8)] for i in range(4)], np.float64)
+    b_mat = np.array([[((4 * i + j) % 5) - 2 for j in range(4)] for i in range(8)], np.float64)
+    pre, _, _ = oracle.linear_bf16(bf16_codes_of(x), bf16_codes_of(a_mat.T))
+    h = np.maximum(pre, 0.0)                                  # the example's ReLU
+    wb = b_mat.T                                              # N x K = 4 x 8
+    p0, _, _ = oracle.linear_bf16(bf16_codes_of(h[:, :4]), bf16_codes_of(wb[:, :4]))
+    p1, _, _ = oracle.linear_bf16(bf16_codes_of(h[:, 4:]), bf16_codes_of(wb[:, 4:]))
+    full, _, _ = oracle.linear_bf16(bf16_codes_of(h), bf16_codes_of(wb))
+    assert p0.tolist() == d["partial0_printed"]
+    assert p1.tolist() == d["partial1_printed"]
+    assert (p0 + p1).tolist() == d["sum_printed"]
+    assert full.tolist() == d["sum_printed"]
+
+
+# --- the tolerance check -------------------------------------------------------
+
+def test_check_accepts_inside_and_rejects_outside_bound():
+    y_ref = np.array([[1.0, -2.0, 0.0]])
+    a = np.array([[10.0, 10.0, 0.0]])
+    ok, worst, _ = oracle.check(y_ref + np.array([[0.0199, -0.0199, 0.9e-6]]), y_ref, a)
+    assert ok and worst < 1.0
+    ok, worst, idx = oracle.check(y_ref + np.array([[0.0, 0.0211, 0.0]]), y_ref, a)
+    assert not ok and idx == (0, 1)
+
+
+def test_threads_do_not_change_results():
+    x = synth.tensor_bf16(0, 9, 4, 1000, 1.0)
+    w = synth.tensor_bf16(0, 10, 77, 1000, 0.02)
+    y1, a1, t1 = oracle.linear_bf16(x, w, threads=1)
+    y5, a5, t5 = oracle.linear_bf16(x, w, threads=5)
+    assert t1 == 1 and t5 == 5
+    assert np.array_equal(y1, y5) and np.array_equal(a1, a5)
+
+
+def test_empty_shapes():
+    y, a, _ = oracle.linear_bf16(np.zeros((2, 0), np.uint16), np.zeros((3, 0), np.uint16))
+    assert y.shape == (2, 3) and np.all(y == 0) and np.all(a == 0)
