@@ -1,0 +1,212 @@
+"""Python binding of the gfx950 skinny-GEMM C ABI (include/skinny_gemm.h).
+
+Argument marshalling only: every step of y = x . W^T runs in the HIP kernels
+of ``libskinny_gemm.so``.  PyTorch supplies device memory (``data_ptr()``)
+and streams (``torch.cuda.current_stream().cuda_stream``).  There is no
+fallback: if the shared library is missing or fails to load, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BF16", "FP8_BS128", "VARIANT_AUTO", "VARIANT_VECTOR", "VARIANT_MFMA", "MAX_M",
+    "SkinnyError", "Linear", "Plan", "lib", "lib_path",
+    "workspace_bytes", "stack_workspace_bytes", "skinny_gemm_bf16", "skinny_gemm_fp8_bs128",
+    "decode_linear_stack", "linear_run", "plan_query", "status_string", "abi_version",
+]
+
+BF16 = 0
+FP8_BS128 = 1
+VARIANT_AUTO = 0
+VARIANT_VECTOR = 1
+VARIANT_MFMA = 2
+MAX_M = 16
+MAX_LINEARS_PER_LAUNCH = 32
+ABI_VERSION = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libskinny_gemm.so"
+
+STATUS_NAMES = {0: "SKINNY_OK", 1: "SKINNY_ERR_INVALID_ARG", 2: "SKINNY_ERR_UNSUPPORTED",
+                3: "SKINNY_ERR_WORKSPACE", 4: "SKINNY_ERR_HIP"}
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class Linear(ctypes.Structure):
+    """struct skinny_linear"""
+    _fields_ = [("dtype", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int),
+                ("reserved", ctypes.c_int), ("w", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class Plan(ctypes.Structure):
+    """struct skinny_plan"""
+    _fields_ = [("variant", ctypes.c_int), ("waves", ctypes.c_int),
+                ("reserved", ctypes.c_int * 6)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def lib():
+    """The loaded C library.  Raises if it is not built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run __graft_entry__.build() or "
+                              "python -m gemv_skinny_gemm_amd._build")
+        L = ctypes.CDLL(path)
+        sz, vp, i = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+        L.skinny_workspace_bytes.restype = sz
+        L.skinny_workspace_bytes.argtypes = [i, i, i, i]
+        L.skinny_stack_workspace_bytes.restype = sz
+        L.skinny_stack_workspace_bytes.argtypes = [ctypes.POINTER(Linear), i, i]
+        L.skinny_gemm_bf16.restype = i
+        L.skinny_gemm_bf16.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+        L.skinny_gemm_fp8_bs128.restype = i
+        L.skinny_gemm_fp8_bs128.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+        L.decode_linear_stack.restype = i
+        L.decode_linear_stack.argtypes = [ctypes.POINTER(Linear), i, i, vp, sz, vp]
+        L.skinny_linear_run.restype = i
+        L.skinny_linear_run.argtypes = [ctypes.POINTER(Linear), i, i, ctypes.POINTER(Plan),
+                                        vp, sz, vp]
+        L.skinny_plan_query.restype = i
+        L.skinny_plan_query.argtypes = [ctypes.POINTER(Linear), i, i, ctypes.POINTER(Plan)]
+        L.skinny_status_string.restype = ctypes.c_char_p
+        L.skinny_status_string.argtypes = [i]
+        L.skinny_abi_version.restype = i
+        L.skinny_abi_version.argtypes = []
+        if L.skinny_abi_version() != ABI_VERSION:
+            raise ImportError(f"{path}: ABI version {L.skinny_abi_version()} != {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    """Device address of a torch tensor, or an int address as given (None = NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SkinnyError(status, where)
+
+
+def status_string(status: int) -> str:
+    return lib().skinny_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().skinny_abi_version()
+
+
+def workspace_bytes(dtype: int, M: int, N: int, K: int) -> int:
+    return lib().skinny_workspace_bytes(dtype, M, N, K)
+
+
+def _linear_array(linears):
+    arr = (Linear * len(linears))()
+    for i, L in enumerate(linears):
+        arr[i] = L
+    return arr
+
+
+def stack_workspace_bytes(linears, M: int) -> int:
+    arr = _linear_array(linears)
+    return lib().skinny_stack_workspace_bytes(arr, len(linears), M)
+
+
+def _shape2(t):
+    if isinstance(t, int):
+        raise TypeError("pass tensors, or call the raw C entry points through lib()")
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, tuple):
+        return workspace
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def skinny_gemm_bf16(x, w, y, workspace, stream=None):
+    """y[M][N] = x[M][K] . w[N][K]^T (bf16 tensors on the GPU; y written in place)."""
+    M, K = _shape2(x)
+    N, _ = _shape2(w)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_gemm_bf16(_ptr(x), _ptr(w), _ptr(y), M, N, K, wp, wb, _stream(stream)),
+           "skinny_gemm_bf16")
+    return y
+
+
+def skinny_gemm_fp8_bs128(x, w_fp8, w_scale, y, workspace, stream=None):
+    """y = x . (e4m3(w_fp8) * block scale)^T; w_fp8 [N][K] uint8 / float8_e4m3fn,
+    w_scale [ceil(N/128)][ceil(K/128)] float32."""
+    M, K = _shape2(x)
+    N, _ = _shape2(w_fp8)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_gemm_fp8_bs128(_ptr(x), _ptr(w_fp8), _ptr(w_scale), _ptr(y), M, N, K,
+                                        wp, wb, _stream(stream)), "skinny_gemm_fp8_bs128")
+    return y
+
+
+def make_linear(x, w, y, w_scale=None, dtype=None) -> Linear:
+    """A skinny_linear from GPU tensors x [M][K], w [N][K], y [M][N] (w_scale for FP8)."""
+    N, K = _shape2(w)
+    if dtype is None:
+        dtype = FP8_BS128 if w_scale is not None else BF16
+    return Linear(dtype, N, K, 0, _ptr(w), _ptr(w_scale), _ptr(x), _ptr(y))
+
+
+def decode_linear_stack(linears, M: int, workspace, stream=None):
+    """Run independent linears (a list of Linear) that share M."""
+    arr = _linear_array(linears)
+    wp, wb = _ws(workspace)
+    _check(lib().decode_linear_stack(arr, len(linears), M, wp, wb, _stream(stream)),
+           "decode_linear_stack")
+
+
+def linear_run(linears, M: int, workspace, variant: int = VARIANT_AUTO, waves: int = 0,
+               stream=None):
+    """decode_linear_stack with a forced variant and/or persistent wave count."""
+    arr = _linear_array(linears)
+    plan = Plan(variant, waves)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_linear_run(arr, len(linears), M, ctypes.byref(plan), wp, wb,
+                                   _stream(stream)), "skinny_linear_run")
+
+
+def plan_query(linears, M: int) -> Plan:
+    arr = _linear_array(linears)
+    plan = Plan()
+    _check(lib().skinny_plan_query(arr, len(linears), M, ctypes.byref(plan)), "skinny_plan_query")
+    return plan

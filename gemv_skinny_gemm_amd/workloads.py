@@ -1,0 +1,85 @@
+"""Linear shapes of the Qwen2.5-72B decode step, as synthetic workloads.
+
+The model has 80 decoder layers and hidden size 8192 ("Developing a custom
+Qwen2.5 72B inference engine from scratch", section 1).  Each layer's linears
+(y = x . W^T, W stored [N][K]) at tensor-parallel degree 1 and at the per-GPU
+shard of degree 8 are:
+
+    TP=1: QKV 10240 x 8192, O 8192 x 8192, gate_up 59136 x 8192, down 8192 x 29568
+    TP=8: QKV  1280 x 8192, O 8192 x 1024, gate_up  7392 x 8192, down 8192 x  3696
+
+Every tensor gets its own Philox stream, so a tensor (or any row of it) can be
+regenerated anywhere: weights ~ N(0, 0.02) rounded to bf16 (FP8 weights are
+those values block-quantized), activations ~ N(0, 1) rounded to bf16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from gemv_skinny_gemm_amd.synth import stream_id
+
+BF16 = 0
+FP8_BS128 = 1
+W_SIGMA = 0.02
+X_SIGMA = 1.0
+LAYERS = 80
+
+TP1_SHAPES = (("qkv", 10240, 8192), ("o", 8192, 8192), ("gate_up", 59136, 8192),
+              ("down", 8192, 29568))
+TP8_SHAPES = (("qkv", 1280, 8192), ("o", 8192, 1024), ("gate_up", 7392, 8192),
+              ("down", 8192, 3696))
+
+
+@dataclass(frozen=True)
+class LinearSpec:
+    name: str
+    N: int
+    K: int
+    dtype: int
+    w_stream: int
+    x_stream: int
+
+    def weight_bytes(self) -> int:
+        return self.N * self.K * (2 if self.dtype == BF16 else 1)
+
+    def scale_bytes(self) -> int:
+        if self.dtype == BF16:
+            return 0
+        return ((self.N + 127) // 128) * ((self.K + 127) // 128) * 4
+
+    def algorithmic_bytes(self, M: int) -> int:
+        """W + block scales + x + y, each counted once."""
+        return self.weight_bytes() + self.scale_bytes() + 2 * M * self.K + 2 * M * self.N
+
+    def flops(self, M: int) -> int:
+        return 2 * M * self.N * self.K
+
+
+def _spec(tag, layer, name, N, K, dtype):
+    return LinearSpec(f"{tag}.L{layer}.{name}" if layer is not None else f"{tag}.{name}", N, K,
+                      dtype, stream_id("qwen2.5-72b", tag, layer, name, "w"),
+                      stream_id("qwen2.5-72b", tag, layer, name, "x"))
+
+
+def qkv_tp8_gemv() -> list[LinearSpec]:
+    """The TP=8 QKV shard as a single GEMV: W 1280 x 8192 bf16."""
+    return [_spec("gemv", None, "qkv", 1280, 8192, BF16)]
+
+
+def tp8_layer(dtype: int = BF16) -> list[LinearSpec]:
+    """One decoder layer's TP=8-shard linears."""
+    return [_spec("tp8", 0, n, N, K, dtype) for n, N, K in TP8_SHAPES]
+
+
+def tp1_stack(dtype: int = BF16, layers: int = LAYERS) -> list[LinearSpec]:
+    """The TP=1 decode linear stack: layers x (QKV, O, gate_up, down), distinct weights."""
+    tag = "tp1" if dtype == BF16 else "tp1fp8"
+    return [_spec(tag, l, n, N, K, dtype) for l in range(layers) for n, N, K in TP1_SHAPES]
+
+
+def algorithmic_bytes(specs, M: int) -> int:
+    return sum(s.algorithmic_bytes(M) for s in specs)
+
+
+def flops(specs, M: int) -> int:
+    return sum(s.flops(M) for s in specs)

@@ -1,0 +1,140 @@
+/*
+ * skinny_gemm.h - C ABI of the MI355X (gfx950) decode-phase linear layer.
+ *
+ * Operation (every entry point):  y[M x N] = x[M x K] . W^T,  M = 1..16 tokens.
+ *
+ *   The decode-phase linear layer is a tall-skinny product of a few token
+ *   rows with a weight matrix that is read from HBM once per step
+ *   ("Developing a custom Qwen2.5 72B inference engine from scratch - what is
+ *   the real bottleneck?", section 2 "The two-phase reality" and section 6.1
+ *   "Decode GEMV: already near the roofline").  A linear layer computes
+ *   y = x W with one row of x per token ("Multi-GPU Inference and Serving at
+ *   Scale", Example 2); here W is stored one row per output feature, so the
+ *   product is x . W^T.
+ *
+ *   FP8 weights are weight-only: activations stay 16-bit and each FP8 weight
+ *   is dequantized with the fp32 scale of the 128 x 128 block it lies in
+ *   ("9% faster GLM-5.3-Flash prefill with GPU-to-GPU IPC (and why TileLang
+ *   didn't help)", section "TileLang: twice as fast, and no faster"; the
+ *   Qwen2.5 72B engine report, section 6.2).
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   x        [M][K]                    bf16
+ *   W        [N][K]                    bf16, or OCP E4M3FN bytes (FP8)
+ *   w_scale  [ceil(N/128)][ceil(K/128)] fp32; weight (n, k) uses
+ *                                       w_scale[n/128][k/128] (FP8 only)
+ *   y        [M][N]                    bf16, round-to-nearest-even
+ *   Accumulation is fp32.  Results are within 2e-3 * sum_k |x w| + 1e-6 of
+ *   the exact product, and bitwise reproducible for a given device and plan.
+ *
+ * Requirements checked on the host before anything is enqueued:
+ *   1 <= M <= SKINNY_MAX_M, N >= 1, K >= 1; K % 8 == 0 (bf16) or
+ *   K % 16 == 0 (FP8); x, W, y and the workspace 16-byte aligned; w_scale
+ *   4-byte aligned; no NULL operand.  Violations return a status and enqueue
+ *   nothing.
+ *
+ * Ownership and concurrency:
+ *   The caller owns every buffer (x, W, w_scale, y, workspace) and keeps it
+ *   alive until the work on `stream` has finished.  The library allocates
+ *   nothing and keeps no pointer after a call returns.  Host arrays passed in
+ *   (the `linears` of a stack) are read during the call only.  y must not
+ *   overlap x, W, w_scale, the workspace or another call's y.  Calls enqueue
+ *   work on `stream` (a hipStream_t; NULL is the default stream) and return
+ *   without waiting for it; execution faults surface at the caller's next
+ *   synchronization.  Calls on different streams need separate workspaces.
+ *   Workspace contents are undefined after a call.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKINNY_ABI_VERSION 1
+#define SKINNY_MAX_M 16
+/* Linears one main-kernel launch carries; longer stacks use several launches. */
+#define SKINNY_MAX_LINEARS_PER_LAUNCH 32
+
+typedef enum skinny_status {
+  SKINNY_OK = 0,
+  SKINNY_ERR_INVALID_ARG = 1, /* NULL operand, M outside 1..16, N < 1, K < 1, count < 1,
+                                 unknown dtype or variant, overlapping output             */
+  SKINNY_ERR_UNSUPPORTED = 2, /* K not a multiple of 8 (bf16) / 16 (FP8), misaligned
+                                 pointer, shape too large, device is not gfx950            */
+  SKINNY_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace_bytes value */
+  SKINNY_ERR_HIP = 4          /* a HIP call failed (device query or kernel launch)          */
+} skinny_status;
+
+enum skinny_dtype { SKINNY_BF16 = 0, SKINNY_FP8_BS128 = 1 };
+
+/* Compute variant of the main kernel. AUTO picks per (dtype, M) from measurement. */
+enum skinny_variant { SKINNY_VARIANT_AUTO = 0, SKINNY_VARIANT_VECTOR = 1, SKINNY_VARIANT_MFMA = 2 };
+
+/* One linear of a stack.  All pointers are device pointers. */
+typedef struct skinny_linear {
+  int dtype;            /* SKINNY_BF16 or SKINNY_FP8_BS128                  */
+  int N;                /* output features: rows of W, columns of y         */
+  int K;                /* input features: columns of W and x               */
+  int reserved;         /* must be 0                                        */
+  const void* w;        /* W[N][K] bf16 or E4M3FN bytes                     */
+  const float* w_scale; /* FP8: [ceil(N/128)][ceil(K/128)] fp32; bf16: NULL */
+  const void* x;        /* x[M][K] bf16                                     */
+  void* y;              /* y[M][N] bf16                                     */
+} skinny_linear;
+
+/* Launch plan override, for tests and benchmarks.  Zero-initialised = automatic. */
+typedef struct skinny_plan {
+  int variant;          /* enum skinny_variant                               */
+  int waves;            /* persistent waves per main launch; 0 = automatic   */
+  int reserved[6];      /* must be 0                                         */
+} skinny_plan;
+
+/* Bytes of workspace a single linear needs (0 is never returned for valid
+ * arguments; returns 0 for invalid ones).  Pure host arithmetic, no HIP call.
+ * Defined by the split-K partial results of the second pass. */
+size_t skinny_workspace_bytes(int dtype, int M, int N, int K);
+
+/* Bytes of workspace decode_linear_stack needs for these linears at this M. */
+size_t skinny_stack_workspace_bytes(const skinny_linear* linears, int count, int M);
+
+/* y = x . W^T with bf16 W. */
+skinny_status skinny_gemm_bf16(const void* x, const void* w, void* y, int M, int N, int K,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* y = x . (e4m3(W) * block scale)^T, weight-only FP8 with 128 x 128 fp32 block scales. */
+skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const float* w_scale,
+                                    void* y, int M, int N, int K, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Runs `count` independent linears that share M, e.g. the QKV, O, gate_up
+ * and down projections of every decoder layer.  Each linear reads its own x
+ * and writes its own y; no y may overlap any x, W, w_scale or other y (checked).
+ * The linears are streamed by one persistent launch per
+ * SKINNY_MAX_LINEARS_PER_LAUNCH group and each group's split-K partial sums
+ * are combined by a second, deterministic pass. */
+skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* decode_linear_stack with an explicit plan (plan may be NULL = automatic). */
+skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
+                                const skinny_plan* plan, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* The plan the library would use on the current device (fills *out). */
+skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
+                                skinny_plan* out);
+
+/* Static text for a status code; never NULL. */
+const char* skinny_status_string(int status);
+
+/* SKINNY_ABI_VERSION of the loaded library. */
+int skinny_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

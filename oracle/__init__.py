@@ -130,17 +130,33 @@ def linear_fp8_bs128(x: np.ndarray, q: np.ndarray, scale: np.ndarray,
     return y, a, t
 
 
-def bound(a: np.ndarray) -> np.ndarray:
-    """Per-output tolerance 2e-3 * A + 1e-6."""
-    return REL_TOL * a + ABS_TOL
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half a bf16 unit in the last place at |v|: the largest error of rounding
+    a real number of that magnitude to bf16 (8 significant bits)."""
+    _, e = np.frexp(np.abs(np.asarray(v, np.float64)))     # |v| = f 2^e, f in [0.5, 1)
+    return np.ldexp(1.0, e - 9)
 
 
-def check(y_gpu: np.ndarray, y_ref: np.ndarray, a: np.ndarray):
+def bound(a: np.ndarray, y_ref: np.ndarray | None = None) -> np.ndarray:
+    """Per-output tolerance 2e-3 * A + 1e-6.
+
+    With ``y_ref`` given, half a bf16 ulp of y_ref is added for the rounding of
+    the output to bf16.  The stated bound alone is tighter than that rounding
+    when an output has little cancellation (|y| > ~0.5 A, e.g. a handful of
+    same-sign terms); the benchmark workloads (thousands of random-sign terms)
+    are checked against the stated bound alone."""
+    b = REL_TOL * np.asarray(a, np.float64) + ABS_TOL
+    if y_ref is not None:
+        b = b + bf16_half_ulp(y_ref)
+    return b
+
+
+def check(y_gpu: np.ndarray, y_ref: np.ndarray, a: np.ndarray, bf16_rounding: bool = False):
     """Compare a GPU result (any float dtype, [M][N]) with the oracle.
 
     Returns (ok, worst ratio err/bound, index of the worst output)."""
     err = np.abs(np.asarray(y_gpu, np.float64) - y_ref)
-    ratio = err / bound(a)
+    ratio = err / bound(a, y_ref if bf16_rounding else None)
     if ratio.size == 0:
         return True, 0.0, None
     idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad arguments on the host before touching the GPU (no compute here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_skinny_gemm_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skinny_gemm.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+A = 0x100000          # aligned fake device addresses: never dereferenced by these tests
+B = 0x2000000
+C = 0x4000000
+WS = 0x8000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["skinny_workspace_bytes", "skinny_stack_workspace_bytes", "skinny_gemm_bf16",
+                 "skinny_gemm_fp8_bs128", "decode_linear_stack", "skinny_linear_run",
+                 "skinny_plan_query", "skinny_status_string", "skinny_abi_version"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sg.lib_path())
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert sg.abi_version() == sg.ABI_VERSION
+    assert sg.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert sg.status_string(s) and sg.status_string(s) != "unknown status"
+    assert sg.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes_is_host_arithmetic():
+    one = sg.workspace_bytes(sg.BF16, 1, 1280, 8192)
+    assert one > 0
+    assert sg.workspace_bytes(sg.BF16, 16, 1280, 8192) == 16 * one
+    assert sg.workspace_bytes(sg.FP8_BS128, 6, 7392, 8192) == 6 * one
+    assert sg.workspace_bytes(sg.BF16, 0, 1, 8) == 0
+    assert sg.workspace_bytes(sg.BF16, 17, 1, 8) == 0
+    assert sg.workspace_bytes(7, 1, 1, 8) == 0
+    lins = [sg.Linear(sg.BF16, 1280, 8192, 0, A, None, B, C)] * 3
+    assert sg.stack_workspace_bytes(lins, 4) == 4 * one
+
+
+def bf16_call(x=B, w=A, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
+    wsb = sg.workspace_bytes(sg.BF16, max(M, 1), 64, 64) if wsb is None else wsb
+    return sg.lib().skinny_gemm_bf16(x, w, y, M, N, K, ws, wsb, None)
+
+
+def fp8_call(x=B, w=A, s=0x300000, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
+    wsb = sg.workspace_bytes(sg.FP8_BS128, max(M, 1), 64, 64) if wsb is None else wsb
+    return sg.lib().skinny_gemm_fp8_bs128(x, w, s, y, M, N, K, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), INVALID), (dict(M=17), INVALID), (dict(N=0), INVALID), (dict(K=0), INVALID),
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(K=12), UNSUPPORTED), (dict(w=A + 2), UNSUPPORTED), (dict(x=B + 8), UNSUPPORTED),
+    (dict(y=C + 4), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=WS + 8), UNSUPPORTED),
+    (dict(y=B), INVALID),                       # y overlaps x
+    (dict(y=A + 64), INVALID),                  # y inside W
+    (dict(y=WS + 4096), INVALID),               # y inside the workspace
+])
+def test_bf16_rejects_bad_arguments(kw, status):
+    assert bf16_call(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(s=None), INVALID), (dict(K=24), UNSUPPORTED), (dict(s=0x300002), UNSUPPORTED),
+    (dict(M=17), INVALID), (dict(wsb=0), WORKSPACE),
+])
+def test_fp8_rejects_bad_arguments(kw, status):
+    assert fp8_call(**kw) == status
+
+
+def test_stack_rejects_bad_arguments():
+    L = sg.lib()
+    good = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)
+    arr = (sg.Linear * 2)(good, sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C))   # same y twice
+    wsb = sg.workspace_bytes(sg.BF16, 1, 64, 64)
+    assert L.decode_linear_stack(arr, 2, 1, WS, wsb, None) == INVALID
+    assert L.decode_linear_stack(arr, 0, 1, WS, wsb, None) == INVALID
+    assert L.decode_linear_stack(None, 1, 1, WS, wsb, None) == INVALID
+    bad_dtype = (sg.Linear * 1)(sg.Linear(5, 64, 64, 0, A, None, B, C))
+    assert L.decode_linear_stack(bad_dtype, 1, 1, WS, wsb, None) == INVALID
+    reserved = (sg.Linear * 1)(sg.Linear(sg.BF16, 64, 64, 1, A, None, B, C))
+    assert L.decode_linear_stack(reserved, 1, 1, WS, wsb, None) == INVALID
+    scale_on_bf16 = (sg.Linear * 1)(sg.Linear(sg.BF16, 64, 64, 0, A, 0x300000, B, C))
+    assert L.decode_linear_stack(scale_on_bf16, 1, 1, WS, wsb, None) == INVALID
+    plan = sg.Plan(9, 0)
+    one = (sg.Linear * 1)(good)
+    assert L.skinny_linear_run(one, 1, 1, ctypes.byref(plan), WS, wsb, None) == INVALID
+    plan = sg.Plan(sg.VARIANT_VECTOR, 0)
+    wsb16 = sg.workspace_bytes(sg.BF16, 16, 64, 64)
+    assert L.skinny_linear_run(one, 1, 16, ctypes.byref(plan), WS, wsb16, None) == UNSUPPORTED
+    plan = sg.Plan(0, -1)
+    assert L.skinny_linear_run(one, 1, 1, ctypes.byref(plan), WS, wsb, None) == INVALID

@@ -271,3 +271,19 @@ def test_threads_do_not_change_results():
 def test_empty_shapes():
     y, a, _ = oracle.linear_bf16(np.zeros((2, 0), np.uint16), np.zeros((3, 0), np.uint16))
     assert y.shape == (2, 3) and np.all(y == 0) and np.all(a == 0)
+
+
+def test_bf16_half_ulp_covers_exact_rounding():
+    # Every bf16 rounding of a random real lies within the half ulp the check allows.
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal(20000) * 2.0 ** rng.integers(-20, 20, 20000)
+    r = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    assert np.all(np.abs(r - v) <= oracle.bf16_half_ulp(v))
+    assert oracle.bf16_half_ulp(np.array([1.0]))[0] == 2.0 ** -8
+    assert oracle.bf16_half_ulp(np.array([0.75]))[0] == 2.0 ** -9
+    ok, _, _ = oracle.check(np.array([[0.0751953125]]), np.array([[0.07497585]]),
+                            np.array([[0.09527504]]))
+    assert not ok                                   # stated bound alone: too tight here
+    ok, _, _ = oracle.check(np.array([[0.0751953125]]), np.array([[0.07497585]]),
+                            np.array([[0.09527504]]), bf16_rounding=True)
+    assert ok

@@ -1,0 +1,219 @@
+"""GPU path vs the fp64 oracle: element by element on seeded inputs, both
+compute variants, forced wave counts (split-K), pins through the GPU, and the
+small full-size configurations."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_skinny_gemm_amd as sg
+import oracle
+from gemv_skinny_gemm_amd import synth
+from tests.gpu_util import (assert_matches_oracle, dev_bf16, dev_f32, dev_u8, host_codes,
+                            host_values, need_gpu, out, run_bf16, run_fp8, variants_for,
+                            workspace)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BF16_ONE = 0x3F80
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+# --- random inputs: several tiles, ragged tails, every M ------------------------
+
+SHAPES = [(1, 8), (17, 264), (100, 1000), (257, 3696), (1280, 8192)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 8, 16])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_bf16_random_vs_oracle(M, N, K):
+    x = synth.tensor_bf16(0, synth.stream_id("t-bf16", M, N, K, "x"), M, K, 1.0)
+    w = synth.tensor_bf16(0, synth.stream_id("t-bf16", N, K, "w"), N, K, 0.02)
+    y_ref, a, _ = oracle.linear_bf16(x, w)
+    for var in variants_for(M):
+        for waves in (0, 1, 7):
+            y = run_bf16(x, w, M, N, variant=var, waves=waves)
+            assert_matches_oracle(y, y_ref, a, f"bf16 M={M} N={N} K={K} var={var} waves={waves}",
+                                  strict=K >= 1000)
+
+
+FP8_SHAPES = [(1, 16), (130, 272), (300, 1024), (257, 3696)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 6, 8, 16])
+@pytest.mark.parametrize("N,K", FP8_SHAPES)
+def test_fp8_random_vs_oracle(M, N, K):
+    x = synth.tensor_bf16(0, synth.stream_id("t-fp8", M, N, K, "x"), M, K, 1.0)
+    q, s, _ = synth.fp8_weight_bs128(0, synth.stream_id("t-fp8", N, K, "w"), N, K)
+    y_ref, a, _ = oracle.linear_fp8_bs128(x, q, s)
+    for var in variants_for(M):
+        for waves in (0, 1, 5):
+            y = run_fp8(x, q, s, M, N, variant=var, waves=waves)
+            assert_matches_oracle(y, y_ref, a, f"fp8 M={M} N={N} K={K} var={var} waves={waves}",
+                                  strict=K >= 1000)
+
+
+# --- pins through the GPU: exact results --------------------------------------
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_identity_is_exact(M):
+    K = 256
+    x = synth.tensor_bf16(0, 7, M, K, 1.0)
+    w = np.zeros((K, K), np.uint16)
+    w[np.arange(K), np.arange(K)] = BF16_ONE
+    q = np.zeros((K, K), np.uint8)
+    q[np.arange(K), np.arange(K)] = 0x38
+    s = np.ones((2, 2), np.float32)
+    for var in variants_for(M):
+        assert np.array_equal(host_codes(run_bf16(x, w, M, K, variant=var)), x)
+        assert np.array_equal(host_codes(run_fp8(x, q, s, M, K, variant=var)), x)
+
+
+def test_permutation_is_exact():
+    K, N, M = 512, 300, 3
+    perm = np.random.default_rng(5).permutation(K)[:N]
+    x = synth.tensor_bf16(0, 8, M, K, 1.0)
+    w = np.zeros((N, K), np.uint16)
+    w[np.arange(N), perm] = BF16_ONE
+    for var in variants_for(M):
+        for waves in (0, 3):
+            assert np.array_equal(host_codes(run_bf16(x, w, M, N, variant=var, waves=waves)),
+                                  x[:, perm])
+
+
+def test_constant_closed_form():
+    K, N, M = 8192, 40, 2
+    x = np.full((M, K), 0x3F00, np.uint16)                   # 0.5
+    w = np.full((N, K), 0x3E00, np.uint16)                   # 0.125
+    q = np.full((N, K), 0x30, np.uint8)                      # 0.5 ...
+    s = np.full((1, K // 128), 0.25, np.float32)             # ... x 0.25 = 0.125
+    for var in variants_for(M):
+        for waves in (0, 1, 13):
+            assert np.all(host_values(run_bf16(x, w, M, N, variant=var, waves=waves)) == 512.0)
+            assert np.all(host_values(run_fp8(x, q, s, M, N, variant=var, waves=waves)) == 512.0)
+
+
+def _ex2():
+    d = json.load(open(os.path.join(GOLDEN, "p2_ex2_column_split.json")))
+    x = np.array(d["x"], np.float64)
+    w = np.array(d["w_kn"], np.float64).T
+    return d, x, w
+
+
+def codes_of(v):
+    return torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_of(v):
+    return torch.tensor(v, dtype=torch.float64).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_page_example_column_split():
+    d, x, w = _ex2()
+    # K = 4 is padded with zeros to the 16-element granularity of the kernels.
+    xp = np.zeros((2, 16)); xp[:, :4] = x
+    wp = np.zeros((6, 16)); wp[:, :4] = w
+    for var in variants_for(2):
+        assert host_values(run_bf16(codes_of(xp), codes_of(wp), 2, 6, variant=var)).tolist() \
+            == d["y_printed"]
+        assert host_values(run_fp8(codes_of(xp), e4m3_of(wp), np.ones((1, 1), np.float32), 2, 6,
+                                   variant=var)).tolist() == d["y_printed"]
+        y0 = run_bf16(codes_of(xp), codes_of(wp[:3]), 2, 3, variant=var)
+        assert host_values(y0).tolist() == d["device0_printed"]
+
+
+def test_page_example_split_k_partials_in_workspace():
+    """The page's MLP example split over K into two halves, as two waves of the
+    split-K pass: each wave's partial slot holds the printed partial and the
+    second pass writes the printed sum."""
+    d = json.load(open(os.path.join(GOLDEN, "p2_ex3_mlp_split.json")))
+    x = np.array(d["x"], np.float64)
+    a_m = np.array([[((8 * i + j) % 7) - 3 for j in range(8)] for i in range(4)], np.float64)
+    b_m = np.array([[((4 * i + j) % 5) - 2 for j in range(4)] for i in range(8)], np.float64)
+    h = np.maximum(x @ a_m, 0.0)                 # inputs of the second product (integers)
+    K = 8192                                     # 256 steps of 32 k: two waves of 128 steps
+    hp = np.zeros((2, K)); hp[:, 0:4] = h[:, 0:4]; hp[:, K // 2:K // 2 + 4] = h[:, 4:8]
+    wp = np.zeros((4, K)); wp[:, 0:4] = b_m[0:4].T; wp[:, K // 2:K // 2 + 4] = b_m[4:8].T
+    for var in variants_for(2):
+        ws = workspace(2)
+        ws.zero_()
+        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=2, ws=ws)
+        assert host_values(y).tolist() == d["sum_printed"]
+        slots = ws.view(torch.float32).cpu().numpy()
+        # Slot layout [slot][M][16 rows]: wave 0 writes slot 0, wave 1 slot 2.
+        p0 = slots[0:32].reshape(2, 16)[:, :4]
+        p1 = slots[64:96].reshape(2, 16)[:, :4]
+        assert p0.tolist() == d["partial0_printed"]
+        assert p1.tolist() == d["partial1_printed"]
+
+
+@pytest.mark.parametrize("M", [1, 6, 16])
+def test_linearity_power_of_two(M):
+    N, K = 300, 2048
+    x = synth.tensor_bf16(0, 31, M, K, 1.0)
+    w = synth.tensor_bf16(0, 32, N, K, 0.02)
+    x4 = codes_of(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy() * 4)
+    for var in variants_for(M):
+        y1 = host_values(run_bf16(x, w, M, N, variant=var))
+        y4 = host_values(run_bf16(x4, w, M, N, variant=var))
+        assert np.array_equal(y4, 4 * y1)
+
+
+# --- determinism and split agreement -----------------------------------------
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_bitwise_repeatable_and_splits_agree(M):
+    N, K = 1280, 8192
+    x = synth.tensor_bf16(0, 41, M, K, 1.0)
+    w = synth.tensor_bf16(0, 42, N, K, 0.02)
+    y_ref, a, _ = oracle.linear_bf16(x, w)
+    for var in variants_for(M):
+        first = host_codes(run_bf16(x, w, M, N, variant=var))
+        for _ in range(3):
+            assert np.array_equal(host_codes(run_bf16(x, w, M, N, variant=var)), first)
+        for waves in (1, 2, 80, 1000, 8192):
+            y = run_bf16(x, w, M, N, variant=var, waves=waves)
+            assert_matches_oracle(y, y_ref, a, f"waves={waves}")
+
+
+# --- configurations at their real sizes ----------------------------------------
+
+def test_qkv_tp8_gemv_seed0():
+    """y[1 x 1280] = x[1 x 8192] . W^T, W ~ N(0, 0.02), x ~ N(0, 1), seed 0."""
+    from gemv_skinny_gemm_amd import workloads
+    lin = workloads.qkv_tp8_gemv()[0]
+    x = synth.tensor_bf16(0, lin.x_stream, 1, lin.K, 1.0)
+    w = synth.tensor_bf16(0, lin.w_stream, lin.N, lin.K, 0.02)
+    y_ref, a, _ = oracle.linear_bf16(x, w)
+    xd, wd, yd = dev_bf16(x), dev_bf16(w), out(1, lin.N)
+    sg.skinny_gemm_bf16(xd, wd, yd, workspace(1))
+    torch.cuda.synchronize()
+    worst = assert_matches_oracle(yd, y_ref, a, "qkv gemv")
+    assert worst < 0.5          # margin: the error is the bf16 output rounding
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 6, 8, 16])
+def test_tp8_layer_stack(M):
+    """One decoder layer's TP=8-shard linears through decode_linear_stack."""
+    from gemv_skinny_gemm_amd import workloads
+    lins = workloads.tp8_layer()
+    host, dev, refs = [], [], []
+    for L in lins:
+        x = synth.tensor_bf16(0, L.x_stream, M, L.K, 1.0)
+        w = synth.tensor_bf16(0, L.w_stream, L.N, L.K, 0.02)
+        refs.append(oracle.linear_bf16(x, w))
+        xd, wd, yd = dev_bf16(x), dev_bf16(w), out(M, L.N)
+        dev.append((xd, wd, yd))
+    descs = [sg.make_linear(xd, wd, yd) for xd, wd, yd in dev]
+    ws = torch.empty(sg.stack_workspace_bytes(descs, M), dtype=torch.uint8, device="cuda")
+    for var in variants_for(M):
+        sg.linear_run(descs, M, ws, variant=var)
+        torch.cuda.synchronize()
+        for L, (xd, wd, yd), (y_ref, a, _) in zip(lins, dev, refs):
+            assert_matches_oracle(yd, y_ref, a, f"{L.name} M={M} var={var}")
