@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-phase linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: every linear of the
+workload streamed once by the C-ABI library (main pass + deterministic
+second pass), with inputs already resident in HBM.
+
+Default workload: the Qwen2.5-72B decode linear stack at tensor-parallel
+degree 1 and M = 1 token -- 80 layers x (QKV 10240x8192, O 8192x8192,
+gate_up 59136x8192, down 8192x29568), bf16, distinct seeded weights
+(140.4 GB), W ~ N(0, 0.02), x ~ N(0, 1).  Weights are made on the GPU by the
+seeded input generator.
+
+Printed: one JSON line with the contract fields, the dominant kernel's
+roofline (HBM bytes / average main-kernel duration from HIP events recorded
+around each launch on the library's stream) and the fp64 oracle timed on a
+bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "achieved HBM GB/s and % of 8 TB/s peak; µs per Qwen2.5-72B decode linear stack"
+
+WORKLOADS = {
+    "qwen2.5-72b-tp1-stack-bf16": "80 layers x (QKV 10240x8192, O 8192x8192, gate_up 59136x8192, "
+                                  "down 8192x29568), bf16 W",
+    "qwen2.5-72b-tp1-stack-fp8": "80 layers x TP=1 shapes, FP8-E4M3 W + 128x128 fp32 block scales",
+    "qwen2.5-72b-tp8-layer-bf16": "one layer's TP=8 shard: QKV 1280x8192, O 8192x1024, "
+                                  "gate_up 7392x8192, down 8192x3696, bf16 W",
+    "qwen2.5-72b-tp8-qkv-gemv-bf16": "QKV shard GEMV 1280x8192, bf16 W",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen2.5-72b-tp1-stack-bf16", choices=sorted(WORKLOADS))
+    p.add_argument("--m", type=int, default=1, help="tokens per step (1..16)")
+    p.add_argument("--variant", default="auto", choices=["auto", "vector", "mfma"])
+    p.add_argument("--waves", type=int, default=0, help="persistent waves (0 = automatic)")
+    p.add_argument("--rotate-bytes", type=float, default=2.5e9,
+                   help="small workloads cycle weight copies totalling at least this many bytes "
+                        "so every step reads HBM, not the 256 MB last-level cache")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=1024)
+    return p.parse_args()
+
+
+def make_workload(name):
+    from gemv_skinny_gemm_amd import workloads as wl
+    if name == "qwen2.5-72b-tp1-stack-bf16":
+        return wl.tp1_stack(wl.BF16)
+    if name == "qwen2.5-72b-tp1-stack-fp8":
+        return wl.tp1_stack(wl.FP8_BS128)
+    if name == "qwen2.5-72b-tp8-layer-bf16":
+        return wl.tp8_layer(wl.BF16)
+    if name == "qwen2.5-72b-tp8-qkv-gemv-bf16":
+        return wl.qkv_tp8_gemv()
+    raise ValueError(name)
+
+
+def materialise(specs, M, copies, seed=0):
+    """Device tensors for `copies` copies of the workload (copy 0 uses the
+    workload's streams; copy c > 0 the same shapes with streams offset by c)."""
+    import torch
+
+    import gemv_skinny_gemm_amd as sg
+    from gemv_skinny_gemm_amd import workloads as wl
+    from gemv_skinny_gemm_amd.synth import gpu as sgpu
+
+    max_fp8 = max((s.N * s.K for s in specs if s.dtype == wl.FP8_BS128), default=0)
+    scratch = torch.empty(max_fp8, dtype=torch.bfloat16, device="cuda") if max_fp8 else None
+    sets = []
+    keep = []
+    for c in range(copies):
+        descs = []
+        for s in specs:
+            ws_ = (s.w_stream + c * 0x9E3779B1) & 0xFFFFFFFF
+            x = sgpu.tensor_bf16(seed, s.x_stream, M, s.K, wl.X_SIGMA)
+            y = torch.zeros((M, s.N), dtype=torch.bfloat16, device="cuda")
+            if s.dtype == wl.BF16:
+                w = sgpu.tensor_bf16(seed, ws_, s.N, s.K, wl.W_SIGMA)
+                descs.append(sg.make_linear(x, w, y))
+                keep.append((x, w, y))
+            else:
+                q, sc = sgpu.fp8_weight_bs128(seed, ws_, s.N, s.K, wl.W_SIGMA, scratch=scratch)
+                descs.append(sg.make_linear(x, q, y, w_scale=sc))
+                keep.append((x, q, sc, y))
+        sets.append(descs)
+    torch.cuda.synchronize()
+    del scratch
+    return sets, keep
+
+
+def cpu_baseline(specs, M, rows, seed=0):
+    """The fp64 oracle on a bounded sample: the first `rows` rows of each linear
+    of the first layer, from the same seeded streams.  Returns the result
+    dict, the sampled reference outputs and the sample description."""
+    import numpy as np
+
+    import oracle
+    from gemv_skinny_gemm_amd import synth
+    from gemv_skinny_gemm_amd import workloads as wl
+
+    layer = specs[:4] if len(specs) >= 4 else specs
+    total_s, total_b, refs, threads = 0.0, 0, [], 0
+    for s in layer:
+        r = min(rows, s.N)
+        x = synth.tensor_bf16(seed, s.x_stream, M, s.K, wl.X_SIGMA)
+        if s.dtype == wl.BF16:
+            w = synth.tensor_bf16(seed, s.w_stream, r, s.K, wl.W_SIGMA)
+            t0 = time.perf_counter()
+            y, a, threads = oracle.linear_bf16(x, w)
+            total_s += time.perf_counter() - t0
+            total_b += r * s.K * 2
+        else:
+            bands = (r + 127) // 128
+            q, sc, _ = synth.fp8_weight_bs128(seed, s.w_stream, s.N, s.K, wl.W_SIGMA, 0, bands)
+            q, r = q[:r], min(r, q.shape[0])
+            t0 = time.perf_counter()
+            y, a, threads = oracle.linear_fp8_bs128(x, q, sc[:(r + 127) // 128])
+            total_s += time.perf_counter() - t0
+            total_b += r * s.K + sc.size * 4
+        total_b += 2 * M * s.K + 2 * M * r
+        refs.append((s, r, y, a))
+    desc = (f"first {rows} rows of each of the {len(layer)} linears of layer 0 "
+            f"({total_b / 1e6:.1f} MB of algorithmic bytes), compute only")
+    return total_s, total_b, threads, refs, desc
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the decode linear "
+                                   "stack is measured at one GPU's share; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if not 1 <= args.m <= 16:
+        sys.exit("--m must be in 1..16")
+
+    import numpy as np
+    import torch
+
+    import gemv_skinny_gemm_amd as sg
+    from gemv_skinny_gemm_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sg.lib()
+    M = args.m
+    specs = make_workload(args.workload)
+    step_bytes = wl.algorithmic_bytes(specs, M)
+    step_flops = wl.flops(specs, M)
+    copies = 1 if step_bytes >= args.rotate_bytes else int(np.ceil(args.rotate_bytes / step_bytes))
+    log(f"workload {args.workload}: {len(specs)} linears, M={M}, {step_bytes / 1e9:.3f} GB/step, "
+        f"{copies} rotating cop{'y' if copies == 1 else 'ies'}")
+    t0 = time.perf_counter()
+    sets, keep = materialise(specs, M, copies)
+    log(f"inputs made on the GPU in {time.perf_counter() - t0:.1f} s")
+
+    variant = {"auto": sg.VARIANT_AUTO, "vector": sg.VARIANT_VECTOR, "mfma": sg.VARIANT_MFMA}[args.variant]
+    ws = torch.empty(sg.stack_workspace_bytes(sets[0], M), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    plan = sg.plan_query(sets[0], M)
+    n_launch = sg.launch_count(sets[0])
+
+    def step(i):
+        sg.linear_run(sets[i % copies], M, ws, variant=variant, waves=args.waves)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps between two events on the library's stream.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"{ms_per_step * 1e3:.1f} us/step")
+
+    # Dominant kernel: events recorded by the library around every main launch.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch * args.steps)]
+    for e in evs:
+        e.record(stream)                     # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
+        sg.linear_run_timed(sets[(args.warmup + i) % copies], M, ws, handles, variant=variant,
+                            waves=args.waves)
+    torch.cuda.synchronize()
+    main_ms = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(n_launch * args.steps)]
+    main_avg_ms = float(np.mean(main_ms))
+    bytes_per_launch = step_bytes / n_launch
+    achieved = bytes_per_launch / (main_avg_ms * 1e-3) / 1e9
+    main_total_ms = float(np.sum(main_ms)) / args.steps
+
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if specs[0].dtype == wl.BF16 else "fp8e4m3 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded Philox4x32-10; W ~ N(0,0.02), x ~ N(0,1), bf16-rounded)",
+        "config": {
+            "workload": args.workload,
+            "description": WORKLOADS[args.workload],
+            "M": M,
+            "linears": len(specs),
+            "algorithmic_bytes_per_step": step_bytes,
+            "flops_per_step": step_flops,
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "weight_copies_rotated": copies,
+            "variant": {0: "auto", 1: "vector", 2: "mfma"}[variant],
+            "auto_plan": {"variant": {1: "vector", 2: "mfma"}.get(plan.variant, plan.variant),
+                          "waves": plan.waves},
+            "main_launches_per_step": n_launch,
+            "gpu": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "kernel": "skinny_main",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(main_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+            "main_us_per_step": round(main_total_ms * 1e3, 2),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        secs, sbytes, threads, refs, desc = cpu_baseline(specs, M, args.cpu_sample_rows)
+        cpu_gbps = sbytes / secs / 1e9
+        # The oracle's sample also spot-checks the GPU outputs of step copy 0.
+        step(0)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for (s, r, y_ref, a), d in zip(refs, sets[0][:len(refs)]):
+            y_gpu = next(t for t in keep if t[-1].data_ptr() == d.y)[-1]
+            yv = y_gpu[:, :r].float().cpu().double().numpy()
+            ok, wr, _ = oracle.check(yv, y_ref, a)
+            worst = max(worst, wr)
+            if not ok:
+                log(f"GPU output of {s.name} outside the bound (worst {wr:.3g})")
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbps, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": desc,
+            "us_per_step_extrapolated": round(step_bytes / (cpu_gbps * 1e9) * 1e6, 1),
+            "cpu": platform.processor() or platform.machine(),
+        }
+        result["config"]["sampled_outputs_worst_err_over_bound"] = round(worst, 4)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

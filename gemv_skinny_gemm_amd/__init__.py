@@ -15,7 +15,8 @@ __all__ = [
     "BF16", "FP8_BS128", "VARIANT_AUTO", "VARIANT_VECTOR", "VARIANT_MFMA", "MAX_M",
     "SkinnyError", "Linear", "Plan", "lib", "lib_path",
     "workspace_bytes", "stack_workspace_bytes", "skinny_gemm_bf16", "skinny_gemm_fp8_bs128",
-    "decode_linear_stack", "linear_run", "plan_query", "status_string", "abi_version",
+    "decode_linear_stack", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
+    "status_string", "abi_version",
 ]
 
 BF16 = 0
@@ -60,6 +61,41 @@ def lib_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
 
+def _bind(path: str):
+    """Load a built library and declare the C signatures of include/skinny_gemm.h."""
+    L = ctypes.CDLL(path)
+    sz, vp, i = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    lp = ctypes.POINTER(Linear)
+    L.skinny_workspace_bytes.restype = sz
+    L.skinny_workspace_bytes.argtypes = [i, i, i, i]
+    L.skinny_stack_workspace_bytes.restype = sz
+    L.skinny_stack_workspace_bytes.argtypes = [lp, i, i]
+    L.skinny_gemm_bf16.restype = i
+    L.skinny_gemm_bf16.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+    L.skinny_gemm_fp8_bs128.restype = i
+    L.skinny_gemm_fp8_bs128.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    L.decode_linear_stack.restype = i
+    L.decode_linear_stack.argtypes = [lp, i, i, vp, sz, vp]
+    L.skinny_linear_run.restype = i
+    L.skinny_linear_run.argtypes = [lp, i, i, ctypes.POINTER(Plan), vp, sz, vp]
+    L.skinny_launch_count.restype = i
+    L.skinny_launch_count.argtypes = [lp, i]
+    L.skinny_linear_run_timed.restype = i
+    L.skinny_linear_run_timed.argtypes = [lp, i, i, ctypes.POINTER(Plan),
+                                          ctypes.POINTER(ctypes.c_void_p), i, vp, sz, vp]
+    L.skinny_band_rows.restype = i
+    L.skinny_band_rows.argtypes = [i, i, i]
+    L.skinny_plan_query.restype = i
+    L.skinny_plan_query.argtypes = [lp, i, i, ctypes.POINTER(Plan)]
+    L.skinny_status_string.restype = ctypes.c_char_p
+    L.skinny_status_string.argtypes = [i]
+    L.skinny_abi_version.restype = i
+    L.skinny_abi_version.argtypes = []
+    if L.skinny_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path}: ABI version {L.skinny_abi_version()} != {ABI_VERSION}")
+    return L
+
+
 def lib():
     """The loaded C library.  Raises if it is not built: there is no fallback."""
     global _lib
@@ -68,30 +104,7 @@ def lib():
         if not os.path.exists(path):
             raise ImportError(f"{path} is not built; run __graft_entry__.build() or "
                               "python -m gemv_skinny_gemm_amd._build")
-        L = ctypes.CDLL(path)
-        sz, vp, i = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
-        L.skinny_workspace_bytes.restype = sz
-        L.skinny_workspace_bytes.argtypes = [i, i, i, i]
-        L.skinny_stack_workspace_bytes.restype = sz
-        L.skinny_stack_workspace_bytes.argtypes = [ctypes.POINTER(Linear), i, i]
-        L.skinny_gemm_bf16.restype = i
-        L.skinny_gemm_bf16.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
-        L.skinny_gemm_fp8_bs128.restype = i
-        L.skinny_gemm_fp8_bs128.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
-        L.decode_linear_stack.restype = i
-        L.decode_linear_stack.argtypes = [ctypes.POINTER(Linear), i, i, vp, sz, vp]
-        L.skinny_linear_run.restype = i
-        L.skinny_linear_run.argtypes = [ctypes.POINTER(Linear), i, i, ctypes.POINTER(Plan),
-                                        vp, sz, vp]
-        L.skinny_plan_query.restype = i
-        L.skinny_plan_query.argtypes = [ctypes.POINTER(Linear), i, i, ctypes.POINTER(Plan)]
-        L.skinny_status_string.restype = ctypes.c_char_p
-        L.skinny_status_string.argtypes = [i]
-        L.skinny_abi_version.restype = i
-        L.skinny_abi_version.argtypes = []
-        if L.skinny_abi_version() != ABI_VERSION:
-            raise ImportError(f"{path}: ABI version {L.skinny_abi_version()} != {ABI_VERSION}")
-        _lib = L
+        _lib = _bind(path)
     return _lib
 
 
@@ -203,6 +216,28 @@ def linear_run(linears, M: int, workspace, variant: int = VARIANT_AUTO, waves: i
     wp, wb = _ws(workspace)
     _check(lib().skinny_linear_run(arr, len(linears), M, ctypes.byref(plan), wp, wb,
                                    _stream(stream)), "skinny_linear_run")
+
+
+def band_rows(dtype: int, variant: int, M: int) -> int:
+    """Rows per band of the main kernel: the workspace slot layout is [slot][M][band_rows]."""
+    return lib().skinny_band_rows(dtype, variant, M)
+
+
+def launch_count(linears) -> int:
+    arr = _linear_array(linears)
+    return lib().skinny_launch_count(arr, len(linears))
+
+
+def linear_run_timed(linears, M: int, workspace, events, variant: int = VARIANT_AUTO,
+                     waves: int = 0, stream=None):
+    """linear_run recording events[2g] / events[2g+1] (hipEvent_t addresses) around
+    main-kernel launch g."""
+    arr = _linear_array(linears)
+    plan = Plan(variant, waves)
+    ev = (ctypes.c_void_p * len(events))(*events)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_linear_run_timed(arr, len(linears), M, ctypes.byref(plan), ev, len(events),
+                                         wp, wb, _stream(stream)), "skinny_linear_run_timed")
 
 
 def plan_query(linears, M: int) -> Plan:

@@ -1,6 +1,8 @@
 """Builds the gfx950 shared libraries in-tree with hipcc.
 
-libskinny_gemm.so   the C-ABI library (kernels + host entry points)
+libskinny_gemm.so          the C-ABI library (kernels + host entry points)
+synth/libskinny_synth.so   the GPU twin of the seeded input generator (test and
+                           benchmark data only; shares no code with the library)
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
           "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}"]
 
 LIBS = {
-    "libskinny_gemm.so": ["skinny_gemm.hip"],
+    "libskinny_gemm.so": [os.path.join(CSRC, "skinny_gemm.hip")],
+    os.path.join("synth", "libskinny_synth.so"): [os.path.join(PKG, "synth", "synth_gpu.hip")],
 }
 
 
@@ -30,7 +33,7 @@ def lib_path(name: str) -> str:
 
 
 def build_lib(name: str, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in LIBS[name]]
+    srcs = LIBS[name]
     out = lib_path(name)
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *COMMON, *srcs, "-o", tmp]

@@ -16,16 +16,18 @@
 //
 // Work decomposition:
 //   tile  = 16 consecutive rows of one linear's W
+//   band  = T consecutive tiles (16 T rows), T in {1, 2, 4}; one wave streams
+//           a band so that each activation chunk it loads serves T weight loads
 //   chunk = 16 bytes of a W row (8 bf16 or 16 e4m3 weights)
-//   step  = one 16-byte load per lane: 16 rows x 4 consecutive chunks, lane
-//           l reads row (l % 16), chunk 4*j + (l / 16).  This is exactly the
-//           B-operand layout of v_mfma_f32_16x16x32_bf16, and the vector path
-//           uses it too.
-//   Steps are numbered globally (linear, tile, step-in-tile); wave w of G
-//   streams steps [w*T/G, (w+1)*T/G).  A tile whose steps a single wave
-//   covers is written straight to y.  A tile cut by a wave boundary has each
+//   step  = one k-step of a band: per tile, 16 rows x 4 consecutive chunks;
+//           lane l reads row (l % 16), chunk 4*j + (l / 16) of every tile.
+//           This is exactly the B-operand layout of v_mfma_f32_16x16x32_bf16,
+//           and the vector path uses it too.
+//   Steps are numbered globally (linear, band, step-in-band); wave w of G
+//   streams steps [w*S/G, (w+1)*S/G).  A band whose steps a single wave
+//   covers is written straight to y.  A band cut by a wave boundary has each
 //   contributing wave write fp32 partial sums to a fixed workspace slot
-//   (slot 2w for the wave's first tile, 2w+1 for its last), and a second
+//   (slot 2w for the wave's first band, 2w+1 for its last), and a second
 //   pass adds the slots in wave order: deterministic, no atomics.
 #include <hip/hip_runtime.h>
 
@@ -44,6 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 16;
+constexpr int kMaxBandTiles = 4;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kMaxWaves = 8192;         // 256 CUs x 32 resident waves
@@ -58,7 +61,7 @@ struct LinDesc {
   int N;
   int K;
   int cpr;               // 16-byte chunks per W row
-  int spt;               // steps per tile = ceil(cpr / 4)
+  int spt;               // steps per band = ceil(cpr / 4)
   int kblocks;           // ceil(K / 128)
   int pad;
   long long step_base;   // global index of this linear's first step
@@ -68,14 +71,14 @@ struct LaunchArgs {
   int nlin;
   int M;
   int G;                 // waves of the main launch
-  int pad;
-  long long T;           // total steps of the launch
-  float* slots;          // [2 G][M][16] fp32 partial sums
+  int band_rows;         // 16 T
+  long long S;           // total steps of the launch
+  float* slots;          // [2 G][M][band_rows] fp32 partial sums
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
 
-__device__ __forceinline__ long long wave_start(long long w, long long T, long long G) {
-  return w * T / G;
+__device__ __forceinline__ long long wave_start(long long w, long long S, long long G) {
+  return w * S / G;
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) {
@@ -108,211 +111,266 @@ __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 q, u32x4& b0, u32x4& b1) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// ---------------------------------------------------------------------------
-// Steps [j0, j1) of one tile.  Per lane: row r = lane % 16 of the tile and
-// chunk group g = lane / 16; step j reads chunk 4 j + g of that row.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
-// Vector path: each lane keeps MT running sums (one per token) for its row;
-// the four lanes of a row are added at the end.
-template <int DT, int MT, int U>
-__device__ __forceinline__ void tile_vector(const LinDesc& L, int tile, int j0, int j1,
-                                            float (&acc)[MT], int lane) {
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int row = tile * kTileRows + r;
-  const bool rowok = row < L.N;
-  const u32x4* wrow = L.w + (size_t)(rowok ? row : 0) * (size_t)L.cpr;
-  const int xcpr = L.K >> 3;                       // x chunks per token row
-  const float* srow = (DT == 1) ? L.scale + (size_t)(tile >> 3) * L.kblocks : nullptr;
+// ---------------------------------------------------------------------------
+// Steps [j0, j1) of one band.  Per lane: row r = lane % 16 of each tile and
+// chunk group g = lane / 16; step j reads chunk 4 j + g of those rows.  A
+// batch of U steps is loaded (W for all T tiles, x once) before it is used;
+// with PIPE the next batch's loads are issued before the current batch is
+// consumed.  XC = 16-byte x chunks per W chunk (1 for bf16, 2 for e4m3).
+
+template <int DT, int M, int T, int U>
+struct Batch {
+  static constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;
+  u32x4 w[U][T];
+  u32x4 x[U][M][XC];
+};
+
+template <int DT, int XM, int T, int U>
+__device__ __forceinline__ void load_batch(Batch<DT, XM, T, U>& b, const LinDesc& L,
+                                           const u32x4* const (&wrow)[T], const bool (&rowok)[T],
+                                           const u32x4* const (&xrow)[XM], const bool (&tokok)[XM],
+                                           int j, int j1, int g) {
+  constexpr int XC = Batch<DT, XM, T, U>::XC;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-  for (int j = j0; j < j1; j += U) {
-    u32x4 wv[U];
+  for (int u = 0; u < U; ++u) {
+    const int c = (j + u) * 4 + g;
+    const bool ok = (j + u < j1) && (c < L.cpr);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (j + u) * 4 + g;
-      const bool ok = rowok && (j + u < j1) && (c < L.cpr);
-      wv[u] = ok ? __builtin_nontemporal_load(wrow + c) : zero4();
-    }
+    for (int t = 0; t < T; ++t) b.w[u][t] = (ok && rowok[t]) ? wrow[t][c] : zero4();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (j + u) * 4 + g;
-      const bool ok = (j + u < j1) && (c < L.cpr);
-      if (DT == 0) {
+    for (int m = 0; m < XM; ++m)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const u32x4 xv = ok ? L.x[(size_t)m * xcpr + c] : zero4();
-          acc[m] = dot8(xv, wv[u], acc[m]);
-        }
-      } else {
-        u32x4 b0, b1;
-        e4m3x16_to_bf16(wv[u], b0, b1);
-        const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const u32x4 x0 = ok ? L.x[(size_t)m * xcpr + 2 * c] : zero4();
-          const u32x4 x1 = ok ? L.x[(size_t)m * xcpr + 2 * c + 1] : zero4();
-          const float p = dot8(x1, b1, dot8(x0, b0, 0.0f));
-          acc[m] = __builtin_fmaf(s, p, acc[m]);
-        }
-      }
-    }
-  }
-  // Add the four lanes that share a row (lanes r, r+16, r+32, r+48), fixed order.
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    acc[m] += __shfl_xor(acc[m], 16);
-    acc[m] += __shfl_xor(acc[m], 32);
+      for (int h = 0; h < XC; ++h) b.x[u][m][h] = (ok && tokok[m]) ? xrow[m][XC * c + h] : zero4();
   }
 }
 
-// MFMA path: D[m][n] += x[m][k] W[n][k] over 32 k per instruction.  A is the
-// token tile (rows m >= M are zero), B the weight tile.  Lane l ends holding
-// D[4 (l / 16) + i][l % 16] for i = 0..3.
-template <int DT, int U>
-__device__ __forceinline__ f32x4 tile_mfma(const LinDesc& L, int M, int tile, int j0, int j1,
-                                           int lane) {
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int row = tile * kTileRows + r;
-  const bool rowok = row < L.N;
-  const u32x4* wrow = L.w + (size_t)(rowok ? row : 0) * (size_t)L.cpr;
-  const int xcpr = L.K >> 3;
-  const bool tokok = r < M;                       // A-operand row m = r
-  const u32x4* xrow = L.x + (size_t)(tokok ? r : 0) * xcpr;
-  const float* srow = (DT == 1) ? L.scale + (size_t)(tile >> 3) * L.kblocks : nullptr;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = j0; j < j1; j += U) {
-    u32x4 wv[U];
+// Vector path: lane keeps T x MT running sums (tile, token) for its row of
+// each tile; the four lanes of a row are added at the end.
+template <int DT, int MT, int T, int U>
+__device__ __forceinline__ void compute_vector(const Batch<DT, MT, T, U>& b, float (&acc)[T][MT],
+                                               const float* srow, int j, int j1) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (j + u) * 4 + g;
-      const bool ok = rowok && (j + u < j1) && (c < L.cpr);
-      wv[u] = ok ? __builtin_nontemporal_load(wrow + c) : zero4();
-    }
+  for (int u = 0; u < U; ++u) {
+    if (DT == SKINNY_BF16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (j + u) * 4 + g;
-      const bool ok = tokok && (j + u < j1) && (c < L.cpr);
-      if (DT == 0) {
-        const u32x4 xv = ok ? xrow[c] : zero4();
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                      __builtin_bit_cast(bf16x8, wv[u]), acc,
-                                                      0, 0, 0);
-      } else {
-        const u32x4 x0 = ok ? xrow[2 * c] : zero4();
-        const u32x4 x1 = ok ? xrow[2 * c + 1] : zero4();
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[t][m] = dot8(b.x[u][m][0], b.w[u][t], acc[t][m]);
+    } else {
+      const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
         u32x4 b0, b1;
-        e4m3x16_to_bf16(wv[u], b0, b1);
-        f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x0),
-                                                    __builtin_bit_cast(bf16x8, b0), t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x1),
-                                                    __builtin_bit_cast(bf16x8, b1), t, 0, 0, 0);
-        const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
-        acc.x = __builtin_fmaf(s, t.x, acc.x);
-        acc.y = __builtin_fmaf(s, t.y, acc.y);
-        acc.z = __builtin_fmaf(s, t.z, acc.z);
-        acc.w = __builtin_fmaf(s, t.w, acc.w);
+        e4m3x16_to_bf16(b.w[u][t], b0, b1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float p = dot8(b.x[u][m][1], b1, dot8(b.x[u][m][0], b0, 0.0f));
+          acc[t][m] = __builtin_fmaf(s, p, acc[t][m]);
+        }
       }
     }
   }
-  return acc;
+}
+
+// MFMA path: D[m][n] += x[m][k] W[n][k] over 32 k per instruction; A is the
+// token tile (lane l supplies token l % 16, zero for tokens >= M), B a weight
+// tile.  Lane l ends holding D[4 (l / 16) + i][l % 16], i = 0..3, per tile.
+template <int DT, int T, int U>
+__device__ __forceinline__ void compute_mfma(const Batch<DT, 1, T, U>& b, f32x4 (&acc)[T],
+                                             const float* srow, int j, int j1) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (DT == SKINNY_BF16) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(b.x[u][0][0], b.w[u][t], acc[t]);
+    } else {
+      const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        u32x4 b0, b1;
+        e4m3x16_to_bf16(b.w[u][t], b0, b1);
+        f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+        p = mfma_bf16(b.x[u][0][0], b0, p);
+        p = mfma_bf16(b.x[u][0][1], b1, p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(s, p[i], acc[t][i]);
+      }
+    }
+  }
+}
+
+// One band's steps [j0, j1).  VAR = vector: acc is float[T][MT]; MFMA: f32x4[T].
+template <int DT, int VAR, int MT, int T, int U, bool PIPE, typename Acc>
+__device__ __forceinline__ void run_band(const LinDesc& L, int M, int band, int j0, int j1,
+                                         Acc& acc, int lane) {
+  constexpr int XM = VAR == SKINNY_VARIANT_VECTOR ? MT : 1;   // x rows a lane loads
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int xcpr = L.K >> 3;                                   // x chunks per token row
+  const u32x4* wrow[T];
+  bool rowok[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int row = band * (kTileRows * T) + t * kTileRows + r;
+    rowok[t] = row < L.N;
+    wrow[t] = L.w + (size_t)(rowok[t] ? row : 0) * (size_t)L.cpr;
+  }
+  const u32x4* xrow[XM];
+  bool tokok[XM];
+#pragma unroll
+  for (int m = 0; m < XM; ++m) {
+    const int tok = (VAR == SKINNY_VARIANT_VECTOR) ? m : r;    // MFMA: A row = lane % 16
+    tokok[m] = tok < M;
+    xrow[m] = L.x + (size_t)(tokok[m] ? tok : 0) * xcpr;
+  }
+  // All rows of a band lie in one 128-row scale block (16 T divides 128).
+  const float* srow = (DT == SKINNY_FP8_BS128)
+                          ? L.scale + (size_t)((band * kTileRows * T) / kScaleBlock) * L.kblocks
+                          : nullptr;
+  auto compute = [&](const Batch<DT, XM, T, U>& bt, int j) {
+    if constexpr (VAR == SKINNY_VARIANT_VECTOR) compute_vector<DT, MT, T, U>(bt, acc, srow, j, j1);
+    else compute_mfma<DT, T, U>(bt, acc, srow, j, j1);
+  };
+  if constexpr (PIPE) {
+    Batch<DT, XM, T, U> b0, b1;
+    load_batch(b0, L, wrow, rowok, xrow, tokok, j0, j1, g);
+    for (int j = j0; j < j1; j += 2 * U) {
+      load_batch(b1, L, wrow, rowok, xrow, tokok, j + U, j1, g);
+      compute(b0, j);
+      load_batch(b0, L, wrow, rowok, xrow, tokok, j + 2 * U, j1, g);
+      compute(b1, j + U);
+    }
+  } else {
+    for (int j = j0; j < j1; j += U) {
+      Batch<DT, XM, T, U> b0;
+      load_batch(b0, L, wrow, rowok, xrow, tokok, j, j1, g);
+      compute(b0, j);
+    }
+  }
 }
 
 // Main pass: wave w streams its equal share of the launch's steps.
-// VAR 1 = vector (MT = M at compile time), VAR 2 = MFMA (MT unused).
-template <int DT, int VAR, int MT, int U>
+template <int DT, int VAR, int MT, int T, int U, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void skinny_main(const LaunchArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (w >= a.G) return;
-  const long long s0 = wave_start(w, a.T, a.G);
-  const long long s1 = wave_start(w + 1, a.T, a.G);
+  const long long s0 = wave_start(w, a.S, a.G);
+  const long long s1 = wave_start(w + 1, a.S, a.G);
   if (s0 >= s1) return;
+  const int M = (VAR == SKINNY_VARIANT_VECTOR) ? MT : a.M;
+  constexpr int kBandRows = kTileRows * T;
+  const int r = lane & 15;
+  const int g = lane >> 4;
   int l = 0;
-  while (l + 1 < a.nlin && a.lin[l + 1].step_base <= s0) ++l;
-  const int M = (VAR == 1) ? MT : a.M;
   long long s = s0;
   bool first = true;
   while (s < s1) {
     while (l + 1 < a.nlin && a.lin[l + 1].step_base <= s) ++l;
     const LinDesc& L = a.lin[l];
     const long long local = s - L.step_base;
-    const int tile = (int)(local / L.spt);
-    const int j0 = (int)(local - (long long)tile * L.spt);
-    const long long tile_end = L.step_base + (long long)(tile + 1) * L.spt;
-    const int j1 = (int)((s1 < tile_end ? s1 : tile_end) - (L.step_base + (long long)tile * L.spt));
+    const int band = (int)(local / L.spt);
+    const int j0 = (int)(local - (long long)band * L.spt);
+    const long long band_end = L.step_base + (long long)(band + 1) * L.spt;
+    const int j1 = (int)((s1 < band_end ? s1 : band_end) - (L.step_base + (long long)band * L.spt));
     const bool whole = (j0 == 0) && (j1 == L.spt);
-    float* slot = a.slots + (size_t)(2 * w + (first ? 0 : 1)) * M * kTileRows;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const int row = tile * kTileRows + r;
-    if (VAR == 1) {
-      float acc[MT > 0 ? MT : 1];
-      tile_vector<DT, (MT > 0 ? MT : 1), U>(L, tile, j0, j1, acc, lane);
+    float* slot = a.slots + (size_t)(2 * w + (first ? 0 : 1)) * M * kBandRows;
+    if constexpr (VAR == SKINNY_VARIANT_VECTOR) {
+      float acc[T][MT];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[t][m] = 0.0f;
+      run_band<DT, VAR, MT, T, U, PIPE>(L, M, band, j0, j1, acc, lane);
+      // Add the four lanes that share a row (r, r+16, r+32, r+48), fixed order.
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          acc[t][m] += __shfl_xor(acc[t][m], 16);
+          acc[t][m] += __shfl_xor(acc[t][m], 32);
+        }
       if (g == 0) {
 #pragma unroll
-        for (int m = 0; m < (MT > 0 ? MT : 1); ++m) {
-          if (whole) {
-            if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[m];
-          } else {
-            slot[m * kTileRows + r] = acc[m];
+        for (int t = 0; t < T; ++t) {
+          const int rr = t * kTileRows + r;
+          const int row = band * kBandRows + rr;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (whole) {
+              if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][m];
+            } else {
+              slot[m * kBandRows + rr] = acc[t][m];
+            }
           }
         }
       }
     } else {
-      const f32x4 acc = tile_mfma<DT, U>(L, M, tile, j0, j1, lane);
+      f32x4 acc[T];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < M) {
-          const float v = acc[i];
-          if (whole) {
-            if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)v;
-          } else {
-            slot[m * kTileRows + r] = v;
+      for (int t = 0; t < T; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      run_band<DT, VAR, 1, T, U, PIPE>(L, M, band, j0, j1, acc, lane);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int rr = t * kTileRows + r;
+        const int row = band * kBandRows + rr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          if (m < M) {
+            if (whole) {
+              if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][i];
+            } else {
+              slot[m * kBandRows + rr] = acc[t][i];
+            }
           }
         }
       }
     }
-    s = tile_end < s1 ? tile_end : s1;
+    s = band_end < s1 ? band_end : s1;
     first = false;
   }
 }
 
-// Second pass: block w handles the tile that contains wave w's first step if
-// that step lies strictly inside the tile and no earlier wave boundary does.
-// Thread t adds token m = t / 16, row r = t % 16 over the contributing waves
-// in increasing order and writes y.
+// Second pass: block w handles the band that contains wave w's first step if
+// that step lies strictly inside the band and no earlier wave boundary does.
+// Its threads add, for every (token, row) of the band, the contributing
+// waves' slots in increasing wave order and write y.
 __global__ __launch_bounds__(kBlockThreads) void skinny_combine(const LaunchArgs a) {
   const int w = blockIdx.x;
   if (w == 0 || w >= a.G) return;
-  const long long b = wave_start(w, a.T, a.G);
-  if (b >= a.T) return;
+  const long long b = wave_start(w, a.S, a.G);
+  if (b >= a.S) return;
   int l = 0;
   while (l + 1 < a.nlin && a.lin[l + 1].step_base <= b) ++l;
   const LinDesc& L = a.lin[l];
   const long long local = b - L.step_base;
-  const int tile = (int)(local / L.spt);
-  const long long tstart = L.step_base + (long long)tile * L.spt;
-  const long long tend = tstart + L.spt;
-  if (b == tstart) return;
-  if (wave_start(w - 1, a.T, a.G) > tstart) return;
-  const int m = threadIdx.x >> 4;
-  const int r = threadIdx.x & 15;
-  if (m >= a.M) return;
-  float sum = 0.0f;
-  for (int v = w - 1; v < a.G; ++v) {
-    const long long sv = wave_start(v, a.T, a.G);
-    if (sv >= tend) break;
-    const long long ev = wave_start(v + 1, a.T, a.G);
-    if (ev <= sv) continue;                       // empty wave
-    const int slot = 2 * v + (sv >= tstart ? 0 : 1);
-    sum += a.slots[((size_t)slot * a.M + m) * kTileRows + r];
+  const int band = (int)(local / L.spt);
+  const long long bstart = L.step_base + (long long)band * L.spt;
+  const long long bend = bstart + L.spt;
+  if (b == bstart) return;
+  if (wave_start(w - 1, a.S, a.G) > bstart) return;
+  const int R = a.band_rows;
+  for (int idx = threadIdx.x; idx < a.M * R; idx += blockDim.x) {
+    const int m = idx / R;
+    const int rr = idx - m * R;
+    float sum = 0.0f;
+    for (int v = w - 1; v < a.G; ++v) {
+      const long long sv = wave_start(v, a.S, a.G);
+      if (sv >= bend) break;
+      const long long ev = wave_start(v + 1, a.S, a.G);
+      if (ev <= sv) continue;                     // empty wave
+      const int slot = 2 * v + (sv >= bstart ? 0 : 1);
+      sum += a.slots[((size_t)slot * a.M + m) * R + rr];
+    }
+    const int row = band * R + rr;
+    if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum;
   }
-  const int row = tile * kTileRows + r;
-  if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -395,32 +453,56 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
 }
 
 size_t workspace_for(int M) {
-  return (size_t)kMaxWaves * kSlotsPerWave * (size_t)M * kTileRows * sizeof(float);
+  return (size_t)kMaxWaves * kSlotsPerWave * (size_t)M * kTileRows * kMaxBandTiles *
+         sizeof(float);
 }
 
+// Measured on MI355X (80-layer TP=1 shapes, M = 1..16, bf16 and FP8): the
+// MFMA path streams faster than the v_dot2 path at every M, because one MFMA
+// replaces four dot2 per chunk plus the cross-lane reduction and its A-operand
+// load serves all tokens.  The vector path stays available through the plan.
 int auto_variant(int dtype, int M) {
   (void)dtype;
-  return M <= 4 ? SKINNY_VARIANT_VECTOR : SKINNY_VARIANT_MFMA;
+  (void)M;
+  return SKINNY_VARIANT_MFMA;
 }
 
-// Loads in flight per lane per batch.  The vector path keeps M x-chunks per
-// step live, so its unroll shrinks as M grows to hold occupancy.
+// Shape of the main loop per (dtype, variant, M): T tiles per band (x reuse),
+// U steps per batch, PIPE = issue the next batch before using this one.
+// Register use grows with T*U (weights) and U*M (activations), and the
+// persistent grid needs enough waves resident to cover HBM latency.
+struct LoopShape {
+  int T, U;
+  bool pipe;
+};
+
 template <int DT, int VAR, int MT>
-constexpr int unroll_for() {
-  if (VAR == SKINNY_VARIANT_MFMA) return 8;
-  if (DT == SKINNY_BF16) return MT <= 1 ? 8 : MT <= 2 ? 4 : 2;
-  return MT <= 1 ? 4 : 2;
+constexpr LoopShape loop_shape() {
+  if (VAR == SKINNY_VARIANT_MFMA) return LoopShape{2, 8, false};
+  if (MT <= 1) return LoopShape{4, 2, true};
+  if (MT <= 2) return LoopShape{2, 2, true};
+  return LoopShape{1, 2, false};
 }
 
 typedef void (*main_fn)(LaunchArgs);
 
+struct KernelChoice {
+  main_fn fn = nullptr;
+  int T = 1;
+};
+
 template <int DT, int VAR, int MT>
-main_fn main_kernel() {
-  return skinny_main<DT, VAR, MT, unroll_for<DT, VAR, MT>()>;
+KernelChoice main_kernel() {
+  constexpr LoopShape ls = loop_shape<DT, VAR, MT>();
+  static_assert(ls.T >= 1 && ls.T <= kMaxBandTiles && (ls.T & (ls.T - 1)) == 0, "bad band");
+  KernelChoice k;
+  k.fn = skinny_main<DT, VAR, MT, ls.T, ls.U, ls.pipe>;
+  k.T = ls.T;
+  return k;
 }
 
 template <int DT>
-main_fn pick_main(int variant, int M) {
+KernelChoice pick_main(int variant, int M) {
   if (variant == SKINNY_VARIANT_MFMA) return main_kernel<DT, SKINNY_VARIANT_MFMA, 0>();
   switch (M) {
     case 1: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 1>();
@@ -431,25 +513,46 @@ main_fn pick_main(int variant, int M) {
     case 6: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 6>();
     case 7: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 7>();
     case 8: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 8>();
-    default: return nullptr;
+    default: return KernelChoice{};
   }
 }
 
-main_fn pick(int dtype, int variant, int M) {
+KernelChoice pick(int dtype, int variant, int M) {
   return dtype == SKINNY_BF16 ? pick_main<SKINNY_BF16>(variant, M)
                               : pick_main<SKINNY_FP8_BS128>(variant, M);
 }
 
 // Persistent grid size: every wave must be resident at once for the equal
 // shares to finish together, so take what the occupancy query allows for
-// this kernel, capped at kTargetWavesPerCU waves per CU.
+// this kernel, capped at kTargetWavesPerCU waves per CU.  The query result is
+// cached per (device, kernel).
 constexpr int kTargetWavesPerCU = 16;
+constexpr int kOccCache = 128;
+struct OccEntry {
+  int dev;
+  main_fn fn;
+  int blocks_per_cu;
+};
+OccEntry g_occ[kOccCache];
+int g_occ_n = 0;
+std::mutex g_occ_mu;
 
 skinny_status auto_waves(const DeviceInfo& d, main_fn fn, int* waves) {
-  int blocks_per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, (const void*)fn,
-                                                   kBlockThreads, 0) != hipSuccess)
-    return SKINNY_ERR_HIP;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
+  int blocks_per_cu = -1;
+  {
+    std::lock_guard<std::mutex> lock(g_occ_mu);
+    for (int i = 0; i < g_occ_n; ++i)
+      if (g_occ[i].dev == dev && g_occ[i].fn == fn) blocks_per_cu = g_occ[i].blocks_per_cu;
+  }
+  if (blocks_per_cu < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, (const void*)fn,
+                                                     kBlockThreads, 0) != hipSuccess)
+      return SKINNY_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_occ_mu);
+    if (g_occ_n < kOccCache) g_occ[g_occ_n++] = OccEntry{dev, fn, blocks_per_cu};
+  }
   int per_cu = blocks_per_cu * kWavesPerBlock;
   if (per_cu > kTargetWavesPerCU) per_cu = kTargetWavesPerCU;
   if (per_cu < kWavesPerBlock) per_cu = kWavesPerBlock;
@@ -462,14 +565,18 @@ skinny_status auto_waves(const DeviceInfo& d, main_fn fn, int* waves) {
 // Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
 // G = 0 sizes the persistent grid from occupancy.
 skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* lin, int count,
-                           int M, int variant, int G, float* slots, hipStream_t stream) {
+                           int M, int variant, int G, float* slots, hipStream_t stream,
+                           hipEvent_t ev_before, hipEvent_t ev_after) {
+  const int dtype = lin[0]->dtype;
+  const KernelChoice k = pick(dtype, variant, M);
+  if (!k.fn) return SKINNY_ERR_INVALID_ARG;
   LaunchArgs a;
   memset(&a, 0, sizeof a);
   a.nlin = count;
   a.M = M;
   a.slots = slots;
-  const int dtype = lin[0]->dtype;
-  long long T = 0;
+  a.band_rows = kTileRows * k.T;
+  long long S = 0;
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = *lin[i];
     LinDesc& d = a.lin[i];
@@ -482,23 +589,24 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     d.cpr = L.K / (dtype == SKINNY_BF16 ? 8 : 16);
     d.spt = (d.cpr + 3) / 4;
     d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
-    d.step_base = T;
-    const long long tiles = (L.N + kTileRows - 1) / kTileRows;
-    T += tiles * d.spt;
+    d.step_base = S;
+    const long long bands = (L.N + a.band_rows - 1) / a.band_rows;
+    S += bands * d.spt;
   }
-  a.T = T;
-  main_fn fn = pick(dtype, variant, M);
-  if (!fn) return SKINNY_ERR_INVALID_ARG;
+  a.S = S;
+  main_fn fn = k.fn;
   if (G == 0) {
     skinny_status st = auto_waves(dev, fn, &G);
     if (st != SKINNY_OK) return st;
   }
-  if (G > T) G = (int)T;
+  if (G > S) G = (int)S;
   if (G < 1) G = 1;
   a.G = G;
   const int blocks = (G + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (ev_before && hipEventRecord(ev_before, stream) != hipSuccess) return SKINNY_ERR_HIP;
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kBlockThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+  if (ev_after && hipEventRecord(ev_after, stream) != hipSuccess) return SKINNY_ERR_HIP;
   if (G > 1) {
     hipLaunchKernelGGL(skinny_combine, dim3(G), dim3(kBlockThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
@@ -506,8 +614,19 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   return SKINNY_OK;
 }
 
+int launch_count(const skinny_linear* lin, int count) {
+  int launches = 0;
+  for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
+    int n = 0;
+    for (int i = 0; i < count; ++i) n += lin[i].dtype == dt;
+    launches += (n + SKINNY_MAX_LINEARS_PER_LAUNCH - 1) / SKINNY_MAX_LINEARS_PER_LAUNCH;
+  }
+  return launches;
+}
+
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
-                  void* ws, size_t ws_bytes, void* stream) {
+                  void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr,
+                  int event_count = 0) {
   if (!lin || count < 1) return SKINNY_ERR_INVALID_ARG;
   if (M < 1 || M > SKINNY_MAX_M) return SKINNY_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
@@ -530,10 +649,13 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
   skinny_status st = check_outputs(lin, count, M, ws, ws_bytes);
   if (st != SKINNY_OK) return st;
+  if (events && event_count < 2 * launch_count(lin, count)) return SKINNY_ERR_INVALID_ARG;
   DeviceInfo d;
   st = device_info(&d);
   if (st != SKINNY_OK) return st;
   if (!d.gfx950) return SKINNY_ERR_UNSUPPORTED;
+  int launch = 0;
+  auto ev = [&](int k) { return events ? (hipEvent_t)events[2 * launch + k] : (hipEvent_t) nullptr; };
   // Group by dtype, in call order, SKINNY_MAX_LINEARS_PER_LAUNCH per launch.
   for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
     const int var = variant == SKINNY_VARIANT_AUTO ? auto_variant(dt, M) : variant;
@@ -543,14 +665,18 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
       if (lin[i].dtype != dt) continue;
       group[n++] = &lin[i];
       if (n == SKINNY_MAX_LINEARS_PER_LAUNCH) {
-        st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream);
+        st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream, ev(0),
+                          ev(1));
         if (st != SKINNY_OK) return st;
+        ++launch;
         n = 0;
       }
     }
     if (n > 0) {
-      st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream);
+      st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream, ev(0),
+                        ev(1));
       if (st != SKINNY_OK) return st;
+      ++launch;
     }
   }
   return SKINNY_OK;
@@ -613,6 +739,30 @@ skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
   return run(linears, count, M, plan, workspace, workspace_bytes, stream);
 }
 
+int skinny_band_rows(int dtype, int variant, int M) {
+  if (dtype != SKINNY_BF16 && dtype != SKINNY_FP8_BS128) return 0;
+  if (M < 1 || M > SKINNY_MAX_M) return 0;
+  if (variant < SKINNY_VARIANT_AUTO || variant > SKINNY_VARIANT_MFMA) return 0;
+  const int var = variant == SKINNY_VARIANT_AUTO ? auto_variant(dtype, M) : variant;
+  const KernelChoice k = pick(dtype, var, M);
+  return k.fn ? kTileRows * k.T : 0;
+}
+
+int skinny_launch_count(const skinny_linear* linears, int count) {
+  if (!linears || count < 1) return 0;
+  for (int i = 0; i < count; ++i)
+    if (linears[i].dtype != SKINNY_BF16 && linears[i].dtype != SKINNY_FP8_BS128) return 0;
+  return launch_count(linears, count);
+}
+
+skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, int M,
+                                      const skinny_plan* plan, void* const* events,
+                                      int event_count, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!events) return SKINNY_ERR_INVALID_ARG;
+  return run(linears, count, M, plan, workspace, workspace_bytes, stream, events, event_count);
+}
+
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out) {
   if (!linears || count < 1 || !out) return SKINNY_ERR_INVALID_ARG;
@@ -625,9 +775,9 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   if (st != SKINNY_OK) return st;
   memset(out, 0, sizeof *out);
   out->variant = auto_variant(linears[0].dtype, M);
-  main_fn fn = pick(linears[0].dtype, out->variant, M);
-  if (!fn) return SKINNY_ERR_INVALID_ARG;
-  return auto_waves(d, fn, &out->waves);
+  const KernelChoice k = pick(linears[0].dtype, out->variant, M);
+  if (!k.fn) return SKINNY_ERR_INVALID_ARG;
+  return auto_waves(d, k.fn, &out->waves);
 }
 
 const char* skinny_status_string(int status) {

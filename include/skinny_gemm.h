@@ -123,6 +123,26 @@ skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
                                 const skinny_plan* plan, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Number of main-kernel launches a call over these linears makes (one per
+ * dtype group of at most SKINNY_MAX_LINEARS_PER_LAUNCH linears); 0 if invalid. */
+int skinny_launch_count(const skinny_linear* linears, int count);
+
+/* skinny_linear_run that also records events around each main-kernel launch,
+ * for benchmarks: events[2 g] just before and events[2 g + 1] just after
+ * launch g, on `stream`.  `events` is a host array of hipEvent_t created by
+ * the caller; event_count must be >= 2 * skinny_launch_count(linears, count).
+ * The second (combine) pass of each launch is enqueued after events[2 g + 1]. */
+skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, int M,
+                                      const skinny_plan* plan, void* const* events,
+                                      int event_count, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Rows of W one wave streams together (16 x tiles per band) for this dtype,
+ * variant (AUTO resolved as the library would) and M; 0 if invalid.  The
+ * split-K workspace holds fp32 partial sums laid out [slot][M][band rows],
+ * slot 2w for wave w's first band and 2w+1 for its last. */
+int skinny_band_rows(int dtype, int variant, int M);
+
 /* The plan the library would use on the current device (fills *out). */
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);

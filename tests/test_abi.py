@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["skinny_workspace_bytes", "skinny_stack_workspace_bytes", "skinny_gemm_bf16",
                  "skinny_gemm_fp8_bs128", "decode_linear_stack", "skinny_linear_run",
-                 "skinny_plan_query", "skinny_status_string", "skinny_abi_version"]:
+                 "skinny_plan_query", "skinny_status_string", "skinny_abi_version",
+                 "skinny_launch_count", "skinny_linear_run_timed", "skinny_band_rows"]:
         assert want in names
 
 
@@ -113,3 +114,20 @@ def test_stack_rejects_bad_arguments():
     assert L.skinny_linear_run(one, 1, 16, ctypes.byref(plan), WS, wsb16, None) == UNSUPPORTED
     plan = sg.Plan(0, -1)
     assert L.skinny_linear_run(one, 1, 1, ctypes.byref(plan), WS, wsb, None) == INVALID
+
+
+def test_band_rows_and_launch_counts():
+    for dt in (sg.BF16, sg.FP8_BS128):
+        for M in (1, 2, 6, 16):
+            for var in (sg.VARIANT_AUTO, sg.VARIANT_MFMA):
+                assert sg.band_rows(dt, var, M) in (16, 32, 64)
+        assert sg.band_rows(dt, sg.VARIANT_VECTOR, 8) in (16, 32, 64)
+        assert sg.band_rows(dt, sg.VARIANT_VECTOR, 9) == 0
+    assert sg.band_rows(sg.BF16, 7, 1) == 0 and sg.band_rows(9, 0, 1) == 0
+    lin = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)
+    fp8 = sg.Linear(sg.FP8_BS128, 64, 64, 0, A, 0x300000, B, C)
+    assert sg.launch_count([lin] * 32) == 1
+    assert sg.launch_count([lin] * 33) == 2
+    assert sg.launch_count([lin] * 320) == 10
+    assert sg.launch_count([lin, fp8, lin]) == 2
+    assert sg.lib().skinny_launch_count(None, 1) == 0

@@ -146,9 +146,10 @@ def test_page_example_split_k_partials_in_workspace():
         y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=2, ws=ws)
         assert host_values(y).tolist() == d["sum_printed"]
         slots = ws.view(torch.float32).cpu().numpy()
-        # Slot layout [slot][M][16 rows]: wave 0 writes slot 0, wave 1 slot 2.
-        p0 = slots[0:32].reshape(2, 16)[:, :4]
-        p1 = slots[64:96].reshape(2, 16)[:, :4]
+        # Slot layout [slot][M][band rows]: wave 0 writes slot 0, wave 1 slot 2.
+        R = sg.band_rows(sg.BF16, var, 2)
+        p0 = slots[0:2 * R].reshape(2, R)[:, :4]
+        p1 = slots[4 * R:6 * R].reshape(2, R)[:, :4]
         assert p0.tolist() == d["partial0_printed"]
         assert p1.tolist() == d["partial1_printed"]
 
