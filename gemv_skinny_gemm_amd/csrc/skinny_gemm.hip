@@ -10,25 +10,38 @@
 //   splitting the long K dimension lets the whole chip stream weights ("9%
 //   faster GLM-5.3-Flash prefill with GPU-to-GPU IPC (and why TileLang didn't
 //   help)", section "TileLang: twice as fast, and no faster").  The page
-//   splits K into fixed slices per block; here every wave of a persistent
-//   grid takes an equal share of all (tile, k-step) work of all linears in the
+//   splits K into fixed slices per block; here every worker of a persistent
+//   grid takes an equal share of all (band, k-step) work of all linears in the
 //   launch, so one launch streams a whole stack with a single ramp and tail.
 //
-// Work decomposition:
-//   tile  = 16 consecutive rows of one linear's W
-//   band  = T consecutive tiles (16 T rows), T in {1, 2, 4}; one wave streams
-//           a band so that each activation chunk it loads serves T weight loads
-//   chunk = 16 bytes of a W row (8 bf16 or 16 e4m3 weights)
-//   step  = one k-step of a band: per tile, 16 rows x 4 consecutive chunks;
-//           lane l reads row (l % 16), chunk 4*j + (l / 16) of every tile.
-//           This is exactly the B-operand layout of v_mfma_f32_16x16x32_bf16,
-//           and the vector path uses it too.
-//   Steps are numbered globally (linear, band, step-in-band); wave w of G
-//   streams steps [w*S/G, (w+1)*S/G).  A band whose steps a single wave
-//   covers is written straight to y.  A band cut by a wave boundary has each
-//   contributing wave write fp32 partial sums to a fixed workspace slot
-//   (slot 2w for the wave's first band, 2w+1 for its last), and a second
-//   pass adds the slots in wave order: deterministic, no atomics.
+// Two main kernels share that decomposition and the second pass:
+//
+//   skinny_rows  (VECTOR variant, small M): a workgroup of 8 waves is the
+//     worker; wave i streams row 8g + i of row group g, lane l reading bytes
+//     [16 l, 16 l + 16) of each 1 KB segment of the row, so every wave reads
+//     its row front to back in 1 KB coalesced loads.  x (all K) sits in LDS,
+//     shared by the 8 waves, with each wave's FP8 scale row beside it.
+//     v_dot2_f32_bf16 accumulates in fp32; a 64-lane butterfly ends each row.
+//     Measured on MI355X, one contiguous stream per wave sustains ~6.3 TB/s,
+//     against ~5.8 TB/s for 16 interleaved rows per wave.  Units (row group,
+//     K-chunk) are dealt round robin rather than as contiguous shares.
+//
+//   skinny_mfma  (MFMA variant, any M): a wave is the worker and streams a
+//     band of T tiles of 16 rows; per k-step lane l reads 16 bytes of row
+//     (l % 16), chunk 4 j + (l / 16) of every tile - the B-operand layout of
+//     v_mfma_f32_16x16x32_bf16 - and one 16-byte x load (the A operand, token
+//     l % 16) serves the T MFMAs.  FP8 chunks are converted to bf16 in
+//     registers (exact) and each k-step's partial product is scaled by its
+//     block scale in fp32.
+//
+//   skinny_mfma numbers its k-steps (linear, band, step); wave w of G streams
+//   steps [w*S/G, (w+1)*S/G).  A band one wave covers entirely is written
+//   straight to y.  A band cut by a wave boundary has each contributing wave
+//   write fp32 partial sums to a fixed workspace slot (slot 2w for the wave's
+//   first band, 2w+1 for its last), and skinny_combine adds the slots in wave
+//   order.  skinny_rows cuts a small launch's row groups into fixed K-chunks,
+//   one slot per chunk, and skinny_rows_combine adds them in chunk order.
+//   Either way the second pass is deterministic and uses no atomics.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -47,11 +60,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 16;
 constexpr int kMaxBandTiles = 4;
+constexpr int kSegChunks = 64;          // 16-byte chunks per 1 KB row segment
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kMaxWaves = 8192;         // 256 CUs x 32 resident waves
-constexpr int kSlotsPerWave = 2;
+constexpr int kSlotsPerWorker = 2;
 constexpr int kScaleBlock = 128;
+constexpr int kMaxLds = 160 * 1024;     // LDS per workgroup on gfx950
+constexpr int kRowsMaxKBlocks = 256;    // skinny_rows FP8: K <= 32768
+// skinny_rows shape, measured on MI355X over the Qwen2.5-72B shapes: 8 waves
+// per workgroup share one copy of x, 8 segments per wave in flight, up to 32
+// waves per CU.
+constexpr int kRowsWavesPerBlock = 8;
+constexpr int kRowsUnroll = 8;
+constexpr int kTargetRowsWavesPerCU = 32;
 
 struct LinDesc {
   const u32x4* w;        // W rows as 16-byte chunks
@@ -61,23 +83,27 @@ struct LinDesc {
   int N;
   int K;
   int cpr;               // 16-byte chunks per W row
-  int spt;               // steps per band = ceil(cpr / 4)
+  int spt;               // steps per band
   int kblocks;           // ceil(K / 128)
-  int pad;
-  long long step_base;   // global index of this linear's first step
+  int chunks;            // skinny_rows: K-chunks per row group (1 = not split)
+  long long step_base;   // global index of this linear's first step (or unit)
+  long long slot_base;   // skinny_rows: first partial slot of a split linear
 };
 
 struct LaunchArgs {
   int nlin;
   int M;
-  int G;                 // waves of the main launch
-  int band_rows;         // 16 T
-  long long S;           // total steps of the launch
-  float* slots;          // [2 G][M][band_rows] fp32 partial sums
+  int G;                 // workers (waves for skinny_mfma, workgroups for skinny_rows)
+  int band_rows;         // rows per band: 16 T, or skinny_rows' waves per workgroup
+  long long S;           // total steps (skinny_mfma) or units (skinny_rows) of the launch
+  float* slots;          // fp32 partial sums: [2 G][M][band_rows] (skinny_mfma),
+                         // [unit][M][band_rows] (skinny_rows)
+  int x_lds_bytes;       // skinny_rows: bytes of LDS for x; scales follow
+  int pad;
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
 
-__device__ __forceinline__ long long wave_start(long long w, long long S, long long G) {
+__device__ __forceinline__ long long worker_start(long long w, long long S, long long G) {
   return w * S / G;
 }
 
@@ -116,26 +142,44 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Steps [j0, j1) of one band.  Per lane: row r = lane % 16 of each tile and
-// chunk group g = lane / 16; step j reads chunk 4 j + g of those rows.  A
-// batch of U steps is loaded (W for all T tiles, x once) before it is used;
-// with PIPE the next batch's loads are issued before the current batch is
-// consumed.  XC = 16-byte x chunks per W chunk (1 for bf16, 2 for e4m3).
-
-template <int DT, int M, int T, int U>
-struct Batch {
-  static constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;
-  u32x4 w[U][T];
-  u32x4 x[U][M][XC];
+// Locates the band of step s: linear index l (advanced in place), band index,
+// step within the band and the band's first step.
+struct BandPos {
+  int band;
+  int j;
+  long long begin;
 };
 
-template <int DT, int XM, int T, int U>
-__device__ __forceinline__ void load_batch(Batch<DT, XM, T, U>& b, const LinDesc& L,
-                                           const u32x4* const (&wrow)[T], const bool (&rowok)[T],
-                                           const u32x4* const (&xrow)[XM], const bool (&tokok)[XM],
-                                           int j, int j1, int g) {
-  constexpr int XC = Batch<DT, XM, T, U>::XC;
+__device__ __forceinline__ BandPos band_of(const LaunchArgs& a, int& l, long long s) {
+  while (l + 1 < a.nlin && a.lin[l + 1].step_base <= s) ++l;
+  const LinDesc& L = a.lin[l];
+  const long long local = s - L.step_base;
+  BandPos p;
+  p.band = (int)(local / L.spt);
+  p.j = (int)(local - (long long)p.band * L.spt);
+  p.begin = L.step_base + (long long)p.band * L.spt;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// skinny_mfma: steps [j0, j1) of one band.  Per lane: row r = lane % 16 of
+// each tile and chunk group g = lane / 16; step j reads chunk 4 j + g of
+// those rows.  A batch of U steps is loaded (W for all T tiles, the x chunk
+// once) before it is used; with PIPE the next batch's loads are issued before
+// the current batch is consumed.  XC = 16-byte x chunks per W chunk.
+
+template <int DT, int T, int U>
+struct MfmaBatch {
+  static constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;
+  u32x4 w[U][T];
+  u32x4 x[U][XC];
+};
+
+template <int DT, int T, int U>
+__device__ __forceinline__ void mfma_load(MfmaBatch<DT, T, U>& b, const LinDesc& L,
+                                          const u32x4* const (&wrow)[T], const bool (&rowok)[T],
+                                          const u32x4* xrow, bool tokok, int j, int j1, int g) {
+  constexpr int XC = MfmaBatch<DT, T, U>::XC;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = (j + u) * 4 + g;
@@ -143,60 +187,31 @@ __device__ __forceinline__ void load_batch(Batch<DT, XM, T, U>& b, const LinDesc
 #pragma unroll
     for (int t = 0; t < T; ++t) b.w[u][t] = (ok && rowok[t]) ? wrow[t][c] : zero4();
 #pragma unroll
-    for (int m = 0; m < XM; ++m)
-#pragma unroll
-      for (int h = 0; h < XC; ++h) b.x[u][m][h] = (ok && tokok[m]) ? xrow[m][XC * c + h] : zero4();
+    for (int h = 0; h < XC; ++h) b.x[u][h] = (ok && tokok) ? xrow[XC * c + h] : zero4();
   }
 }
 
-// Vector path: lane keeps T x MT running sums (tile, token) for its row of
-// each tile; the four lanes of a row are added at the end.
-template <int DT, int MT, int T, int U>
-__device__ __forceinline__ void compute_vector(const Batch<DT, MT, T, U>& b, float (&acc)[T][MT],
-                                               const float* srow, int j, int j1) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (DT == SKINNY_BF16) {
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[t][m] = dot8(b.x[u][m][0], b.w[u][t], acc[t][m]);
-    } else {
-      const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        u32x4 b0, b1;
-        e4m3x16_to_bf16(b.w[u][t], b0, b1);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const float p = dot8(b.x[u][m][1], b1, dot8(b.x[u][m][0], b0, 0.0f));
-          acc[t][m] = __builtin_fmaf(s, p, acc[t][m]);
-        }
-      }
-    }
-  }
-}
-
-// MFMA path: D[m][n] += x[m][k] W[n][k] over 32 k per instruction; A is the
-// token tile (lane l supplies token l % 16, zero for tokens >= M), B a weight
-// tile.  Lane l ends holding D[4 (l / 16) + i][l % 16], i = 0..3, per tile.
+// D[m][n] += x[m][k] W[n][k] over 32 k per instruction; A is the token tile
+// (lane l supplies token l % 16, zero for tokens >= M), B a weight tile.
+// Lane l ends holding D[4 (l / 16) + i][l % 16], i = 0..3, for each tile.
 template <int DT, int T, int U>
-__device__ __forceinline__ void compute_mfma(const Batch<DT, 1, T, U>& b, f32x4 (&acc)[T],
+__device__ __forceinline__ void mfma_compute(const MfmaBatch<DT, T, U>& b, f32x4 (&acc)[T],
                                              const float* srow, int j, int j1) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (DT == SKINNY_BF16) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(b.x[u][0][0], b.w[u][t], acc[t]);
+      for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(b.x[u][0], b.w[u][t], acc[t]);
     } else {
+      // Step j covers k in [64 j, 64 j + 64): one 128-wide scale block, j / 2.
       const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         u32x4 b0, b1;
         e4m3x16_to_bf16(b.w[u][t], b0, b1);
         f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-        p = mfma_bf16(b.x[u][0][0], b0, p);
-        p = mfma_bf16(b.x[u][0][1], b1, p);
+        p = mfma_bf16(b.x[u][0], b0, p);
+        p = mfma_bf16(b.x[u][1], b1, p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(s, p[i], acc[t][i]);
       }
@@ -204,66 +219,15 @@ __device__ __forceinline__ void compute_mfma(const Batch<DT, 1, T, U>& b, f32x4 
   }
 }
 
-// One band's steps [j0, j1).  VAR = vector: acc is float[T][MT]; MFMA: f32x4[T].
-template <int DT, int VAR, int MT, int T, int U, bool PIPE, typename Acc>
-__device__ __forceinline__ void run_band(const LinDesc& L, int M, int band, int j0, int j1,
-                                         Acc& acc, int lane) {
-  constexpr int XM = VAR == SKINNY_VARIANT_VECTOR ? MT : 1;   // x rows a lane loads
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int xcpr = L.K >> 3;                                   // x chunks per token row
-  const u32x4* wrow[T];
-  bool rowok[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int row = band * (kTileRows * T) + t * kTileRows + r;
-    rowok[t] = row < L.N;
-    wrow[t] = L.w + (size_t)(rowok[t] ? row : 0) * (size_t)L.cpr;
-  }
-  const u32x4* xrow[XM];
-  bool tokok[XM];
-#pragma unroll
-  for (int m = 0; m < XM; ++m) {
-    const int tok = (VAR == SKINNY_VARIANT_VECTOR) ? m : r;    // MFMA: A row = lane % 16
-    tokok[m] = tok < M;
-    xrow[m] = L.x + (size_t)(tokok[m] ? tok : 0) * xcpr;
-  }
-  // All rows of a band lie in one 128-row scale block (16 T divides 128).
-  const float* srow = (DT == SKINNY_FP8_BS128)
-                          ? L.scale + (size_t)((band * kTileRows * T) / kScaleBlock) * L.kblocks
-                          : nullptr;
-  auto compute = [&](const Batch<DT, XM, T, U>& bt, int j) {
-    if constexpr (VAR == SKINNY_VARIANT_VECTOR) compute_vector<DT, MT, T, U>(bt, acc, srow, j, j1);
-    else compute_mfma<DT, T, U>(bt, acc, srow, j, j1);
-  };
-  if constexpr (PIPE) {
-    Batch<DT, XM, T, U> b0, b1;
-    load_batch(b0, L, wrow, rowok, xrow, tokok, j0, j1, g);
-    for (int j = j0; j < j1; j += 2 * U) {
-      load_batch(b1, L, wrow, rowok, xrow, tokok, j + U, j1, g);
-      compute(b0, j);
-      load_batch(b0, L, wrow, rowok, xrow, tokok, j + 2 * U, j1, g);
-      compute(b1, j + U);
-    }
-  } else {
-    for (int j = j0; j < j1; j += U) {
-      Batch<DT, XM, T, U> b0;
-      load_batch(b0, L, wrow, rowok, xrow, tokok, j, j1, g);
-      compute(b0, j);
-    }
-  }
-}
-
-// Main pass: wave w streams its equal share of the launch's steps.
-template <int DT, int VAR, int MT, int T, int U, bool PIPE>
-__global__ __launch_bounds__(kBlockThreads) void skinny_main(const LaunchArgs a) {
+template <int DT, int T, int U, bool PIPE>
+__global__ __launch_bounds__(kBlockThreads) void skinny_mfma(const LaunchArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (w >= a.G) return;
-  const long long s0 = wave_start(w, a.S, a.G);
-  const long long s1 = wave_start(w + 1, a.S, a.G);
+  const long long s0 = worker_start(w, a.S, a.G);
+  const long long s1 = worker_start(w + 1, a.S, a.G);
   if (s0 >= s1) return;
-  const int M = (VAR == SKINNY_VARIANT_VECTOR) ? MT : a.M;
+  const int M = a.M;
   constexpr int kBandRows = kTileRows * T;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -271,63 +235,58 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_main(const LaunchArgs a)
   long long s = s0;
   bool first = true;
   while (s < s1) {
-    while (l + 1 < a.nlin && a.lin[l + 1].step_base <= s) ++l;
+    const BandPos p = band_of(a, l, s);
     const LinDesc& L = a.lin[l];
-    const long long local = s - L.step_base;
-    const int band = (int)(local / L.spt);
-    const int j0 = (int)(local - (long long)band * L.spt);
-    const long long band_end = L.step_base + (long long)(band + 1) * L.spt;
-    const int j1 = (int)((s1 < band_end ? s1 : band_end) - (L.step_base + (long long)band * L.spt));
+    const long long band_end = p.begin + L.spt;
+    const int j0 = p.j;
+    const int j1 = (int)((s1 < band_end ? s1 : band_end) - p.begin);
     const bool whole = (j0 == 0) && (j1 == L.spt);
-    float* slot = a.slots + (size_t)(2 * w + (first ? 0 : 1)) * M * kBandRows;
-    if constexpr (VAR == SKINNY_VARIANT_VECTOR) {
-      float acc[T][MT];
+    const u32x4* wrow[T];
+    bool rowok[T];
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t) {
+      const int row = p.band * kBandRows + t * kTileRows + r;
+      rowok[t] = row < L.N;
+      wrow[t] = L.w + (size_t)(rowok[t] ? row : 0) * (size_t)L.cpr;
+    }
+    const bool tokok = r < M;                              // A-operand row = lane % 16
+    const u32x4* xrow = L.x + (size_t)(tokok ? r : 0) * (size_t)(L.K >> 3);
+    // All rows of a band lie in one 128-row scale block (16 T divides 128).
+    const float* srow = (DT == SKINNY_FP8_BS128)
+                            ? L.scale + (size_t)((p.band * kBandRows) / kScaleBlock) * L.kblocks
+                            : nullptr;
+    f32x4 acc[T];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[t][m] = 0.0f;
-      run_band<DT, VAR, MT, T, U, PIPE>(L, M, band, j0, j1, acc, lane);
-      // Add the four lanes that share a row (r, r+16, r+32, r+48), fixed order.
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          acc[t][m] += __shfl_xor(acc[t][m], 16);
-          acc[t][m] += __shfl_xor(acc[t][m], 32);
-        }
-      if (g == 0) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const int rr = t * kTileRows + r;
-          const int row = band * kBandRows + rr;
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (whole) {
-              if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][m];
-            } else {
-              slot[m * kBandRows + rr] = acc[t][m];
-            }
-          }
-        }
+    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (PIPE) {
+      MfmaBatch<DT, T, U> b0, b1;
+      mfma_load(b0, L, wrow, rowok, xrow, tokok, j0, j1, g);
+      for (int j = j0; j < j1; j += 2 * U) {
+        mfma_load(b1, L, wrow, rowok, xrow, tokok, j + U, j1, g);
+        mfma_compute(b0, acc, srow, j, j1);
+        mfma_load(b0, L, wrow, rowok, xrow, tokok, j + 2 * U, j1, g);
+        mfma_compute(b1, acc, srow, j + U, j1);
       }
     } else {
-      f32x4 acc[T];
+      for (int j = j0; j < j1; j += U) {
+        MfmaBatch<DT, T, U> b0;
+        mfma_load(b0, L, wrow, rowok, xrow, tokok, j, j1, g);
+        mfma_compute(b0, acc, srow, j, j1);
+      }
+    }
+    float* slot = a.slots + (size_t)(2 * w + (first ? 0 : 1)) * M * kBandRows;
 #pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      run_band<DT, VAR, 1, T, U, PIPE>(L, M, band, j0, j1, acc, lane);
+    for (int t = 0; t < T; ++t) {
+      const int rr = t * kTileRows + r;
+      const int row = p.band * kBandRows + rr;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int rr = t * kTileRows + r;
-        const int row = band * kBandRows + rr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * g + i;
-          if (m < M) {
-            if (whole) {
-              if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][i];
-            } else {
-              slot[m * kBandRows + rr] = acc[t][i];
-            }
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < M) {
+          if (whole) {
+            if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][i];
+          } else {
+            slot[m * kBandRows + rr] = acc[t][i];
           }
         }
       }
@@ -337,38 +296,185 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_main(const LaunchArgs a)
   }
 }
 
-// Second pass: block w handles the band that contains wave w's first step if
-// that step lies strictly inside the band and no earlier wave boundary does.
-// Its threads add, for every (token, row) of the band, the contributing
-// waves' slots in increasing wave order and write y.
+// ---------------------------------------------------------------------------
+// skinny_rows: a workgroup streams row groups of 4 rows (wave i takes row
+// 4 g + i).  Work units are (row group, K-chunk): a chunk is seg_per_chunk
+// 1 KB segments, and a linear is split into several chunks only when the
+// launch is too small to occupy every workgroup otherwise.  Units go round
+// robin: workgroup b takes units b, b + G, b + 2G, ... in order, so at any
+// moment all workgroups read neighbouring rows - measured on MI355X this
+// compact moving window streams faster than giving each workgroup its own
+// contiguous share.  LDS holds x[M][K] of the current linear, restaged
+// between two barriers when the linear changes (the same for all 4 waves),
+// and per wave the FP8 scale row of the current 128-row block.
+template <int DT, int MT, int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
+  constexpr int kThreads = 64 * WPB;                 // one row per wave: row group = WPB rows
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  // FP8: each wave keeps its own copy of the current scale row (no barrier
+  // needed) and prefetches the next unit's row into registers meanwhile.
+  float* ss = reinterpret_cast<float*>(lds + a.x_lds_bytes) + wv * kRowsMaxKBlocks;
+  float spre[kRowsMaxKBlocks / 64];
+  auto unit_of = [&](long long u, int& l, int& grp, int& chunk) {
+    while (l + 1 < a.nlin && a.lin[l + 1].step_base <= u) ++l;
+    const LinDesc& L = a.lin[l];
+    const long long local = u - L.step_base;
+    grp = (int)(local / L.chunks);
+    chunk = (int)(local - (long long)grp * L.chunks);
+  };
+  auto prefetch_scales = [&](long long u, int l) {
+    if (DT == SKINNY_FP8_BS128 && u < a.S) {
+      int grp, chunk;
+      unit_of(u, l, grp, chunk);
+      const LinDesc& L = a.lin[l];
+      const float* src = L.scale + (size_t)((grp * WPB) / kScaleBlock) * L.kblocks;
+#pragma unroll
+      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) {
+        const int k = 64 * i + lane;
+        spre[i] = k < L.kblocks ? src[k] : 0.0f;
+      }
+    }
+  };
+  auto store_scales = [&]() {
+    if (DT == SKINNY_FP8_BS128) {
+#pragma unroll
+      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) ss[64 * i + lane] = spre[i];
+    }
+  };
+  int l = 0;
+  int staged_l = -1;
+  long long u = blockIdx.x;
+  prefetch_scales(u, 0);
+  store_scales();
+  for (; u < a.S; u += a.G) {
+    int grp, chunk;
+    unit_of(u, l, grp, chunk);
+    const LinDesc& L = a.lin[l];
+    const long long local = (long long)grp * L.chunks + chunk;
+    const int spc = (L.spt + L.chunks - 1) / L.chunks;          // segments per chunk
+    const int j0 = chunk * spc;
+    const int j1 = min(j0 + spc, L.spt);
+    const int xcpr = L.K >> 3;                                   // x chunks per token row
+    if (l != staged_l) {                                         // same for all 4 waves
+      __syncthreads();                                           // all done with the old x
+      for (int i = threadIdx.x; i < MT * xcpr; i += kThreads) xs[i] = L.x[i];
+      __syncthreads();
+      staged_l = l;
+    }
+    prefetch_scales(u + a.G, l);
+    const int row = grp * WPB + wv;
+    const bool rowok = row < L.N;
+    const u32x4* wrow = L.w + (size_t)(rowok ? row : 0) * (size_t)L.cpr;
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    for (int j = j0; j < j1; j += U) {
+      u32x4 wq[U];
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int c = (j + v) * kSegChunks + lane;
+        wq[v] = (rowok && (j + v < j1) && c < L.cpr) ? wrow[c] : zero4();
+      }
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int c = (j + v) * kSegChunks + lane;
+        const bool ok = (j + v < j1) && c < L.cpr;
+        if (DT == SKINNY_BF16) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m] = dot8(ok ? xs[m * xcpr + c] : zero4(), wq[v], acc[m]);
+        } else {
+          // Chunk c holds k in [16 c, 16 c + 16): scale block c / 8.
+          const float sc = ok ? ss[c >> 3] : 0.0f;
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(wq[v], b0, b1);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 x0 = ok ? xs[m * xcpr + 2 * c] : zero4();
+            const u32x4 x1 = ok ? xs[m * xcpr + 2 * c + 1] : zero4();
+            acc[m] = __builtin_fmaf(sc, dot8(x1, b1, dot8(x0, b0, 0.0f)), acc[m]);
+          }
+        }
+      }
+    }
+    // This wave's reads of the current scales are done: install the next unit's.
+    store_scales();
+    // 64-lane butterfly; lane 0's sum has a fixed order.
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (L.chunks == 1) {
+          if (rowok) L.y[(size_t)m * L.N + row] = (__bf16)acc[m];
+        } else {
+          a.slots[((size_t)(L.slot_base + local) * MT + m) * WPB + wv] = acc[m];
+        }
+      }
+    }
+  }
+}
+
+// Second pass of skinny_rows: for every output of a split linear, the sum of
+// its K-chunks' partial results in chunk order.
+__global__ __launch_bounds__(kBlockThreads) void skinny_rows_combine(const LaunchArgs a) {
+  const int R = a.band_rows;
+  for (int l = 0; l < a.nlin; ++l) {
+    const LinDesc& L = a.lin[l];
+    if (L.chunks == 1) continue;
+    const long long outs = (long long)a.M * L.N;
+    for (long long i = blockIdx.x * (long long)kBlockThreads + threadIdx.x; i < outs;
+         i += (long long)gridDim.x * kBlockThreads) {
+      const int m = (int)(i / L.N);
+      const int row = (int)(i - (long long)m * L.N);
+      const int grp = row / R;
+      const int rr = row - grp * R;
+      float sum = 0.0f;
+      for (int c = 0; c < L.chunks; ++c)
+        sum += a.slots[((size_t)(L.slot_base + (long long)grp * L.chunks + c) * a.M + m) * R + rr];
+      L.y[(size_t)m * L.N + row] = (__bf16)sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Second pass.  Wave i of workgroup q handles boundary w = 4 q + i: if worker
+// w's first step lies strictly inside a band and no earlier boundary does,
+// the wave adds, for every (token, row) of that band, the contributing
+// workers' slots in increasing worker order and writes y.
 __global__ __launch_bounds__(kBlockThreads) void skinny_combine(const LaunchArgs a) {
-  const int w = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (w == 0 || w >= a.G) return;
-  const long long b = wave_start(w, a.S, a.G);
+  const long long b = worker_start(w, a.S, a.G);
   if (b >= a.S) return;
   int l = 0;
-  while (l + 1 < a.nlin && a.lin[l + 1].step_base <= b) ++l;
+  const BandPos p = band_of(a, l, b);
   const LinDesc& L = a.lin[l];
-  const long long local = b - L.step_base;
-  const int band = (int)(local / L.spt);
-  const long long bstart = L.step_base + (long long)band * L.spt;
+  const long long bstart = p.begin;
   const long long bend = bstart + L.spt;
   if (b == bstart) return;
-  if (wave_start(w - 1, a.S, a.G) > bstart) return;
+  if (worker_start(w - 1, a.S, a.G) > bstart) return;
+  // Contributing workers: w - 1 .. last, in order.
+  int last = w;
+  while (last + 1 < a.G && worker_start(last + 1, a.S, a.G) < bend) ++last;
   const int R = a.band_rows;
-  for (int idx = threadIdx.x; idx < a.M * R; idx += blockDim.x) {
+  for (int idx = lane; idx < a.M * R; idx += 64) {
     const int m = idx / R;
     const int rr = idx - m * R;
     float sum = 0.0f;
-    for (int v = w - 1; v < a.G; ++v) {
-      const long long sv = wave_start(v, a.S, a.G);
-      if (sv >= bend) break;
-      const long long ev = wave_start(v + 1, a.S, a.G);
-      if (ev <= sv) continue;                     // empty wave
+    for (int v = w - 1; v <= last; ++v) {
+      const long long sv = worker_start(v, a.S, a.G);
+      if (worker_start(v + 1, a.S, a.G) <= sv) continue;    // empty worker
       const int slot = 2 * v + (sv >= bstart ? 0 : 1);
       sum += a.slots[((size_t)slot * a.M + m) * R + rr];
     }
-    const int row = band * R + rr;
+    const int row = p.band * R + rr;
     if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum;
   }
 }
@@ -414,7 +520,7 @@ skinny_status check_linear(const skinny_linear& L, int M) {
   if (L.K % (L.dtype == SKINNY_BF16 ? 8 : 16) != 0) return SKINNY_ERR_UNSUPPORTED;
   if (!aligned(L.w, 16) || !aligned(L.x, 16) || !aligned(L.y, 16)) return SKINNY_ERR_UNSUPPORTED;
   if (L.w_scale && !aligned(L.w_scale, 4)) return SKINNY_ERR_UNSUPPORTED;
-  // Index arithmetic inside the kernels is 32-bit per tile and per row.
+  // Index arithmetic inside the kernels is 32-bit per band and per row.
   if (L.N > (1 << 30) || L.K > (1 << 28)) return SKINNY_ERR_UNSUPPORTED;
   return SKINNY_OK;
 }
@@ -452,131 +558,228 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
   return SKINNY_OK;
 }
 
+// Slots for the largest layout: kMaxWaves MFMA workers with 64-row bands.
 size_t workspace_for(int M) {
-  return (size_t)kMaxWaves * kSlotsPerWave * (size_t)M * kTileRows * kMaxBandTiles *
+  return (size_t)kMaxWaves * kSlotsPerWorker * (size_t)M * kTileRows * kMaxBandTiles *
          sizeof(float);
 }
 
-// Measured on MI355X (80-layer TP=1 shapes, M = 1..16, bf16 and FP8): the
-// MFMA path streams faster than the v_dot2 path at every M, because one MFMA
-// replaces four dot2 per chunk plus the cross-lane reduction and its A-operand
-// load serves all tokens.  The vector path stays available through the plan.
-int auto_variant(int dtype, int M) {
-  (void)dtype;
-  (void)M;
-  return SKINNY_VARIANT_MFMA;
+// LDS skinny_rows needs for a group: x[M][K] of its widest linear plus, for
+// FP8, one scale row per wave.  Returns -1 when that exceeds a workgroup's
+// LDS (or, for FP8, K exceeds 32768).
+int rows_lds_bytes(const skinny_linear* const* lin, int count, int M, int* x_bytes,
+                   int wpb = kRowsWavesPerBlock) {
+  long long kmax = 0, kbmax = 0;
+  for (int i = 0; i < count; ++i) {
+    if (lin[i]->K > kmax) kmax = lin[i]->K;
+    const long long kb = (lin[i]->K + kScaleBlock - 1) / kScaleBlock;
+    if (kb > kbmax) kbmax = kb;
+  }
+  const long long xb = ((long long)M * kmax * 2 + 15) / 16 * 16;
+  const bool fp8 = lin[0]->dtype == SKINNY_FP8_BS128;
+  if (fp8 && kbmax > kRowsMaxKBlocks) return -1;
+  const long long total = xb + (fp8 ? (long long)wpb * kRowsMaxKBlocks * 4 : 0);
+  if (total > kMaxLds) return -1;
+  *x_bytes = (int)xb;
+  return (int)total;
 }
 
-// Shape of the main loop per (dtype, variant, M): T tiles per band (x reuse),
-// U steps per batch, PIPE = issue the next batch before using this one.
-// Register use grows with T*U (weights) and U*M (activations), and the
-// persistent grid needs enough waves resident to cover HBM latency.
-struct LoopShape {
-  int T, U;
-  bool pipe;
-};
+// Variant choice, measured on MI355X over the Qwen2.5-72B shapes: row
+// streaming (x in LDS) leads for M <= 2 when x fits in LDS; beyond that the
+// LDS reads of x per weight load grow and the MFMA band kernel leads.
+constexpr int kRowsMaxAutoM = 2;
+constexpr int kRowsMaxM = 8;
 
-template <int DT, int VAR, int MT>
-constexpr LoopShape loop_shape() {
-  if (VAR == SKINNY_VARIANT_MFMA) return LoopShape{2, 8, false};
-  if (MT <= 1) return LoopShape{4, 2, true};
-  if (MT <= 2) return LoopShape{2, 2, true};
-  return LoopShape{1, 2, false};
+int auto_variant(const skinny_linear* const* lin, int count, int M) {
+  int xb = 0;
+  if (M <= kRowsMaxAutoM && rows_lds_bytes(lin, count, M, &xb) > 0) return SKINNY_VARIANT_VECTOR;
+  return SKINNY_VARIANT_MFMA;
 }
 
 typedef void (*main_fn)(LaunchArgs);
 
 struct KernelChoice {
   main_fn fn = nullptr;
-  int T = 1;
+  int band_rows = 0;
+  int wpb = kWavesPerBlock;    // waves per workgroup
+  bool rows = false;
 };
 
-template <int DT, int VAR, int MT>
-KernelChoice main_kernel() {
-  constexpr LoopShape ls = loop_shape<DT, VAR, MT>();
-  static_assert(ls.T >= 1 && ls.T <= kMaxBandTiles && (ls.T & (ls.T - 1)) == 0, "bad band");
+// MFMA band shape per dtype: T tiles per band, U k-steps per batch, PIPE.
+template <int DT>
+KernelChoice mfma_kernel() {
+  constexpr int T = 2, U = 8;
+  constexpr bool PIPE = false;
+  static_assert(T <= kMaxBandTiles && (kTileRows * T) <= kScaleBlock, "band too tall");
   KernelChoice k;
-  k.fn = skinny_main<DT, VAR, MT, ls.T, ls.U, ls.pipe>;
-  k.T = ls.T;
+  k.fn = skinny_mfma<DT, T, U, PIPE>;
+  k.band_rows = kTileRows * T;
+  return k;
+}
+
+template <int DT, int MT>
+KernelChoice rows_kernel() {
+  constexpr int WPB = kRowsWavesPerBlock;
+  constexpr int U = MT <= 2 ? kRowsUnroll : kRowsUnroll / 2;
+  KernelChoice k;
+  k.fn = skinny_rows<DT, MT, U, WPB>;
+  k.band_rows = WPB;
+  k.wpb = WPB;
+  k.rows = true;
   return k;
 }
 
 template <int DT>
-KernelChoice pick_main(int variant, int M) {
-  if (variant == SKINNY_VARIANT_MFMA) return main_kernel<DT, SKINNY_VARIANT_MFMA, 0>();
+KernelChoice pick_dt(int variant, int M) {
+  if (variant == SKINNY_VARIANT_MFMA) return mfma_kernel<DT>();
   switch (M) {
-    case 1: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 1>();
-    case 2: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 2>();
-    case 3: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 3>();
-    case 4: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 4>();
-    case 5: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 5>();
-    case 6: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 6>();
-    case 7: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 7>();
-    case 8: return main_kernel<DT, SKINNY_VARIANT_VECTOR, 8>();
+    case 1: return rows_kernel<DT, 1>();
+    case 2: return rows_kernel<DT, 2>();
+    case 3: return rows_kernel<DT, 3>();
+    case 4: return rows_kernel<DT, 4>();
+    case 5: return rows_kernel<DT, 5>();
+    case 6: return rows_kernel<DT, 6>();
+    case 7: return rows_kernel<DT, 7>();
+    case 8: return rows_kernel<DT, 8>();
     default: return KernelChoice{};
   }
 }
 
 KernelChoice pick(int dtype, int variant, int M) {
-  return dtype == SKINNY_BF16 ? pick_main<SKINNY_BF16>(variant, M)
-                              : pick_main<SKINNY_FP8_BS128>(variant, M);
+  return dtype == SKINNY_BF16 ? pick_dt<SKINNY_BF16>(variant, M)
+                              : pick_dt<SKINNY_FP8_BS128>(variant, M);
 }
 
-// Persistent grid size: every wave must be resident at once for the equal
-// shares to finish together, so take what the occupancy query allows for
-// this kernel, capped at kTargetWavesPerCU waves per CU.  The query result is
-// cached per (device, kernel).
+// Persistent grid size: every worker must be resident at once for the equal
+// shares to finish together, so take what the occupancy query allows for the
+// kernel (and its LDS), capped at kTargetWavesPerCU waves per CU.  Query
+// results are cached per (device, kernel, LDS bytes).
 constexpr int kTargetWavesPerCU = 16;
-constexpr int kOccCache = 128;
+constexpr int kOccCache = 256;
 struct OccEntry {
   int dev;
   main_fn fn;
+  int lds;
   int blocks_per_cu;
 };
 OccEntry g_occ[kOccCache];
 int g_occ_n = 0;
 std::mutex g_occ_mu;
 
-skinny_status auto_waves(const DeviceInfo& d, main_fn fn, int* waves) {
+skinny_status blocks_per_cu(main_fn fn, int lds, int threads, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
-  int blocks_per_cu = -1;
   {
     std::lock_guard<std::mutex> lock(g_occ_mu);
     for (int i = 0; i < g_occ_n; ++i)
-      if (g_occ[i].dev == dev && g_occ[i].fn == fn) blocks_per_cu = g_occ[i].blocks_per_cu;
+      if (g_occ[i].dev == dev && g_occ[i].fn == fn && g_occ[i].lds == lds) {
+        *out = g_occ[i].blocks_per_cu;
+        return SKINNY_OK;
+      }
   }
-  if (blocks_per_cu < 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, (const void*)fn,
-                                                     kBlockThreads, 0) != hipSuccess)
-      return SKINNY_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_occ_mu);
-    if (g_occ_n < kOccCache) g_occ[g_occ_n++] = OccEntry{dev, fn, blocks_per_cu};
-  }
-  int per_cu = blocks_per_cu * kWavesPerBlock;
-  if (per_cu > kTargetWavesPerCU) per_cu = kTargetWavesPerCU;
-  if (per_cu < kWavesPerBlock) per_cu = kWavesPerBlock;
-  long long g = (long long)d.cus * per_cu;
-  if (g > kMaxWaves) g = kMaxWaves;
-  *waves = (int)g;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, threads, lds) !=
+      hipSuccess)
+    return SKINNY_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_occ_mu);
+  if (g_occ_n < kOccCache) g_occ[g_occ_n++] = OccEntry{dev, fn, lds, n};
+  *out = n;
   return SKINNY_OK;
 }
 
+// Dynamic LDS above the default limit must be granted per kernel; the
+// largest size granted so far is remembered per (device, kernel).
+struct LdsEntry {
+  int dev;
+  main_fn fn;
+  int bytes;
+};
+LdsEntry g_lds[kOccCache];
+int g_lds_n = 0;
+
+skinny_status ensure_lds(main_fn fn, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_occ_mu);
+  int slot = -1;
+  for (int i = 0; i < g_lds_n; ++i)
+    if (g_lds[i].dev == dev && g_lds[i].fn == fn) slot = i;
+  if (slot >= 0 && g_lds[slot].bytes >= bytes) return SKINNY_OK;
+  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+      hipSuccess)
+    return SKINNY_ERR_HIP;
+  if (slot >= 0) g_lds[slot].bytes = bytes;
+  else if (g_lds_n < kOccCache) g_lds[g_lds_n++] = LdsEntry{dev, fn, bytes};
+  return SKINNY_OK;
+}
+
+// Workers of the persistent grid: waves for skinny_mfma, workgroups for skinny_rows.
+skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, int* workers) {
+  int bpc = 0;
+  skinny_status st = blocks_per_cu(k.fn, lds, 64 * k.wpb, &bpc);
+  if (st != SKINNY_OK) return st;
+  if (bpc < 1) return SKINNY_ERR_UNSUPPORTED;
+  int waves_per_cu = bpc * k.wpb;
+  const int cap = k.rows ? kTargetRowsWavesPerCU : kTargetWavesPerCU;
+  if (waves_per_cu > cap) waves_per_cu = cap < k.wpb ? k.wpb : cap;
+  long long g = (long long)d.cus * waves_per_cu;
+  if (g > kMaxWaves) g = kMaxWaves;
+  if (k.rows) g /= k.wpb;
+  *workers = (int)g;
+  return SKINNY_OK;
+}
+
+// skinny_rows splits a linear's rows into K-chunks only when the launch is
+// too small to give every workgroup about kUnitsPerWorker units: a row group
+// larger than the target unit size is cut into that many chunks (at most one
+// per 1 KB segment).  Split linears get consecutive workspace slots, one per
+// unit; if they would not fit in the workspace nothing is split.
+constexpr int kUnitsPerWorker = 16;
+void plan_row_chunks(LaunchArgs& a, int count, int G) {
+  const int R = a.band_rows;
+  const long long max_slots = (long long)kMaxWaves * kSlotsPerWorker * kTileRows * kMaxBandTiles / R;
+  long long total = 0;
+  for (int i = 0; i < count; ++i) total += (long long)a.lin[i].N * a.lin[i].cpr * 16;
+  long long target = total / ((long long)kUnitsPerWorker * G);
+  if (target < 1) target = 1;
+  long long slots = 0;
+  for (int i = 0; i < count; ++i) {
+    LinDesc& d = a.lin[i];
+    const long long grp_bytes = (long long)R * d.cpr * 16;
+    long long c = (grp_bytes + target - 1) / target;
+    if (c > d.spt) c = d.spt;
+    if (c < 1) c = 1;
+    d.chunks = (int)c;
+    d.slot_base = slots;
+    if (c > 1) slots += (long long)((d.N + R - 1) / R) * c;
+  }
+  if (slots > max_slots)
+    for (int i = 0; i < count; ++i) a.lin[i].chunks = 1;
+}
+
 // Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
-// G = 0 sizes the persistent grid from occupancy.
+// workers = 0 sizes the persistent grid from occupancy; otherwise it is the
+// number of waves to run (rounded down to whole workgroups for skinny_rows).
 skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* lin, int count,
-                           int M, int variant, int G, float* slots, hipStream_t stream,
+                           int M, int variant, int workers, float* slots, hipStream_t stream,
                            hipEvent_t ev_before, hipEvent_t ev_after) {
   const int dtype = lin[0]->dtype;
+  if (variant == SKINNY_VARIANT_AUTO) variant = auto_variant(lin, count, M);
   const KernelChoice k = pick(dtype, variant, M);
-  if (!k.fn) return SKINNY_ERR_INVALID_ARG;
+  if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   LaunchArgs a;
   memset(&a, 0, sizeof a);
   a.nlin = count;
   a.M = M;
   a.slots = slots;
-  a.band_rows = kTileRows * k.T;
-  long long S = 0;
+  a.band_rows = k.band_rows;
+  int lds = 0;
+  if (k.rows) {
+    lds = rows_lds_bytes(lin, count, M, &a.x_lds_bytes);
+    if (lds < 0) return SKINNY_ERR_UNSUPPORTED;
+    skinny_status st = ensure_lds(k.fn, lds);
+    if (st != SKINNY_OK) return st;
+  }
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = *lin[i];
     LinDesc& d = a.lin[i];
@@ -587,28 +790,48 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     d.N = L.N;
     d.K = L.K;
     d.cpr = L.K / (dtype == SKINNY_BF16 ? 8 : 16);
-    d.spt = (d.cpr + 3) / 4;
+    d.spt = k.rows ? (d.cpr + kSegChunks - 1) / kSegChunks : (d.cpr + 3) / 4;
     d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
+    d.chunks = 1;
+  }
+  int G = workers;
+  if (G == 0) {
+    skinny_status st = auto_workers(dev, k, lds, &G);
+    if (st != SKINNY_OK) return st;
+  } else if (k.rows) {
+    G = G / k.wpb > 0 ? G / k.wpb : 1;
+  }
+  if (k.rows) plan_row_chunks(a, count, G);
+  long long S = 0;
+  for (int i = 0; i < count; ++i) {
+    LinDesc& d = a.lin[i];
     d.step_base = S;
-    const long long bands = (L.N + a.band_rows - 1) / a.band_rows;
-    S += bands * d.spt;
+    const long long bands = (d.N + a.band_rows - 1) / a.band_rows;
+    S += bands * (k.rows ? d.chunks : d.spt);
   }
   a.S = S;
-  main_fn fn = k.fn;
-  if (G == 0) {
-    skinny_status st = auto_waves(dev, fn, &G);
-    if (st != SKINNY_OK) return st;
-  }
   if (G > S) G = (int)S;
   if (G < 1) G = 1;
   a.G = G;
-  const int blocks = (G + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int blocks = k.rows ? G : (G + kWavesPerBlock - 1) / kWavesPerBlock;
   if (ev_before && hipEventRecord(ev_before, stream) != hipSuccess) return SKINNY_ERR_HIP;
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(kBlockThreads), 0, stream, a);
+  hipLaunchKernelGGL(k.fn, dim3(blocks), dim3(64 * k.wpb), lds, stream, a);
   if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
   if (ev_after && hipEventRecord(ev_after, stream) != hipSuccess) return SKINNY_ERR_HIP;
-  if (G > 1) {
-    hipLaunchKernelGGL(skinny_combine, dim3(G), dim3(kBlockThreads), 0, stream, a);
+  if (k.rows) {
+    long long outs = 0;
+    for (int i = 0; i < count; ++i)
+      if (a.lin[i].chunks > 1) outs += (long long)M * a.lin[i].N;
+    if (outs > 0) {
+      long long cblocks = (outs + kBlockThreads - 1) / kBlockThreads;
+      if (cblocks > 1024) cblocks = 1024;
+      hipLaunchKernelGGL(skinny_rows_combine, dim3((unsigned)cblocks), dim3(kBlockThreads), 0,
+                         stream, a);
+      if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+    }
+  } else if (G > 1) {
+    const int cblocks = (G + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(skinny_combine, dim3(cblocks), dim3(kBlockThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
   }
   return SKINNY_OK;
@@ -622,6 +845,30 @@ int launch_count(const skinny_linear* lin, int count) {
     launches += (n + SKINNY_MAX_LINEARS_PER_LAUNCH - 1) / SKINNY_MAX_LINEARS_PER_LAUNCH;
   }
   return launches;
+}
+
+// Calls fn(group, n) for each launch group: in call order, by dtype, at most
+// SKINNY_MAX_LINEARS_PER_LAUNCH linears per group.  Stops at the first error.
+template <typename Fn>
+skinny_status for_each_group(const skinny_linear* lin, int count, Fn&& fn) {
+  const skinny_linear* group[SKINNY_MAX_LINEARS_PER_LAUNCH];
+  for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+      if (lin[i].dtype != dt) continue;
+      group[n++] = &lin[i];
+      if (n == SKINNY_MAX_LINEARS_PER_LAUNCH) {
+        skinny_status st = fn(group, n);
+        if (st != SKINNY_OK) return st;
+        n = 0;
+      }
+    }
+    if (n > 0) {
+      skinny_status st = fn(group, n);
+      if (st != SKINNY_OK) return st;
+    }
+  }
+  return SKINNY_OK;
 }
 
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
@@ -643,43 +890,33 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
     if (variant < SKINNY_VARIANT_AUTO || variant > SKINNY_VARIANT_MFMA) return SKINNY_ERR_INVALID_ARG;
     if (waves < 0 || waves > kMaxWaves) return SKINNY_ERR_INVALID_ARG;
   }
-  if (variant == SKINNY_VARIANT_VECTOR && M > 8) return SKINNY_ERR_UNSUPPORTED;
+  if (variant == SKINNY_VARIANT_VECTOR && M > kRowsMaxM) return SKINNY_ERR_UNSUPPORTED;
   if (!ws) return SKINNY_ERR_WORKSPACE;
   if (ws_bytes < workspace_for(M)) return SKINNY_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
   skinny_status st = check_outputs(lin, count, M, ws, ws_bytes);
   if (st != SKINNY_OK) return st;
   if (events && event_count < 2 * launch_count(lin, count)) return SKINNY_ERR_INVALID_ARG;
+  // A VECTOR plan whose x does not fit in LDS is rejected before anything is enqueued.
+  if (variant == SKINNY_VARIANT_VECTOR) {
+    st = for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
+      int xb = 0;
+      return rows_lds_bytes(g, n, M, &xb) < 0 ? SKINNY_ERR_UNSUPPORTED : SKINNY_OK;
+    });
+    if (st != SKINNY_OK) return st;
+  }
   DeviceInfo d;
   st = device_info(&d);
   if (st != SKINNY_OK) return st;
   if (!d.gfx950) return SKINNY_ERR_UNSUPPORTED;
   int launch = 0;
-  auto ev = [&](int k) { return events ? (hipEvent_t)events[2 * launch + k] : (hipEvent_t) nullptr; };
-  // Group by dtype, in call order, SKINNY_MAX_LINEARS_PER_LAUNCH per launch.
-  for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
-    const int var = variant == SKINNY_VARIANT_AUTO ? auto_variant(dt, M) : variant;
-    const skinny_linear* group[SKINNY_MAX_LINEARS_PER_LAUNCH];
-    int n = 0;
-    for (int i = 0; i < count; ++i) {
-      if (lin[i].dtype != dt) continue;
-      group[n++] = &lin[i];
-      if (n == SKINNY_MAX_LINEARS_PER_LAUNCH) {
-        st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream, ev(0),
-                          ev(1));
-        if (st != SKINNY_OK) return st;
-        ++launch;
-        n = 0;
-      }
-    }
-    if (n > 0) {
-      st = launch_group(d, group, n, M, var, waves, (float*)ws, (hipStream_t)stream, ev(0),
-                        ev(1));
-      if (st != SKINNY_OK) return st;
-      ++launch;
-    }
-  }
-  return SKINNY_OK;
+  return for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
+    hipEvent_t before = events ? (hipEvent_t)events[2 * launch] : nullptr;
+    hipEvent_t after = events ? (hipEvent_t)events[2 * launch + 1] : nullptr;
+    ++launch;
+    return launch_group(d, g, n, M, variant, waves, (float*)ws, (hipStream_t)stream, before,
+                        after);
+  });
 }
 
 }  // namespace
@@ -742,10 +979,8 @@ skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
 int skinny_band_rows(int dtype, int variant, int M) {
   if (dtype != SKINNY_BF16 && dtype != SKINNY_FP8_BS128) return 0;
   if (M < 1 || M > SKINNY_MAX_M) return 0;
-  if (variant < SKINNY_VARIANT_AUTO || variant > SKINNY_VARIANT_MFMA) return 0;
-  const int var = variant == SKINNY_VARIANT_AUTO ? auto_variant(dtype, M) : variant;
-  const KernelChoice k = pick(dtype, var, M);
-  return k.fn ? kTileRows * k.T : 0;
+  if (variant != SKINNY_VARIANT_VECTOR && variant != SKINNY_VARIANT_MFMA) return 0;
+  return pick(dtype, variant, M).band_rows;
 }
 
 int skinny_launch_count(const skinny_linear* linears, int count) {
@@ -770,14 +1005,28 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
     skinny_status st = check_linear(linears[i], M);
     if (st != SKINNY_OK) return st;
   }
+  // The plan of the first launch group.
+  const skinny_linear* group[SKINNY_MAX_LINEARS_PER_LAUNCH];
+  int n = 0;
+  for (int i = 0; i < count && n < SKINNY_MAX_LINEARS_PER_LAUNCH; ++i)
+    if (linears[i].dtype == linears[0].dtype) group[n++] = &linears[i];
   DeviceInfo d;
   skinny_status st = device_info(&d);
   if (st != SKINNY_OK) return st;
   memset(out, 0, sizeof *out);
-  out->variant = auto_variant(linears[0].dtype, M);
+  out->variant = auto_variant(group, n, M);
   const KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
-  return auto_waves(d, k.fn, &out->waves);
+  int lds = 0, xb = 0;
+  if (k.rows) {
+    lds = rows_lds_bytes(group, n, M, &xb);
+    st = ensure_lds(k.fn, lds);
+    if (st != SKINNY_OK) return st;
+  }
+  int workers = 0;
+  st = auto_workers(d, k, lds, &workers);
+  out->waves = k.rows ? workers * k.wpb : workers;
+  return st;
 }
 
 const char* skinny_status_string(int status) {

@@ -137,10 +137,12 @@ skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, i
                                       int event_count, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
-/* Rows of W one wave streams together (16 x tiles per band) for this dtype,
- * variant (AUTO resolved as the library would) and M; 0 if invalid.  The
- * split-K workspace holds fp32 partial sums laid out [slot][M][band rows],
- * slot 2w for wave w's first band and 2w+1 for its last. */
+/* Rows of W in one band of the main kernel of this dtype, variant (VECTOR or
+ * MFMA; 0 for AUTO, whose choice depends on the shapes) and M; 0 if invalid.
+ * The split-K workspace holds fp32 partial sums: for MFMA laid out
+ * [slot][M][band rows], slot 2w for wave w's first band and 2w+1 for its
+ * last; for VECTOR [unit][M][band rows], one slot per K-chunk of each row
+ * group of a linear the launch splits, linears and row groups in order. */
 int skinny_band_rows(int dtype, int variant, int M);
 
 /* The plan the library would use on the current device (fills *out). */

@@ -119,9 +119,9 @@ def test_stack_rejects_bad_arguments():
 def test_band_rows_and_launch_counts():
     for dt in (sg.BF16, sg.FP8_BS128):
         for M in (1, 2, 6, 16):
-            for var in (sg.VARIANT_AUTO, sg.VARIANT_MFMA):
-                assert sg.band_rows(dt, var, M) in (16, 32, 64)
-        assert sg.band_rows(dt, sg.VARIANT_VECTOR, 8) in (16, 32, 64)
+            assert sg.band_rows(dt, sg.VARIANT_MFMA, M) in (16, 32, 64)
+            assert sg.band_rows(dt, sg.VARIANT_AUTO, M) == 0      # depends on the shapes
+        assert sg.band_rows(dt, sg.VARIANT_VECTOR, 8) == 8
         assert sg.band_rows(dt, sg.VARIANT_VECTOR, 9) == 0
     assert sg.band_rows(sg.BF16, 7, 1) == 0 and sg.band_rows(9, 0, 1) == 0
     lin = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)

@@ -37,7 +37,7 @@ def test_bf16_random_vs_oracle(M, N, K):
     w = synth.tensor_bf16(0, synth.stream_id("t-bf16", N, K, "w"), N, K, 0.02)
     y_ref, a, _ = oracle.linear_bf16(x, w)
     for var in variants_for(M):
-        for waves in (0, 1, 7):
+        for waves in (0, 4, 28):           # skinny_rows runs waves / 4 workgroups
             y = run_bf16(x, w, M, N, variant=var, waves=waves)
             assert_matches_oracle(y, y_ref, a, f"bf16 M={M} N={N} K={K} var={var} waves={waves}",
                                   strict=K >= 1000)
@@ -53,7 +53,7 @@ def test_fp8_random_vs_oracle(M, N, K):
     q, s, _ = synth.fp8_weight_bs128(0, synth.stream_id("t-fp8", N, K, "w"), N, K)
     y_ref, a, _ = oracle.linear_fp8_bs128(x, q, s)
     for var in variants_for(M):
-        for waves in (0, 1, 5):
+        for waves in (0, 4, 20):
             y = run_fp8(x, q, s, M, N, variant=var, waves=waves)
             assert_matches_oracle(y, y_ref, a, f"fp8 M={M} N={N} K={K} var={var} waves={waves}",
                                   strict=K >= 1000)
@@ -82,7 +82,7 @@ def test_permutation_is_exact():
     w = np.zeros((N, K), np.uint16)
     w[np.arange(N), perm] = BF16_ONE
     for var in variants_for(M):
-        for waves in (0, 3):
+        for waves in (0, 12):
             assert np.array_equal(host_codes(run_bf16(x, w, M, N, variant=var, waves=waves)),
                                   x[:, perm])
 
@@ -94,7 +94,7 @@ def test_constant_closed_form():
     q = np.full((N, K), 0x30, np.uint8)                      # 0.5 ...
     s = np.full((1, K // 128), 0.25, np.float32)             # ... x 0.25 = 0.125
     for var in variants_for(M):
-        for waves in (0, 1, 13):
+        for waves in (0, 4, 52):
             assert np.all(host_values(run_bf16(x, w, M, N, variant=var, waves=waves)) == 512.0)
             assert np.all(host_values(run_fp8(x, q, s, M, N, variant=var, waves=waves)) == 512.0)
 
@@ -143,13 +143,22 @@ def test_page_example_split_k_partials_in_workspace():
     for var in variants_for(2):
         ws = workspace(2)
         ws.zero_()
-        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=2, ws=ws)
+        waves = 8 if var == sg.VARIANT_VECTOR else 2     # two workers either way
+        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=waves, ws=ws)
         assert host_values(y).tolist() == d["sum_printed"]
         slots = ws.view(torch.float32).cpu().numpy()
-        # Slot layout [slot][M][band rows]: wave 0 writes slot 0, wave 1 slot 2.
         R = sg.band_rows(sg.BF16, var, 2)
-        p0 = slots[0:2 * R].reshape(2, R)[:, :4]
-        p1 = slots[4 * R:6 * R].reshape(2, R)[:, :4]
+        if var == sg.VARIANT_MFMA:
+            # Stream-K slots [slot][M][band rows]: wave 0 writes slot 0, wave 1 slot 2.
+            p0 = slots[0:2 * R].reshape(2, R)[:, :4]
+            p1 = slots[4 * R:6 * R].reshape(2, R)[:, :4]
+        else:
+            # One slot [M][4 rows] per K-chunk of the row group, in K order; only
+            # the chunks holding k = 0..3 and k = 4096..4099 are nonzero.
+            per = slots[:64 * 2 * R].reshape(64, 2, R)
+            nz = [c for c in range(64) if np.any(per[c] != 0)]
+            assert len(nz) == 2, nz
+            p0, p1 = per[nz[0]][:, :4], per[nz[1]][:, :4]
         assert p0.tolist() == d["partial0_printed"]
         assert p1.tolist() == d["partial1_printed"]
 
@@ -178,7 +187,7 @@ def test_bitwise_repeatable_and_splits_agree(M):
         first = host_codes(run_bf16(x, w, M, N, variant=var))
         for _ in range(3):
             assert np.array_equal(host_codes(run_bf16(x, w, M, N, variant=var)), first)
-        for waves in (1, 2, 80, 1000, 8192):
+        for waves in (4, 8, 80, 1000, 8192):
             y = run_bf16(x, w, M, N, variant=var, waves=waves)
             assert_matches_oracle(y, y_ref, a, f"waves={waves}")
 
