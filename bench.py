@@ -59,7 +59,11 @@ def parse():
                    help="small workloads cycle weight copies totalling at least this many bytes "
                         "so every step reads HBM, not the 256 MB last-level cache")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=1024)
+    p.add_argument("--cpu-sample-rows", type=int, default=2048)
+    p.add_argument("--calibration-copy-mib", type=int, default=0,
+                   help="after timing, run one plain elementwise copy of this many MiB "
+                        "(torch.neg into a second buffer): a kernel of known HBM traffic that "
+                        "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
 
 
@@ -76,40 +80,38 @@ def make_workload(name):
     raise ValueError(name)
 
 
-def materialise(specs, M, copies, seed=0):
-    """Device tensors for `copies` copies of the workload (copy 0 uses the
-    workload's streams; copy c > 0 the same shapes with streams offset by c)."""
+def measured_traffic(workload, M):
+    """HBM bytes per main launch from the committed rocprofv3 counter summary,
+    or None when there is none for this workload or the kernels changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    try:
+        t = json.load(open(path))
+        src = os.path.join(ROOT, t["kernel_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != t["kernel_source_sha256"]:
+            return None
+        e = t["entries"].get(f"{workload}/M{M}")
+        return int(e["traffic_bytes_per_launch"]) if e else None
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def calibrate_spin(stream):
+    """GPU spin-kernel cycles per millisecond (torch.cuda._sleep)."""
     import torch
-
-    import gemv_skinny_gemm_amd as sg
-    from gemv_skinny_gemm_amd import workloads as wl
-    from gemv_skinny_gemm_amd.synth import gpu as sgpu
-
-    max_fp8 = max((s.N * s.K for s in specs if s.dtype == wl.FP8_BS128), default=0)
-    scratch = torch.empty(max_fp8, dtype=torch.bfloat16, device="cuda") if max_fp8 else None
-    sets = []
-    keep = []
-    for c in range(copies):
-        descs = []
-        for s in specs:
-            ws_ = (s.w_stream + c * 0x9E3779B1) & 0xFFFFFFFF
-            x = sgpu.tensor_bf16(seed, s.x_stream, M, s.K, wl.X_SIGMA)
-            y = torch.zeros((M, s.N), dtype=torch.bfloat16, device="cuda")
-            if s.dtype == wl.BF16:
-                w = sgpu.tensor_bf16(seed, ws_, s.N, s.K, wl.W_SIGMA)
-                descs.append(sg.make_linear(x, w, y))
-                keep.append((x, w, y))
-            else:
-                q, sc = sgpu.fp8_weight_bs128(seed, ws_, s.N, s.K, wl.W_SIGMA, scratch=scratch)
-                descs.append(sg.make_linear(x, q, y, w_scale=sc))
-                keep.append((x, q, sc, y))
-        sets.append(descs)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    n = 1_000_000
+    torch.cuda._sleep(n)
     torch.cuda.synchronize()
-    del scratch
-    return sets, keep
+    a.record(stream)
+    torch.cuda._sleep(n)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return n / max(a.elapsed_time(b), 1e-3)
 
 
-def cpu_baseline(specs, M, rows, seed=0):
+def cpu_baseline(specs, M, rows, seed=0, repeats=5):
     """The fp64 oracle on a bounded sample: the first `rows` rows of each linear
     of the first layer, from the same seeded streams.  Returns the result
     dict, the sampled reference outputs and the sample description."""
@@ -124,24 +126,30 @@ def cpu_baseline(specs, M, rows, seed=0):
     for s in layer:
         r = min(rows, s.N)
         x = synth.tensor_bf16(seed, s.x_stream, M, s.K, wl.X_SIGMA)
+        times = []
         if s.dtype == wl.BF16:
             w = synth.tensor_bf16(seed, s.w_stream, r, s.K, wl.W_SIGMA)
-            t0 = time.perf_counter()
-            y, a, threads = oracle.linear_bf16(x, w)
-            total_s += time.perf_counter() - t0
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                y, a, threads = oracle.linear_bf16(x, w)
+                times.append(time.perf_counter() - t0)
             total_b += r * s.K * 2
         else:
             bands = (r + 127) // 128
             q, sc, _ = synth.fp8_weight_bs128(seed, s.w_stream, s.N, s.K, wl.W_SIGMA, 0, bands)
             q, r = q[:r], min(r, q.shape[0])
-            t0 = time.perf_counter()
-            y, a, threads = oracle.linear_fp8_bs128(x, q, sc[:(r + 127) // 128])
-            total_s += time.perf_counter() - t0
-            total_b += r * s.K + sc.size * 4
+            scr = sc[:(r + 127) // 128]
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                y, a, threads = oracle.linear_fp8_bs128(x, q, scr)
+                times.append(time.perf_counter() - t0)
+            total_b += r * s.K + scr.size * 4
+        total_s += float(np.median(times))
         total_b += 2 * M * s.K + 2 * M * r
         refs.append((s, r, y, a))
     desc = (f"first {rows} rows of each of the {len(layer)} linears of layer 0 "
-            f"({total_b / 1e6:.1f} MB of algorithmic bytes), compute only")
+            f"({total_b / 1e6:.1f} MB of algorithmic bytes), compute only, median of "
+            f"{repeats} runs")
     return total_s, total_b, threads, refs, desc
 
 
@@ -173,7 +181,8 @@ def main():
     log(f"workload {args.workload}: {len(specs)} linears, M={M}, {step_bytes / 1e9:.3f} GB/step, "
         f"{copies} rotating cop{'y' if copies == 1 else 'ies'}")
     t0 = time.perf_counter()
-    sets, keep = materialise(specs, M, copies)
+    from gemv_skinny_gemm_amd.synth import gpu as sgpu
+    sets, tensors = sgpu.materialise(specs, M, copies)
     log(f"inputs made on the GPU in {time.perf_counter() - t0:.1f} s")
 
     variant = {"auto": sg.VARIANT_AUTO, "vector": sg.VARIANT_VECTOR, "mfma": sg.VARIANT_MFMA}[args.variant]
@@ -189,10 +198,19 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # A GPU spin kernel ahead of each timed region keeps the stream busy while
+    # the host enqueues, so the timed launches run back to back on the GPU
+    # and host launch overhead stays out of the figures.
+    spin_cycles = calibrate_spin(stream)
+
+    def prefill(expected_ms):
+        torch.cuda._sleep(int(spin_cycles * (expected_ms + 5.0)))
+
     # Timed region: K whole steps between two events on the library's stream.
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    prefill(args.steps * 0.05)
     e0.record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
@@ -206,6 +224,7 @@ def main():
     for e in evs:
         e.record(stream)                     # creates the underlying hipEvent_t
     torch.cuda.synchronize()
+    prefill(args.steps * 0.1)
     for i in range(args.steps):
         handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
         sg.linear_run_timed(sets[(args.warmup + i) % copies], M, ws, handles, variant=variant,
@@ -254,12 +273,22 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, M),
             "avg_launch_us": round(main_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
             "main_us_per_step": round(main_total_ms * 1e3, 2),
         },
     }
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 19                 # bf16 elements
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        result["config"]["calibration_copy_bytes"] = 2 * n
+        del src, dst
 
     if not args.no_cpu_baseline:
         import oracle
@@ -269,9 +298,8 @@ def main():
         step(0)
         torch.cuda.synchronize()
         worst = 0.0
-        for (s, r, y_ref, a), d in zip(refs, sets[0][:len(refs)]):
-            y_gpu = next(t for t in keep if t[-1].data_ptr() == d.y)[-1]
-            yv = y_gpu[:, :r].float().cpu().double().numpy()
+        for (s, r, y_ref, a), t in zip(refs, tensors[0][:len(refs)]):
+            yv = t[3][:, :r].float().cpu().double().numpy()
             ok, wr, _ = oracle.check(yv, y_ref, a)
             worst = max(worst, wr)
             if not ok:

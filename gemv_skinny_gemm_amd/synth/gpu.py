@@ -85,3 +85,41 @@ def fp8_weight_bs128(seed: int, stream: int, N: int, K: int, sigma: float = 0.02
     w = scratch[:N * K].view(N, K)
     normal_bf16_(w, seed, stream, sigma)
     return quantize_bs128(w)
+
+
+def materialise(specs, M: int, copies: int = 1, seed: int = 0):
+    """Device tensors and skinny_linear descriptors for `copies` copies of a
+    workload (a list of workloads.LinearSpec).  Copy 0 uses each tensor's own
+    stream; copy c > 0 offsets the weight stream so every copy is distinct.
+
+    Returns (sets, tensors): sets[c] is the list of descriptors of copy c and
+    tensors[c][i] = (x, w, scale or None, y) of linear i."""
+    import gemv_skinny_gemm_amd as sg
+    from gemv_skinny_gemm_amd import workloads as wl
+
+    max_fp8 = max((s.N * s.K for s in specs if s.dtype == wl.FP8_BS128), default=0)
+    scratch = torch.empty(max_fp8, dtype=torch.bfloat16, device="cuda") if max_fp8 else None
+    sets, tensors = [], []
+    for c in range(copies):
+        descs, ts = [], []
+        for s in specs:
+            wstream = weight_stream(s, c)
+            x = tensor_bf16(seed, s.x_stream, M, s.K, wl.X_SIGMA)
+            y = torch.zeros((M, s.N), dtype=torch.bfloat16, device="cuda")
+            if s.dtype == wl.BF16:
+                w = tensor_bf16(seed, wstream, s.N, s.K, wl.W_SIGMA)
+                descs.append(sg.make_linear(x, w, y))
+                ts.append((x, w, None, y))
+            else:
+                q, sc = fp8_weight_bs128(seed, wstream, s.N, s.K, wl.W_SIGMA, scratch=scratch)
+                descs.append(sg.make_linear(x, q, y, w_scale=sc))
+                ts.append((x, q, sc, y))
+        sets.append(descs)
+        tensors.append(ts)
+    torch.cuda.synchronize()
+    return sets, tensors
+
+
+def weight_stream(spec, copy: int = 0) -> int:
+    """Philox stream of a weight tensor's copy `copy` (copy 0 = the spec's own)."""
+    return (spec.w_stream + copy * 0x9E3779B1) & 0xFFFFFFFF
