@@ -72,7 +72,6 @@ constexpr int kRowsMaxKBlocks = 256;    // skinny_rows FP8: K <= 32768
 // per workgroup share one copy of x, 8 segments per wave in flight, up to 32
 // waves per CU.
 constexpr int kRowsWavesPerBlock = 8;
-constexpr int kRowsUnroll = 8;
 constexpr int kTargetRowsWavesPerCU = 32;
 
 struct LinDesc {
@@ -297,40 +296,47 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_mfma(const LaunchArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// skinny_rows: a workgroup streams row groups of 4 rows (wave i takes row
-// 4 g + i).  Work units are (row group, K-chunk): a chunk is seg_per_chunk
-// 1 KB segments, and a linear is split into several chunks only when the
-// launch is too small to occupy every workgroup otherwise.  Units go round
-// robin: workgroup b takes units b, b + G, b + 2G, ... in order, so at any
-// moment all workgroups read neighbouring rows - measured on MI355X this
-// compact moving window streams faster than giving each workgroup its own
-// contiguous share.  LDS holds x[M][K] of the current linear, restaged
-// between two barriers when the linear changes (the same for all 4 waves),
-// and per wave the FP8 scale row of the current 128-row block.
-template <int DT, int MT, int U, int WPB>
+// skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
+// wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
+// along K: lane l reads bytes [16 l, 16 l + 16) of each 1 KB segment of a
+// row, so each wave reads its rows front to back in 1 KB coalesced loads.
+// Work units are (K-chunk, row group), chunk-major within a linear; a chunk is
+// spc consecutive segments.  A linear has more than one chunk when its x
+// window would not fit the LDS budget or when the launch is too small to
+// keep every workgroup busy.  Units go round robin: workgroup b takes units
+// b, b + G, b + 2G, ..., so at any moment all workgroups read neighbouring
+// rows - measured on MI355X this compact moving window streams faster than
+// giving each workgroup its own contiguous share.  LDS holds x[M][window] of
+// the current (linear, chunk), restaged between two barriers when it changes
+// (the same for all waves), and per wave the FP8 scale row of the current
+// 128-row block, prefetched one unit ahead.  One x read from LDS serves the
+// wave's R rows.
+template <int DT, int MT, int U, int R, int WPB>
 __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
-  constexpr int kThreads = 64 * WPB;                 // one row per wave: row group = WPB rows
+  constexpr int kThreads = 64 * WPB;
+  constexpr int kGroupRows = WPB * R;
+  constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   u32x4* xs = reinterpret_cast<u32x4*>(lds);
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  // FP8: each wave keeps its own copy of the current scale row (no barrier
-  // needed) and prefetches the next unit's row into registers meanwhile.
   float* ss = reinterpret_cast<float*>(lds + a.x_lds_bytes) + wv * kRowsMaxKBlocks;
   float spre[kRowsMaxKBlocks / 64];
   auto unit_of = [&](long long u, int& l, int& grp, int& chunk) {
     while (l + 1 < a.nlin && a.lin[l + 1].step_base <= u) ++l;
     const LinDesc& L = a.lin[l];
+    const int groups = (L.N + kGroupRows - 1) / kGroupRows;
     const long long local = u - L.step_base;
-    grp = (int)(local / L.chunks);
-    chunk = (int)(local - (long long)grp * L.chunks);
+    chunk = (int)(local / groups);
+    grp = (int)(local - (long long)chunk * groups);
   };
   auto prefetch_scales = [&](long long u, int l) {
     if (DT == SKINNY_FP8_BS128 && u < a.S) {
       int grp, chunk;
       unit_of(u, l, grp, chunk);
       const LinDesc& L = a.lin[l];
-      const float* src = L.scale + (size_t)((grp * WPB) / kScaleBlock) * L.kblocks;
+      // The row group lies in one 128-row scale block (kGroupRows divides 128).
+      const float* src = L.scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks;
 #pragma unroll
       for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) {
         const int k = 64 * i + lane;
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
   };
   int l = 0;
   int staged_l = -1;
+  int staged_c = -1;
   long long u = blockIdx.x;
   prefetch_scales(u, 0);
   store_scales();
@@ -353,69 +360,97 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
     int grp, chunk;
     unit_of(u, l, grp, chunk);
     const LinDesc& L = a.lin[l];
-    const long long local = (long long)grp * L.chunks + chunk;
     const int spc = (L.spt + L.chunks - 1) / L.chunks;          // segments per chunk
     const int j0 = chunk * spc;
     const int j1 = min(j0 + spc, L.spt);
     const int xcpr = L.K >> 3;                                   // x chunks per token row
-    if (l != staged_l) {                                         // same for all 4 waves
-      __syncthreads();                                           // all done with the old x
-      for (int i = threadIdx.x; i < MT * xcpr; i += kThreads) xs[i] = L.x[i];
+    const int win = spc * kSegChunks * XC;                       // x chunks per token in LDS
+    const int xw0 = j0 * kSegChunks * XC;                        // first x chunk of the window
+    if (l != staged_l || chunk != staged_c) {                    // same for all waves
+      __syncthreads();                                           // all done with the old window
+      const int wlen = min(win, xcpr - xw0);
+      for (int i = threadIdx.x; i < MT * wlen; i += kThreads) {
+        const int m = i / wlen;
+        const int c = i - m * wlen;
+        xs[m * win + c] = L.x[(size_t)m * xcpr + xw0 + c];
+      }
       __syncthreads();
       staged_l = l;
+      staged_c = chunk;
     }
     prefetch_scales(u + a.G, l);
-    const int row = grp * WPB + wv;
-    const bool rowok = row < L.N;
-    const u32x4* wrow = L.w + (size_t)(rowok ? row : 0) * (size_t)L.cpr;
-    float acc[MT];
+    const int row0 = grp * kGroupRows + wv * R;
+    const u32x4* wrow[R];
+    bool rowok[R];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    for (int r = 0; r < R; ++r) {
+      rowok[r] = row0 + r < L.N;
+      wrow[r] = L.w + (size_t)(rowok[r] ? row0 + r : 0) * (size_t)L.cpr;
+    }
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
     for (int j = j0; j < j1; j += U) {
-      u32x4 wq[U];
+      u32x4 wq[U][R];
 #pragma unroll
       for (int v = 0; v < U; ++v) {
-        const int c = (j + v) * kSegChunks + lane;
-        wq[v] = (rowok && (j + v < j1) && c < L.cpr) ? wrow[c] : zero4();
+        const int cw = (j + v) * kSegChunks + lane;
+        const bool ok = (j + v < j1) && cw < L.cpr;
+#pragma unroll
+        for (int r = 0; r < R; ++r) wq[v][r] = (ok && rowok[r]) ? wrow[r][cw] : zero4();
       }
 #pragma unroll
       for (int v = 0; v < U; ++v) {
-        const int c = (j + v) * kSegChunks + lane;
-        const bool ok = (j + v < j1) && c < L.cpr;
+        const int cw = (j + v) * kSegChunks + lane;
+        const bool ok = (j + v < j1) && cw < L.cpr;
+        const int xl = cw * XC - xw0;                            // chunk index in the window
         if (DT == SKINNY_BF16) {
 #pragma unroll
-          for (int m = 0; m < MT; ++m)
-            acc[m] = dot8(ok ? xs[m * xcpr + c] : zero4(), wq[v], acc[m]);
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 xv = ok ? xs[m * win + xl] : zero4();
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = dot8(xv, wq[v][r], acc[r][m]);
+          }
         } else {
-          // Chunk c holds k in [16 c, 16 c + 16): scale block c / 8.
-          const float sc = ok ? ss[c >> 3] : 0.0f;
-          u32x4 b0, b1;
-          e4m3x16_to_bf16(wq[v], b0, b1);
+          // W chunk cw holds k in [16 cw, 16 cw + 16): scale block cw / 8.
+          const float sc = ok ? ss[cw >> 3] : 0.0f;
+          u32x4 b0[R], b1[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) e4m3x16_to_bf16(wq[v][r], b0[r], b1[r]);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            const u32x4 x0 = ok ? xs[m * xcpr + 2 * c] : zero4();
-            const u32x4 x1 = ok ? xs[m * xcpr + 2 * c + 1] : zero4();
-            acc[m] = __builtin_fmaf(sc, dot8(x1, b1, dot8(x0, b0, 0.0f)), acc[m]);
+            const u32x4 x0 = ok ? xs[m * win + xl] : zero4();
+            const u32x4 x1 = ok ? xs[m * win + xl + 1] : zero4();
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              acc[r][m] = __builtin_fmaf(sc, dot8(x1, b1[r], dot8(x0, b0[r], 0.0f)), acc[r][m]);
           }
         }
       }
     }
     // This wave's reads of the current scales are done: install the next unit's.
     store_scales();
-    // 64-lane butterfly; lane 0's sum has a fixed order.
+    // 64-lane butterflies; lane 0's sums have a fixed order.
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[r][m] += __shfl_xor(acc[r][m], off);
     if (lane == 0) {
+      const long long slot = L.slot_base + (long long)grp * L.chunks + chunk;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (L.chunks == 1) {
-          if (rowok) L.y[(size_t)m * L.N + row] = (__bf16)acc[m];
-        } else {
-          a.slots[((size_t)(L.slot_base + local) * MT + m) * WPB + wv] = acc[m];
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (L.chunks == 1) {
+            if (rowok[r]) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
+          } else {
+            a.slots[((size_t)slot * MT + m) * kGroupRows + wv * R + r] = acc[r][m];
+          }
         }
-      }
     }
   }
 }
@@ -558,42 +593,76 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
   return SKINNY_OK;
 }
 
-// Slots for the largest layout: kMaxWaves MFMA workers with 64-row bands.
-size_t workspace_for(int M) {
+// skinny_rows shape per M: R rows per wave (one LDS read of x serves R weight
+// loads, so LDS traffic stays at <= 2 x reads per weight load up to M = 8) and
+// U segments per row in flight, R x U = 8 loads per wave.
+constexpr int rows_r(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : 4; }
+constexpr int rows_u(int M) { return 8 / rows_r(M); }
+constexpr int kRowsXBudget = 64 * 1024;   // LDS for x per workgroup: two workgroups per CU
+constexpr int kRowsMaxM = 8;
+constexpr int kUnitsPerWorker = 16;
+
+// Fewest K-chunks of a linear whose x window (M tokens x chunk) fits the budget.
+int rows_lds_chunks(int dtype, int M, int K) {
+  const int xc = dtype == SKINNY_BF16 ? 1 : 2;
+  const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunks - 1) / kSegChunks;
+  const long long seg_bytes = (long long)M * kSegChunks * xc * 16;   // x bytes per segment
+  const int max_spc = (int)(kRowsXBudget / seg_bytes);
+  if (max_spc < 1) return -1;
+  return (spt + max_spc - 1) / max_spc;
+}
+
+// Most K-chunks the planner may give a linear (LDS need, or a small launch's
+// parallelism with >= U segments per chunk): bounds the workspace slots.
+int rows_max_chunks(int dtype, int M, int K) {
+  const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunks - 1) / kSegChunks;
+  int c = spt / rows_u(M);
+  if (c < 1) c = 1;
+  const int lds = rows_lds_chunks(dtype, M, K);
+  return lds > c ? lds : c;
+}
+
+bool rows_supported(const skinny_linear& L, int M) {
+  if (M > kRowsMaxM) return false;
+  if (L.dtype == SKINNY_FP8_BS128 && (L.K + kScaleBlock - 1) / kScaleBlock > kRowsMaxKBlocks)
+    return false;
+  return rows_lds_chunks(L.dtype, M, L.K) > 0;
+}
+
+// Workspace: the MFMA stream-K slots (8192 waves x 2 slots x 64 rows) or the
+// row kernel's per-chunk slots of one launch group, whichever is larger.
+size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int rows) {
+  long long slots = 0;
+  for (int i = 0; i < count; ++i) {
+    const int c = rows_max_chunks(lin[i]->dtype, M, lin[i]->K);
+    if (c > 1) slots += (long long)((lin[i]->N + rows - 1) / rows) * c;
+  }
+  return (size_t)slots * M * rows * sizeof(float);
+}
+
+size_t mfma_slots_bytes(int M) {
   return (size_t)kMaxWaves * kSlotsPerWorker * (size_t)M * kTileRows * kMaxBandTiles *
          sizeof(float);
 }
 
-// LDS skinny_rows needs for a group: x[M][K] of its widest linear plus, for
-// FP8, one scale row per wave.  Returns -1 when that exceeds a workgroup's
-// LDS (or, for FP8, K exceeds 32768).
-int rows_lds_bytes(const skinny_linear* const* lin, int count, int M, int* x_bytes,
-                   int wpb = kRowsWavesPerBlock) {
-  long long kmax = 0, kbmax = 0;
-  for (int i = 0; i < count; ++i) {
-    if (lin[i]->K > kmax) kmax = lin[i]->K;
-    const long long kb = (lin[i]->K + kScaleBlock - 1) / kScaleBlock;
-    if (kb > kbmax) kbmax = kb;
-  }
-  const long long xb = ((long long)M * kmax * 2 + 15) / 16 * 16;
-  const bool fp8 = lin[0]->dtype == SKINNY_FP8_BS128;
-  if (fp8 && kbmax > kRowsMaxKBlocks) return -1;
-  const long long total = xb + (fp8 ? (long long)wpb * kRowsMaxKBlocks * 4 : 0);
-  if (total > kMaxLds) return -1;
-  *x_bytes = (int)xb;
-  return (int)total;
-}
-
-// Variant choice, measured on MI355X over the Qwen2.5-72B shapes: row
-// streaming (x in LDS) leads for M <= 2 when x fits in LDS; beyond that the
-// LDS reads of x per weight load grow and the MFMA band kernel leads.
-constexpr int kRowsMaxAutoM = 2;
-constexpr int kRowsMaxM = 8;
+// Variant choice, measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers
+// and the TP=8 layer, M = 1..16): row streaming leads for bf16 up to M = 4
+// (6.06 / 5.85 / 5.45 TB/s against 5.60 / 5.54 / 5.29 for MFMA at M = 1 / 2 / 4)
+// and for FP8 at M = 1 (5.62 against 4.98).  Beyond that its dot2 work per
+// weight (M per bf16 pair, plus the FP8 conversion) outgrows the vector ALUs and
+// the MFMA kernel leads (bf16 M = 8: 4.82 against 4.13; FP8 M = 2: 4.89 against
+// 4.79, M = 6: 4.29 against 2.84).
+constexpr int kRowsMaxAutoMBf16 = 4;
+constexpr int kRowsMaxAutoMFp8 = 1;
 
 int auto_variant(const skinny_linear* const* lin, int count, int M) {
-  int xb = 0;
-  if (M <= kRowsMaxAutoM && rows_lds_bytes(lin, count, M, &xb) > 0) return SKINNY_VARIANT_VECTOR;
-  return SKINNY_VARIANT_MFMA;
+  const int cap = lin[0]->dtype == SKINNY_BF16 ? kRowsMaxAutoMBf16 : kRowsMaxAutoMFp8;
+  if (M > cap) return SKINNY_VARIANT_MFMA;
+  for (int i = 0; i < count; ++i)
+    if (!rows_supported(*lin[i], M)) return SKINNY_VARIANT_MFMA;
+  return SKINNY_VARIANT_VECTOR;
 }
 
 typedef void (*main_fn)(LaunchArgs);
@@ -620,10 +689,11 @@ KernelChoice mfma_kernel() {
 template <int DT, int MT>
 KernelChoice rows_kernel() {
   constexpr int WPB = kRowsWavesPerBlock;
-  constexpr int U = MT <= 2 ? kRowsUnroll : kRowsUnroll / 2;
+  constexpr int R = rows_r(MT);
+  static_assert(128 % (WPB * R) == 0, "a row group must sit in one scale block");
   KernelChoice k;
-  k.fn = skinny_rows<DT, MT, U, WPB>;
-  k.band_rows = WPB;
+  k.fn = skinny_rows<DT, MT, rows_u(MT), R, WPB>;
+  k.band_rows = WPB * R;
   k.wpb = WPB;
   k.rows = true;
   return k;
@@ -729,32 +799,36 @@ skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, 
   return SKINNY_OK;
 }
 
-// skinny_rows splits a linear's rows into K-chunks only when the launch is
-// too small to give every workgroup about kUnitsPerWorker units: a row group
-// larger than the target unit size is cut into that many chunks (at most one
-// per 1 KB segment).  Split linears get consecutive workspace slots, one per
-// unit; if they would not fit in the workspace nothing is split.
-constexpr int kUnitsPerWorker = 16;
-void plan_row_chunks(LaunchArgs& a, int count, int G) {
-  const int R = a.band_rows;
-  const long long max_slots = (long long)kMaxWaves * kSlotsPerWorker * kTileRows * kMaxBandTiles / R;
-  long long total = 0;
-  for (int i = 0; i < count; ++i) total += (long long)a.lin[i].N * a.lin[i].cpr * 16;
-  long long target = total / ((long long)kUnitsPerWorker * G);
-  if (target < 1) target = 1;
+// skinny_rows K-chunks per linear: enough for its x window to fit the LDS
+// budget, and, when the launch is too small to give every workgroup about
+// kUnitsPerWorker units, more - but never fewer than U segments per chunk,
+// so each wave keeps R x U loads in flight.  Returns the LDS bytes for x.
+int plan_row_chunks(LaunchArgs& a, int count, int G, int dtype) {
+  const int M = a.M;
+  const int rows = a.band_rows;
+  const int xc = dtype == SKINNY_BF16 ? 1 : 2;
+  long long groups = 0;
+  for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
+  const long long want = (long long)kUnitsPerWorker * G;
+  const long long par = (want + groups - 1) / groups;
   long long slots = 0;
+  int x_bytes = 16;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
-    const long long grp_bytes = (long long)R * d.cpr * 16;
-    long long c = (grp_bytes + target - 1) / target;
+    int c_par = d.spt / rows_u(M);
+    if (c_par < 1) c_par = 1;
+    if (par < c_par) c_par = (int)par;
+    const int c_lds = rows_lds_chunks(dtype, M, d.K);
+    int c = c_par > c_lds ? c_par : c_lds;
     if (c > d.spt) c = d.spt;
-    if (c < 1) c = 1;
-    d.chunks = (int)c;
+    d.chunks = c;
     d.slot_base = slots;
-    if (c > 1) slots += (long long)((d.N + R - 1) / R) * c;
+    if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
+    const int spc = (d.spt + c - 1) / c;
+    const int xb = M * spc * kSegChunks * xc * 16;
+    if (xb > x_bytes) x_bytes = xb;
   }
-  if (slots > max_slots)
-    for (int i = 0; i < count; ++i) a.lin[i].chunks = 1;
+  return x_bytes;
 }
 
 // Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
@@ -773,10 +847,18 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   a.M = M;
   a.slots = slots;
   a.band_rows = k.band_rows;
-  int lds = 0;
+  if (k.rows)
+    for (int i = 0; i < count; ++i)
+      if (!rows_supported(*lin[i], M)) return SKINNY_ERR_UNSUPPORTED;
+  // LDS of skinny_rows: the x budget plus one FP8 scale row per wave.  The
+  // occupancy query uses the full budget so the grid does not depend on the
+  // shapes of the launch.
+  const int lds = k.rows ? kRowsXBudget + (dtype == SKINNY_FP8_BS128
+                                               ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float)
+                                               : 0)
+                         : 0;
+  a.x_lds_bytes = kRowsXBudget;
   if (k.rows) {
-    lds = rows_lds_bytes(lin, count, M, &a.x_lds_bytes);
-    if (lds < 0) return SKINNY_ERR_UNSUPPORTED;
     skinny_status st = ensure_lds(k.fn, lds);
     if (st != SKINNY_OK) return st;
   }
@@ -801,7 +883,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   } else if (k.rows) {
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
-  if (k.rows) plan_row_chunks(a, count, G);
+  if (k.rows) plan_row_chunks(a, count, G, dtype);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
@@ -871,6 +953,17 @@ skinny_status for_each_group(const skinny_linear* lin, int count, Fn&& fn) {
   return SKINNY_OK;
 }
 
+// Workspace a call over these linears needs (pure host arithmetic).
+size_t required_workspace(const skinny_linear* lin, int count, int M) {
+  size_t need = mfma_slots_bytes(M);
+  for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
+    const size_t b = group_slots_bytes(g, n, M, kRowsWavesPerBlock * rows_r(M));
+    if (b > need) need = b;
+    return SKINNY_OK;
+  });
+  return need;
+}
+
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
                   void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr,
                   int event_count = 0) {
@@ -892,19 +985,15 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   }
   if (variant == SKINNY_VARIANT_VECTOR && M > kRowsMaxM) return SKINNY_ERR_UNSUPPORTED;
   if (!ws) return SKINNY_ERR_WORKSPACE;
-  if (ws_bytes < workspace_for(M)) return SKINNY_ERR_WORKSPACE;
+  if (ws_bytes < required_workspace(lin, count, M)) return SKINNY_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
   skinny_status st = check_outputs(lin, count, M, ws, ws_bytes);
   if (st != SKINNY_OK) return st;
   if (events && event_count < 2 * launch_count(lin, count)) return SKINNY_ERR_INVALID_ARG;
-  // A VECTOR plan whose x does not fit in LDS is rejected before anything is enqueued.
-  if (variant == SKINNY_VARIANT_VECTOR) {
-    st = for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
-      int xb = 0;
-      return rows_lds_bytes(g, n, M, &xb) < 0 ? SKINNY_ERR_UNSUPPORTED : SKINNY_OK;
-    });
-    if (st != SKINNY_OK) return st;
-  }
+  // A VECTOR plan the row kernel cannot run is rejected before anything is enqueued.
+  if (variant == SKINNY_VARIANT_VECTOR)
+    for (int i = 0; i < count; ++i)
+      if (!rows_supported(lin[i], M)) return SKINNY_ERR_UNSUPPORTED;
   DeviceInfo d;
   st = device_info(&d);
   if (st != SKINNY_OK) return st;
@@ -926,14 +1015,22 @@ extern "C" {
 size_t skinny_workspace_bytes(int dtype, int M, int N, int K) {
   if (dtype != SKINNY_BF16 && dtype != SKINNY_FP8_BS128) return 0;
   if (M < 1 || M > SKINNY_MAX_M || N < 1 || K < 1) return 0;
-  return workspace_for(M);
+  skinny_linear L;
+  memset(&L, 0, sizeof L);
+  L.dtype = dtype;
+  L.N = N;
+  L.K = K;
+  return required_workspace(&L, 1, M);
 }
 
 size_t skinny_stack_workspace_bytes(const skinny_linear* linears, int count, int M) {
   if (!linears || count < 1 || M < 1 || M > SKINNY_MAX_M) return 0;
-  for (int i = 0; i < count; ++i)
-    if (skinny_workspace_bytes(linears[i].dtype, M, linears[i].N, linears[i].K) == 0) return 0;
-  return workspace_for(M);
+  for (int i = 0; i < count; ++i) {
+    const skinny_linear& L = linears[i];
+    if (L.dtype != SKINNY_BF16 && L.dtype != SKINNY_FP8_BS128) return 0;
+    if (L.N < 1 || L.K < 1) return 0;
+  }
+  return required_workspace(linears, count, M);
 }
 
 skinny_status skinny_gemm_bf16(const void* x, const void* w, void* y, int M, int N, int K,
@@ -1017,9 +1114,10 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   out->variant = auto_variant(group, n, M);
   const KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
-  int lds = 0, xb = 0;
+  int lds = 0;
   if (k.rows) {
-    lds = rows_lds_bytes(group, n, M, &xb);
+    lds = kRowsXBudget +
+          (linears[0].dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
     st = ensure_lds(k.fn, lds);
     if (st != SKINNY_OK) return st;
   }

@@ -36,8 +36,8 @@ def host_codes(y: torch.Tensor) -> np.ndarray:
     return y.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def workspace(M: int) -> torch.Tensor:
-    return torch.empty(sg.workspace_bytes(sg.BF16, M, 1, 8), dtype=torch.uint8, device="cuda")
+def workspace(M: int, N: int = 1, K: int = 8, dtype: int = sg.BF16) -> torch.Tensor:
+    return torch.empty(sg.workspace_bytes(dtype, M, N, K), dtype=torch.uint8, device="cuda")
 
 
 def out(M: int, N: int) -> torch.Tensor:
@@ -47,7 +47,7 @@ def out(M: int, N: int) -> torch.Tensor:
 
 def run_bf16(x, w, M, N, variant=sg.VARIANT_AUTO, waves=0, ws=None):
     xd, wd, yd = dev_bf16(x), dev_bf16(w), out(M, N)
-    ws = workspace(M) if ws is None else ws
+    ws = workspace(M, N, x.shape[1], sg.BF16) if ws is None else ws
     sg.linear_run([sg.make_linear(xd, wd, yd)], M, ws, variant=variant, waves=waves)
     torch.cuda.synchronize()
     return yd
@@ -55,7 +55,7 @@ def run_bf16(x, w, M, N, variant=sg.VARIANT_AUTO, waves=0, ws=None):
 
 def run_fp8(x, q, s, M, N, variant=sg.VARIANT_AUTO, waves=0, ws=None):
     xd, qd, sd, yd = dev_bf16(x), dev_u8(q), dev_f32(s), out(M, N)
-    ws = workspace(M) if ws is None else ws
+    ws = workspace(M, N, x.shape[1], sg.FP8_BS128) if ws is None else ws
     sg.linear_run([sg.make_linear(xd, qd, yd, w_scale=sd)], M, ws, variant=variant, waves=waves)
     torch.cuda.synchronize()
     return yd

@@ -121,7 +121,7 @@ def test_band_rows_and_launch_counts():
         for M in (1, 2, 6, 16):
             assert sg.band_rows(dt, sg.VARIANT_MFMA, M) in (16, 32, 64)
             assert sg.band_rows(dt, sg.VARIANT_AUTO, M) == 0      # depends on the shapes
-        assert sg.band_rows(dt, sg.VARIANT_VECTOR, 8) == 8
+        assert [sg.band_rows(dt, sg.VARIANT_VECTOR, m) for m in (1, 2, 3, 4, 8)] == [8, 8, 16, 16, 32]
         assert sg.band_rows(dt, sg.VARIANT_VECTOR, 9) == 0
     assert sg.band_rows(sg.BF16, 7, 1) == 0 and sg.band_rows(9, 0, 1) == 0
     lin = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)
