@@ -456,32 +456,34 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
 }
 
 // Second pass of skinny_rows: for every output of a split linear, the sum of
-// its K-chunks' partial results in chunk order.
+// its K-chunks' partial results in chunk order.  blockIdx.y is the linear.
 __global__ __launch_bounds__(kBlockThreads) void skinny_rows_combine(const LaunchArgs a) {
+  const LinDesc& L = a.lin[blockIdx.y];
+  if (L.chunks == 1) return;
   const int R = a.band_rows;
-  for (int l = 0; l < a.nlin; ++l) {
-    const LinDesc& L = a.lin[l];
-    if (L.chunks == 1) continue;
-    const long long outs = (long long)a.M * L.N;
-    for (long long i = blockIdx.x * (long long)kBlockThreads + threadIdx.x; i < outs;
-         i += (long long)gridDim.x * kBlockThreads) {
-      const int m = (int)(i / L.N);
-      const int row = (int)(i - (long long)m * L.N);
-      const int grp = row / R;
-      const int rr = row - grp * R;
-      float sum = 0.0f;
-      for (int c = 0; c < L.chunks; ++c)
-        sum += a.slots[((size_t)(L.slot_base + (long long)grp * L.chunks + c) * a.M + m) * R + rr];
-      L.y[(size_t)m * L.N + row] = (__bf16)sum;
-    }
+  const int outs = a.M * L.N;
+  for (int i = blockIdx.x * kBlockThreads + threadIdx.x; i < outs; i += gridDim.x * kBlockThreads) {
+    const int m = i / L.N;
+    const int row = i - m * L.N;
+    const int grp = row / R;
+    const int rr = row - grp * R;
+    const float* p = a.slots + ((size_t)(L.slot_base + (long long)grp * L.chunks) * a.M + m) * R + rr;
+    const size_t stride = (size_t)a.M * R;
+    float sum = 0.0f;
+    for (int c = 0; c < L.chunks; ++c) sum += p[c * stride];
+    L.y[(size_t)m * L.N + row] = (__bf16)sum;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Second pass.  Wave i of workgroup q handles boundary w = 4 q + i: if worker
-// w's first step lies strictly inside a band and no earlier boundary does,
-// the wave adds, for every (token, row) of that band, the contributing
-// workers' slots in increasing worker order and writes y.
+// Second pass of skinny_mfma.  Wave i of workgroup q handles boundary
+// w = 4 q + i: if wave w's first step lies strictly inside a band and no
+// earlier boundary does, the wave adds, for every (token, row) of that band,
+// the contributing waves' slots in increasing wave order and writes y.  The
+// contributors are resolved once; each lane accumulates up to
+// kCombinePerLane outputs (M x band rows <= 16 x 64).
+constexpr int kCombinePerLane = SKINNY_MAX_M * kTileRows * kMaxBandTiles / 64;
+
 __global__ __launch_bounds__(kBlockThreads) void skinny_combine(const LaunchArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -495,22 +497,31 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_combine(const LaunchArgs
   const long long bend = bstart + L.spt;
   if (b == bstart) return;
   if (worker_start(w - 1, a.S, a.G) > bstart) return;
-  // Contributing workers: w - 1 .. last, in order.
-  int last = w;
-  while (last + 1 < a.G && worker_start(last + 1, a.S, a.G) < bend) ++last;
   const int R = a.band_rows;
-  for (int idx = lane; idx < a.M * R; idx += 64) {
-    const int m = idx / R;
-    const int rr = idx - m * R;
-    float sum = 0.0f;
-    for (int v = w - 1; v <= last; ++v) {
-      const long long sv = worker_start(v, a.S, a.G);
-      if (worker_start(v + 1, a.S, a.G) <= sv) continue;    // empty worker
+  const int n = a.M * R;
+  float sum[kCombinePerLane];
+#pragma unroll
+  for (int i = 0; i < kCombinePerLane; ++i) sum[i] = 0.0f;
+  long long sv = worker_start(w - 1, a.S, a.G);
+  for (int v = w - 1; v < a.G && sv < bend; ++v) {
+    const long long ev = worker_start(v + 1, a.S, a.G);
+    if (ev > sv) {                                   // an empty worker wrote nothing
       const int slot = 2 * v + (sv >= bstart ? 0 : 1);
-      sum += a.slots[((size_t)slot * a.M + m) * R + rr];
+      const float* src = a.slots + (size_t)slot * n;
+#pragma unroll
+      for (int i = 0; i < kCombinePerLane; ++i)
+        if (lane + 64 * i < n) sum[i] += src[lane + 64 * i];
     }
-    const int row = p.band * R + rr;
-    if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum;
+    sv = ev;
+  }
+#pragma unroll
+  for (int i = 0; i < kCombinePerLane; ++i) {
+    const int idx = lane + 64 * i;
+    if (idx < n) {
+      const int m = idx / R;
+      const int row = p.band * R + (idx - m * R);
+      if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum[i];
+    }
   }
 }
 
@@ -555,8 +566,9 @@ skinny_status check_linear(const skinny_linear& L, int M) {
   if (L.K % (L.dtype == SKINNY_BF16 ? 8 : 16) != 0) return SKINNY_ERR_UNSUPPORTED;
   if (!aligned(L.w, 16) || !aligned(L.x, 16) || !aligned(L.y, 16)) return SKINNY_ERR_UNSUPPORTED;
   if (L.w_scale && !aligned(L.w_scale, 4)) return SKINNY_ERR_UNSUPPORTED;
-  // Index arithmetic inside the kernels is 32-bit per band and per row.
-  if (L.N > (1 << 30) || L.K > (1 << 28)) return SKINNY_ERR_UNSUPPORTED;
+  // Index arithmetic inside the kernels is 32-bit per band, per row and per
+  // (token, row) output of a linear.
+  if (L.N > (1 << 26) || L.K > (1 << 28)) return SKINNY_ERR_UNSUPPORTED;
   return SKINNY_OK;
 }
 
@@ -905,10 +917,13 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     for (int i = 0; i < count; ++i)
       if (a.lin[i].chunks > 1) outs += (long long)M * a.lin[i].N;
     if (outs > 0) {
-      long long cblocks = (outs + kBlockThreads - 1) / kBlockThreads;
-      if (cblocks > 1024) cblocks = 1024;
-      hipLaunchKernelGGL(skinny_rows_combine, dim3((unsigned)cblocks), dim3(kBlockThreads), 0,
-                         stream, a);
+      long long most = 0;
+      for (int i = 0; i < count; ++i)
+        if (a.lin[i].chunks > 1 && (long long)M * a.lin[i].N > most) most = (long long)M * a.lin[i].N;
+      long long cblocks = (most + kBlockThreads - 1) / kBlockThreads;
+      if (cblocks > 256) cblocks = 256;
+      hipLaunchKernelGGL(skinny_rows_combine, dim3((unsigned)cblocks, count), dim3(kBlockThreads),
+                         0, stream, a);
       if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
     }
   } else if (G > 1) {

@@ -131,3 +131,9 @@ def test_band_rows_and_launch_counts():
     assert sg.launch_count([lin] * 320) == 10
     assert sg.launch_count([lin, fp8, lin]) == 2
     assert sg.lib().skinny_launch_count(None, 1) == 0
+
+
+def test_rejects_shapes_beyond_32_bit_indexing():
+    wsb = sg.workspace_bytes(sg.BF16, 1, 64, 64)
+    assert bf16_call(N=(1 << 26) + 1, wsb=wsb) == UNSUPPORTED
+    assert bf16_call(K=(1 << 28) + 8, wsb=wsb) == UNSUPPORTED
