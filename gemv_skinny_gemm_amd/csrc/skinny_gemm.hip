@@ -10,44 +10,38 @@
 //   splitting the long K dimension lets the whole chip stream weights ("9%
 //   faster GLM-5.3-Flash prefill with GPU-to-GPU IPC (and why TileLang didn't
 //   help)", section "TileLang: twice as fast, and no faster").  The page
-//   splits K into fixed slices per block; here every worker of a persistent
-//   grid takes an equal share of all (band, k-step) work of all linears in the
-//   launch, so one launch streams a whole stack with a single ramp and tail.
+//   splits K into fixed slices per block; here a persistent grid deals the
+//   work units (row group, K-chunk) of all linears in the launch round robin
+//   to its workgroups, so one launch streams a whole stack with a single ramp
+//   and tail, and a launch too small to fill the chip is cut into more
+//   K-chunks.
 //
 // Two main kernels share that decomposition and the second pass:
 //
-//   skinny_rows  (VECTOR variant, small M): a workgroup of 8 waves is the
-//     worker; wave i streams row 8g + i of row group g, lane l reading bytes
-//     [16 l, 16 l + 16) of each 1 KB segment of the row, so every wave reads
-//     its row front to back in 1 KB coalesced loads.  x (all K) sits in LDS,
-//     shared by the 8 waves, with each wave's FP8 scale row beside it.
-//     v_dot2_f32_bf16 accumulates in fp32; a 64-lane butterfly ends each row.
-//     Measured on MI355X, one contiguous stream per wave sustains ~6.3 TB/s,
-//     against ~5.8 TB/s for 16 interleaved rows per wave.  Units (row group,
-//     K-chunk) are dealt round robin rather than as contiguous shares.
+//   skinny_rows  (VECTOR variant, small M): wave i of a workgroup streams
+//     its rows of the row group front to back, lane l reading bytes
+//     [16 l, 16 l + 16) of each 1 KB segment; x of the current K-chunk sits in
+//     LDS, shared by the workgroup.  v_dot2_f32_bf16 accumulates in fp32 and
+//     a 64-lane butterfly ends each row.  Measured on MI355X, one contiguous
+//     stream per wave sustains ~6.3 TB/s.
 //
-//   skinny_mfma  (MFMA variant, any M): a wave is the worker and streams a
-//     band of T tiles of 16 rows; per k-step lane l reads 16 bytes of row
-//     (l % 16), chunk 4 j + (l / 16) of every tile - the B-operand layout of
-//     v_mfma_f32_16x16x32_bf16 - and one 16-byte x load (the A operand, token
-//     l % 16) serves the T MFMAs.  FP8 chunks are converted to bf16 in
-//     registers (exact) and each k-step's partial product is scaled by its
-//     block scale in fp32.
+//   skinny_tiles (MFMA variant): each wave streams 16 rows in whole cache
+//     lines (512 contiguous bytes per row per load), turns them around
+//     through a private LDS tile into the B-operand layout of
+//     v_mfma_f32_16x16x32_bf16, and reads the A operand (x, token = lane % 16)
+//     from LDS.  The matrix cores make the arithmetic per weight independent
+//     of M, which the vector path's is not.
 //
-//   skinny_mfma numbers its k-steps (linear, band, step); wave w of G streams
-//   steps [w*S/G, (w+1)*S/G).  A band one wave covers entirely is written
-//   straight to y.  A band cut by a wave boundary has each contributing wave
-//   write fp32 partial sums to a fixed workspace slot (slot 2w for the wave's
-//   first band, 2w+1 for its last), and skinny_combine adds the slots in wave
-//   order.  skinny_rows cuts a small launch's row groups into fixed K-chunks,
-//   one slot per chunk, and skinny_rows_combine adds them in chunk order.
-//   Either way the second pass is deterministic and uses no atomics.
+//   A linear cut into K-chunks has each unit write fp32 partial sums to its
+//   own workspace slot; skinny_combine adds a row's slots in chunk order.
+//   The second pass is deterministic and uses no atomics.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "skinny_gemm.h"
 
@@ -58,15 +52,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileRows = 16;
-constexpr int kMaxBandTiles = 4;
-constexpr int kSegChunks = 64;          // 16-byte chunks per 1 KB row segment
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = 64 * kWavesPerBlock;
+constexpr int kTileRows = 16;          // rows of one MFMA B operand
+constexpr int kSegChunks = 64;          // 16-byte chunks per 1 KB row segment (skinny_rows)
+constexpr int kCombineThreads = 256;
 constexpr int kMaxWaves = 8192;         // 256 CUs x 32 resident waves
-constexpr int kSlotsPerWorker = 2;
 constexpr int kScaleBlock = 128;
-constexpr int kMaxLds = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kRowsMaxKBlocks = 256;    // skinny_rows FP8: K <= 32768
 // skinny_rows shape, measured on MI355X over the Qwen2.5-72B shapes: 8 waves
 // per workgroup share one copy of x, 8 segments per wave in flight, up to 32
@@ -82,29 +72,24 @@ struct LinDesc {
   int N;
   int K;
   int cpr;               // 16-byte chunks per W row
-  int spt;               // steps per band
+  int spt;               // segments per W row (1 KB for skinny_rows, 512 B for skinny_tiles)
   int kblocks;           // ceil(K / 128)
-  int chunks;            // skinny_rows: K-chunks per row group (1 = not split)
-  long long step_base;   // global index of this linear's first step (or unit)
-  long long slot_base;   // skinny_rows: first partial slot of a split linear
+  int chunks;            // K-chunks per row group (1 = not split)
+  long long unit_base;   // index of this linear's first unit in the launch
+  long long slot_base;   // first partial slot of a split linear
 };
 
 struct LaunchArgs {
   int nlin;
   int M;
-  int G;                 // workers (waves for skinny_mfma, workgroups for skinny_rows)
-  int band_rows;         // rows per band: 16 T, or skinny_rows' waves per workgroup
-  long long S;           // total steps (skinny_mfma) or units (skinny_rows) of the launch
-  float* slots;          // fp32 partial sums: [2 G][M][band_rows] (skinny_mfma),
-                         // [unit][M][band_rows] (skinny_rows)
-  int x_lds_bytes;       // skinny_rows: bytes of LDS for x; scales follow
+  int G;                 // workgroups of the persistent grid
+  int band_rows;         // rows per row group
+  long long S;           // units of the launch
+  float* slots;          // fp32 partial sums [slot][M][band_rows], one slot per split unit
+  int x_lds_bytes;       // LDS bytes for x; the kernel's other LDS follows
   int pad;
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
-
-__device__ __forceinline__ long long worker_start(long long w, long long S, long long G) {
-  return w * S / G;
-}
 
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) {
   return __builtin_bit_cast(bf16x2, u);
@@ -141,160 +126,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Locates the band of step s: linear index l (advanced in place), band index,
-// step within the band and the band's first step.
-struct BandPos {
-  int band;
-  int j;
-  long long begin;
-};
-
-__device__ __forceinline__ BandPos band_of(const LaunchArgs& a, int& l, long long s) {
-  while (l + 1 < a.nlin && a.lin[l + 1].step_base <= s) ++l;
-  const LinDesc& L = a.lin[l];
-  const long long local = s - L.step_base;
-  BandPos p;
-  p.band = (int)(local / L.spt);
-  p.j = (int)(local - (long long)p.band * L.spt);
-  p.begin = L.step_base + (long long)p.band * L.spt;
-  return p;
-}
-
-// ---------------------------------------------------------------------------
-// skinny_mfma: steps [j0, j1) of one band.  Per lane: row r = lane % 16 of
-// each tile and chunk group g = lane / 16; step j reads chunk 4 j + g of
-// those rows.  A batch of U steps is loaded (W for all T tiles, the x chunk
-// once) before it is used; with PIPE the next batch's loads are issued before
-// the current batch is consumed.  XC = 16-byte x chunks per W chunk.
-
-template <int DT, int T, int U>
-struct MfmaBatch {
-  static constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;
-  u32x4 w[U][T];
-  u32x4 x[U][XC];
-};
-
-template <int DT, int T, int U>
-__device__ __forceinline__ void mfma_load(MfmaBatch<DT, T, U>& b, const LinDesc& L,
-                                          const u32x4* const (&wrow)[T], const bool (&rowok)[T],
-                                          const u32x4* xrow, bool tokok, int j, int j1, int g) {
-  constexpr int XC = MfmaBatch<DT, T, U>::XC;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = (j + u) * 4 + g;
-    const bool ok = (j + u < j1) && (c < L.cpr);
-#pragma unroll
-    for (int t = 0; t < T; ++t) b.w[u][t] = (ok && rowok[t]) ? wrow[t][c] : zero4();
-#pragma unroll
-    for (int h = 0; h < XC; ++h) b.x[u][h] = (ok && tokok) ? xrow[XC * c + h] : zero4();
-  }
-}
-
-// D[m][n] += x[m][k] W[n][k] over 32 k per instruction; A is the token tile
-// (lane l supplies token l % 16, zero for tokens >= M), B a weight tile.
-// Lane l ends holding D[4 (l / 16) + i][l % 16], i = 0..3, for each tile.
-template <int DT, int T, int U>
-__device__ __forceinline__ void mfma_compute(const MfmaBatch<DT, T, U>& b, f32x4 (&acc)[T],
-                                             const float* srow, int j, int j1) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (DT == SKINNY_BF16) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) acc[t] = mfma_bf16(b.x[u][0], b.w[u][t], acc[t]);
-    } else {
-      // Step j covers k in [64 j, 64 j + 64): one 128-wide scale block, j / 2.
-      const float s = (j + u < j1) ? srow[(j + u) >> 1] : 0.0f;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        u32x4 b0, b1;
-        e4m3x16_to_bf16(b.w[u][t], b0, b1);
-        f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-        p = mfma_bf16(b.x[u][0], b0, p);
-        p = mfma_bf16(b.x[u][1], b1, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(s, p[i], acc[t][i]);
-      }
-    }
-  }
-}
-
-template <int DT, int T, int U, bool PIPE>
-__global__ __launch_bounds__(kBlockThreads) void skinny_mfma(const LaunchArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (w >= a.G) return;
-  const long long s0 = worker_start(w, a.S, a.G);
-  const long long s1 = worker_start(w + 1, a.S, a.G);
-  if (s0 >= s1) return;
-  const int M = a.M;
-  constexpr int kBandRows = kTileRows * T;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  int l = 0;
-  long long s = s0;
-  bool first = true;
-  while (s < s1) {
-    const BandPos p = band_of(a, l, s);
-    const LinDesc& L = a.lin[l];
-    const long long band_end = p.begin + L.spt;
-    const int j0 = p.j;
-    const int j1 = (int)((s1 < band_end ? s1 : band_end) - p.begin);
-    const bool whole = (j0 == 0) && (j1 == L.spt);
-    const u32x4* wrow[T];
-    bool rowok[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int row = p.band * kBandRows + t * kTileRows + r;
-      rowok[t] = row < L.N;
-      wrow[t] = L.w + (size_t)(rowok[t] ? row : 0) * (size_t)L.cpr;
-    }
-    const bool tokok = r < M;                              // A-operand row = lane % 16
-    const u32x4* xrow = L.x + (size_t)(tokok ? r : 0) * (size_t)(L.K >> 3);
-    // All rows of a band lie in one 128-row scale block (16 T divides 128).
-    const float* srow = (DT == SKINNY_FP8_BS128)
-                            ? L.scale + (size_t)((p.band * kBandRows) / kScaleBlock) * L.kblocks
-                            : nullptr;
-    f32x4 acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (PIPE) {
-      MfmaBatch<DT, T, U> b0, b1;
-      mfma_load(b0, L, wrow, rowok, xrow, tokok, j0, j1, g);
-      for (int j = j0; j < j1; j += 2 * U) {
-        mfma_load(b1, L, wrow, rowok, xrow, tokok, j + U, j1, g);
-        mfma_compute(b0, acc, srow, j, j1);
-        mfma_load(b0, L, wrow, rowok, xrow, tokok, j + 2 * U, j1, g);
-        mfma_compute(b1, acc, srow, j + U, j1);
-      }
-    } else {
-      for (int j = j0; j < j1; j += U) {
-        MfmaBatch<DT, T, U> b0;
-        mfma_load(b0, L, wrow, rowok, xrow, tokok, j, j1, g);
-        mfma_compute(b0, acc, srow, j, j1);
-      }
-    }
-    float* slot = a.slots + (size_t)(2 * w + (first ? 0 : 1)) * M * kBandRows;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int rr = t * kTileRows + r;
-      const int row = p.band * kBandRows + rr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < M) {
-          if (whole) {
-            if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[t][i];
-          } else {
-            slot[m * kBandRows + rr] = acc[t][i];
-          }
-        }
-      }
-    }
-    s = band_end < s1 ? band_end : s1;
-    first = false;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
 // wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
@@ -323,10 +154,10 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
   float* ss = reinterpret_cast<float*>(lds + a.x_lds_bytes) + wv * kRowsMaxKBlocks;
   float spre[kRowsMaxKBlocks / 64];
   auto unit_of = [&](long long u, int& l, int& grp, int& chunk) {
-    while (l + 1 < a.nlin && a.lin[l + 1].step_base <= u) ++l;
+    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
     const LinDesc& L = a.lin[l];
     const int groups = (L.N + kGroupRows - 1) / kGroupRows;
-    const long long local = u - L.step_base;
+    const long long local = u - L.unit_base;
     chunk = (int)(local / groups);
     grp = (int)(local - (long long)chunk * groups);
   };
@@ -455,14 +286,235 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
   }
 }
 
-// Second pass of skinny_rows: for every output of a split linear, the sum of
-// its K-chunks' partial results in chunk order.  blockIdx.y is the linear.
-__global__ __launch_bounds__(kBlockThreads) void skinny_rows_combine(const LaunchArgs a) {
+// ---------------------------------------------------------------------------
+// skinny_tiles: matrix cores fed by rows streamed front to back.
+//
+// The MFMA B operand wants lane l to hold 16 bytes of W row (l % 16), so
+// loading it straight from HBM gives 64-byte pieces of 16 rows per wave
+// instruction: half cache lines, measured on MI355X to stream at most
+// ~5.8 TB/s.  Here every global load covers whole lines of two rows (lanes
+// 0-31 one row, 32-63 the next, 512 contiguous bytes each) and each wave
+// turns its 16 rows around through a private LDS tile, skewed by 16 bytes
+// per row so the operand reads hit 16 different bank groups.
+//
+// A workgroup of WPB waves handles a row group of 16 WPB rows (inside one
+// 128-row FP8 scale block); wave i owns the 16 rows from 16 i.  Work
+// units are (K-chunk, row group), chunk-major within a linear, dealt round
+// robin over the workgroups as in skinny_rows, with x[M][window] of the
+// current (linear, K-chunk) in LDS (token rows padded by one chunk).  A
+// segment is 512 bytes of each of the wave's rows: 8 loads, 8 LDS writes,
+// then 8 k-steps of one operand read each; bf16 needs one MFMA per k-step,
+// FP8 two (its 16-byte chunk holds 16 k) and the block scale is applied in
+// fp32 to each 128-k partial sum.  The next segment's loads are issued
+// before the current one is consumed.
+// Shape measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers and the
+// TP=8 layer, M = 1..16): 512-byte segments, 4 waves per workgroup and two
+// workgroups per CU beat 256- or 1024-byte segments and 8-wave workgroups.
+constexpr int kSegBytesT = 512;                       // bytes of one row per segment
+constexpr int kSegChunksT = kSegBytesT / 16;          // chunks
+constexpr int kRowStrideT = kSegBytesT + 16;          // LDS bytes per staged row
+constexpr int kLoadsT = kTileRows * kSegChunksT / 64; // wave loads per segment
+constexpr int kLanesPerRowT = kSegChunksT;            // lanes of a load on one row
+constexpr int kRowsPerLoadT = 64 / kLanesPerRowT;
+constexpr int kStepsT = kSegChunksT / 4;              // k-steps per segment
+constexpr int kTilesWavesPerBlock = 4;
+constexpr int kTilesLds = 80 * 1024;                  // two workgroups per 160 KB CU
+constexpr int kTilesWBytes = kTilesWavesPerBlock * kTileRows * kRowStrideT;
+constexpr int kTilesXBudget = kTilesLds - kTilesWBytes;
+
+template <int DT>
+struct TileSeg {
+  u32x4 w[kLoadsT];
+  float sc;              // FP8: lane i holds the scale of block (seg blocks) j + i % (seg blocks)
+};
+
+template <int DT, int WPB>
+__global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
+  constexpr int kThreads = 64 * WPB;
+  constexpr int kGroupRows = kTileRows * WPB;
+  constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  unsigned char* wt = lds + a.x_lds_bytes + wv * (kTileRows * kRowStrideT);
+  const int n = lane & 15;                             // operand row: token (A) / W row (B)
+  const int g = lane >> 4;                             // operand k-group
+  const int lrow = lane / kLanesPerRowT;              // load q: row q kRowsPerLoadT + lrow
+  const int lchunk = lane % kLanesPerRowT;             // load: chunk of the segment
+  int l = 0, staged_l = -1, staged_c = -1;
+  for (long long u = blockIdx.x; u < a.S; u += a.G) {
+    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
+    const LinDesc& L = a.lin[l];
+    // Units are row-group-major: with a power-of-two chunk count dividing
+    // the grid, workgroup b keeps K-chunk (b - base) % chunks all linear long.
+    const long long local = u - L.unit_base;
+    const int grp = (int)(local / L.chunks);
+    const int chunk = (int)(local - (long long)grp * L.chunks);
+    // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
+    // empty (chunks <= spt) and none is longer than the window.
+    const int spc = (L.spt + L.chunks - 1) / L.chunks;           // window, in segments
+    const int j0 = (int)((long long)chunk * L.spt / L.chunks);
+    const int j1 = (int)((long long)(chunk + 1) * L.spt / L.chunks);
+    const int xcpr = L.K >> 3;                                   // x chunks per token
+    const int win = spc * kSegChunksT * XC;                      // x chunks per token in LDS
+    const int xstride = win + 1;
+    const int xw0 = j0 * kSegChunksT * XC;
+    if (l != staged_l || chunk != staged_c) {                    // same for all waves
+      __syncthreads();
+      // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
+      // then a zero row that lanes of absent tokens read.
+      const int wlen = min(win, xcpr - xw0);
+      const int n = a.M * wlen;
+      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = min(b + r * kThreads, n - 1);
+          const int m = i / wlen;
+          v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = b + r * kThreads;
+          const int m = i / wlen;
+          if (i < n) xs[m * xstride + (i - m * wlen)] = v[r];
+        }
+      }
+      const int pad = win - wlen;
+      for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
+        const int m = i / pad;
+        xs[m * xstride + wlen + (i - m * pad)] = zero4();
+      }
+      for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
+      __syncthreads();
+      staged_l = l;
+      staged_c = chunk;
+    }
+    const int row0 = grp * kGroupRows + wv * kTileRows;
+    if (row0 >= L.N) continue;                                   // a tile wholly past N
+    // Rows past N read row N - 1 instead: a B column only feeds its own
+    // output, which is not written.
+    const u32x4* src[kLoadsT];
+#pragma unroll
+    for (int q = 0; q < kLoadsT; ++q)
+      src[q] = L.w + (size_t)min(row0 + kRowsPerLoadT * q + lrow, L.N - 1) * (size_t)L.cpr;
+    const float* srow = DT == SKINNY_FP8_BS128
+                            ? L.scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks
+                            : nullptr;
+    const u32x4* xrow = xs + (n < a.M ? n : a.M) * xstride;
+    // FULL: segment j lies wholly inside the row (plain loads, no selects, so
+    // the compiler keeps them unconditional and the waits exact).
+    auto load = [&](TileSeg<DT>& s, int j, auto full) {
+      const int c = j * kSegChunksT + lchunk;
+      if constexpr (decltype(full)::value) {
+#pragma unroll
+        for (int q = 0; q < kLoadsT; ++q) s.w[q] = src[q][c];
+        // Keep the loads ahead of the previous segment's work.
+        __builtin_amdgcn_sched_barrier(0);
+      } else {                                                   // the row's ragged end
+        const bool cok = c < L.cpr;
+#pragma unroll
+        for (int q = 0; q < kLoadsT; ++q) s.w[q] = cok ? src[q][cok ? c : 0] : zero4();
+      }
+      if (DT == SKINNY_FP8_BS128) {
+        // Blocks past K cover only zero weights; clamping keeps the read in bounds.
+        constexpr int kSegBlocks = kSegBytesT / kScaleBlock;     // FP8: 1 byte per k
+        const int kb = min(kSegBlocks * j + (lane % kSegBlocks), L.kblocks - 1);
+        s.sc = srow[kb];
+      }
+    };
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto consume = [&](const TileSeg<DT>& s, int j) {
+#pragma unroll
+      for (int q = 0; q < kLoadsT; ++q)
+        *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kRowStrideT + lchunk * 16) =
+            s.w[q];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < kStepsT; ++t) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(wt + n * kRowStrideT + (4 * t + g) * 16);
+        const int xc = (j * kSegChunksT + 4 * t + g) * XC - xw0;  // x chunk in the window
+        if (DT == SKINNY_BF16) {
+          acc = mfma_bf16(xrow[xc], b, acc);
+        } else {
+          const u32x4 x0 = xrow[xc];
+          const u32x4 x1 = xrow[xc + 1];
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(b, b0, b1);
+          p = mfma_bf16(x0, b0, p);
+          p = mfma_bf16(x1, b1, p);
+          if (t & 1) {
+            // Steps 2 i and 2 i + 1 cover the 128 k of the segment's block i.
+            const float sc = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.sc), t >> 1));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, p[i], acc[i]);
+            p = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    using Full = std::true_type;
+    using Ragged = std::false_type;
+    // Whole segments [j0, jw) run two buffers deep; a ragged last segment of
+    // the row comes after them.
+    const int jw = (j1 == L.spt && L.cpr % kSegChunksT != 0) ? j1 - 1 : j1;
+    TileSeg<DT> s0, s1;
+    if (j0 < jw) {
+      int j = j0;
+      load(s0, j, Full{});
+      for (; j + 2 < jw; j += 2) {
+        load(s1, j + 1, Full{});
+        consume(s0, j);
+        load(s0, j + 2, Full{});
+        consume(s1, j + 1);
+      }
+      if (j + 2 == jw) {
+        load(s1, j + 1, Full{});
+        consume(s0, j);
+        consume(s1, j + 1);
+      } else {
+        consume(s0, j);
+      }
+    }
+    if (jw < j1) {
+      load(s0, jw, Ragged{});
+      consume(s0, jw);
+    }
+    // Lane (n, g) holds D[4 g + i][n]: token 4 g + i, row row0 + n.
+    const int row = row0 + n;
+    const long long slot = L.slot_base + (long long)grp * L.chunks + chunk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < a.M) {
+        if (L.chunks == 1) {
+          if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[i];
+        } else {
+          a.slots[((size_t)slot * a.M + m) * kGroupRows + wv * kTileRows + n] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Second pass: for every output of a split linear, the sum of its K-chunks'
+// partial results in chunk order.  blockIdx.y is the linear.
+__global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchArgs a) {
   const LinDesc& L = a.lin[blockIdx.y];
   if (L.chunks == 1) return;
   const int R = a.band_rows;
   const int outs = a.M * L.N;
-  for (int i = blockIdx.x * kBlockThreads + threadIdx.x; i < outs; i += gridDim.x * kBlockThreads) {
+  for (int i = blockIdx.x * kCombineThreads + threadIdx.x; i < outs;
+       i += gridDim.x * kCombineThreads) {
     const int m = i / L.N;
     const int row = i - m * L.N;
     const int grp = row / R;
@@ -472,56 +524,6 @@ __global__ __launch_bounds__(kBlockThreads) void skinny_rows_combine(const Launc
     float sum = 0.0f;
     for (int c = 0; c < L.chunks; ++c) sum += p[c * stride];
     L.y[(size_t)m * L.N + row] = (__bf16)sum;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Second pass of skinny_mfma.  Wave i of workgroup q handles boundary
-// w = 4 q + i: if wave w's first step lies strictly inside a band and no
-// earlier boundary does, the wave adds, for every (token, row) of that band,
-// the contributing waves' slots in increasing wave order and writes y.  The
-// contributors are resolved once; each lane accumulates up to
-// kCombinePerLane outputs (M x band rows <= 16 x 64).
-constexpr int kCombinePerLane = SKINNY_MAX_M * kTileRows * kMaxBandTiles / 64;
-
-__global__ __launch_bounds__(kBlockThreads) void skinny_combine(const LaunchArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (w == 0 || w >= a.G) return;
-  const long long b = worker_start(w, a.S, a.G);
-  if (b >= a.S) return;
-  int l = 0;
-  const BandPos p = band_of(a, l, b);
-  const LinDesc& L = a.lin[l];
-  const long long bstart = p.begin;
-  const long long bend = bstart + L.spt;
-  if (b == bstart) return;
-  if (worker_start(w - 1, a.S, a.G) > bstart) return;
-  const int R = a.band_rows;
-  const int n = a.M * R;
-  float sum[kCombinePerLane];
-#pragma unroll
-  for (int i = 0; i < kCombinePerLane; ++i) sum[i] = 0.0f;
-  long long sv = worker_start(w - 1, a.S, a.G);
-  for (int v = w - 1; v < a.G && sv < bend; ++v) {
-    const long long ev = worker_start(v + 1, a.S, a.G);
-    if (ev > sv) {                                   // an empty worker wrote nothing
-      const int slot = 2 * v + (sv >= bstart ? 0 : 1);
-      const float* src = a.slots + (size_t)slot * n;
-#pragma unroll
-      for (int i = 0; i < kCombinePerLane; ++i)
-        if (lane + 64 * i < n) sum[i] += src[lane + 64 * i];
-    }
-    sv = ev;
-  }
-#pragma unroll
-  for (int i = 0; i < kCombinePerLane; ++i) {
-    const int idx = lane + 64 * i;
-    if (idx < n) {
-      const int m = idx / R;
-      const int row = p.band * R + (idx - m * R);
-      if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)sum[i];
-    }
   }
 }
 
@@ -643,30 +645,61 @@ bool rows_supported(const skinny_linear& L, int M) {
   return rows_lds_chunks(L.dtype, M, L.K) > 0;
 }
 
-// Workspace: the MFMA stream-K slots (8192 waves x 2 slots x 64 rows) or the
-// row kernel's per-chunk slots of one launch group, whichever is larger.
-size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int rows) {
+// skinny_tiles: fewest K-chunks of a linear whose x window fits the LDS
+// budget (token rows padded by one chunk), or -1 if not even one segment fits.
+constexpr int kTilesMinSegs = 4;          // segments per chunk when splitting for parallelism
+int tiles_lds_chunks(int dtype, int M, int K) {
+  const int xc = dtype == SKINNY_BF16 ? 1 : 2;
+  const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
+  const int max_spc = (kTilesXBudget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
+  if (max_spc < 1) return -1;
+  return (spt + max_spc - 1) / max_spc;
+}
+
+// K-chunks of a linear with spt segments: at least c_lds (LDS) and, up to
+// spt / kTilesMinSegs, par (parallelism of a small launch); rounded up to a
+// power of two, which divides the persistent grid, so every workgroup keeps
+// one K-chunk - one x window - for the whole linear.
+int tiles_chunks(int spt, int c_lds, long long par) {
+  int c_par = spt / kTilesMinSegs;
+  if (c_par < 1) c_par = 1;
+  if (par < c_par) c_par = (int)par;
+  const int need = c_par > c_lds ? c_par : c_lds;
+  int c = 1;
+  while (c < need) c *= 2;
+  return c <= spt ? c : need;
+}
+
+int tiles_max_chunks(int dtype, int M, int K) {
+  const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
+  return tiles_chunks(spt, tiles_lds_chunks(dtype, M, K), 1LL << 40);
+}
+
+bool tiles_supported(const skinny_linear& L, int M) {
+  return tiles_lds_chunks(L.dtype, M, L.K) > 0;
+}
+
+// Workspace slots of one launch group: every linear at the most K-chunks the
+// planner may give it, for the kernel of this variant (rows per row group).
+size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int variant) {
+  const int rows = variant == SKINNY_VARIANT_MFMA ? kTileRows * kTilesWavesPerBlock
+                                                  : kRowsWavesPerBlock * rows_r(M);
   long long slots = 0;
   for (int i = 0; i < count; ++i) {
-    const int c = rows_max_chunks(lin[i]->dtype, M, lin[i]->K);
+    const int c = variant == SKINNY_VARIANT_MFMA ? tiles_max_chunks(lin[i]->dtype, M, lin[i]->K)
+                                                 : rows_max_chunks(lin[i]->dtype, M, lin[i]->K);
     if (c > 1) slots += (long long)((lin[i]->N + rows - 1) / rows) * c;
   }
   return (size_t)slots * M * rows * sizeof(float);
 }
 
-size_t mfma_slots_bytes(int M) {
-  return (size_t)kMaxWaves * kSlotsPerWorker * (size_t)M * kTileRows * kMaxBandTiles *
-         sizeof(float);
-}
-
 // Variant choice, measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers
-// and the TP=8 layer, M = 1..16): row streaming leads for bf16 up to M = 4
-// (6.06 / 5.85 / 5.45 TB/s against 5.60 / 5.54 / 5.29 for MFMA at M = 1 / 2 / 4)
-// and for FP8 at M = 1 (5.62 against 4.98).  Beyond that its dot2 work per
-// weight (M per bf16 pair, plus the FP8 conversion) outgrows the vector ALUs and
-// the MFMA kernel leads (bf16 M = 8: 4.82 against 4.13; FP8 M = 2: 4.89 against
-// 4.79, M = 6: 4.29 against 2.84).
-constexpr int kRowsMaxAutoMBf16 = 4;
+// and the TP=8 layer): see kRowsMaxAutoM*.  Row streaming keeps one contiguous
+// stream per wave, but its vector work per weight grows with M (and FP8 adds
+// a half-rate conversion); the matrix-core kernel's does not.
+constexpr int kRowsMaxAutoMBf16 = 2;
 constexpr int kRowsMaxAutoMFp8 = 1;
 
 int auto_variant(const skinny_linear* const* lin, int count, int M) {
@@ -681,20 +714,20 @@ typedef void (*main_fn)(LaunchArgs);
 
 struct KernelChoice {
   main_fn fn = nullptr;
-  int band_rows = 0;
-  int wpb = kWavesPerBlock;    // waves per workgroup
-  bool rows = false;
+  int band_rows = 0;           // rows per row group
+  int wpb = 0;                 // waves per workgroup
+  bool tiles = false;          // skinny_tiles (else skinny_rows)
 };
 
-// MFMA band shape per dtype: T tiles per band, U k-steps per batch, PIPE.
 template <int DT>
-KernelChoice mfma_kernel() {
-  constexpr int T = 2, U = 8;
-  constexpr bool PIPE = false;
-  static_assert(T <= kMaxBandTiles && (kTileRows * T) <= kScaleBlock, "band too tall");
+KernelChoice tiles_kernel() {
+  constexpr int WPB = kTilesWavesPerBlock;
+  static_assert(kScaleBlock % (kTileRows * WPB) == 0, "a row group must sit in one scale block");
   KernelChoice k;
-  k.fn = skinny_mfma<DT, T, U, PIPE>;
-  k.band_rows = kTileRows * T;
+  k.fn = skinny_tiles<DT, WPB>;
+  k.band_rows = kTileRows * WPB;
+  k.wpb = WPB;
+  k.tiles = true;
   return k;
 }
 
@@ -702,18 +735,17 @@ template <int DT, int MT>
 KernelChoice rows_kernel() {
   constexpr int WPB = kRowsWavesPerBlock;
   constexpr int R = rows_r(MT);
-  static_assert(128 % (WPB * R) == 0, "a row group must sit in one scale block");
+  static_assert(kScaleBlock % (WPB * R) == 0, "a row group must sit in one scale block");
   KernelChoice k;
   k.fn = skinny_rows<DT, MT, rows_u(MT), R, WPB>;
   k.band_rows = WPB * R;
   k.wpb = WPB;
-  k.rows = true;
   return k;
 }
 
 template <int DT>
 KernelChoice pick_dt(int variant, int M) {
-  if (variant == SKINNY_VARIANT_MFMA) return mfma_kernel<DT>();
+  if (variant == SKINNY_VARIANT_MFMA) return tiles_kernel<DT>();
   switch (M) {
     case 1: return rows_kernel<DT, 1>();
     case 2: return rows_kernel<DT, 2>();
@@ -734,9 +766,8 @@ KernelChoice pick(int dtype, int variant, int M) {
 
 // Persistent grid size: every worker must be resident at once for the equal
 // shares to finish together, so take what the occupancy query allows for the
-// kernel (and its LDS), capped at kTargetWavesPerCU waves per CU.  Query
+// kernel (and its LDS), capped at kTargetRowsWavesPerCU waves per CU.  Query
 // results are cached per (device, kernel, LDS bytes).
-constexpr int kTargetWavesPerCU = 16;
 constexpr int kOccCache = 256;
 struct OccEntry {
   int dev;
@@ -795,20 +826,28 @@ skinny_status ensure_lds(main_fn fn, int bytes) {
   return SKINNY_OK;
 }
 
-// Workers of the persistent grid: waves for skinny_mfma, workgroups for skinny_rows.
+// Workgroups of the persistent grid: as many as are resident at once.
 skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, int* workers) {
   int bpc = 0;
   skinny_status st = blocks_per_cu(k.fn, lds, 64 * k.wpb, &bpc);
   if (st != SKINNY_OK) return st;
   if (bpc < 1) return SKINNY_ERR_UNSUPPORTED;
   int waves_per_cu = bpc * k.wpb;
-  const int cap = k.rows ? kTargetRowsWavesPerCU : kTargetWavesPerCU;
-  if (waves_per_cu > cap) waves_per_cu = cap < k.wpb ? k.wpb : cap;
+  if (waves_per_cu > kTargetRowsWavesPerCU)
+    waves_per_cu = kTargetRowsWavesPerCU < k.wpb ? k.wpb : kTargetRowsWavesPerCU;
   long long g = (long long)d.cus * waves_per_cu;
   if (g > kMaxWaves) g = kMaxWaves;
-  if (k.rows) g /= k.wpb;
-  *workers = (int)g;
+  *workers = (int)(g / k.wpb);
   return SKINNY_OK;
+}
+
+// LDS bytes a main kernel is launched with.  skinny_rows: the x budget plus one
+// FP8 scale row per wave; the occupancy query uses the full budget so the grid
+// does not depend on the shapes of the launch.
+int kernel_lds(const KernelChoice& k, int dtype) {
+  if (k.tiles) return kTilesLds;
+  return kRowsXBudget +
+         (dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
 }
 
 // skinny_rows K-chunks per linear: enough for its x window to fit the LDS
@@ -843,9 +882,28 @@ int plan_row_chunks(LaunchArgs& a, int count, int G, int dtype) {
   return x_bytes;
 }
 
+// skinny_tiles K-chunks per linear: enough for the x window to fit the LDS
+// budget and, when the launch is too small to give every workgroup about
+// kUnitsPerWorker units, more - but at least kTilesMinSegs segments each.
+void plan_tile_chunks(LaunchArgs& a, int count, int G, int dtype) {
+  const int rows = a.band_rows;
+  long long groups = 0;
+  for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
+  const long long want = (long long)kUnitsPerWorker * G;
+  const long long par = (want + groups - 1) / groups;
+  long long slots = 0;
+  for (int i = 0; i < count; ++i) {
+    LinDesc& d = a.lin[i];
+    const int c = tiles_chunks(d.spt, tiles_lds_chunks(dtype, a.M, d.K), par);
+    d.chunks = c;
+    d.slot_base = slots;
+    if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
+  }
+}
+
 // Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
 // workers = 0 sizes the persistent grid from occupancy; otherwise it is the
-// number of waves to run (rounded down to whole workgroups for skinny_rows).
+// number of waves to run (rounded down to whole workgroups, at least one).
 skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* lin, int count,
                            int M, int variant, int workers, float* slots, hipStream_t stream,
                            hipEvent_t ev_before, hipEvent_t ev_after) {
@@ -859,21 +917,13 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   a.M = M;
   a.slots = slots;
   a.band_rows = k.band_rows;
-  if (k.rows)
-    for (int i = 0; i < count; ++i)
-      if (!rows_supported(*lin[i], M)) return SKINNY_ERR_UNSUPPORTED;
-  // LDS of skinny_rows: the x budget plus one FP8 scale row per wave.  The
-  // occupancy query uses the full budget so the grid does not depend on the
-  // shapes of the launch.
-  const int lds = k.rows ? kRowsXBudget + (dtype == SKINNY_FP8_BS128
-                                               ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float)
-                                               : 0)
-                         : 0;
-  a.x_lds_bytes = kRowsXBudget;
-  if (k.rows) {
-    skinny_status st = ensure_lds(k.fn, lds);
-    if (st != SKINNY_OK) return st;
-  }
+  for (int i = 0; i < count; ++i)
+    if (!(k.tiles ? tiles_supported(*lin[i], M) : rows_supported(*lin[i], M)))
+      return SKINNY_ERR_UNSUPPORTED;
+  const int lds = kernel_lds(k, dtype);
+  a.x_lds_bytes = k.tiles ? kTilesXBudget : kRowsXBudget;
+  skinny_status st = ensure_lds(k.fn, lds);
+  if (st != SKINNY_OK) return st;
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = *lin[i];
     LinDesc& d = a.lin[i];
@@ -884,51 +934,43 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     d.N = L.N;
     d.K = L.K;
     d.cpr = L.K / (dtype == SKINNY_BF16 ? 8 : 16);
-    d.spt = k.rows ? (d.cpr + kSegChunks - 1) / kSegChunks : (d.cpr + 3) / 4;
+    d.spt = k.tiles ? (d.cpr + kSegChunksT - 1) / kSegChunksT
+                    : (d.cpr + kSegChunks - 1) / kSegChunks;
     d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
     d.chunks = 1;
   }
   int G = workers;
   if (G == 0) {
-    skinny_status st = auto_workers(dev, k, lds, &G);
+    st = auto_workers(dev, k, lds, &G);
     if (st != SKINNY_OK) return st;
-  } else if (k.rows) {
+  } else {
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
-  if (k.rows) plan_row_chunks(a, count, G, dtype);
+  if (k.tiles) plan_tile_chunks(a, count, G, dtype);
+  else plan_row_chunks(a, count, G, dtype);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
-    d.step_base = S;
-    const long long bands = (d.N + a.band_rows - 1) / a.band_rows;
-    S += bands * (k.rows ? d.chunks : d.spt);
+    d.unit_base = S;
+    S += (long long)((d.N + a.band_rows - 1) / a.band_rows) * d.chunks;
   }
   a.S = S;
   if (G > S) G = (int)S;
   if (G < 1) G = 1;
   a.G = G;
-  const int blocks = k.rows ? G : (G + kWavesPerBlock - 1) / kWavesPerBlock;
   if (ev_before && hipEventRecord(ev_before, stream) != hipSuccess) return SKINNY_ERR_HIP;
-  hipLaunchKernelGGL(k.fn, dim3(blocks), dim3(64 * k.wpb), lds, stream, a);
+  hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), lds, stream, a);
   if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
   if (ev_after && hipEventRecord(ev_after, stream) != hipSuccess) return SKINNY_ERR_HIP;
-  if (k.rows) {
-    long long outs = 0;
-    for (int i = 0; i < count; ++i)
-      if (a.lin[i].chunks > 1) outs += (long long)M * a.lin[i].N;
-    if (outs > 0) {
-      long long most = 0;
-      for (int i = 0; i < count; ++i)
-        if (a.lin[i].chunks > 1 && (long long)M * a.lin[i].N > most) most = (long long)M * a.lin[i].N;
-      long long cblocks = (most + kBlockThreads - 1) / kBlockThreads;
-      if (cblocks > 256) cblocks = 256;
-      hipLaunchKernelGGL(skinny_rows_combine, dim3((unsigned)cblocks, count), dim3(kBlockThreads),
-                         0, stream, a);
-      if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
-    }
-  } else if (G > 1) {
-    const int cblocks = (G + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(skinny_combine, dim3(cblocks), dim3(kBlockThreads), 0, stream, a);
+  // Second pass over the split linears (grid row y = linear; unsplit ones return).
+  long long most = 0;
+  for (int i = 0; i < count; ++i)
+    if (a.lin[i].chunks > 1 && (long long)M * a.lin[i].N > most) most = (long long)M * a.lin[i].N;
+  if (most > 0) {
+    long long cblocks = (most + kCombineThreads - 1) / kCombineThreads;
+    if (cblocks > 256) cblocks = 256;
+    hipLaunchKernelGGL(skinny_combine, dim3((unsigned)cblocks, count), dim3(kCombineThreads), 0,
+                       stream, a);
     if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
   }
   return SKINNY_OK;
@@ -968,12 +1010,16 @@ skinny_status for_each_group(const skinny_linear* lin, int count, Fn&& fn) {
   return SKINNY_OK;
 }
 
-// Workspace a call over these linears needs (pure host arithmetic).
+// Workspace a call over these linears needs (pure host arithmetic): the
+// largest launch group's partial slots under either variant, and never less
+// than SKINNY_MIN_WORKSPACE_BYTES.
 size_t required_workspace(const skinny_linear* lin, int count, int M) {
-  size_t need = mfma_slots_bytes(M);
+  size_t need = SKINNY_MIN_WORKSPACE_BYTES;
   for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
-    const size_t b = group_slots_bytes(g, n, M, kRowsWavesPerBlock * rows_r(M));
-    if (b > need) need = b;
+    for (int v = SKINNY_VARIANT_VECTOR; v <= SKINNY_VARIANT_MFMA; ++v) {
+      const size_t b = group_slots_bytes(g, n, M, v);
+      if (b > need) need = b;
+    }
     return SKINNY_OK;
   });
   return need;
@@ -1005,10 +1051,14 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   skinny_status st = check_outputs(lin, count, M, ws, ws_bytes);
   if (st != SKINNY_OK) return st;
   if (events && event_count < 2 * launch_count(lin, count)) return SKINNY_ERR_INVALID_ARG;
-  // A VECTOR plan the row kernel cannot run is rejected before anything is enqueued.
-  if (variant == SKINNY_VARIANT_VECTOR)
-    for (int i = 0; i < count; ++i)
-      if (!rows_supported(lin[i], M)) return SKINNY_ERR_UNSUPPORTED;
+  // A plan the chosen kernel cannot run is rejected before anything is enqueued
+  // (AUTO falls back to the matrix-core kernel where the row kernel cannot run).
+  for (int i = 0; i < count; ++i) {
+    if (variant == SKINNY_VARIANT_VECTOR && !rows_supported(lin[i], M))
+      return SKINNY_ERR_UNSUPPORTED;
+    if (variant != SKINNY_VARIANT_VECTOR && !tiles_supported(lin[i], M))
+      return SKINNY_ERR_UNSUPPORTED;
+  }
   DeviceInfo d;
   st = device_info(&d);
   if (st != SKINNY_OK) return st;
@@ -1129,16 +1179,12 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   out->variant = auto_variant(group, n, M);
   const KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
-  int lds = 0;
-  if (k.rows) {
-    lds = kRowsXBudget +
-          (linears[0].dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
-    st = ensure_lds(k.fn, lds);
-    if (st != SKINNY_OK) return st;
-  }
+  const int lds = kernel_lds(k, linears[0].dtype);
+  st = ensure_lds(k.fn, lds);
+  if (st != SKINNY_OK) return st;
   int workers = 0;
   st = auto_workers(d, k, lds, &workers);
-  out->waves = k.rows ? workers * k.wpb : workers;
+  out->waves = workers * k.wpb;
   return st;
 }
 

@@ -57,6 +57,8 @@ extern "C" {
 #define SKINNY_MAX_M 16
 /* Linears one main-kernel launch carries; longer stacks use several launches. */
 #define SKINNY_MAX_LINEARS_PER_LAUNCH 32
+/* Smallest workspace any call asks for (bytes). */
+#define SKINNY_MIN_WORKSPACE_BYTES 256
 
 typedef enum skinny_status {
   SKINNY_OK = 0,
@@ -70,7 +72,10 @@ typedef enum skinny_status {
 
 enum skinny_dtype { SKINNY_BF16 = 0, SKINNY_FP8_BS128 = 1 };
 
-/* Compute variant of the main kernel. AUTO picks per (dtype, M) from measurement. */
+/* Compute variant of the main kernel.  VECTOR streams one row per wave and
+ * multiplies on the vector ALUs (M <= 8); MFMA streams 16-row tiles and
+ * multiplies on the matrix cores (any M).  AUTO picks per (dtype, M) from
+ * measurement. */
 enum skinny_variant { SKINNY_VARIANT_AUTO = 0, SKINNY_VARIANT_VECTOR = 1, SKINNY_VARIANT_MFMA = 2 };
 
 /* One linear of a stack.  All pointers are device pointers. */
@@ -92,9 +97,12 @@ typedef struct skinny_plan {
   int reserved[6];      /* must be 0                                         */
 } skinny_plan;
 
-/* Bytes of workspace a single linear needs (0 is never returned for valid
- * arguments; returns 0 for invalid ones).  Pure host arithmetic, no HIP call.
- * Defined by the split-K partial results of the second pass. */
+/* Bytes of workspace a single linear needs: at least SKINNY_MIN_WORKSPACE_BYTES
+ * for valid arguments, 0 for invalid ones.  Pure host arithmetic, no HIP call.
+ * The workspace holds the fp32 partial sums of K-chunks that the second pass
+ * adds: for every row group of a linear that the launch splits into C > 1
+ * K-chunks, C slots of [M][band rows] floats.  The value covers the largest
+ * split either variant may choose. */
 size_t skinny_workspace_bytes(int dtype, int M, int N, int K);
 
 /* Bytes of workspace decode_linear_stack needs for these linears at this M. */
@@ -137,12 +145,11 @@ skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, i
                                       int event_count, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
-/* Rows of W in one band of the main kernel of this dtype, variant (VECTOR or
- * MFMA; 0 for AUTO, whose choice depends on the shapes) and M; 0 if invalid.
- * The split-K workspace holds fp32 partial sums: for MFMA laid out
- * [slot][M][band rows], slot 2w for wave w's first band and 2w+1 for its
- * last; for VECTOR [unit][M][band rows], one slot per K-chunk of each row
- * group of a linear the launch splits, linears and row groups in order. */
+/* Rows of W in one row group of the main kernel of this dtype, variant
+ * (VECTOR or MFMA; 0 for AUTO, whose choice depends on the shapes) and M; 0 if
+ * invalid.  The split-K workspace holds fp32 partial sums laid out
+ * [slot][M][band rows]: one slot per K-chunk of each row group of a linear the
+ * launch splits; linears in order, then row groups, then K-chunks in K order. */
 int skinny_band_rows(int dtype, int variant, int M);
 
 /* The plan the library would use on the current device (fills *out). */

@@ -18,6 +18,14 @@ C = 0x4000000
 WS = 0x8000000
 
 
+def header_define(name):
+    m = re.search(r"#define\s+%s\s+(\d+)" % name, open(HEADER).read())
+    return int(m.group(1))
+
+
+MIN_WORKSPACE = header_define("SKINNY_MIN_WORKSPACE_BYTES")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -49,15 +57,23 @@ def test_abi_version_and_status_strings():
 
 
 def test_workspace_bytes_is_host_arithmetic():
-    one = sg.workspace_bytes(sg.BF16, 1, 1280, 8192)
-    assert one > 0
-    assert sg.workspace_bytes(sg.BF16, 16, 1280, 8192) == 16 * one
-    assert sg.workspace_bytes(sg.FP8_BS128, 6, 7392, 8192) == 6 * one
+    # Split-K partial slots: fp32 [slot][M][rows of a row group], one slot per
+    # K-chunk of every row group of a split linear.
+    one = sg.workspace_bytes(sg.BF16, 4, 1280, 8192)
+    assert one > MIN_WORKSPACE and one % (4 * 4 * 64) == 0
+    # Proportional to the rows when N is a multiple of every row-group height,
+    assert sg.workspace_bytes(sg.BF16, 4, 2560, 8192) == 2 * one
+    # never below the minimum, growing with M,
+    assert sg.workspace_bytes(sg.BF16, 1, 64, 64) == MIN_WORKSPACE
+    for dt in (sg.BF16, sg.FP8_BS128):
+        sizes = [sg.workspace_bytes(dt, M, 7392, 8192) for M in range(1, 17)]
+        assert sizes == sorted(sizes) and sizes[-1] > sizes[0]
+    # and a launch group needs the sum over its linears.
+    lins = [sg.Linear(sg.BF16, 1280, 8192, 0, A, None, B, C)] * 3
+    assert sg.stack_workspace_bytes(lins, 4) == 3 * one
     assert sg.workspace_bytes(sg.BF16, 0, 1, 8) == 0
     assert sg.workspace_bytes(sg.BF16, 17, 1, 8) == 0
     assert sg.workspace_bytes(7, 1, 1, 8) == 0
-    lins = [sg.Linear(sg.BF16, 1280, 8192, 0, A, None, B, C)] * 3
-    assert sg.stack_workspace_bytes(lins, 4) == 4 * one
 
 
 def bf16_call(x=B, w=A, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
@@ -75,10 +91,11 @@ def fp8_call(x=B, w=A, s=0x300000, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
     (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
     (dict(K=12), UNSUPPORTED), (dict(w=A + 2), UNSUPPORTED), (dict(x=B + 8), UNSUPPORTED),
     (dict(y=C + 4), UNSUPPORTED),
-    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=WS + 8), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(wsb=MIN_WORKSPACE - 1), WORKSPACE),
+    (dict(ws=WS + 8), UNSUPPORTED),
     (dict(y=B), INVALID),                       # y overlaps x
     (dict(y=A + 64), INVALID),                  # y inside W
-    (dict(y=WS + 4096), INVALID),               # y inside the workspace
+    (dict(y=WS + 128), INVALID),                # y inside the workspace
 ])
 def test_bf16_rejects_bad_arguments(kw, status):
     assert bf16_call(**kw) == status

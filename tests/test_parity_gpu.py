@@ -37,7 +37,7 @@ def test_bf16_random_vs_oracle(M, N, K):
     w = synth.tensor_bf16(0, synth.stream_id("t-bf16", N, K, "w"), N, K, 0.02)
     y_ref, a, _ = oracle.linear_bf16(x, w)
     for var in variants_for(M):
-        for waves in (0, 4, 28):           # skinny_rows runs waves / 4 workgroups
+        for waves in (0, 4, 28):           # forced grids: whole workgroups, at least one
             y = run_bf16(x, w, M, N, variant=var, waves=waves)
             assert_matches_oracle(y, y_ref, a, f"bf16 M={M} N={N} K={K} var={var} waves={waves}",
                                   strict=K >= 1000)
@@ -129,22 +129,22 @@ def test_page_example_column_split():
 
 
 def test_page_example_split_k_partials_in_workspace():
-    """The page's MLP example split over K into two halves, as two waves of the
-    split-K pass: each wave's partial slot holds the printed partial and the
-    second pass writes the printed sum."""
+    """The page's MLP example split over K into two halves that land in two
+    different K-chunks of the split-K pass: each chunk's partial slot holds the
+    printed partial and the second pass writes the printed sum."""
     d = json.load(open(os.path.join(GOLDEN, "p2_ex3_mlp_split.json")))
     x = np.array(d["x"], np.float64)
     a_m = np.array([[((8 * i + j) % 7) - 3 for j in range(8)] for i in range(4)], np.float64)
     b_m = np.array([[((4 * i + j) % 5) - 2 for j in range(4)] for i in range(8)], np.float64)
     h = np.maximum(x @ a_m, 0.0)                 # inputs of the second product (integers)
-    K = 8192                                     # 256 steps of 32 k: two waves of 128 steps
+    K = 8192                                     # halves 4096 apart: never in one K-chunk
     hp = np.zeros((2, K)); hp[:, 0:4] = h[:, 0:4]; hp[:, K // 2:K // 2 + 4] = h[:, 4:8]
     wp = np.zeros((4, K)); wp[:, 0:4] = b_m[0:4].T; wp[:, K // 2:K // 2 + 4] = b_m[4:8].T
     for var in variants_for(2):
         ws = workspace(2, 4, K)
         ws.zero_()
-        waves = 8 if var == sg.VARIANT_VECTOR else 2     # two workers either way
-        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=waves, ws=ws)
+        # A small grid makes the planner cut K into several chunks.
+        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=8, ws=ws)
         assert host_values(y).tolist() == d["sum_printed"]
         slots = ws.view(torch.float32).cpu().numpy()
         # Slots [slot][M][band rows]; only the two slots whose K range holds
