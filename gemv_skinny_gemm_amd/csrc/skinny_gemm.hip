@@ -130,18 +130,22 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 // skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
 // wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
 // along K: lane l reads bytes [16 l, 16 l + 16) of each 1 KB segment of a
-// row, so each wave reads its rows front to back in 1 KB coalesced loads.
-// Work units are (K-chunk, row group), chunk-major within a linear; a chunk is
-// spc consecutive segments.  A linear has more than one chunk when its x
-// window would not fit the LDS budget or when the launch is too small to
-// keep every workgroup busy.  Units go round robin: workgroup b takes units
-// b, b + G, b + 2G, ..., so at any moment all workgroups read neighbouring
-// rows - measured on MI355X this compact moving window streams faster than
-// giving each workgroup its own contiguous share.  LDS holds x[M][window] of
-// the current (linear, chunk), restaged between two barriers when it changes
-// (the same for all waves), and per wave the FP8 scale row of the current
-// 128-row block, prefetched one unit ahead.  One x read from LDS serves the
-// wave's R rows.
+// row, so each wave reads its rows front to back in 1 KB coalesced loads, U
+// segments per batch and two batches in flight.  Work units (row group,
+// K-chunk) are dealt round robin: workgroup b takes units b, b + G, ..., so
+// at any moment all workgroups read neighbouring rows - measured on MI355X
+// this compact moving window streams faster than giving each workgroup its
+// own contiguous share.  As in skinny_tiles, units are row-group-major and
+// the chunk count a power of two, so a workgroup keeps one K-chunk per
+// linear.  LDS holds x[M][window] of the current (linear, chunk), restaged
+// between two barriers when it changes, and per wave the FP8 scale row of
+// the current 128-row block, prefetched one unit ahead.  One x read from LDS
+// serves the wave's R rows.
+template <int DT, int R, int U>
+struct RowBatch {
+  u32x4 w[U][R];
+};
+
 template <int DT, int MT, int U, int R, int WPB>
 __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
   constexpr int kThreads = 64 * WPB;
@@ -156,10 +160,9 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
   auto unit_of = [&](long long u, int& l, int& grp, int& chunk) {
     while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
     const LinDesc& L = a.lin[l];
-    const int groups = (L.N + kGroupRows - 1) / kGroupRows;
     const long long local = u - L.unit_base;
-    chunk = (int)(local / groups);
-    grp = (int)(local - (long long)chunk * groups);
+    grp = (int)(local / L.chunks);
+    chunk = (int)(local - (long long)grp * L.chunks);
   };
   auto prefetch_scales = [&](long long u, int l) {
     if (DT == SKINNY_FP8_BS128 && u < a.S) {
@@ -191,65 +194,53 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
     int grp, chunk;
     unit_of(u, l, grp, chunk);
     const LinDesc& L = a.lin[l];
-    const int spc = (L.spt + L.chunks - 1) / L.chunks;          // segments per chunk
-    const int j0 = chunk * spc;
-    const int j1 = min(j0 + spc, L.spt);
+    // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks).
+    const int spc = (L.spt + L.chunks - 1) / L.chunks;          // window, in segments
+    const int j0 = (int)((long long)chunk * L.spt / L.chunks);
+    const int j1 = (int)((long long)(chunk + 1) * L.spt / L.chunks);
     const int xcpr = L.K >> 3;                                   // x chunks per token row
     const int win = spc * kSegChunks * XC;                       // x chunks per token in LDS
     const int xw0 = j0 * kSegChunks * XC;                        // first x chunk of the window
-    if (l != staged_l || chunk != staged_c) {                    // same for all waves
-      __syncthreads();                                           // all done with the old window
-      const int wlen = min(win, xcpr - xw0);
-      for (int i = threadIdx.x; i < MT * wlen; i += kThreads) {
-        const int m = i / wlen;
-        const int c = i - m * wlen;
-        xs[m * win + c] = L.x[(size_t)m * xcpr + xw0 + c];
-      }
-      __syncthreads();
-      staged_l = l;
-      staged_c = chunk;
-    }
-    prefetch_scales(u + a.G, l);
     const int row0 = grp * kGroupRows + wv * R;
+    // Rows past N read row N - 1 instead; their sums are not written.
     const u32x4* wrow[R];
-    bool rowok[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      rowok[r] = row0 + r < L.N;
-      wrow[r] = L.w + (size_t)(rowok[r] ? row0 + r : 0) * (size_t)L.cpr;
-    }
+    for (int r = 0; r < R; ++r) wrow[r] = L.w + (size_t)min(row0 + r, L.N - 1) * (size_t)L.cpr;
     float acc[R][MT];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-    for (int j = j0; j < j1; j += U) {
-      u32x4 wq[U][R];
+    // A batch of U whole segments: plain loads (no selects, so the compiler
+    // keeps them unconditional and the waits exact) ...
+    auto load = [&](RowBatch<DT, R, U>& b, int j) {
+#pragma unroll
+      for (int v = 0; v < U; ++v)
+#pragma unroll
+        for (int r = 0; r < R; ++r) b.w[v][r] = wrow[r][(j + v) * kSegChunks + lane];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // ... and its products.  OK marks the chunks inside the row (a ragged end).
+    auto consume = [&](const RowBatch<DT, R, U>& b, int j, auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
       for (int v = 0; v < U; ++v) {
         const int cw = (j + v) * kSegChunks + lane;
-        const bool ok = (j + v < j1) && cw < L.cpr;
-#pragma unroll
-        for (int r = 0; r < R; ++r) wq[v][r] = (ok && rowok[r]) ? wrow[r][cw] : zero4();
-      }
-#pragma unroll
-      for (int v = 0; v < U; ++v) {
-        const int cw = (j + v) * kSegChunks + lane;
-        const bool ok = (j + v < j1) && cw < L.cpr;
+        const bool ok = !kMasked || ((j + v < j1) && cw < L.cpr);
         const int xl = cw * XC - xw0;                            // chunk index in the window
         if (DT == SKINNY_BF16) {
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             const u32x4 xv = ok ? xs[m * win + xl] : zero4();
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][m] = dot8(xv, wq[v][r], acc[r][m]);
+            for (int r = 0; r < R; ++r) acc[r][m] = dot8(xv, b.w[v][r], acc[r][m]);
           }
         } else {
           // W chunk cw holds k in [16 cw, 16 cw + 16): scale block cw / 8.
           const float sc = ok ? ss[cw >> 3] : 0.0f;
           u32x4 b0[R], b1[R];
 #pragma unroll
-          for (int r = 0; r < R; ++r) e4m3x16_to_bf16(wq[v][r], b0[r], b1[r]);
+          for (int r = 0; r < R; ++r) e4m3x16_to_bf16(b.w[v][r], b0[r], b1[r]);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             const u32x4 x0 = ok ? xs[m * win + xl] : zero4();
@@ -260,6 +251,66 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
           }
         }
       }
+    };
+    using Plain = std::false_type;
+    using Masked = std::true_type;
+    // Whole batches [j0, jb) run two deep; the rest of the chunk (a short
+    // batch or the row's ragged end) takes the masked path.  The first
+    // batch's loads go out before x is staged, so the two fetches overlap.
+    const int jf = (j1 == L.spt && L.cpr % kSegChunks != 0) ? j1 - 1 : j1;   // whole segments
+    const int nb = (jf - j0) / U;
+    const int jb = j0 + nb * U;
+    RowBatch<DT, R, U> b0, b1;
+    if (nb > 0) load(b0, j0);
+    if (l != staged_l || chunk != staged_c) {                    // same for all waves
+      __syncthreads();                                           // all done with the old window
+      const int wlen = min(win, xcpr - xw0);
+      const int n = MT * wlen;
+      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {      // eight loads in flight
+        u32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = min(b + q * kThreads, n - 1);
+          const int m = i / wlen;
+          v[q] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = b + q * kThreads;
+          const int m = i / wlen;
+          if (i < n) xs[m * win + (i - m * wlen)] = v[q];
+        }
+      }
+      __syncthreads();
+      staged_l = l;
+      staged_c = chunk;
+    }
+    prefetch_scales(u + a.G, l);
+    if (nb > 0) {
+      int b = 0;
+      for (; b + 2 < nb; b += 2) {
+        load(b1, j0 + (b + 1) * U);
+        consume(b0, j0 + b * U, Plain{});
+        load(b0, j0 + (b + 2) * U);
+        consume(b1, j0 + (b + 1) * U, Plain{});
+      }
+      if (b + 2 == nb) {
+        load(b1, j0 + (b + 1) * U);
+        consume(b0, j0 + b * U, Plain{});
+        consume(b1, j0 + (b + 1) * U, Plain{});
+      } else {
+        consume(b0, j0 + b * U, Plain{});
+      }
+    }
+    for (int j = jb; j < j1; j += U) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int cw = (j + v) * kSegChunks + lane;
+        const bool ok = (j + v < j1) && cw < L.cpr;
+#pragma unroll
+        for (int r = 0; r < R; ++r) b1.w[v][r] = ok ? wrow[r][ok ? cw : 0] : zero4();
+      }
+      consume(b1, j, Masked{});
     }
     // This wave's reads of the current scales are done: install the next unit's.
     store_scales();
@@ -277,7 +328,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (L.chunks == 1) {
-            if (rowok[r]) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
+            if (row0 + r < L.N) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
           } else {
             a.slots[((size_t)slot * MT + m) * kGroupRows + wv * R + r] = acc[r][m];
           }
@@ -360,39 +411,8 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     const int win = spc * kSegChunksT * XC;                      // x chunks per token in LDS
     const int xstride = win + 1;
     const int xw0 = j0 * kSegChunksT * XC;
-    if (l != staged_l || chunk != staged_c) {                    // same for all waves
-      __syncthreads();
-      // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
-      // then a zero row that lanes of absent tokens read.
-      const int wlen = min(win, xcpr - xw0);
-      const int n = a.M * wlen;
-      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {
-        u32x4 v[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int i = min(b + r * kThreads, n - 1);
-          const int m = i / wlen;
-          v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int i = b + r * kThreads;
-          const int m = i / wlen;
-          if (i < n) xs[m * xstride + (i - m * wlen)] = v[r];
-        }
-      }
-      const int pad = win - wlen;
-      for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
-        const int m = i / pad;
-        xs[m * xstride + wlen + (i - m * pad)] = zero4();
-      }
-      for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
-      __syncthreads();
-      staged_l = l;
-      staged_c = chunk;
-    }
     const int row0 = grp * kGroupRows + wv * kTileRows;
-    if (row0 >= L.N) continue;                                   // a tile wholly past N
+    const bool active = row0 < L.N;                              // else a tile wholly past N
     // Rows past N read row N - 1 instead: a B column only feeds its own
     // output, which is not written.
     const u32x4* src[kLoadsT];
@@ -464,12 +484,45 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     using Full = std::true_type;
     using Ragged = std::false_type;
     // Whole segments [j0, jw) run two buffers deep; a ragged last segment of
-    // the row comes after them.
+    // the row comes after them.  The first segment's loads go out before x is
+    // staged, so the two fetches overlap.
     const int jw = (j1 == L.spt && L.cpr % kSegChunksT != 0) ? j1 - 1 : j1;
     TileSeg<DT> s0, s1;
+    if (active && j0 < jw) load(s0, j0, Full{});
+    if (l != staged_l || chunk != staged_c) {                    // same for all waves
+      __syncthreads();
+      // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
+      // then a zero row that lanes of absent tokens read.
+      const int wlen = min(win, xcpr - xw0);
+      const int n = a.M * wlen;
+      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = min(b + r * kThreads, n - 1);
+          const int m = i / wlen;
+          v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int i = b + r * kThreads;
+          const int m = i / wlen;
+          if (i < n) xs[m * xstride + (i - m * wlen)] = v[r];
+        }
+      }
+      const int pad = win - wlen;
+      for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
+        const int m = i / pad;
+        xs[m * xstride + wlen + (i - m * pad)] = zero4();
+      }
+      for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
+      __syncthreads();
+      staged_l = l;
+      staged_c = chunk;
+    }
+    if (!active) continue;
     if (j0 < jw) {
       int j = j0;
-      load(s0, j, Full{});
       for (; j + 2 < jw; j += 2) {
         load(s1, j + 1, Full{});
         consume(s0, j);
@@ -609,9 +662,10 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
 
 // skinny_rows shape per M: R rows per wave (one LDS read of x serves R weight
 // loads, so LDS traffic stays at <= 2 x reads per weight load up to M = 8) and
-// U segments per row in flight, R x U = 8 loads per wave.
+// U segments per batch, R x U = 8 loads (bf16) or 4 (FP8, whose conversion
+// needs the registers) per batch, two batches in flight.
 constexpr int rows_r(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : 4; }
-constexpr int rows_u(int M) { return 8 / rows_r(M); }
+constexpr int rows_u(int M, int dtype) { return (dtype == SKINNY_BF16 ? 8 : 4) / rows_r(M); }
 constexpr int kRowsXBudget = 64 * 1024;   // LDS for x per workgroup: two workgroups per CU
 constexpr int kRowsMaxM = 8;
 constexpr int kUnitsPerWorker = 16;
@@ -629,14 +683,28 @@ int rows_lds_chunks(int dtype, int M, int K) {
 
 // Most K-chunks the planner may give a linear (LDS need, or a small launch's
 // parallelism with >= U segments per chunk): bounds the workspace slots.
-int rows_max_chunks(int dtype, int M, int K) {
+// K-chunks of a linear with spt segments: at least c_lds (LDS) and, up to
+// spt / min_segs, par (parallelism of a small launch); rounded up to a power
+// of two, which divides the persistent grid, so every workgroup keeps one
+// K-chunk - one x window - for the whole linear.
+int chunk_count(int spt, int c_lds, long long par, int min_segs) {
+  int c_par = spt / min_segs;
+  if (c_par < 1) c_par = 1;
+  if (par < c_par) c_par = (int)par;
+  const int need = c_par > c_lds ? c_par : c_lds;
+  int c = 1;
+  while (c < need) c *= 2;
+  return c <= spt ? c : need;
+}
+
+int rows_chunks(int dtype, int M, int K, long long par) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunks - 1) / kSegChunks;
-  int c = spt / rows_u(M);
-  if (c < 1) c = 1;
-  const int lds = rows_lds_chunks(dtype, M, K);
-  return lds > c ? lds : c;
+  return chunk_count(spt, rows_lds_chunks(dtype, M, K), par, rows_u(M, dtype));
 }
+
+// Most K-chunks the planner may give a linear: bounds the workspace slots.
+int rows_max_chunks(int dtype, int M, int K) { return rows_chunks(dtype, M, K, 1LL << 40); }
 
 bool rows_supported(const skinny_linear& L, int M) {
   if (M > kRowsMaxM) return false;
@@ -657,25 +725,13 @@ int tiles_lds_chunks(int dtype, int M, int K) {
   return (spt + max_spc - 1) / max_spc;
 }
 
-// K-chunks of a linear with spt segments: at least c_lds (LDS) and, up to
-// spt / kTilesMinSegs, par (parallelism of a small launch); rounded up to a
-// power of two, which divides the persistent grid, so every workgroup keeps
-// one K-chunk - one x window - for the whole linear.
-int tiles_chunks(int spt, int c_lds, long long par) {
-  int c_par = spt / kTilesMinSegs;
-  if (c_par < 1) c_par = 1;
-  if (par < c_par) c_par = (int)par;
-  const int need = c_par > c_lds ? c_par : c_lds;
-  int c = 1;
-  while (c < need) c *= 2;
-  return c <= spt ? c : need;
-}
-
-int tiles_max_chunks(int dtype, int M, int K) {
+int tiles_chunks(int dtype, int M, int K, long long par) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  return tiles_chunks(spt, tiles_lds_chunks(dtype, M, K), 1LL << 40);
+  return chunk_count(spt, tiles_lds_chunks(dtype, M, K), par, kTilesMinSegs);
 }
+
+int tiles_max_chunks(int dtype, int M, int K) { return tiles_chunks(dtype, M, K, 1LL << 40); }
 
 bool tiles_supported(const skinny_linear& L, int M) {
   return tiles_lds_chunks(L.dtype, M, L.K) > 0;
@@ -696,11 +752,13 @@ size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int 
 }
 
 // Variant choice, measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers
-// and the TP=8 layer): see kRowsMaxAutoM*.  Row streaming keeps one contiguous
-// stream per wave, but its vector work per weight grows with M (and FP8 adds
-// a half-rate conversion); the matrix-core kernel's does not.
+// and stacks, the TP=8 layer).  Row streaming keeps one contiguous stream per
+// wave, but its vector work per weight grows with M (and FP8 adds a half-rate
+// conversion); the matrix-core kernel's does not.  bf16 TP=1 layer, rows vs
+// tiles: 6.10 / 5.92 TB/s at M = 1, 5.72 / 5.66 at M = 2, 5.37 / 5.42 at
+// M = 4; FP8 TP=1 stack at M = 1: 5.85 / 5.93.
 constexpr int kRowsMaxAutoMBf16 = 2;
-constexpr int kRowsMaxAutoMFp8 = 1;
+constexpr int kRowsMaxAutoMFp8 = 0;
 
 int auto_variant(const skinny_linear* const* lin, int count, int M) {
   const int cap = lin[0]->dtype == SKINNY_BF16 ? kRowsMaxAutoMBf16 : kRowsMaxAutoMFp8;
@@ -737,7 +795,7 @@ KernelChoice rows_kernel() {
   constexpr int R = rows_r(MT);
   static_assert(kScaleBlock % (WPB * R) == 0, "a row group must sit in one scale block");
   KernelChoice k;
-  k.fn = skinny_rows<DT, MT, rows_u(MT), R, WPB>;
+  k.fn = skinny_rows<DT, MT, rows_u(MT, DT), R, WPB>;
   k.band_rows = WPB * R;
   k.wpb = WPB;
   return k;
@@ -850,42 +908,11 @@ int kernel_lds(const KernelChoice& k, int dtype) {
          (dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
 }
 
-// skinny_rows K-chunks per linear: enough for its x window to fit the LDS
-// budget, and, when the launch is too small to give every workgroup about
-// kUnitsPerWorker units, more - but never fewer than U segments per chunk,
-// so each wave keeps R x U loads in flight.  Returns the LDS bytes for x.
-int plan_row_chunks(LaunchArgs& a, int count, int G, int dtype) {
-  const int M = a.M;
-  const int rows = a.band_rows;
-  const int xc = dtype == SKINNY_BF16 ? 1 : 2;
-  long long groups = 0;
-  for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
-  const long long want = (long long)kUnitsPerWorker * G;
-  const long long par = (want + groups - 1) / groups;
-  long long slots = 0;
-  int x_bytes = 16;
-  for (int i = 0; i < count; ++i) {
-    LinDesc& d = a.lin[i];
-    int c_par = d.spt / rows_u(M);
-    if (c_par < 1) c_par = 1;
-    if (par < c_par) c_par = (int)par;
-    const int c_lds = rows_lds_chunks(dtype, M, d.K);
-    int c = c_par > c_lds ? c_par : c_lds;
-    if (c > d.spt) c = d.spt;
-    d.chunks = c;
-    d.slot_base = slots;
-    if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
-    const int spc = (d.spt + c - 1) / c;
-    const int xb = M * spc * kSegChunks * xc * 16;
-    if (xb > x_bytes) x_bytes = xb;
-  }
-  return x_bytes;
-}
-
-// skinny_tiles K-chunks per linear: enough for the x window to fit the LDS
+// K-chunks per linear (either kernel): enough for the x window to fit the LDS
 // budget and, when the launch is too small to give every workgroup about
-// kUnitsPerWorker units, more - but at least kTilesMinSegs segments each.
-void plan_tile_chunks(LaunchArgs& a, int count, int G, int dtype) {
+// kUnitsPerWorker units, more - but never fewer segments per chunk than a
+// wave keeps in flight.  Assigns the partial slots of the split linears.
+void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
   const int rows = a.band_rows;
   long long groups = 0;
   for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
@@ -894,7 +921,7 @@ void plan_tile_chunks(LaunchArgs& a, int count, int G, int dtype) {
   long long slots = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
-    const int c = tiles_chunks(d.spt, tiles_lds_chunks(dtype, a.M, d.K), par);
+    const int c = tiles ? tiles_chunks(dtype, a.M, d.K, par) : rows_chunks(dtype, a.M, d.K, par);
     d.chunks = c;
     d.slot_base = slots;
     if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
@@ -946,8 +973,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   } else {
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
-  if (k.tiles) plan_tile_chunks(a, count, G, dtype);
-  else plan_row_chunks(a, count, G, dtype);
+  plan_chunks(a, count, G, dtype, k.tiles);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
