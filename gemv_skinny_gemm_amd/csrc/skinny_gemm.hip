@@ -349,15 +349,18 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
 // per row so the operand reads hit 16 different bank groups.
 //
 // A workgroup of WPB waves handles a row group of 16 WPB rows (inside one
-// 128-row FP8 scale block); wave i owns the 16 rows from 16 i.  Work
-// units are (K-chunk, row group), chunk-major within a linear, dealt round
-// robin over the workgroups as in skinny_rows, with x[M][window] of the
-// current (linear, K-chunk) in LDS (token rows padded by one chunk).  A
+// 128-row FP8 scale block); wave i owns the 16 rows from 16 i.  Work units
+// (row group, K-chunk) are dealt round robin over the workgroups as in
+// skinny_rows, with x[M][window] of the current (linear, K-chunk) in LDS
+// (token rows padded by one chunk, then a zero row for absent tokens).  A
 // segment is 512 bytes of each of the wave's rows: 8 loads, 8 LDS writes,
 // then 8 k-steps of one operand read each; bf16 needs one MFMA per k-step,
 // FP8 two (its 16-byte chunk holds 16 k) and the block scale is applied in
-// fp32 to each 128-k partial sum.  The next segment's loads are issued
-// before the current one is consumed.
+// fp32 to each 128-k partial sum.  Loads run one segment ahead of the
+// products, across unit boundaries too: the last segment of a unit is
+// consumed after the next unit's first loads are out, so the stream never
+// drains between units and the x staging hides under those loads.
+//
 // Shape measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers and the
 // TP=8 layer, M = 1..16): 512-byte segments, 4 waves per workgroup and two
 // workgroups per CU beat 256- or 1024-byte segments and 8-wave workgroups.
@@ -368,6 +371,7 @@ constexpr int kLoadsT = kTileRows * kSegChunksT / 64; // wave loads per segment
 constexpr int kLanesPerRowT = kSegChunksT;            // lanes of a load on one row
 constexpr int kRowsPerLoadT = 64 / kLanesPerRowT;
 constexpr int kStepsT = kSegChunksT / 4;              // k-steps per segment
+constexpr int kSegBlocksT = kSegBytesT / kScaleBlock; // FP8 scale blocks per segment
 constexpr int kTilesWavesPerBlock = 4;
 constexpr int kTilesLds = 80 * 1024;                  // two workgroups per 160 KB CU
 constexpr int kTilesWBytes = kTilesWavesPerBlock * kTileRows * kRowStrideT;
@@ -376,7 +380,16 @@ constexpr int kTilesXBudget = kTilesLds - kTilesWBytes;
 template <int DT>
 struct TileSeg {
   u32x4 w[kLoadsT];
-  float sc;              // FP8: lane i holds the scale of block (seg blocks) j + i % (seg blocks)
+  float sc;              // FP8: lane i holds the scale of the segment's block i % kSegBlocksT
+};
+
+// One work unit as every wave of the workgroup sees it (uniform values).
+struct TileUnit {
+  int l;                 // linear
+  int grp;               // row group
+  int chunk;             // K-chunk
+  int j0, j1;            // segments [j0, j1) of each row
+  int spc;               // x window, in segments
 };
 
 template <int DT, int WPB>
@@ -391,159 +404,143 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   unsigned char* wt = lds + a.x_lds_bytes + wv * (kTileRows * kRowStrideT);
   const int n = lane & 15;                             // operand row: token (A) / W row (B)
   const int g = lane >> 4;                             // operand k-group
-  const int lrow = lane / kLanesPerRowT;              // load q: row q kRowsPerLoadT + lrow
+  const int lrow = lane / kLanesPerRowT;               // load q: row q kRowsPerLoadT + lrow
   const int lchunk = lane % kLanesPerRowT;             // load: chunk of the segment
-  int l = 0, staged_l = -1, staged_c = -1;
-  for (long long u = blockIdx.x; u < a.S; u += a.G) {
-    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
-    const LinDesc& L = a.lin[l];
-    // Units are row-group-major: with a power-of-two chunk count dividing
-    // the grid, workgroup b keeps K-chunk (b - base) % chunks all linear long.
+
+  // Units are row-group-major: with a power-of-two chunk count dividing the
+  // grid, workgroup b keeps K-chunk (b - base) % chunks all linear long.
+  // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
+  // empty (chunks <= spt) and none is longer than the window.
+  int ldec = 0;
+  auto decode = [&](long long u) {
+    while (ldec + 1 < a.nlin && a.lin[ldec + 1].unit_base <= u) ++ldec;
+    const LinDesc& L = a.lin[ldec];
     const long long local = u - L.unit_base;
-    const int grp = (int)(local / L.chunks);
-    const int chunk = (int)(local - (long long)grp * L.chunks);
-    // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
-    // empty (chunks <= spt) and none is longer than the window.
-    const int spc = (L.spt + L.chunks - 1) / L.chunks;           // window, in segments
-    const int j0 = (int)((long long)chunk * L.spt / L.chunks);
-    const int j1 = (int)((long long)(chunk + 1) * L.spt / L.chunks);
-    const int xcpr = L.K >> 3;                                   // x chunks per token
-    const int win = spc * kSegChunksT * XC;                      // x chunks per token in LDS
-    const int xstride = win + 1;
-    const int xw0 = j0 * kSegChunksT * XC;
-    const int row0 = grp * kGroupRows + wv * kTileRows;
-    const bool active = row0 < L.N;                              // else a tile wholly past N
-    // Rows past N read row N - 1 instead: a B column only feeds its own
-    // output, which is not written.
-    const u32x4* src[kLoadsT];
+    TileUnit t;
+    t.l = ldec;
+    t.grp = (int)(local / L.chunks);
+    t.chunk = (int)(local - (long long)t.grp * L.chunks);
+    t.spc = (L.spt + L.chunks - 1) / L.chunks;
+    t.j0 = (int)((long long)t.chunk * L.spt / L.chunks);
+    t.j1 = (int)((long long)(t.chunk + 1) * L.spt / L.chunks);
+    return t;
+  };
+  // Segment j of unit t into s.  Rows past N read row N - 1 (a B column only
+  // feeds its own output, which is not written) and chunks past the row's
+  // end read its last chunk (zeroed in LDS before use), so every load is
+  // unconditional and in bounds and the compiler's waits stay exact.
+  auto load = [&](TileSeg<DT>& s, const TileUnit& t, int j) {
+    const LinDesc& L = a.lin[t.l];
+    const int row0 = t.grp * kGroupRows + wv * kTileRows;
+    const int c = min(j * kSegChunksT + lchunk, L.cpr - 1);
+#pragma unroll
+    for (int q = 0; q < kLoadsT; ++q) {
+      const int row = min(row0 + kRowsPerLoadT * q + lrow, L.N - 1);
+      s.w[q] = L.w[(size_t)row * L.cpr + c];
+    }
+    if (DT == SKINNY_FP8_BS128) {
+      // The row group lies in one 128-row scale block.  Blocks past K cover
+      // only zeroed weights; clamping keeps the read in bounds.
+      const float* srow = L.scale + (size_t)((t.grp * kGroupRows) / kScaleBlock) * L.kblocks;
+      s.sc = srow[min(kSegBlocksT * j + lane % kSegBlocksT, L.kblocks - 1)];
+    }
+    // Keep the loads ahead of the previous segment's work.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int xw0 = 0, xstride = 1;                            // x window of the current unit
+  const u32x4* xrow = xs;
+  auto consume = [&](const TileSeg<DT>& s, const TileUnit& t, int j) {
+    const LinDesc& L = a.lin[t.l];
 #pragma unroll
     for (int q = 0; q < kLoadsT; ++q)
-      src[q] = L.w + (size_t)min(row0 + kRowsPerLoadT * q + lrow, L.N - 1) * (size_t)L.cpr;
-    const float* srow = DT == SKINNY_FP8_BS128
-                            ? L.scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks
-                            : nullptr;
-    const u32x4* xrow = xs + (n < a.M ? n : a.M) * xstride;
-    // FULL: segment j lies wholly inside the row (plain loads, no selects, so
-    // the compiler keeps them unconditional and the waits exact).
-    auto load = [&](TileSeg<DT>& s, int j, auto full) {
-      const int c = j * kSegChunksT + lchunk;
-      if constexpr (decltype(full)::value) {
-#pragma unroll
-        for (int q = 0; q < kLoadsT; ++q) s.w[q] = src[q][c];
-        // Keep the loads ahead of the previous segment's work.
-        __builtin_amdgcn_sched_barrier(0);
-      } else {                                                   // the row's ragged end
-        const bool cok = c < L.cpr;
-#pragma unroll
-        for (int q = 0; q < kLoadsT; ++q) s.w[q] = cok ? src[q][cok ? c : 0] : zero4();
-      }
-      if (DT == SKINNY_FP8_BS128) {
-        // Blocks past K cover only zero weights; clamping keeps the read in bounds.
-        constexpr int kSegBlocks = kSegBytesT / kScaleBlock;     // FP8: 1 byte per k
-        const int kb = min(kSegBlocks * j + (lane % kSegBlocks), L.kblocks - 1);
-        s.sc = srow[kb];
-      }
-    };
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto consume = [&](const TileSeg<DT>& s, int j) {
+      *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kRowStrideT + lchunk * 16) =
+          s.w[q];
+    if ((j + 1) * kSegChunksT > L.cpr && j * kSegChunksT + lchunk >= L.cpr) {
+      // The row's ragged end: zero the chunks past it (written after the
+      // clamped data, so these writes win).
 #pragma unroll
       for (int q = 0; q < kLoadsT; ++q)
         *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kRowStrideT + lchunk * 16) =
-            s.w[q];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int t = 0; t < kStepsT; ++t) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(wt + n * kRowStrideT + (4 * t + g) * 16);
-        const int xc = (j * kSegChunksT + 4 * t + g) * XC - xw0;  // x chunk in the window
-        if (DT == SKINNY_BF16) {
-          acc = mfma_bf16(xrow[xc], b, acc);
-        } else {
-          const u32x4 x0 = xrow[xc];
-          const u32x4 x1 = xrow[xc + 1];
-          u32x4 b0, b1;
-          e4m3x16_to_bf16(b, b0, b1);
-          p = mfma_bf16(x0, b0, p);
-          p = mfma_bf16(x1, b1, p);
-          if (t & 1) {
-            // Steps 2 i and 2 i + 1 cover the 128 k of the segment's block i.
-            const float sc = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.sc), t >> 1));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, p[i], acc[i]);
-            p = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    using Full = std::true_type;
-    using Ragged = std::false_type;
-    // Whole segments [j0, jw) run two buffers deep; a ragged last segment of
-    // the row comes after them.  The first segment's loads go out before x is
-    // staged, so the two fetches overlap.
-    const int jw = (j1 == L.spt && L.cpr % kSegChunksT != 0) ? j1 - 1 : j1;
-    TileSeg<DT> s0, s1;
-    if (active && j0 < jw) load(s0, j0, Full{});
-    if (l != staged_l || chunk != staged_c) {                    // same for all waves
-      __syncthreads();
-      // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
-      // then a zero row that lanes of absent tokens read.
-      const int wlen = min(win, xcpr - xw0);
-      const int n = a.M * wlen;
-      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {
-        u32x4 v[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int i = min(b + r * kThreads, n - 1);
-          const int m = i / wlen;
-          v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int i = b + r * kThreads;
-          const int m = i / wlen;
-          if (i < n) xs[m * xstride + (i - m * wlen)] = v[r];
-        }
-      }
-      const int pad = win - wlen;
-      for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
-        const int m = i / pad;
-        xs[m * xstride + wlen + (i - m * pad)] = zero4();
-      }
-      for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
-      __syncthreads();
-      staged_l = l;
-      staged_c = chunk;
+            zero4();
     }
-    if (!active) continue;
-    if (j0 < jw) {
-      int j = j0;
-      for (; j + 2 < jw; j += 2) {
-        load(s1, j + 1, Full{});
-        consume(s0, j);
-        load(s0, j + 2, Full{});
-        consume(s1, j + 1);
-      }
-      if (j + 2 == jw) {
-        load(s1, j + 1, Full{});
-        consume(s0, j);
-        consume(s1, j + 1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < kStepsT; ++st) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(wt + n * kRowStrideT + (4 * st + g) * 16);
+      const int xc = (j * kSegChunksT + 4 * st + g) * XC - xw0;  // x chunk in the window
+      if (DT == SKINNY_BF16) {
+        acc = mfma_bf16(xrow[xc], b, acc);
       } else {
-        consume(s0, j);
+        const u32x4 x0 = xrow[xc];
+        const u32x4 x1 = xrow[xc + 1];
+        u32x4 b0, b1;
+        e4m3x16_to_bf16(b, b0, b1);
+        p = mfma_bf16(x0, b0, p);
+        p = mfma_bf16(x1, b1, p);
+        if (st & 1) {
+          // Steps 2 i and 2 i + 1 cover the 128 k of the segment's block i.
+          const float sc = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s.sc), st >> 1));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, p[i], acc[i]);
+          p = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
       }
     }
-    if (jw < j1) {
-      load(s0, jw, Ragged{});
-      consume(s0, jw);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // x[M][window] of unit t into LDS, between two barriers, if it is not
+  // there already (the same decision in every wave).
+  int staged_l = -1, staged_c = -1;
+  auto stage = [&](const TileUnit& t) {
+    const LinDesc& L = a.lin[t.l];
+    const int win = t.spc * kSegChunksT * XC;                    // x chunks per token in LDS
+    xstride = win + 1;
+    xw0 = t.j0 * kSegChunksT * XC;
+    xrow = xs + (n < a.M ? n : a.M) * xstride;
+    if (t.l == staged_l && t.chunk == staged_c) return;
+    staged_l = t.l;
+    staged_c = t.chunk;
+    const int xcpr = L.K >> 3;                                   // x chunks per token
+    __syncthreads();                                             // all done with the old window
+    // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
+    // then a zero row that lanes of absent tokens read.
+    const int wlen = min(win, xcpr - xw0);
+    const int cnt = a.M * wlen;
+    for (int b = threadIdx.x; b < cnt; b += 8 * kThreads) {
+      u32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = min(b + r * kThreads, cnt - 1);
+        const int m = i / wlen;
+        v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = b + r * kThreads;
+        const int m = i / wlen;
+        if (i < cnt) xs[m * xstride + (i - m * wlen)] = v[r];
+      }
     }
+    const int pad = win - wlen;
+    for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
+      const int m = i / pad;
+      xs[m * xstride + wlen + (i - m * pad)] = zero4();
+    }
+    for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
+    __syncthreads();
+  };
+  auto epilogue = [&](const TileUnit& t) {
     // Lane (n, g) holds D[4 g + i][n]: token 4 g + i, row row0 + n.
-    const int row = row0 + n;
-    const long long slot = L.slot_base + (long long)grp * L.chunks + chunk;
+    const LinDesc& L = a.lin[t.l];
+    const int row = t.grp * kGroupRows + wv * kTileRows + n;
+    const long long slot = L.slot_base + (long long)t.grp * L.chunks + t.chunk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
@@ -555,29 +552,82 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
         }
       }
     }
+    acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  // The segments of unit t, the first of which is already loading into A.
+  // Ends with the first segment of unit nx (if has_next) loading into A when
+  // t has an even number of segments, into B when odd; returns which.
+  auto run_unit = [&](TileSeg<DT>& A, TileSeg<DT>& B, const TileUnit& t, const TileUnit& nx,
+                      bool has_next) {
+    int j = t.j0;
+    for (; j + 2 < t.j1; j += 2) {
+      load(B, t, j + 1);
+      consume(A, t, j);
+      load(A, t, j + 2);
+      consume(B, t, j + 1);
+    }
+    if (j + 2 == t.j1) {
+      load(B, t, j + 1);
+      consume(A, t, j);
+      if (has_next) load(A, nx, nx.j0);
+      consume(B, t, j + 1);
+      return 0;
+    }
+    if (has_next) load(B, nx, nx.j0);
+    consume(A, t, j);
+    return 1;
+  };
+  long long u = blockIdx.x;
+  if (u >= a.S) return;
+  TileSeg<DT> s0, s1;
+  TileUnit cur = decode(u);
+  load(s0, cur, cur.j0);
+  int in_b = 0;                                         // the current unit's first segment is in s1
+  for (;;) {
+    const bool has_next = u + a.G < a.S;
+    const TileUnit nx = has_next ? decode(u + a.G) : cur;
+    stage(cur);
+    const int flip = in_b ? run_unit(s1, s0, cur, nx, has_next)
+                          : run_unit(s0, s1, cur, nx, has_next);
+    epilogue(cur);
+    if (!has_next) break;
+    in_b ^= flip;
+    cur = nx;
+    u += a.G;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Second pass: for every output of a split linear, the sum of its K-chunks'
-// partial results in chunk order.  blockIdx.y is the linear.
+// partial results in chunk order.  blockIdx.y is the linear; thread t of
+// the grid row takes four adjacent rows (one 16-byte slot read per chunk; a
+// row group's height is a multiple of four) of one token, so the chunks'
+// loads of a thread are all in flight together.
+constexpr int kCombineRows = 4;
 __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchArgs a) {
   const LinDesc& L = a.lin[blockIdx.y];
   if (L.chunks == 1) return;
   const int R = a.band_rows;
-  const int outs = a.M * L.N;
-  for (int i = blockIdx.x * kCombineThreads + threadIdx.x; i < outs;
-       i += gridDim.x * kCombineThreads) {
-    const int m = i / L.N;
-    const int row = i - m * L.N;
-    const int grp = row / R;
-    const int rr = row - grp * R;
-    const float* p = a.slots + ((size_t)(L.slot_base + (long long)grp * L.chunks) * a.M + m) * R + rr;
-    const size_t stride = (size_t)a.M * R;
-    float sum = 0.0f;
-    for (int c = 0; c < L.chunks; ++c) sum += p[c * stride];
-    L.y[(size_t)m * L.N + row] = (__bf16)sum;
+  const int quads = (L.N + kCombineRows - 1) / kCombineRows;   // per token
+  const int i = blockIdx.x * kCombineThreads + threadIdx.x;
+  if (i >= a.M * quads) return;
+  const int m = i / quads;
+  const int row = (i - m * quads) * kCombineRows;
+  const int grp = row / R;
+  const int rr = row - grp * R;
+  const f32x4* p = reinterpret_cast<const f32x4*>(
+      a.slots + ((size_t)(L.slot_base + (long long)grp * L.chunks) * a.M + m) * R + rr);
+  const size_t stride = (size_t)a.M * R / kCombineRows;        // one chunk's slot, in f32x4
+  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < L.chunks; ++c) {
+    const f32x4 v = p[c * stride];
+#pragma unroll
+    for (int r = 0; r < kCombineRows; ++r) sum[r] += v[r];
   }
+  __bf16* y = L.y + (size_t)m * L.N + row;
+#pragma unroll
+  for (int r = 0; r < kCombineRows; ++r)
+    if (row + r < L.N) y[r] = (__bf16)sum[r];
 }
 
 // ---------------------------------------------------------------------------
@@ -781,6 +831,7 @@ template <int DT>
 KernelChoice tiles_kernel() {
   constexpr int WPB = kTilesWavesPerBlock;
   static_assert(kScaleBlock % (kTileRows * WPB) == 0, "a row group must sit in one scale block");
+  static_assert((kTileRows * WPB) % kCombineRows == 0, "second-pass quads");
   KernelChoice k;
   k.fn = skinny_tiles<DT, WPB>;
   k.band_rows = kTileRows * WPB;
@@ -794,6 +845,7 @@ KernelChoice rows_kernel() {
   constexpr int WPB = kRowsWavesPerBlock;
   constexpr int R = rows_r(MT);
   static_assert(kScaleBlock % (WPB * R) == 0, "a row group must sit in one scale block");
+  static_assert((WPB * R) % kCombineRows == 0, "second-pass quads");
   KernelChoice k;
   k.fn = skinny_rows<DT, MT, rows_u(MT, DT), R, WPB>;
   k.band_rows = WPB * R;
@@ -990,11 +1042,12 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   if (ev_after && hipEventRecord(ev_after, stream) != hipSuccess) return SKINNY_ERR_HIP;
   // Second pass over the split linears (grid row y = linear; unsplit ones return).
   long long most = 0;
-  for (int i = 0; i < count; ++i)
-    if (a.lin[i].chunks > 1 && (long long)M * a.lin[i].N > most) most = (long long)M * a.lin[i].N;
+  for (int i = 0; i < count; ++i) {
+    const long long quads = (long long)M * ((a.lin[i].N + kCombineRows - 1) / kCombineRows);
+    if (a.lin[i].chunks > 1 && quads > most) most = quads;
+  }
   if (most > 0) {
-    long long cblocks = (most + kCombineThreads - 1) / kCombineThreads;
-    if (cblocks > 256) cblocks = 256;
+    const long long cblocks = (most + kCombineThreads - 1) / kCombineThreads;
     hipLaunchKernelGGL(skinny_combine, dim3((unsigned)cblocks, count), dim3(kCombineThreads), 0,
                        stream, a);
     if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
