@@ -718,7 +718,13 @@ constexpr int rows_r(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : 4; }
 constexpr int rows_u(int M, int dtype) { return (dtype == SKINNY_BF16 ? 8 : 4) / rows_r(M); }
 constexpr int kRowsXBudget = 64 * 1024;   // LDS for x per workgroup: two workgroups per CU
 constexpr int kRowsMaxM = 8;
-constexpr int kUnitsPerWorker = 16;
+// Units per workgroup below which a launch cuts K into more chunks for
+// parallelism.  Measured on MI355X (TP=8 layer, QKV GEMV): for the row kernel
+// the second pass a split needs costs more than the idle workgroups (GEMV
+// 10.7 -> 8.0 us without it); the tile kernel's units are 64 rows high and
+// it gains from the split (TP=8 layer at M = 1: 52.8 -> 45.5 us).
+constexpr int kRowsUnitsPerWorker = 0;
+constexpr int kTilesUnitsPerWorker = 16;
 
 // Fewest K-chunks of a linear whose x window (M tokens x chunk) fits the budget.
 int rows_lds_chunks(int dtype, int M, int K) {
@@ -961,14 +967,14 @@ int kernel_lds(const KernelChoice& k, int dtype) {
 }
 
 // K-chunks per linear (either kernel): enough for the x window to fit the LDS
-// budget and, when the launch is too small to give every workgroup about
-// kUnitsPerWorker units, more - but never fewer segments per chunk than a
-// wave keeps in flight.  Assigns the partial slots of the split linears.
+// budget and, when the launch is too small to give every workgroup the
+// kernel's units per worker, more - but never fewer segments per chunk than
+// a wave keeps in flight.  Assigns the partial slots of the split linears.
 void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
   const int rows = a.band_rows;
   long long groups = 0;
   for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
-  const long long want = (long long)kUnitsPerWorker * G;
+  const long long want = (long long)(tiles ? kTilesUnitsPerWorker : kRowsUnitsPerWorker) * G;
   const long long par = (want + groups - 1) / groups;
   long long slots = 0;
   for (int i = 0; i < count; ++i) {

@@ -137,14 +137,15 @@ def test_page_example_split_k_partials_in_workspace():
     a_m = np.array([[((8 * i + j) % 7) - 3 for j in range(8)] for i in range(4)], np.float64)
     b_m = np.array([[((4 * i + j) % 5) - 2 for j in range(4)] for i in range(8)], np.float64)
     h = np.maximum(x @ a_m, 0.0)                 # inputs of the second product (integers)
-    K = 8192                                     # halves 4096 apart: never in one K-chunk
+    # x of two tokens over K = 32768 is larger than either kernel's LDS window,
+    # so both cut K into chunks and the halves, K / 2 apart, land in different ones.
+    K = 32768
     hp = np.zeros((2, K)); hp[:, 0:4] = h[:, 0:4]; hp[:, K // 2:K // 2 + 4] = h[:, 4:8]
     wp = np.zeros((4, K)); wp[:, 0:4] = b_m[0:4].T; wp[:, K // 2:K // 2 + 4] = b_m[4:8].T
     for var in variants_for(2):
         ws = workspace(2, 4, K)
         ws.zero_()
-        # A small grid makes the planner cut K into several chunks.
-        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, waves=8, ws=ws)
+        y = run_bf16(codes_of(hp), codes_of(wp), 2, 4, variant=var, ws=ws)
         assert host_values(y).tolist() == d["sum_printed"]
         slots = ws.view(torch.float32).cpu().numpy()
         # Slots [slot][M][band rows]; only the two slots whose K range holds
