@@ -811,9 +811,10 @@ size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int 
 // and stacks, the TP=8 layer).  Row streaming keeps one contiguous stream per
 // wave, but its vector work per weight grows with M (and FP8 adds a half-rate
 // conversion); the matrix-core kernel's does not.  bf16 TP=1 layer, rows vs
-// tiles: 6.10 / 5.92 TB/s at M = 1, 5.72 / 5.66 at M = 2, 5.37 / 5.42 at
-// M = 4; FP8 TP=1 stack at M = 1: 5.85 / 5.93.
-constexpr int kRowsMaxAutoMBf16 = 2;
+// tiles: 6.10 / 5.92 TB/s at M = 1, 5.81 / 5.82 at M = 2, 5.37 / 5.42 at
+// M = 4; TP=8 layer at M = 2: 53.8 / 45.7 us (the row kernel's registers
+// leave one workgroup per CU there); FP8 TP=1 stack at M = 1: 5.85 / 5.93.
+constexpr int kRowsMaxAutoMBf16 = 1;
 constexpr int kRowsMaxAutoMFp8 = 0;
 
 int auto_variant(const skinny_linear* const* lin, int count, int M) {
