@@ -267,7 +267,8 @@ def main():
             "gpu": torch.cuda.get_device_name(0),
         },
         "roofline": {
-            "kernel": "skinny_main",
+            "kernel": {1: "skinny_rows", 2: "skinny_tiles"}.get(
+                plan.variant if variant == sg.VARIANT_AUTO else variant, "skinny_main"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -27,7 +27,8 @@ def _gpu():
 
 # --- random inputs: several tiles, ragged tails, every M ------------------------
 
-SHAPES = [(1, 8), (17, 264), (100, 1000), (257, 3696), (1280, 8192)]
+# K = 20480: an odd number of whole row-kernel batches; K = 3696: ragged row ends.
+SHAPES = [(1, 8), (17, 264), (100, 1000), (257, 3696), (1280, 8192), (300, 20480)]
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 8, 16])
