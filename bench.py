@@ -39,6 +39,8 @@ WORKLOADS = {
     "qwen2.5-72b-tp8-layer-bf16": "one layer's TP=8 shard: QKV 1280x8192, O 8192x1024, "
                                   "gate_up 7392x8192, down 8192x3696, bf16 W",
     "qwen2.5-72b-tp8-qkv-gemv-bf16": "QKV shard GEMV 1280x8192, bf16 W",
+    "qwen2.5-72b-lm-head-argmax-bf16": "vocabulary projection 152064x8192, bf16 W, then the greedy "
+                                       "token of each row on the device",
 }
 
 
@@ -77,6 +79,8 @@ def make_workload(name):
         return wl.tp8_layer(wl.BF16)
     if name == "qwen2.5-72b-tp8-qkv-gemv-bf16":
         return wl.qkv_tp8_gemv()
+    if name == "qwen2.5-72b-lm-head-argmax-bf16":
+        return wl.lm_head(wl.BF16)
     raise ValueError(name)
 
 
@@ -175,7 +179,9 @@ def main():
     sg.lib()
     M = args.m
     specs = make_workload(args.workload)
-    step_bytes = wl.algorithmic_bytes(specs, M)
+    head = args.workload.startswith("qwen2.5-72b-lm-head")
+    # The greedy token adds M int32 outputs to the step's bytes.
+    step_bytes = wl.algorithmic_bytes(specs, M) + (4 * M if head else 0)
     step_flops = wl.flops(specs, M)
     copies = 1 if step_bytes >= args.rotate_bytes else int(np.ceil(args.rotate_bytes / step_bytes))
     log(f"workload {args.workload}: {len(specs)} linears, M={M}, {step_bytes / 1e9:.3f} GB/step, "
@@ -191,8 +197,15 @@ def main():
     plan = sg.plan_query(sets[0], M)
     n_launch = sg.launch_count(sets[0])
 
+    tokens = [torch.zeros(M, dtype=torch.int32, device="cuda") for _ in range(copies)]
+
     def step(i):
-        sg.linear_run(sets[i % copies], M, ws, variant=variant, waves=args.waves)
+        if head:
+            if variant != sg.VARIANT_AUTO or args.waves:
+                sys.exit("the lm-head workload runs the automatic plan")
+            sg.lm_head_argmax(sets[i % copies][0], M, tokens[i % copies], ws)
+        else:
+            sg.linear_run(sets[i % copies], M, ws, variant=variant, waves=args.waves)
 
     for i in range(args.warmup):
         step(i)

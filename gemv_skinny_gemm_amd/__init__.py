@@ -16,7 +16,8 @@ __all__ = [
     "SkinnyError", "Linear", "Plan", "lib", "lib_path",
     "workspace_bytes", "stack_workspace_bytes", "skinny_gemm_bf16", "skinny_gemm_fp8_bs128",
     "decode_linear_stack", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
-    "status_string", "abi_version",
+    "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
+    "lm_head_workspace_bytes",
 ]
 
 BF16 = 0
@@ -87,6 +88,14 @@ def _bind(path: str):
     L.skinny_band_rows.argtypes = [i, i, i]
     L.skinny_plan_query.restype = i
     L.skinny_plan_query.argtypes = [lp, i, i, ctypes.POINTER(Plan)]
+    L.skinny_argmax_workspace_bytes.restype = sz
+    L.skinny_argmax_workspace_bytes.argtypes = [i, i]
+    L.skinny_argmax_bf16.restype = i
+    L.skinny_argmax_bf16.argtypes = [vp, i, i, vp, vp, sz, vp]
+    L.skinny_lm_head_workspace_bytes.restype = sz
+    L.skinny_lm_head_workspace_bytes.argtypes = [lp, i]
+    L.skinny_lm_head_argmax.restype = i
+    L.skinny_lm_head_argmax.argtypes = [lp, i, vp, vp, sz, vp]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_status_string.argtypes = [i]
     L.skinny_abi_version.restype = i
@@ -245,3 +254,31 @@ def plan_query(linears, M: int) -> Plan:
     plan = Plan()
     _check(lib().skinny_plan_query(arr, len(linears), M, ctypes.byref(plan)), "skinny_plan_query")
     return plan
+
+
+def argmax_workspace_bytes(M: int, N: int) -> int:
+    return lib().skinny_argmax_workspace_bytes(M, N)
+
+
+def argmax_bf16(y, idx, workspace, stream=None):
+    """idx[m] = smallest index of the largest value of y[m] (bf16 [M][N] and
+    int32 [M] tensors on the GPU; idx written in place)."""
+    M, N = _shape2(y)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_argmax_bf16(_ptr(y), M, N, _ptr(idx), wp, wb, _stream(stream)),
+           "skinny_argmax_bf16")
+    return idx
+
+
+def lm_head_workspace_bytes(head: Linear, M: int) -> int:
+    return lib().skinny_lm_head_workspace_bytes(_linear_array([head]), M)
+
+
+def lm_head_argmax(head: Linear, M: int, next_token, workspace, stream=None):
+    """Run the vocabulary projection `head` (its y = logits) and write the
+    greedy token of each of the M rows into next_token (int32 [M] on the GPU)."""
+    arr = _linear_array([head])
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_lm_head_argmax(arr, M, _ptr(next_token), wp, wb, _stream(stream)),
+           "skinny_lm_head_argmax")
+    return next_token

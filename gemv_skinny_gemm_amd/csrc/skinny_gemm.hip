@@ -631,6 +631,100 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchAr
 }
 
 // ---------------------------------------------------------------------------
+// Greedy next token: for each token, the smallest index of the largest logit
+// ("Developing a custom Qwen2.5 72B inference engine from scratch - what is
+// the real bottleneck?", section 5, third lever: pick the next token on the
+// GPU instead of copying the logits to the host).  Two passes, no atomics:
+// workgroup (b, m) of the first reduces slice b of row m (kArgmaxSlice
+// logits) to one (value, index) pair in the workspace; the second reduces
+// each row's pairs.  Pairs are ordered by value, then by lower index, so
+// the result does not depend on the reduction order.  NaN compares below
+// every number.
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxSlice = 4096;                    // logits per first-pass workgroup
+constexpr int kArgmaxMaxSlices = 1 << 20;
+
+__device__ __forceinline__ void argmax_take(float v, int i, float& bv, int& bi) {
+  if (v != v) v = -__builtin_inff();
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+// (value, index) of the workgroup into lane 0 of wave 0.
+__device__ __forceinline__ void argmax_block(float& bv, int& bi) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    argmax_take(ov, oi, bv, bi);
+  }
+  __shared__ float sv[kArgmaxThreads / 64];
+  __shared__ int si[kArgmaxThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wv] = bv;
+    si[wv] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kArgmaxThreads / 64; ++w) argmax_take(sv[w], si[w], bv, bi);
+}
+
+struct ArgmaxPair {
+  float v;
+  int i;
+};
+
+// VEC: N % 8 == 0 and 16-byte aligned rows, 8 logits per load.
+template <bool VEC>
+__global__ __launch_bounds__(kArgmaxThreads) void skinny_argmax_slices(const __bf16* y, int N,
+                                                                       ArgmaxPair* pairs) {
+  const int m = blockIdx.y;
+  const int n0 = blockIdx.x * kArgmaxSlice;
+  const int n1 = min(n0 + kArgmaxSlice, N);
+  const __bf16* row = y + (size_t)m * N;
+  float bv = -__builtin_inff();
+  int bi = N;                                         // loses to any element
+  if constexpr (VEC) {
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
+    constexpr int kPer = kArgmaxSlice / 8 / kArgmaxThreads;   // loads per thread
+    u32x4 v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) v[q] = r4[min((n0 / 8) + q * kArgmaxThreads + (int)threadIdx.x,
+                                                  N / 8 - 1)];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int c = n0 / 8 + q * kArgmaxThreads + threadIdx.x;
+      if (8 * c < n1) {
+        const bf16x8 e = __builtin_bit_cast(bf16x8, v[q]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) argmax_take((float)e[k], 8 * c + k, bv, bi);
+      }
+    }
+  } else {
+    for (int n = n0 + threadIdx.x; n < n1; n += kArgmaxThreads) argmax_take((float)row[n], n, bv, bi);
+  }
+  argmax_block(bv, bi);
+  if (threadIdx.x == 0) pairs[(size_t)m * gridDim.x + blockIdx.x] = ArgmaxPair{bv, bi};
+}
+
+__global__ __launch_bounds__(kArgmaxThreads) void skinny_argmax_rows(const ArgmaxPair* pairs,
+                                                                     int slices, int N, int* idx) {
+  const int m = blockIdx.x;
+  float bv = -__builtin_inff();
+  int bi = N;
+  for (int b = threadIdx.x; b < slices; b += kArgmaxThreads) {
+    const ArgmaxPair p = pairs[(size_t)m * slices + b];
+    argmax_take(p.v, p.i, bv, bi);
+  }
+  argmax_block(bv, bi);
+  if (threadIdx.x == 0) idx[m] = bi;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 struct DeviceInfo {
@@ -1159,6 +1253,43 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   });
 }
 
+int argmax_slices(int N) { return (N + kArgmaxSlice - 1) / kArgmaxSlice; }
+
+size_t argmax_workspace(int M, int N) {
+  const size_t b = (size_t)M * argmax_slices(N) * sizeof(ArgmaxPair);
+  return b > SKINNY_MIN_WORKSPACE_BYTES ? b : SKINNY_MIN_WORKSPACE_BYTES;
+}
+
+skinny_status launch_argmax(const void* y, int M, int N, int* idx, void* ws, hipStream_t stream) {
+  const int slices = argmax_slices(N);
+  ArgmaxPair* pairs = (ArgmaxPair*)ws;
+  if (N % 8 == 0 && aligned(y, 16))
+    hipLaunchKernelGGL(skinny_argmax_slices<true>, dim3(slices, M), dim3(kArgmaxThreads), 0,
+                       stream, (const __bf16*)y, N, pairs);
+  else
+    hipLaunchKernelGGL(skinny_argmax_slices<false>, dim3(slices, M), dim3(kArgmaxThreads), 0,
+                       stream, (const __bf16*)y, N, pairs);
+  if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+  hipLaunchKernelGGL(skinny_argmax_rows, dim3(M), dim3(kArgmaxThreads), 0, stream,
+                     (const ArgmaxPair*)pairs, slices, N, idx);
+  return hipGetLastError() == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP;
+}
+
+// y, idx and the workspace: present, aligned, within limits and disjoint.
+skinny_status check_argmax(const void* y, int M, int N, const int* idx, const void* ws,
+                           size_t ws_bytes) {
+  if (!y || !idx || M < 1 || M > SKINNY_MAX_M || N < 1) return SKINNY_ERR_INVALID_ARG;
+  if (argmax_slices(N) > kArgmaxMaxSlices) return SKINNY_ERR_UNSUPPORTED;
+  if (!aligned(y, 2) || !aligned(idx, 4)) return SKINNY_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < argmax_workspace(M, N)) return SKINNY_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
+  const Range yr{(uintptr_t)y, (uintptr_t)y + (size_t)M * N * 2};
+  const Range ir{(uintptr_t)idx, (uintptr_t)idx + (size_t)M * 4};
+  const Range wr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
+  if (overlap(yr, ir) || overlap(yr, wr) || overlap(ir, wr)) return SKINNY_ERR_INVALID_ARG;
+  return SKINNY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1272,6 +1403,57 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   st = auto_workers(d, k, lds, &workers);
   out->waves = workers * k.wpb;
   return st;
+}
+
+size_t skinny_argmax_workspace_bytes(int M, int N) {
+  if (M < 1 || M > SKINNY_MAX_M || N < 1) return 0;
+  return argmax_workspace(M, N);
+}
+
+skinny_status skinny_argmax_bf16(const void* y, int M, int N, int* idx, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  skinny_status st = check_argmax(y, M, N, idx, workspace, workspace_bytes);
+  if (st != SKINNY_OK) return st;
+  DeviceInfo d;
+  st = device_info(&d);
+  if (st != SKINNY_OK) return st;
+  if (!d.gfx950) return SKINNY_ERR_UNSUPPORTED;
+  return launch_argmax(y, M, N, idx, workspace, (hipStream_t)stream);
+}
+
+size_t skinny_lm_head_workspace_bytes(const skinny_linear* head, int M) {
+  if (!head || M < 1 || M > SKINNY_MAX_M) return 0;
+  const size_t lin = skinny_stack_workspace_bytes(head, 1, M);
+  if (lin == 0) return 0;
+  const size_t am = argmax_workspace(M, head->N);
+  return lin > am ? lin : am;
+}
+
+skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_token,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!head) return SKINNY_ERR_INVALID_ARG;
+  skinny_status st = check_linear(*head, M);
+  if (st != SKINNY_OK) return st;
+  st = check_argmax(head->y, M, head->N, next_token, workspace, workspace_bytes);
+  if (st != SKINNY_OK) return st;
+  // next_token must not overlap any operand of the linear either.
+  const Range ir{(uintptr_t)next_token, (uintptr_t)next_token + (size_t)M * 4};
+  const size_t wbytes = (size_t)head->N * head->K * (head->dtype == SKINNY_BF16 ? 2 : 1);
+  const Range others[] = {
+      {(uintptr_t)head->x, (uintptr_t)head->x + (size_t)M * head->K * 2},
+      {(uintptr_t)head->w, (uintptr_t)head->w + wbytes}};
+  for (const Range& r : others)
+    if (overlap(ir, r)) return SKINNY_ERR_INVALID_ARG;
+  if (head->w_scale) {
+    const size_t sb = (size_t)((head->N + 127) / 128) * ((head->K + 127) / 128) * 4;
+    if (overlap(ir, Range{(uintptr_t)head->w_scale, (uintptr_t)head->w_scale + sb}))
+      return SKINNY_ERR_INVALID_ARG;
+  }
+  // The workspace serves the linear's partial sums, then (stream order: the
+  // linear is done with them) the argmax pairs.
+  st = run(head, 1, M, nullptr, workspace, workspace_bytes, stream);
+  if (st != SKINNY_OK) return st;
+  return launch_argmax(head->y, M, head->N, next_token, workspace, (hipStream_t)stream);
 }
 
 const char* skinny_status_string(int status) {

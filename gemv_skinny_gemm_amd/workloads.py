@@ -77,6 +77,18 @@ def tp1_stack(dtype: int = BF16, layers: int = LAYERS) -> list[LinearSpec]:
     return [_spec(tag, l, n, N, K, dtype) for l in range(layers) for n, N, K in TP1_SHAPES]
 
 
+# The page gives the vocabulary as ~152k; 152,064 (a multiple of 128, so the
+# FP8 scale blocks tile it) is taken as the concrete size.
+VOCAB = 152064
+HIDDEN = 8192
+
+
+def lm_head(dtype: int = BF16) -> list[LinearSpec]:
+    """The vocabulary projection after the last layer: W VOCAB x HIDDEN (the
+    logits of the greedy next token)."""
+    return [_spec("head", None, "lm_head", VOCAB, HIDDEN, dtype)]
+
+
 def algorithmic_bytes(specs, M: int) -> int:
     return sum(s.algorithmic_bytes(M) for s in specs)
 

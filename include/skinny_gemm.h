@@ -156,6 +156,35 @@ int skinny_band_rows(int dtype, int variant, int M);
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);
 
+/* Greedy next token: idx[m] = the smallest n such that y[m][n] is the largest
+ * of y[m][0..N), comparing the bf16 values (NaN compares below every number,
+ * so a row of NaNs gives 0).  This is the decode step's on-device argmax
+ * ("Developing a custom Qwen2.5 72B inference engine from scratch - what is
+ * the real bottleneck?", section 5, third lever: pick the next token on the
+ * GPU rather than copying the logits back to the host).
+ *   y          [M][N] bf16, device, 2-byte aligned (read 16 bytes at a time
+ *              when y is 16-byte aligned and N % 8 == 0)
+ *   idx        [M] int32, device, 4-byte aligned, written
+ *   workspace  device, 16-byte aligned, >= skinny_argmax_workspace_bytes(M, N)
+ *              (a (value, index) pair per 4096 logits of a row)
+ * y, idx and the workspace must not overlap.  1 <= M <= SKINNY_MAX_M, N >= 1;
+ * errors are returned before anything is enqueued.  Two launches, no
+ * atomics; the result does not depend on the launch. */
+size_t skinny_argmax_workspace_bytes(int M, int N);
+skinny_status skinny_argmax_bf16(const void* y, int M, int N, int* idx, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* The vocabulary projection and its greedy token in one call (same section
+ * and lever): runs the one linear `head` (N = vocabulary size, K = hidden
+ * size, head->y = the logits [M][N], written) exactly as decode_linear_stack
+ * would, then skinny_argmax_bf16 over those logits into next_token[M] (device
+ * int32).  next_token must not overlap x, W, w_scale, y or the workspace.  The
+ * workspace serves the linear, then the argmax (stream order), so it needs
+ * skinny_lm_head_workspace_bytes(head, M) bytes (0 for invalid arguments). */
+size_t skinny_lm_head_workspace_bytes(const skinny_linear* head, int M);
+skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_token,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* skinny_status_string(int status);
 

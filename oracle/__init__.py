@@ -7,6 +7,10 @@ loads it, and it loads nothing of the GPU library.
 The arithmetic lives in ``oracle.c`` (plain C, fp64, threaded over output
 rows).  This module builds it with gcc when needed and marshals numpy arrays.
 
+Greedy next token (``argmax_first``): the smallest index of the largest logit
+of each token row, NaN below every number; ``greedy_valid`` decides whether a
+GPU's choice is one the stated error bound allows.
+
 Definition followed (see oracle.c for the citations):
     y_ref[m][n] = sum_k x[m][k] * w[n][k]            in fp64
     w[n][k]     = bf16 value                         (bf16 weights)
@@ -162,3 +166,35 @@ def check(y_gpu: np.ndarray, y_ref: np.ndarray, a: np.ndarray, bf16_rounding: bo
     idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     worst = float(ratio[idx])
     return bool(np.all(ratio <= 1.0)), worst, idx
+
+
+def argmax_first(values: np.ndarray) -> np.ndarray:
+    """Greedy token of every row of ``values`` [M][N]: the smallest n whose
+    value is the largest of the row, NaN counting below every number (so a row
+    of NaNs gives 0).  The decode step picks its next token this way on the
+    device ("Developing a custom Qwen2.5 72B inference engine from scratch",
+    section 5, third lever).  A plain scan, row by row."""
+    v = np.asarray(values, np.float64)
+    out = np.zeros(v.shape[0], np.int64)
+    for m in range(v.shape[0]):
+        best_i = 0
+        best_v = -np.inf if np.isnan(v[m, 0]) else v[m, 0]
+        for n in range(1, v.shape[1]):
+            x = v[m, n]
+            if not np.isnan(x) and x > best_v:
+                best_v, best_i = x, n
+        out[m] = best_i
+    return out
+
+
+def greedy_valid(idx: np.ndarray, y_ref: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """Whether each chosen token idx[m] is a largest logit of some set of
+    outputs within the per-output bound of the exact ones: with |y - y_ref| <=
+    b (b = the bound plus half a bf16 ulp of y_ref, the output rounding), a
+    token i beats every j only if y_ref[i] + b[i] >= max_j (y_ref[j] - b[j]).
+    When the exact winner leads every other logit by more than both bounds,
+    this admits it alone."""
+    b = bound(a, y_ref)
+    lo = np.max(y_ref - b, axis=1)
+    rows = np.arange(y_ref.shape[0])
+    return (y_ref[rows, idx] + b[rows, idx]) >= lo

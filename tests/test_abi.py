@@ -154,3 +154,38 @@ def test_rejects_shapes_beyond_32_bit_indexing():
     wsb = sg.workspace_bytes(sg.BF16, 1, 64, 64)
     assert bf16_call(N=(1 << 26) + 1, wsb=wsb) == UNSUPPORTED
     assert bf16_call(K=(1 << 28) + 8, wsb=wsb) == UNSUPPORTED
+
+
+def test_argmax_rejects_bad_arguments():
+    L = sg.lib()
+    wsb = sg.argmax_workspace_bytes(2, 64)
+    assert wsb == MIN_WORKSPACE and sg.argmax_workspace_bytes(1, 152064) == 38 * 8
+    assert sg.argmax_workspace_bytes(16, 152064) == 16 * 38 * 8      # a pair per 4096 logits
+    assert sg.argmax_workspace_bytes(0, 64) == 0 and sg.argmax_workspace_bytes(17, 64) == 0
+    Y, I = B, C                                          # y [2][64] at B, idx at C
+    assert L.skinny_argmax_bf16(None, 2, 64, I, WS, wsb, None) == INVALID
+    assert L.skinny_argmax_bf16(Y, 0, 64, I, WS, wsb, None) == INVALID
+    assert L.skinny_argmax_bf16(Y, 17, 64, I, WS, wsb, None) == INVALID
+    assert L.skinny_argmax_bf16(Y, 2, 0, I, WS, wsb, None) == INVALID
+    assert L.skinny_argmax_bf16(Y, 2, 64, Y + 4, WS, wsb, None) == INVALID          # idx in y
+    assert L.skinny_argmax_bf16(Y, 2, 64, WS + 16, WS, wsb, None) == INVALID        # idx in ws
+    assert L.skinny_argmax_bf16(Y, 2, 64, I + 2, WS, wsb, None) == UNSUPPORTED      # misaligned
+    assert L.skinny_argmax_bf16(Y + 1, 2, 64, I, WS, wsb, None) == UNSUPPORTED
+    assert L.skinny_argmax_bf16(Y, 2, 64, I, None, wsb, None) == WORKSPACE
+    assert L.skinny_argmax_bf16(Y, 2, 64, I, WS, wsb - 1, None) == WORKSPACE
+
+
+def test_lm_head_rejects_bad_arguments():
+    L = sg.lib()
+    head = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)
+    arr = (sg.Linear * 1)(head)
+    wsb = sg.lm_head_workspace_bytes(head, 1)
+    assert wsb >= MIN_WORKSPACE and sg.lm_head_workspace_bytes(head, 0) == 0
+    T = 0x6000000                                        # next_token
+    assert L.skinny_lm_head_argmax(None, 1, T, WS, wsb, None) == INVALID
+    assert L.skinny_lm_head_argmax(arr, 1, None, WS, wsb, None) == INVALID
+    assert L.skinny_lm_head_argmax(arr, 1, A + 64, WS, wsb, None) == INVALID       # inside W
+    assert L.skinny_lm_head_argmax(arr, 1, B, WS, wsb, None) == INVALID            # inside x
+    assert L.skinny_lm_head_argmax(arr, 1, C + 4, WS, wsb, None) == INVALID        # inside y
+    assert L.skinny_lm_head_argmax(arr, 1, T, WS, 0, None) == WORKSPACE
+    assert L.skinny_lm_head_argmax(arr, 17, T, WS, wsb, None) == INVALID

@@ -287,3 +287,34 @@ def test_bf16_half_ulp_covers_exact_rounding():
     ok, _, _ = oracle.check(np.array([[0.0751953125]]), np.array([[0.07497585]]),
                             np.array([[0.09527504]]), bf16_rounding=True)
     assert ok
+
+
+# --- greedy next token ------------------------------------------------------
+
+def test_argmax_first_fixed_cases():
+    inf, nan = np.inf, np.nan
+    cases = [([[1.0, 3.0, 3.0, 2.0]], [1]),            # ties: the first
+             ([[nan, -inf, -5.0]], [2]),                # NaN below every number
+             ([[nan, nan]], [0]),                       # a row of NaNs
+             ([[-inf, -inf, -inf]], [0]),
+             ([[0.0, -0.0]], [0]),                      # -0 == +0: the first
+             ([[5.0], [-1.0]], [0, 0]),
+             ([[1.0, 2.0, inf, inf, nan]], [2])]
+    for v, want in cases:
+        assert oracle.argmax_first(np.array(v)).tolist() == want
+
+
+def test_argmax_first_matches_numpy_on_random_rows():
+    rng = np.random.default_rng(11)
+    v = rng.integers(-20, 20, size=(7, 5000)).astype(np.float64)   # many ties
+    assert oracle.argmax_first(v).tolist() == np.argmax(v, axis=1).tolist()
+
+
+def test_greedy_valid_admits_only_the_winner_when_the_gap_is_wide():
+    y_ref = np.array([[1.0, 5.0, 4.9, -2.0]])
+    a = np.array([[1.0, 1.0, 1.0, 1.0]])              # bounds 2e-3 + half a bf16 ulp (1/64 at 5)
+    assert oracle.greedy_valid(np.array([1]), y_ref, a).tolist() == [True]
+    assert oracle.greedy_valid(np.array([2]), y_ref, a).tolist() == [False]
+    wide = np.array([[1.0, 5000.0, 5000.0, 1.0]])     # bounds of 10: 4.9 is within reach
+    assert oracle.greedy_valid(np.array([2]), y_ref, wide).tolist() == [True]
+    assert oracle.greedy_valid(np.array([3]), y_ref, wide).tolist() == [False]
