@@ -41,6 +41,9 @@ WORKLOADS = {
     "qwen2.5-72b-tp8-qkv-gemv-bf16": "QKV shard GEMV 1280x8192, bf16 W",
     "qwen2.5-72b-lm-head-argmax-bf16": "vocabulary projection 152064x8192, bf16 W, then the greedy "
                                        "token of each row on the device",
+    "qwen2.5-72b-tp1-mlp-swiglu-bf16": "one layer's gated MLP at TP=1: gate_up 59136x8192, silu(g)*u "
+                                       "fused into down's input staging, down 8192x29568, bf16 W",
+    "qwen2.5-72b-tp1-mlp-swiglu-fp8": "the same gated MLP with FP8-E4M3 W + 128x128 fp32 block scales",
 }
 
 
@@ -81,6 +84,10 @@ def make_workload(name):
         return wl.qkv_tp8_gemv()
     if name == "qwen2.5-72b-lm-head-argmax-bf16":
         return wl.lm_head(wl.BF16)
+    if name == "qwen2.5-72b-tp1-mlp-swiglu-bf16":
+        return wl.mlp(1, wl.BF16)
+    if name == "qwen2.5-72b-tp1-mlp-swiglu-fp8":
+        return wl.mlp(1, wl.FP8_BS128)
     raise ValueError(name)
 
 
@@ -180,8 +187,13 @@ def main():
     M = args.m
     specs = make_workload(args.workload)
     head = args.workload.startswith("qwen2.5-72b-lm-head")
-    # The greedy token adds M int32 outputs to the step's bytes.
-    step_bytes = wl.algorithmic_bytes(specs, M) + (4 * M if head else 0)
+    mlp = "-mlp-" in args.workload
+    # The greedy token adds M int32 outputs to the step's bytes; a gated MLP
+    # counts its [M][2I] intermediate written and read.
+    if mlp:
+        step_bytes = wl.mlp_algorithmic_bytes(specs, M)
+    else:
+        step_bytes = wl.algorithmic_bytes(specs, M) + (4 * M if head else 0)
     step_flops = wl.flops(specs, M)
     copies = 1 if step_bytes >= args.rotate_bytes else int(np.ceil(args.rotate_bytes / step_bytes))
     log(f"workload {args.workload}: {len(specs)} linears, M={M}, {step_bytes / 1e9:.3f} GB/step, "
@@ -192,18 +204,29 @@ def main():
     log(f"inputs made on the GPU in {time.perf_counter() - t0:.1f} s")
 
     variant = {"auto": sg.VARIANT_AUTO, "vector": sg.VARIANT_VECTOR, "mfma": sg.VARIANT_MFMA}[args.variant]
-    ws = torch.empty(sg.stack_workspace_bytes(sets[0], M), dtype=torch.uint8, device="cuda")
+    if mlp:
+        mlps = [sg.make_mlp(t[0][0], t[0][1], t[1][1], t[1][3], t[0][2], t[1][2]) for t in tensors]
+        ws = torch.empty(sg.mlp_workspace_bytes(mlps[0], M), dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.empty(sg.stack_workspace_bytes(sets[0], M), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    plan = sg.plan_query(sets[0], M)
-    n_launch = sg.launch_count(sets[0])
+    # The dominant kernel: the stack's main launches, or an MLP's gate_up
+    # launch (two thirds of its bytes), timed through the same entry point.
+    timed_sets = [st[:1] for st in sets] if mlp else sets
+    timed_bytes = wl.algorithmic_bytes(specs[:1], M) if mlp else step_bytes
+    plan = sg.plan_query(timed_sets[0], M)
+    n_launch = sg.launch_count(timed_sets[0])
 
     tokens = [torch.zeros(M, dtype=torch.int32, device="cuda") for _ in range(copies)]
 
     def step(i):
-        if head:
+        if head or mlp:
             if variant != sg.VARIANT_AUTO or args.waves:
-                sys.exit("the lm-head workload runs the automatic plan")
+                sys.exit("the lm-head and MLP workloads run the automatic plan")
+        if head:
             sg.lm_head_argmax(sets[i % copies][0], M, tokens[i % copies], ws)
+        elif mlp:
+            sg.mlp_swiglu(mlps[i % copies], M, ws)
         else:
             sg.linear_run(sets[i % copies], M, ws, variant=variant, waves=args.waves)
 
@@ -240,12 +263,12 @@ def main():
     prefill(args.steps * 0.1)
     for i in range(args.steps):
         handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
-        sg.linear_run_timed(sets[(args.warmup + i) % copies], M, ws, handles, variant=variant,
-                            waves=args.waves)
+        sg.linear_run_timed(timed_sets[(args.warmup + i) % copies], M, ws, handles,
+                            variant=variant, waves=args.waves)
     torch.cuda.synchronize()
     main_ms = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(n_launch * args.steps)]
     main_avg_ms = float(np.mean(main_ms))
-    bytes_per_launch = step_bytes / n_launch
+    bytes_per_launch = timed_bytes / n_launch
     achieved = bytes_per_launch / (main_avg_ms * 1e-3) / 1e9
     main_total_ms = float(np.sum(main_ms)) / args.steps
 
@@ -312,7 +335,8 @@ def main():
         step(0)
         torch.cuda.synchronize()
         worst = 0.0
-        for (s, r, y_ref, a), t in zip(refs, tensors[0][:len(refs)]):
+        # (An MLP's linears run chained, so their outputs are not the sample's.)
+        for (s, r, y_ref, a), t in zip([] if mlp else refs, tensors[0][:len(refs)]):
             yv = t[3][:, :r].float().cpu().double().numpy()
             ok, wr, _ = oracle.check(yv, y_ref, a)
             worst = max(worst, wr)

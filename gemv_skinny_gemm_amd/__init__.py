@@ -17,7 +17,7 @@ __all__ = [
     "workspace_bytes", "stack_workspace_bytes", "skinny_gemm_bf16", "skinny_gemm_fp8_bs128",
     "decode_linear_stack", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
     "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
-    "lm_head_workspace_bytes",
+    "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
 ]
 
 BF16 = 0
@@ -47,6 +47,14 @@ class Linear(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int),
                 ("reserved", ctypes.c_int), ("w", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
                 ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class Mlp(ctypes.Structure):
+    """struct skinny_mlp"""
+    _fields_ = [("dtype", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int),
+                ("reserved", ctypes.c_int), ("w_gate_up", ctypes.c_void_p),
+                ("s_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class Plan(ctypes.Structure):
@@ -96,6 +104,11 @@ def _bind(path: str):
     L.skinny_lm_head_workspace_bytes.argtypes = [lp, i]
     L.skinny_lm_head_argmax.restype = i
     L.skinny_lm_head_argmax.argtypes = [lp, i, vp, vp, sz, vp]
+    mp = ctypes.POINTER(Mlp)
+    L.skinny_mlp_workspace_bytes.restype = sz
+    L.skinny_mlp_workspace_bytes.argtypes = [mp, i]
+    L.skinny_mlp_swiglu.restype = i
+    L.skinny_mlp_swiglu.argtypes = [mp, i, vp, sz, vp]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_status_string.argtypes = [i]
     L.skinny_abi_version.restype = i
@@ -282,3 +295,23 @@ def lm_head_argmax(head: Linear, M: int, next_token, workspace, stream=None):
     _check(lib().skinny_lm_head_argmax(arr, M, _ptr(next_token), wp, wb, _stream(stream)),
            "skinny_lm_head_argmax")
     return next_token
+
+
+def make_mlp(x, w_gate_up, w_down, y, s_gate_up=None, s_down=None) -> Mlp:
+    """A skinny_mlp from GPU tensors x [M][H], w_gate_up [2I][H] (gate rows
+    first), w_down [H][I], y [M][H] (scales for FP8)."""
+    H, I = _shape2(w_down)
+    dtype = FP8_BS128 if s_gate_up is not None else BF16
+    return Mlp(dtype, H, I, 0, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down), _ptr(s_down),
+               _ptr(x), _ptr(y))
+
+
+def mlp_workspace_bytes(mlp: Mlp, M: int) -> int:
+    return lib().skinny_mlp_workspace_bytes(ctypes.byref(mlp), M)
+
+
+def mlp_swiglu(mlp: Mlp, M: int, workspace, stream=None):
+    """y = down(silu(gate) * up) with [gate | up] = x . W_gate_up^T."""
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_mlp_swiglu(ctypes.byref(mlp), M, wp, wb, _stream(stream)),
+           "skinny_mlp_swiglu")

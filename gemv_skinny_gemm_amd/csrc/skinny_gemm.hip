@@ -77,7 +77,13 @@ struct LinDesc {
   int chunks;            // K-chunks per row group (1 = not split)
   long long unit_base;   // index of this linear's first unit in the launch
   long long slot_base;   // first partial slot of a split linear
+  int act;               // kActNone, or kActSwiGLU: x is [M][2K] = [gate | up], the
+                         // linear's input is silu(gate) * up
+  int pad;
 };
+
+constexpr int kActNone = 0;
+constexpr int kActSwiGLU = 1;
 
 struct LaunchArgs {
   int nlin;
@@ -124,6 +130,66 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Eight gated-MLP inputs: bf16(silu(g) * u) for the bf16 pairs of g and u,
+// in fp32 (silu(g) = g / (1 + e^-g)), rounded to nearest even ("Multi-GPU
+// Inference and Serving at Scale", Example 3: the MLP's activation sits
+// between its two linears; Qwen2.5's is the SiLU-gated unit).
+__device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
+  const bf16x8 gv = __builtin_bit_cast(bf16x8, g);
+  const bf16x8 uv = __builtin_bit_cast(bf16x8, u);
+  bf16x8 h;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a = (float)gv[k];
+    h[k] = (__bf16)(a / (1.0f + expf(-a)) * (float)uv[k]);
+  }
+  return __builtin_bit_cast(u32x4, h);
+}
+
+// x[m][xw0, xw0 + wlen) of tokens m < M into dst[m * stride + c], several
+// loads in flight per thread.  With kActSwiGLU the linear's x holds [gate |
+// up] per token (2 xcpr chunks) and the staged value is swiglu8(gate, up).
+template <int THREADS>
+__device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
+                                        u32x4* dst, int stride) {
+  const int n = M * wlen;
+  if (L.act == kActNone) {
+    for (int b = threadIdx.x; b < n; b += 8 * THREADS) {
+      u32x4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = min(b + q * THREADS, n - 1);
+        const int m = i / wlen;
+        v[q] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = b + q * THREADS;
+        const int m = i / wlen;
+        if (i < n) dst[m * stride + (i - m * wlen)] = v[q];
+      }
+    }
+  } else {
+    for (int b = threadIdx.x; b < n; b += 4 * THREADS) {
+      u32x4 g[4], u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = min(b + q * THREADS, n - 1);
+        const int m = i / wlen;
+        const u32x4* row = L.x + (size_t)m * 2 * xcpr + xw0 + (i - m * wlen);
+        g[q] = row[0];
+        u[q] = row[xcpr];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = b + q * THREADS;
+        const int m = i / wlen;
+        if (i < n) dst[m * stride + (i - m * wlen)] = swiglu8(g[q], u[q]);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -264,23 +330,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
     if (nb > 0) load(b0, j0);
     if (l != staged_l || chunk != staged_c) {                    // same for all waves
       __syncthreads();                                           // all done with the old window
-      const int wlen = min(win, xcpr - xw0);
-      const int n = MT * wlen;
-      for (int b = threadIdx.x; b < n; b += 8 * kThreads) {      // eight loads in flight
-        u32x4 v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = min(b + q * kThreads, n - 1);
-          const int m = i / wlen;
-          v[q] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = b + q * kThreads;
-          const int m = i / wlen;
-          if (i < n) xs[m * win + (i - m * wlen)] = v[q];
-        }
-      }
+      stage_x<kThreads>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win);
       __syncthreads();
       staged_l = l;
       staged_c = chunk;
@@ -509,25 +559,10 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     staged_c = t.chunk;
     const int xcpr = L.K >> 3;                                   // x chunks per token
     __syncthreads();                                             // all done with the old window
-    // Token rows 0..M-1 (eight loads in flight per thread), zeros past K,
-    // then a zero row that lanes of absent tokens read.
+    // Token rows 0..M-1, zeros past K, then a zero row that lanes of absent
+    // tokens read.
     const int wlen = min(win, xcpr - xw0);
-    const int cnt = a.M * wlen;
-    for (int b = threadIdx.x; b < cnt; b += 8 * kThreads) {
-      u32x4 v[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int i = min(b + r * kThreads, cnt - 1);
-        const int m = i / wlen;
-        v[r] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int i = b + r * kThreads;
-        const int m = i / wlen;
-        if (i < cnt) xs[m * xstride + (i - m * wlen)] = v[r];
-      }
-    }
+    stage_x<kThreads>(L, a.M, xcpr, xw0, wlen, xs, xstride);
     const int pad = win - wlen;
     for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
       const int m = i / pad;
@@ -755,9 +790,11 @@ skinny_status device_info(DeviceInfo* out) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-skinny_status check_linear(const skinny_linear& L, int M) {
+// allow_act: the library's own chained linears carry their input activation
+// in `reserved` (kActSwiGLU); a caller's linear must have 0 there.
+skinny_status check_linear(const skinny_linear& L, int M, bool allow_act = false) {
   if (L.dtype != SKINNY_BF16 && L.dtype != SKINNY_FP8_BS128) return SKINNY_ERR_INVALID_ARG;
-  if (L.reserved != 0) return SKINNY_ERR_INVALID_ARG;
+  if (L.reserved != 0 && !(allow_act && L.reserved == kActSwiGLU)) return SKINNY_ERR_INVALID_ARG;
   if (M < 1 || M > SKINNY_MAX_M || L.N < 1 || L.K < 1) return SKINNY_ERR_INVALID_ARG;
   if (!L.w || !L.x || !L.y) return SKINNY_ERR_INVALID_ARG;
   if (L.dtype == SKINNY_FP8_BS128 && !L.w_scale) return SKINNY_ERR_INVALID_ARG;
@@ -787,7 +824,8 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
     for (int j = 0; j < count; ++j) {
       const skinny_linear& O = lin[j];
       const size_t wbytes = (size_t)O.N * O.K * (O.dtype == SKINNY_BF16 ? 2 : 1);
-      Range x{(uintptr_t)O.x, (uintptr_t)O.x + (size_t)M * O.K * 2};
+      const size_t xbytes = (size_t)M * O.K * 2 * (O.reserved == kActSwiGLU ? 2 : 1);
+      Range x{(uintptr_t)O.x, (uintptr_t)O.x + xbytes};
       Range w{(uintptr_t)O.w, (uintptr_t)O.w + wbytes};
       if (overlap(y, x) || overlap(y, w)) return SKINNY_ERR_INVALID_ARG;
       if (O.w_scale) {
@@ -1118,6 +1156,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
                     : (d.cpr + kSegChunks - 1) / kSegChunks;
     d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
     d.chunks = 1;
+    d.act = L.reserved;
   }
   int G = workers;
   if (G == 0) {
@@ -1207,11 +1246,11 @@ size_t required_workspace(const skinny_linear* lin, int count, int M) {
 
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
                   void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr,
-                  int event_count = 0) {
+                  int event_count = 0, bool allow_act = false) {
   if (!lin || count < 1) return SKINNY_ERR_INVALID_ARG;
   if (M < 1 || M > SKINNY_MAX_M) return SKINNY_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
-    skinny_status st = check_linear(lin[i], M);
+    skinny_status st = check_linear(lin[i], M, allow_act);
     if (st != SKINNY_OK) return st;
   }
   int variant = SKINNY_VARIANT_AUTO;
@@ -1288,6 +1327,43 @@ skinny_status check_argmax(const void* y, int M, int N, const int* idx, const vo
   const Range wr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
   if (overlap(yr, ir) || overlap(yr, wr) || overlap(ir, wr)) return SKINNY_ERR_INVALID_ARG;
   return SKINNY_OK;
+}
+
+// The two linears of a gated MLP: gate_up writes [gate | up] into the
+// intermediate buffer `gu`, down reads it through the fused activation.
+constexpr size_t kWorkspaceAlign = 256;
+size_t mlp_gu_bytes(const skinny_mlp& P, int M) {
+  const size_t b = (size_t)M * 2 * P.I * 2;
+  return (b + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+}
+
+void mlp_linears(const skinny_mlp& P, void* gu, skinny_linear* gate_up, skinny_linear* down) {
+  memset(gate_up, 0, sizeof *gate_up);
+  gate_up->dtype = P.dtype;
+  gate_up->N = 2 * P.I;
+  gate_up->K = P.H;
+  gate_up->w = P.w_gate_up;
+  gate_up->w_scale = P.s_gate_up;
+  gate_up->x = P.x;
+  gate_up->y = gu;
+  memset(down, 0, sizeof *down);
+  down->dtype = P.dtype;
+  down->N = P.H;
+  down->K = P.I;
+  down->reserved = kActSwiGLU;
+  down->w = P.w_down;
+  down->w_scale = P.s_down;
+  down->x = gu;
+  down->y = P.y;
+}
+
+size_t mlp_workspace(const skinny_mlp& P, int M) {
+  // Shapes only: stand-in non-null pointers keep the planner's checks quiet.
+  skinny_linear g, d;
+  mlp_linears(P, (void*)kWorkspaceAlign, &g, &d);
+  const size_t a = required_workspace(&g, 1, M);
+  const size_t b = required_workspace(&d, 1, M);
+  return mlp_gu_bytes(P, M) + (a > b ? a : b);
 }
 
 }  // namespace
@@ -1454,6 +1530,57 @@ skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_
   st = run(head, 1, M, nullptr, workspace, workspace_bytes, stream);
   if (st != SKINNY_OK) return st;
   return launch_argmax(head->y, M, head->N, next_token, workspace, (hipStream_t)stream);
+}
+
+size_t skinny_mlp_workspace_bytes(const skinny_mlp* mlp, int M) {
+  if (!mlp || M < 1 || M > SKINNY_MAX_M || mlp->H < 1 || mlp->I < 1) return 0;
+  if (mlp->dtype != SKINNY_BF16 && mlp->dtype != SKINNY_FP8_BS128) return 0;
+  if ((long long)2 * mlp->I > (1 << 26)) return 0;
+  return mlp_workspace(*mlp, M);
+}
+
+skinny_status skinny_mlp_swiglu(const skinny_mlp* mlp, int M, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!mlp || mlp->reserved != 0) return SKINNY_ERR_INVALID_ARG;
+  const skinny_mlp& P = *mlp;
+  if (M < 1 || M > SKINNY_MAX_M || P.H < 1 || P.I < 1) return SKINNY_ERR_INVALID_ARG;
+  if (P.dtype != SKINNY_BF16 && P.dtype != SKINNY_FP8_BS128) return SKINNY_ERR_INVALID_ARG;
+  if ((long long)2 * P.I > (1 << 26)) return SKINNY_ERR_UNSUPPORTED;
+  if (!workspace) return SKINNY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SKINNY_ERR_UNSUPPORTED;
+  if (workspace_bytes < mlp_workspace(P, M)) return SKINNY_ERR_WORKSPACE;
+  skinny_linear g, d;
+  mlp_linears(P, workspace, &g, &d);
+  skinny_status st = check_linear(g, M);
+  if (st == SKINNY_OK) st = check_linear(d, M, true);
+  if (st != SKINNY_OK) return st;
+  // y must not overlap the MLP's input, weights or the workspace; x must not
+  // overlap the workspace (the intermediate is written there).
+  const Range yr{(uintptr_t)P.y, (uintptr_t)P.y + (size_t)M * P.H * 2};
+  const Range xr{(uintptr_t)P.x, (uintptr_t)P.x + (size_t)M * P.H * 2};
+  const Range wr{(uintptr_t)workspace, (uintptr_t)workspace + workspace_bytes};
+  const size_t eb = P.dtype == SKINNY_BF16 ? 2 : 1;
+  const Range gw{(uintptr_t)P.w_gate_up, (uintptr_t)P.w_gate_up + (size_t)2 * P.I * P.H * eb};
+  const Range dw{(uintptr_t)P.w_down, (uintptr_t)P.w_down + (size_t)P.H * P.I * eb};
+  if (overlap(yr, xr) || overlap(yr, wr) || overlap(yr, gw) || overlap(yr, dw) || overlap(xr, wr))
+    return SKINNY_ERR_INVALID_ARG;
+  if (P.s_gate_up) {
+    const size_t sb = (size_t)((2 * P.I + 127) / 128) * ((P.H + 127) / 128) * 4;
+    if (overlap(yr, Range{(uintptr_t)P.s_gate_up, (uintptr_t)P.s_gate_up + sb}))
+      return SKINNY_ERR_INVALID_ARG;
+  }
+  if (P.s_down) {
+    const size_t sb = (size_t)((P.H + 127) / 128) * ((P.I + 127) / 128) * 4;
+    if (overlap(yr, Range{(uintptr_t)P.s_down, (uintptr_t)P.s_down + sb}))
+      return SKINNY_ERR_INVALID_ARG;
+  }
+  // gate_up, then down through the fused activation; the partial-sum slots
+  // follow the intermediate in the workspace.
+  const size_t gub = mlp_gu_bytes(P, M);
+  void* slots = (char*)workspace + gub;
+  st = run(&g, 1, M, nullptr, slots, workspace_bytes - gub, stream);
+  if (st != SKINNY_OK) return st;
+  return run(&d, 1, M, nullptr, slots, workspace_bytes - gub, stream, nullptr, 0, true);
 }
 
 const char* skinny_status_string(int status) {

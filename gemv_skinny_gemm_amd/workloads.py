@@ -89,6 +89,22 @@ def lm_head(dtype: int = BF16) -> list[LinearSpec]:
     return [_spec("head", None, "lm_head", VOCAB, HIDDEN, dtype)]
 
 
+def mlp(tp: int = 1, dtype: int = BF16) -> list[LinearSpec]:
+    """One layer's gated MLP as [gate_up, down] (gate rows first in gate_up);
+    the down linear's x is the activation of gate_up's output, not its own."""
+    shapes = TP1_SHAPES if tp == 1 else TP8_SHAPES
+    tag = f"mlp-tp{tp}" + ("" if dtype == BF16 else "-fp8")
+    return [_spec(tag, 0, n, N, K, dtype) for n, N, K in shapes if n in ("gate_up", "down")]
+
+
+def mlp_algorithmic_bytes(specs, M: int) -> int:
+    """W + scales of both linears, x and y once, and the [M][2I] bf16
+    intermediate written by gate_up and read by down."""
+    gate_up, down = specs
+    return (gate_up.weight_bytes() + gate_up.scale_bytes() + down.weight_bytes() +
+            down.scale_bytes() + 2 * M * gate_up.K + 2 * M * down.N + 2 * (2 * M * gate_up.N))
+
+
 def algorithmic_bytes(specs, M: int) -> int:
     return sum(s.algorithmic_bytes(M) for s in specs)
 

@@ -185,6 +185,40 @@ size_t skinny_lm_head_workspace_bytes(const skinny_linear* head, int M);
 skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_token,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One gated MLP of a decoder layer (Qwen2.5's SiLU-gated unit): y = down(h),
+ * h = silu(g) * u, [g | u] = x . W_gate_up^T ("Multi-GPU Inference and
+ * Serving at Scale", Example 3: a column-split linear, the activation, then a
+ * row-split linear; the Qwen2.5 72B engine report, section 3, the MLP of each
+ * layer).  All pointers are device pointers:
+ *   x          [M][H] bf16                    y          [M][H] bf16, written
+ *   w_gate_up  [2I][H] bf16 or E4M3FN: rows 0..I-1 the gate, I..2I-1 the up
+ *   w_down     [H][I] bf16 or E4M3FN
+ *   s_gate_up  [ceil(2I/128)][ceil(H/128)] fp32, s_down [ceil(H/128)][ceil(I/128)]
+ *              fp32 (FP8 only; NULL for bf16)
+ * g and u are the gate_up linear's bf16 outputs; h = bf16(silu(g) * u) is
+ * computed in fp32 (silu(g) = g / (1 + e^-g)) while down stages its input, so
+ * no separate activation pass runs.  Both linears accumulate in fp32 and are
+ * within the bound of each linear.  The intermediate [M][2I] bf16 lives in
+ * the workspace (skinny_mlp_workspace_bytes(mlp, M), 0 for invalid
+ * arguments).  H % 8 == 0 and I % 8 == 0 (bf16) or % 16 (FP8); y must not
+ * overlap x, the weights, the scales or the workspace, and x must not overlap
+ * the workspace.  reserved must be 0. */
+typedef struct skinny_mlp {
+  int dtype;
+  int H;
+  int I;
+  int reserved;
+  const void* w_gate_up;
+  const float* s_gate_up;
+  const void* w_down;
+  const float* s_down;
+  const void* x;
+  void* y;
+} skinny_mlp;
+size_t skinny_mlp_workspace_bytes(const skinny_mlp* mlp, int M);
+skinny_status skinny_mlp_swiglu(const skinny_mlp* mlp, int M, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* skinny_status_string(int status);
 

@@ -11,6 +11,10 @@ Greedy next token (``argmax_first``): the smallest index of the largest logit
 of each token row, NaN below every number; ``greedy_valid`` decides whether a
 GPU's choice is one the stated error bound allows.
 
+Gated MLP (``mlp_swiglu``): the two linears above with the activation h =
+silu(g) * u between them, g and u and h rounded to bf16 as the method's
+16-bit activations are (``bf16_encode``: round to nearest, ties to even).
+
 Definition followed (see oracle.c for the citations):
     y_ref[m][n] = sum_k x[m][k] * w[n][k]            in fp64
     w[n][k]     = bf16 value                         (bf16 weights)
@@ -198,3 +202,57 @@ def greedy_valid(idx: np.ndarray, y_ref: np.ndarray, a: np.ndarray) -> np.ndarra
     lo = np.max(y_ref - b, axis=1)
     rows = np.arange(y_ref.shape[0])
     return (y_ref[rows, idx] + b[rows, idx]) >= lo
+
+
+def bf16_encode(v: np.ndarray) -> np.ndarray:
+    """bf16 codes of the fp64 values ``v`` rounded to the nearest bf16 value,
+    ties to even (8 significant bits; subnormals below 2^-126 on a 2^-133
+    grid; beyond the largest finite value, infinity; NaN to 0x7FC0)."""
+    v = np.asarray(v, np.float64)
+    mag = np.abs(v)
+    f, e = np.frexp(mag)                           # mag = f 2^e, f in [0.5, 1)
+    normal = mag >= 2.0 ** -126
+    # Normal: 8 significant bits, the integer significand in [128, 256].
+    sig = np.rint(f * 256.0)                       # numpy rounds halves to even
+    r_norm = np.ldexp(sig, e - 8)
+    r_sub = np.rint(mag / 2.0 ** -133) * 2.0 ** -133
+    r = np.where(normal, r_norm, r_sub)
+    r = np.where(r > 3.3895313892515355e38, np.inf, r)   # above (2 - 2^-7) 2^127
+    r = np.copysign(r, v)
+    # Every rounded value is exact in binary32; its upper half is the code.
+    codes = (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return np.where(np.isnan(v), np.uint16(0x7FC0), codes)
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """v / (1 + e^-v) in fp64."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def bf16_decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of bf16 codes (the upper half of a binary32)."""
+    c = np.asarray(codes, np.uint16).astype(np.uint32) << 16
+    return c.view(np.float32).astype(np.float64)
+
+
+def mlp_swiglu(x: np.ndarray, w_gate_up, w_down, scales=None, threads: int | None = None):
+    """The gated MLP y = down(h), h = bf16(silu(g) * u), [g | u] = bf16(x . W_gate_up^T).
+
+    bf16 weights: w_gate_up [2I][H] and w_down [H][I] bf16 codes.  FP8:
+    e4m3 codes with ``scales`` = (s_gate_up, s_down).  Returns (y_ref, A, h
+    codes) of the down linear; A bounds its error as for any linear."""
+    I = w_down.shape[1]
+    if scales is None:
+        gu, _, _ = linear_bf16(x, w_gate_up, threads)
+    else:
+        gu, _, _ = linear_fp8_bs128(x, w_gate_up, scales[0], threads)
+    g = bf16_decode(bf16_encode(gu[:, :I]))
+    u = bf16_decode(bf16_encode(gu[:, I:]))
+    h = bf16_encode(silu(g) * u)
+    if scales is None:
+        y, a, _ = linear_bf16(h, w_down, threads)
+    else:
+        y, a, _ = linear_fp8_bs128(h, w_down, scales[1], threads)
+    return y, a, h

@@ -189,3 +189,25 @@ def test_lm_head_rejects_bad_arguments():
     assert L.skinny_lm_head_argmax(arr, 1, C + 4, WS, wsb, None) == INVALID        # inside y
     assert L.skinny_lm_head_argmax(arr, 1, T, WS, 0, None) == WORKSPACE
     assert L.skinny_lm_head_argmax(arr, 17, T, WS, wsb, None) == INVALID
+
+
+def test_mlp_workspace_and_bad_arguments():
+    L = sg.lib()
+    mlp = sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, B, C)
+    wsb = sg.mlp_workspace_bytes(mlp, 2)
+    # The [M][2I] bf16 intermediate (rounded to 256 B) comes first.
+    assert wsb >= 256 + MIN_WORKSPACE and wsb % 16 == 0
+    assert sg.mlp_workspace_bytes(mlp, 0) == 0 and sg.mlp_workspace_bytes(mlp, 17) == 0
+    bad = sg.Mlp(sg.BF16, 64, 0, 0, A, None, A + 0x10000, None, B, C)
+    assert sg.mlp_workspace_bytes(bad, 1) == 0
+    call = lambda m, M=2, ws=WS, n=wsb: L.skinny_mlp_swiglu(ctypes.byref(m), M, ws, n, None)
+    assert L.skinny_mlp_swiglu(None, 2, WS, wsb, None) == INVALID
+    assert call(mlp, M=0) == INVALID
+    assert call(mlp, ws=None) == WORKSPACE
+    assert call(mlp, n=wsb - 1) == WORKSPACE
+    assert call(sg.Mlp(sg.BF16, 64, 32, 1, A, None, A + 0x10000, None, B, C)) == INVALID  # reserved
+    assert call(sg.Mlp(sg.BF16, 64, 12, 0, A, None, A + 0x10000, None, B, C)) == UNSUPPORTED
+    assert call(sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, B, B)) == INVALID   # y = x
+    assert call(sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, B, WS + 64)) == INVALID
+    assert call(sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, WS + 64, C)) == INVALID
+    assert call(sg.Mlp(sg.FP8_BS128, 64, 32, 0, A, None, A + 0x10000, None, B, C)) == INVALID

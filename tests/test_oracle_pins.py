@@ -318,3 +318,53 @@ def test_greedy_valid_admits_only_the_winner_when_the_gap_is_wide():
     wide = np.array([[1.0, 5000.0, 5000.0, 1.0]])     # bounds of 10: 4.9 is within reach
     assert oracle.greedy_valid(np.array([2]), y_ref, wide).tolist() == [True]
     assert oracle.greedy_valid(np.array([3]), y_ref, wide).tolist() == [False]
+
+
+# --- the gated MLP's activation ---------------------------------------------
+
+def test_bf16_encode_is_the_nearest_code_ties_to_even():
+    """Brute force over every finite bf16 value: the nearest one, the even code
+    on a tie (halfway points included on purpose)."""
+    lib = oracle._load()
+    codes = np.arange(0, 0x7F80, dtype=np.uint32)                    # +0 .. largest finite
+    vals = np.array([lib.oracle_bf16_value(int(c)) for c in codes])
+    rng = np.random.default_rng(21)
+    picks = rng.integers(1, len(vals) - 1, 4000)
+    mids = (vals[picks] + vals[picks + 1]) / 2                        # exact halfway points
+    rand = np.exp(rng.uniform(np.log(1e-40), np.log(3e38), 4000))
+    probe = np.concatenate([mids, rand, vals[picks], [0.0, 2.0 ** -133, 1.5 * 2.0 ** -133]])
+    for v in probe:
+        d = np.abs(vals - v)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        got = int(oracle.bf16_encode(np.array([v]))[0])
+        assert got == int(codes[want]), (v, hex(got), hex(int(codes[want])))
+        assert int(oracle.bf16_encode(np.array([-v]))[0]) == (got | 0x8000)
+    assert oracle.bf16_encode(np.array([1e39, np.nan])).tolist() == [0x7F80, 0x7FC0]
+
+
+def test_silu_closed_forms():
+    v = np.linspace(-30, 30, 601)
+    assert np.allclose(oracle.silu(v) - oracle.silu(-v), v, rtol=0, atol=1e-12)   # silu(v) - silu(-v) = v
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-15
+    assert abs(oracle.silu(np.array([-800.0]))[0]) < 1e-300                     # no overflow error
+    assert abs(oracle.silu(np.array([1.0]))[0] - 1.0 / (1.0 + np.e ** -1)) < 1e-15
+
+
+def test_mlp_swiglu_matches_a_direct_computation():
+    """Small MLP against fractions-free direct fp64 algebra on exact inputs:
+    x and W with few bits make every product and sum exact."""
+    rng = np.random.default_rng(23)
+    M, H, I = 2, 16, 8
+    x = bf16_codes_of(rng.integers(-4, 5, (M, H)) / 4)
+    wg = bf16_codes_of(rng.integers(-4, 5, (2 * I, H)) / 8)
+    wd = bf16_codes_of(rng.integers(-4, 5, (H, I)) / 8)
+    y, a, h = oracle.mlp_swiglu(x, wg, wd)
+    xv, wgv, wdv = (torch_bf16_values(c).numpy() for c in (x, wg, wd))
+    gu = xv @ wgv.T                                        # exact: few-bit operands
+    hv = oracle.silu(gu[:, :I]) * gu[:, I:]
+    hb = torch_bf16_values(oracle.bf16_encode(hv)).numpy()
+    assert np.array_equal(h, oracle.bf16_encode(hv))
+    assert np.allclose(y, hb @ wdv.T, rtol=1e-14, atol=1e-14)
+    assert np.allclose(a, np.abs(hb) @ np.abs(wdv).T, rtol=1e-14, atol=1e-14)
