@@ -247,3 +247,22 @@ def fp8_weight_bs128(seed: int, stream: int, N: int, K: int, sigma: float = 0.02
     w = tensor_bf16(seed, stream, r1 - r0, K, sigma, row_begin=r0)
     q, s = quantize_bs128(w)
     return q, s, r0
+
+
+def route_topk(seed: int, stream: int, T: int, E: int, topk: int, hot: int = 2,
+               hot_bias: float = 1.0) -> np.ndarray:
+    """Synthetic router choices for T tokens over E experts: ids [T][topk] int32.
+
+    Token t scores expert e with a N(0, 1) draw (rounded to bf16, element
+    t * E + e of the stream) plus ``hot_bias`` for the first ``hot`` experts,
+    so a few experts are busier than the rest, as real routers are
+    ("Multi-GPU Inference and Serving at Scale", Example 8, which routes to
+    the top 2 of 8 experts with experts 0 and 1 favoured by +1.0).  Each
+    token takes its topk best experts, best first, ties to the lower index:
+    the experts of one token are distinct."""
+    if topk > E:
+        raise ValueError("topk must not exceed E")
+    s = _bf16_code_values(normal_bf16(seed, stream, 0, T * E, 1.0)).astype(np.float64)
+    s = s.reshape(T, E) + np.where(np.arange(E) < hot, hot_bias, 0.0)
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -s), axis=1)
+    return np.ascontiguousarray(order[:, :topk], np.int32)

@@ -15,6 +15,9 @@ Gated MLP (``mlp_swiglu``): the two linears above with the activation h =
 silu(g) * u between them, g and u and h rounded to bf16 as the method's
 16-bit activations are (``bf16_encode``: round to nearest, ties to even).
 
+Mixture-of-experts linear (``moe_linear``): each route (token, choice) of a
+batch goes through its own expert's linear; a route to no expert gives zeros.
+
 Definition followed (see oracle.c for the citations):
     y_ref[m][n] = sum_k x[m][k] * w[n][k]            in fp64
     w[n][k]     = bf16 value                         (bf16 weights)
@@ -256,3 +259,53 @@ def mlp_swiglu(x: np.ndarray, w_gate_up, w_down, scales=None, threads: int | Non
     else:
         y, a, _ = linear_fp8_bs128(h, w_down, scales[1], threads)
     return y, a, h
+
+
+def moe_linear(x: np.ndarray, ids: np.ndarray, w: np.ndarray, scales=None,
+               x_per_route: bool = False, swiglu: bool = False, threads: int | None = None):
+    """One linear of a mixture-of-experts layer, over the routes of a batch.
+
+    A router sends each token to its top-k experts, each expert being its own
+    small network ("Multi-GPU Inference and Serving at Scale", Example 8); in a
+    decode verify step a handful of tokens pass through the weight-only FP8
+    expert matmuls ("9% faster GLM-5.3-Flash prefill with GPU-to-GPU IPC",
+    section "TileLang: twice as fast, and no faster").  Route r = t * topk + j
+    is token t's j-th choice, expert e = ids[t][j]:
+
+        y[r] = x_r . W_e^T                      (an ordinary linear per route)
+        x_r  = x[r] if x_per_route else x[t]
+        x_r  = bf16(silu(g) * u) of x's row [g | u] when swiglu
+        y[r] = 0 when e is outside [0, E)
+
+    x: bf16 codes, [T][K] (or [T * topk][K] per route; 2K columns with swiglu);
+    ids: [T][topk] ints; w: [E][N][K] bf16 codes, or e4m3 codes with
+    ``scales`` [E][ceil(N/128)][ceil(K/128)] fp32.  Routes of one expert go
+    through the linear together; every output is its own dot product.
+
+    Returns (y_ref, A): fp64 [T * topk][N] each (A = 0 on zero rows)."""
+    ids = np.asarray(ids)
+    T, topk = ids.shape
+    E, N, K = w.shape
+    routes = T * topk
+    x = np.asarray(x)
+    if swiglu:
+        g = bf16_decode(x[:, :K])
+        u = bf16_decode(x[:, K:])
+        x = bf16_encode(silu(g) * u)
+    if x.shape != ((routes if x_per_route else T), K):
+        raise ValueError("x rows or columns do not match the routes and K")
+    y = np.zeros((routes, N), np.float64)
+    a = np.zeros((routes, N), np.float64)
+    flat = ids.reshape(-1)
+    for e in range(E):
+        rs = np.nonzero(flat == e)[0]
+        if rs.size == 0:
+            continue
+        xr = x[rs] if x_per_route else x[rs // topk]
+        if scales is None:
+            ye, ae, _ = linear_bf16(xr, w[e], threads)
+        else:
+            ye, ae, _ = linear_fp8_bs128(xr, w[e], scales[e], threads)
+        y[rs] = ye
+        a[rs] = ae
+    return y, a

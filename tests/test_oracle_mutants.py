@@ -54,3 +54,35 @@ def test_some_pin_catches_mutant(mutant, tmp_path):
     finally:
         oracle._lib = saved
     assert caught, f"no pin catches the mutant {mutant}"
+
+
+# Mistakes in the Python-level routing of the mixture-of-experts linear: each
+# planted in a copy of oracle.moe_linear must make one of the MoE pins fail.
+MOE_MUTANTS = {
+    "token_row_for_shared_x": ("x[rs] if x_per_route else x[rs // topk]", "x[rs]"),
+    "route_row_for_per_route_x": ("x[rs] if x_per_route else x[rs // topk]", "x[rs // topk]"),
+    "first_expert_scales": ("scales[e], threads", "scales[0], threads"),
+    "wraps_negative_ids": ("rs = np.nonzero(flat == e)[0]", "rs = np.nonzero(flat % E == e)[0]"),
+    "swiglu_gate_up_swapped": ("bf16_encode(silu(g) * u)", "bf16_encode(silu(u) * g)"),
+    "first_choice_only": ("flat = ids.reshape(-1)", "flat = np.repeat(ids[:, 0], topk)"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MOE_MUTANTS))
+def test_some_moe_pin_catches_mutant(mutant, monkeypatch):
+    old, new = MOE_MUTANTS[mutant]
+    src = inspect.getsource(oracle.moe_linear)
+    assert src.count(old) == 1, "mutation site moved; update the mutant"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), "<moe_mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, "moe_linear", ns["moe_linear"])
+    caught = []
+    calls = [(n, fn, {}) for n, fn in _pin_functions() if "moe" in n]
+    calls += [("test_moe_linear_vs_exact_rationals_bf16", pins.test_moe_linear_vs_exact_rationals_bf16,
+               {"x_per_route": v}) for v in (False, True)]
+    for name, fn, params in calls:
+        try:
+            fn(**params)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(name)
+    assert caught, f"no pin catches the mutant {mutant}"

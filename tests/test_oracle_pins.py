@@ -368,3 +368,117 @@ def test_mlp_swiglu_matches_a_direct_computation():
     assert np.array_equal(h, oracle.bf16_encode(hv))
     assert np.allclose(y, hb @ wdv.T, rtol=1e-14, atol=1e-14)
     assert np.allclose(a, np.abs(hb) @ np.abs(wdv).T, rtol=1e-14, atol=1e-14)
+
+
+# --- mixture-of-experts linear ---------------------------------------------
+
+def _moe_exact(xv, ids, wv, x_per_route):
+    """Route-by-route exact rational products (Fractions) and |.| sums."""
+    T, topk = ids.shape
+    E, N, K = wv.shape
+    y, a = [], []
+    for t in range(T):
+        for j in range(topk):
+            r = t * topk + j
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                y.append([Fraction(0)] * N)
+                a.append([Fraction(0)] * N)
+                continue
+            xr = xv[r] if x_per_route else xv[t]
+            y.append([sum(Fraction(float(xr[k])) * Fraction(float(wv[e, n, k])) for k in range(K))
+                      for n in range(N)])
+            a.append([sum(abs(Fraction(float(xr[k])) * Fraction(float(wv[e, n, k]))) for k in range(K))
+                      for n in range(N)])
+    return y, a
+
+
+@pytest.mark.parametrize("x_per_route", [False, True])
+def test_moe_linear_vs_exact_rationals_bf16(x_per_route):
+    """Every route against its expert by brute force, with a duplicate expert
+    in one token, an expert no token picks, and ids outside [0, E)."""
+    rng = np.random.default_rng(31)
+    T, topk, E, N, K = 3, 3, 4, 5, 24
+    ids = np.array([[2, 0, 2], [-1, 1, 0], [0, 4, 1]], np.int32)   # expert 3 unused
+    x = bf16_codes_of(np.round(rng.standard_normal((T * topk if x_per_route else T, K)) * 32) / 32)
+    w = rng.integers(0, 65536, size=(E, N, K)).astype(np.uint16)
+    w[((w >> 7) & 0xFF) == 0xFF] = BF16_ONE
+    y, a = oracle.moe_linear(x, ids, w, x_per_route=x_per_route, threads=2)
+    y_ex, a_ex = _moe_exact(torch_bf16_values(x).numpy(), ids,
+                            torch_bf16_values(w.reshape(E * N, K)).numpy().reshape(E, N, K),
+                            x_per_route)
+    _assert_close_to_exact(y, a, y_ex, a_ex, K)
+    assert not y[3].any() and not y[7].any() and not a[3].any()    # ids -1 and 4
+
+
+def test_moe_linear_vs_exact_rationals_fp8_own_scales():
+    """FP8 experts, each with its own block scales (two K blocks, ragged N)."""
+    rng = np.random.default_rng(32)
+    T, topk, E, N, K = 2, 2, 3, 130, 256
+    ids = np.array([[1, 2], [2, 0]], np.int32)
+    x = bf16_codes_of(np.round(rng.standard_normal((T, K)) * 16) / 16)
+    q = rng.integers(0, 256, size=(E, N, K)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38
+    s = rng.uniform(0.25, 4.0, size=(E, 2, 2)).astype(np.float32)
+    s *= np.array([1, 2, 4], np.float32)[:, None, None]            # experts' scales differ
+    y, a = oracle.moe_linear(x, ids, q, scales=s, threads=3)
+    wv = torch_e4m3_values(q.reshape(E * N, K)).numpy().reshape(E, N, K)
+    wv = wv * np.repeat(np.repeat(s.astype(np.float64), 128, 1), 128, 2)[:, :N, :K]
+    y_ex, a_ex = _moe_exact(torch_bf16_values(x).numpy(), ids, wv, False)
+    _assert_close_to_exact(y, a, y_ex, a_ex, K)
+
+
+def test_moe_linear_scaled_identity_experts():
+    """Expert e = (e + 1) I: each route returns its token row times e + 1, bit
+    for bit (shared x), and its own row (x per route)."""
+    T, topk, E, K = 4, 2, 3, 16
+    ids = np.array([[0, 2], [1, 0], [2, 1], [0, 1]], np.int32)
+    w = np.stack([bf16_codes_of(np.eye(K) * (e + 1)) for e in range(E)])
+    x = bf16_codes_of(np.arange(T * K).reshape(T, K) / 64 - 1)
+    y, _ = oracle.moe_linear(x, ids, w)
+    xv = torch_bf16_values(x).numpy()
+    want = np.stack([xv[t] * (ids[t, j] + 1) for t in range(T) for j in range(topk)])
+    assert np.array_equal(y, want)
+    xr = bf16_codes_of(np.arange(T * topk * K).reshape(T * topk, K) / 128 - 1)
+    y, _ = oracle.moe_linear(xr, ids, w, x_per_route=True)
+    xrv = torch_bf16_values(xr).numpy()
+    assert np.array_equal(y, xrv * (ids.reshape(-1, 1) + 1))
+
+
+def test_moe_linear_relabelled_experts_give_the_same_routes():
+    rng = np.random.default_rng(33)
+    T, topk, E, N, K = 5, 2, 6, 7, 32
+    ids = synth.route_topk(0, 77, T, E, topk)
+    x = synth.tensor_bf16(0, 78, T, K, 1.0)
+    w = synth.tensor_bf16(0, 79, E * N, K, 0.02).reshape(E, N, K)
+    perm = rng.permutation(E)                                       # expert e becomes perm[e]
+    w2 = np.empty_like(w)
+    w2[perm] = w
+    y1, a1 = oracle.moe_linear(x, ids, w)
+    y2, a2 = oracle.moe_linear(x, perm[ids], w2)
+    assert np.array_equal(y1, y2) and np.array_equal(a1, a2)
+
+
+def test_moe_linear_swiglu_input_per_route():
+    """Down projection of the experts: route r's input is bf16(silu(g) u) of
+    its own row [g | u]; few-bit values keep the products exact."""
+    rng = np.random.default_rng(34)
+    T, topk, E, N, I = 2, 2, 3, 4, 8
+    ids = np.array([[2, 0], [0, 1]], np.int32)
+    gu = bf16_codes_of(rng.integers(-8, 9, (T * topk, 2 * I)) / 4)
+    w = bf16_codes_of(rng.integers(-4, 5, (E * N, I)) / 8).reshape(E, N, I)
+    y, _ = oracle.moe_linear(gu, ids, w, x_per_route=True, swiglu=True)
+    g = torch_bf16_values(gu[:, :I]).numpy()
+    u = torch_bf16_values(gu[:, I:]).numpy()
+    h = torch_bf16_values(oracle.bf16_encode(g / (1 + np.exp(-g)) * u)).numpy()
+    wv = torch_bf16_values(w.reshape(E * N, I)).numpy().reshape(E, N, I)
+    want = np.stack([h[r] @ wv[ids.reshape(-1)[r]].T for r in range(T * topk)])
+    assert np.allclose(y, want, rtol=1e-14, atol=1e-14)
+
+
+def test_route_topk_picks_distinct_best_experts():
+    ids = synth.route_topk(0, 91, 64, 8, 2)
+    assert ids.shape == (64, 2) and ids.dtype == np.int32
+    assert all(len(set(r)) == 2 for r in ids.tolist())
+    counts = np.bincount(ids.ravel(), minlength=8)
+    assert counts.sum() == 128 and counts[:2].min() > counts[2:].max() // 2
