@@ -18,6 +18,8 @@ __all__ = [
     "decode_linear_stack", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
     "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
     "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
+    "Experts", "make_experts", "moe_workspace_bytes", "moe_linear", "moe_linear_timed",
+    "MOE_X_PER_ROUTE", "MOE_SWIGLU", "MAX_TOPK",
 ]
 
 BF16 = 0
@@ -27,6 +29,9 @@ VARIANT_VECTOR = 1
 VARIANT_MFMA = 2
 MAX_M = 16
 MAX_LINEARS_PER_LAUNCH = 32
+MAX_TOPK = 16
+MOE_X_PER_ROUTE = 1
+MOE_SWIGLU = 2
 ABI_VERSION = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +60,12 @@ class Mlp(ctypes.Structure):
                 ("reserved", ctypes.c_int), ("w_gate_up", ctypes.c_void_p),
                 ("s_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("s_down", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class Experts(ctypes.Structure):
+    """struct skinny_experts"""
+    _fields_ = [("dtype", ctypes.c_int), ("E", ctypes.c_int), ("N", ctypes.c_int),
+                ("K", ctypes.c_int), ("w", ctypes.c_void_p), ("w_scale", ctypes.c_void_p)]
 
 
 class Plan(ctypes.Structure):
@@ -109,6 +120,13 @@ def _bind(path: str):
     L.skinny_mlp_workspace_bytes.argtypes = [mp, i]
     L.skinny_mlp_swiglu.restype = i
     L.skinny_mlp_swiglu.argtypes = [mp, i, vp, sz, vp]
+    ep = ctypes.POINTER(Experts)
+    L.skinny_moe_workspace_bytes.restype = sz
+    L.skinny_moe_workspace_bytes.argtypes = [ep, i, i, i]
+    L.skinny_moe_linear.restype = i
+    L.skinny_moe_linear.argtypes = [ep, vp, vp, i, i, i, vp, vp, sz, vp]
+    L.skinny_moe_linear_timed.restype = i
+    L.skinny_moe_linear_timed.argtypes = [ep, vp, vp, i, i, i, vp, ctypes.POINTER(vp), vp, sz, vp]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_status_string.argtypes = [i]
     L.skinny_abi_version.restype = i
@@ -315,3 +333,48 @@ def mlp_swiglu(mlp: Mlp, M: int, workspace, stream=None):
     wp, wb = _ws(workspace)
     _check(lib().skinny_mlp_swiglu(ctypes.byref(mlp), M, wp, wb, _stream(stream)),
            "skinny_mlp_swiglu")
+
+
+def make_experts(w, w_scale=None) -> Experts:
+    """A skinny_experts from GPU tensors w [E][N][K] (bf16, or uint8 E4M3FN
+    codes with w_scale [E][ceil(N/128)][ceil(K/128)] fp32)."""
+    if isinstance(w, int) or w.dim() != 3:
+        raise ValueError("w must be a 3-D tensor [E][N][K]")
+    E, N, K = (int(v) for v in w.shape)
+    return Experts(FP8_BS128 if w_scale is not None else BF16, E, N, K, _ptr(w), _ptr(w_scale))
+
+
+def _moe_flags(x_per_route: bool, swiglu: bool) -> int:
+    return (MOE_X_PER_ROUTE if x_per_route else 0) | (MOE_SWIGLU if swiglu else 0)
+
+
+def moe_workspace_bytes(experts: Experts, T: int, topk: int, x_per_route: bool = False,
+                        swiglu: bool = False) -> int:
+    return lib().skinny_moe_workspace_bytes(ctypes.byref(experts), T, topk,
+                                            _moe_flags(x_per_route, swiglu))
+
+
+def moe_linear(experts: Experts, x, ids, y, workspace, x_per_route: bool = False,
+               swiglu: bool = False, stream=None):
+    """y[t * topk + j] = x_r . W_{ids[t][j]}^T for the T x topk routes of ids
+    (int32 [T][topk] on the GPU); x_r = x[t], or x[r] with x_per_route, or
+    silu(g) * u of that row [g | u] with swiglu."""
+    T, topk = _shape2(ids)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_moe_linear(ctypes.byref(experts), _ptr(x), _ptr(ids), T, topk,
+                                   _moe_flags(x_per_route, swiglu), _ptr(y), wp, wb,
+                                   _stream(stream)), "skinny_moe_linear")
+    return y
+
+
+def moe_linear_timed(experts: Experts, x, ids, y, workspace, events, x_per_route: bool = False,
+                     swiglu: bool = False, stream=None):
+    """moe_linear recording the two hipEvent_t handles in `events` around its
+    main launch."""
+    T, topk = _shape2(ids)
+    wp, wb = _ws(workspace)
+    ev = (ctypes.c_void_p * 2)(*events)
+    _check(lib().skinny_moe_linear_timed(ctypes.byref(experts), _ptr(x), _ptr(ids), T, topk,
+                                         _moe_flags(x_per_route, swiglu), _ptr(y), ev, wp, wb,
+                                         _stream(stream)), "skinny_moe_linear_timed")
+    return y

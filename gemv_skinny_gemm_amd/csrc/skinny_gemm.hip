@@ -85,6 +85,25 @@ struct LinDesc {
 constexpr int kActNone = 0;
 constexpr int kActSwiGLU = 1;
 
+// Mixture-of-experts launch (skinny_tiles<DT, WPB, true>): lin[0] describes
+// one expert (w, scale: expert 0; x, y: the routes' rows).  Work units are
+// (slice, row group, K-chunk); a slice is up to `cap` routes of one expert,
+// found on the device from the router's choices (see moe_setup).
+struct MoeArgs {
+  const int* ids;        // [routes] expert of route r = t * topk + j
+  int* table;            // slice table copy for the second pass (NULL: unsplit)
+  long long w_stride;    // 16-byte chunks of one expert's W
+  long long s_stride;    // scales of one expert
+  int E;
+  int routes;
+  int topk;
+  int cap;               // routes per slice (the token count)
+  int per_route;         // x holds a row per route (else a row per token)
+  int max_slices;        // slices the routes can make, at most
+  int units_per_slice;
+  int table_lds;         // LDS offset of the slice table
+};
+
 struct LaunchArgs {
   int nlin;
   int M;
@@ -94,6 +113,7 @@ struct LaunchArgs {
   float* slots;          // fp32 partial sums [slot][M][band_rows], one slot per split unit
   int x_lds_bytes;       // LDS bytes for x; the kernel's other LDS follows
   int pad;
+  MoeArgs moe;
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
 
@@ -151,9 +171,10 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
 // x[m][xw0, xw0 + wlen) of tokens m < M into dst[m * stride + c], several
 // loads in flight per thread.  With kActSwiGLU the linear's x holds [gate |
 // up] per token (2 xcpr chunks) and the staged value is swiglu8(gate, up).
-template <int THREADS>
+// GATHER: staged row m is x's row rows[m].
+template <int THREADS, bool GATHER>
 __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
-                                        u32x4* dst, int stride) {
+                                        u32x4* dst, int stride, const unsigned char* rows) {
   const int n = M * wlen;
   if (L.act == kActNone) {
     for (int b = threadIdx.x; b < n; b += 8 * THREADS) {
@@ -162,7 +183,8 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
       for (int q = 0; q < 8; ++q) {
         const int i = min(b + q * THREADS, n - 1);
         const int m = i / wlen;
-        v[q] = L.x[(size_t)m * xcpr + xw0 + (i - m * wlen)];
+        const int src = GATHER ? rows[m] : m;
+        v[q] = L.x[(size_t)src * xcpr + xw0 + (i - m * wlen)];
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -178,7 +200,8 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
       for (int q = 0; q < 4; ++q) {
         const int i = min(b + q * THREADS, n - 1);
         const int m = i / wlen;
-        const u32x4* row = L.x + (size_t)m * 2 * xcpr + xw0 + (i - m * wlen);
+        const int src = GATHER ? rows[m] : m;
+        const u32x4* row = L.x + (size_t)src * 2 * xcpr + xw0 + (i - m * wlen);
         g[q] = row[0];
         u[q] = row[xcpr];
       }
@@ -330,7 +353,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
     if (nb > 0) load(b0, j0);
     if (l != staged_l || chunk != staged_c) {                    // same for all waves
       __syncthreads();                                           // all done with the old window
-      stage_x<kThreads>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win);
+      stage_x<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
       __syncthreads();
       staged_l = l;
       staged_c = chunk;
@@ -440,9 +463,102 @@ struct TileUnit {
   int chunk;             // K-chunk
   int j0, j1;            // segments [j0, j1) of each row
   int spc;               // x window, in segments
+  int slice;             // MoE: slice (else the linear)
+  int e;                 // MoE: expert
+  int m;                 // tokens (MoE: routes of the slice)
 };
 
-template <int DT, int WPB>
+// ---------------------------------------------------------------------------
+// Mixture-of-experts slices.  A router sends token t to topk experts; route r
+// = t * topk + j goes to expert ids[r] ("Multi-GPU Inference and Serving at
+// Scale", Example 8).  The routes of one expert share its weights, so the
+// launch streams each chosen expert's W once for all of its routes: slice s
+// is up to `cap` routes of one expert, slices ordered by expert, routes by
+// index.  Every workgroup derives the same table from ids at its start (one
+// thread per route, two passes over the routes in LDS), so the routing needs
+// neither a host round trip nor a launch of its own.  Routes whose expert is
+// outside [0, E) belong to no slice; their y rows are zeroed.
+constexpr int kMoeMaxRoutes = 256;
+constexpr int kMoeMaxCap = 16;
+
+struct MoeTable {
+  int* head;             // [2]: slices, invalid routes
+  int* expert;           // [max_slices]
+  int* rows;             // [max_slices] routes in the slice
+  unsigned char* yrow;   // [max_slices][16] route of slice row m (= its y row)
+  unsigned char* xrow;   // [max_slices][16] x row of slice row m
+  unsigned char* inv;    // [routes] routes with no expert
+};
+
+__device__ __forceinline__ MoeTable moe_table(unsigned char* base, int max_slices) {
+  MoeTable t;
+  t.head = reinterpret_cast<int*>(base);
+  t.expert = t.head + 2;
+  t.rows = t.expert + max_slices;
+  t.yrow = reinterpret_cast<unsigned char*>(t.rows + max_slices);
+  t.xrow = t.yrow + max_slices * kMoeMaxCap;
+  t.inv = t.xrow + max_slices * kMoeMaxCap;
+  return t;
+}
+
+// Builds the table in LDS (scratch: 2 x kMoeMaxRoutes ints, free until the
+// caller's next barrier).  Needs THREADS >= routes.
+template <int THREADS>
+__device__ void moe_setup(const MoeArgs& mo, const MoeTable& tb, int* scratch) {
+  static_assert(THREADS >= kMoeMaxRoutes, "one thread per route");
+  int* ids = scratch;
+  int* head = scratch + kMoeMaxRoutes;
+  const int r = threadIdx.x;
+  int e = -1;
+  if (r < mo.routes) {
+    const int v = mo.ids[r];
+    e = v >= 0 && v < mo.E ? v : -1;
+    ids[r] = e;
+  }
+  __syncthreads();
+  int rank = 0, count = 0, inv_rank = 0;
+  if (r < mo.routes) {
+    for (int q = 0; q < mo.routes; ++q) {
+      const int f = ids[q];
+      count += f == e;
+      rank += f == e && q < r;
+      inv_rank += f < 0 && q < r;
+    }
+    head[r] = e >= 0 && rank % mo.cap == 0;        // first route of a slice
+  }
+  __syncthreads();
+  if (r < mo.routes) {
+    int before = 0, slices = 0, invalid = 0;
+    for (int q = 0; q < mo.routes; ++q) {
+      const int h = head[q];
+      const int f = ids[q];
+      before += h && f < e;                        // slices of lower experts
+      slices += h;
+      invalid += f < 0;
+    }
+    if (e >= 0) {
+      const int sl = before + rank / mo.cap;
+      const int m = rank % mo.cap;
+      if (sl < mo.max_slices) {
+        tb.yrow[sl * kMoeMaxCap + m] = (unsigned char)r;
+        tb.xrow[sl * kMoeMaxCap + m] = (unsigned char)(mo.per_route ? r : r / mo.topk);
+        if (m == 0) {
+          tb.expert[sl] = e;
+          tb.rows[sl] = min(mo.cap, count - rank);
+        }
+      }
+    } else {
+      tb.inv[inv_rank] = (unsigned char)r;
+    }
+    if (r == 0) {
+      tb.head[0] = min(slices, mo.max_slices);
+      tb.head[1] = invalid;
+    }
+  }
+  __syncthreads();
+}
+
+template <int DT, int WPB, bool MOE>
 __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = kTileRows * WPB;
@@ -457,17 +573,55 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   const int lrow = lane / kLanesPerRowT;               // load q: row q kRowsPerLoadT + lrow
   const int lchunk = lane % kLanesPerRowT;             // load: chunk of the segment
 
+  long long S = a.S;
+  MoeTable tb{};
+  if constexpr (MOE) {
+    // The slice table, then this workgroup's share of the zero rows; the
+    // first workgroup also leaves the table for the second pass.
+    const MoeArgs& mo = a.moe;
+    const LinDesc& L = a.lin[0];
+    tb = moe_table(lds + mo.table_lds, mo.max_slices);
+    moe_setup<kThreads>(mo, tb, reinterpret_cast<int*>(lds + a.x_lds_bytes));
+    const int slices = tb.head[0];
+    if (blockIdx.x == 0 && mo.table) {
+      for (int i = threadIdx.x; i < slices; i += kThreads) mo.table[1 + i] = tb.rows[i];
+      for (int i = threadIdx.x; i < slices * kMoeMaxCap; i += kThreads)
+        mo.table[1 + mo.max_slices + i] = tb.yrow[i];
+      if (threadIdx.x == 0) mo.table[0] = slices;
+    }
+    const long long zeros = (long long)tb.head[1] * L.N;
+    for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < zeros;
+         i += (long long)a.G * kThreads) {
+      const int q = (int)(i / L.N);
+      L.y[(size_t)tb.inv[q] * L.N + (i - (long long)q * L.N)] = (__bf16)0.0f;
+    }
+    S = (long long)slices * mo.units_per_slice;
+  }
+
   // Units are row-group-major: with a power-of-two chunk count dividing the
   // grid, workgroup b keeps K-chunk (b - base) % chunks all linear long.
   // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
   // empty (chunks <= spt) and none is longer than the window.
   int ldec = 0;
   auto decode = [&](long long u) {
-    while (ldec + 1 < a.nlin && a.lin[ldec + 1].unit_base <= u) ++ldec;
-    const LinDesc& L = a.lin[ldec];
-    const long long local = u - L.unit_base;
     TileUnit t;
-    t.l = ldec;
+    long long local;
+    if constexpr (MOE) {
+      const int sl = (int)(u / a.moe.units_per_slice);
+      local = u - (long long)sl * a.moe.units_per_slice;
+      t.l = 0;
+      t.slice = sl;
+      t.e = __builtin_amdgcn_readfirstlane(tb.expert[sl]);
+      t.m = __builtin_amdgcn_readfirstlane(tb.rows[sl]);
+    } else {
+      while (ldec + 1 < a.nlin && a.lin[ldec + 1].unit_base <= u) ++ldec;
+      local = u - a.lin[ldec].unit_base;
+      t.l = ldec;
+      t.slice = ldec;
+      t.e = 0;
+      t.m = a.M;
+    }
+    const LinDesc& L = a.lin[t.l];
     t.grp = (int)(local / L.chunks);
     t.chunk = (int)(local - (long long)t.grp * L.chunks);
     t.spc = (L.spt + L.chunks - 1) / L.chunks;
@@ -483,15 +637,17 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     const LinDesc& L = a.lin[t.l];
     const int row0 = t.grp * kGroupRows + wv * kTileRows;
     const int c = min(j * kSegChunksT + lchunk, L.cpr - 1);
+    const u32x4* w = MOE ? L.w + (size_t)t.e * a.moe.w_stride : L.w;
 #pragma unroll
     for (int q = 0; q < kLoadsT; ++q) {
       const int row = min(row0 + kRowsPerLoadT * q + lrow, L.N - 1);
-      s.w[q] = L.w[(size_t)row * L.cpr + c];
+      s.w[q] = w[(size_t)row * L.cpr + c];
     }
     if (DT == SKINNY_FP8_BS128) {
       // The row group lies in one 128-row scale block.  Blocks past K cover
       // only zeroed weights; clamping keeps the read in bounds.
-      const float* srow = L.scale + (size_t)((t.grp * kGroupRows) / kScaleBlock) * L.kblocks;
+      const float* scale = MOE ? L.scale + (size_t)t.e * a.moe.s_stride : L.scale;
+      const float* srow = scale + (size_t)((t.grp * kGroupRows) / kScaleBlock) * L.kblocks;
       s.sc = srow[min(kSegBlocksT * j + lane % kSegBlocksT, L.kblocks - 1)];
     }
     // Keep the loads ahead of the previous segment's work.
@@ -553,35 +709,38 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     const int win = t.spc * kSegChunksT * XC;                    // x chunks per token in LDS
     xstride = win + 1;
     xw0 = t.j0 * kSegChunksT * XC;
-    xrow = xs + (n < a.M ? n : a.M) * xstride;
-    if (t.l == staged_l && t.chunk == staged_c) return;
-    staged_l = t.l;
+    xrow = xs + (n < t.m ? n : t.m) * xstride;
+    if (t.slice == staged_l && t.chunk == staged_c) return;
+    staged_l = t.slice;
     staged_c = t.chunk;
     const int xcpr = L.K >> 3;                                   // x chunks per token
     __syncthreads();                                             // all done with the old window
     // Token rows 0..M-1, zeros past K, then a zero row that lanes of absent
     // tokens read.
     const int wlen = min(win, xcpr - xw0);
-    stage_x<kThreads>(L, a.M, xcpr, xw0, wlen, xs, xstride);
+    stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride,
+                           MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr);
     const int pad = win - wlen;
-    for (int i = threadIdx.x; i < a.M * pad; i += kThreads) {
+    for (int i = threadIdx.x; i < t.m * pad; i += kThreads) {
       const int m = i / pad;
       xs[m * xstride + wlen + (i - m * pad)] = zero4();
     }
-    for (int c = threadIdx.x; c < win; c += kThreads) xs[a.M * xstride + c] = zero4();
+    for (int c = threadIdx.x; c < win; c += kThreads) xs[t.m * xstride + c] = zero4();
     __syncthreads();
   };
   auto epilogue = [&](const TileUnit& t) {
     // Lane (n, g) holds D[4 g + i][n]: token 4 g + i, row row0 + n.
     const LinDesc& L = a.lin[t.l];
     const int row = t.grp * kGroupRows + wv * kTileRows + n;
-    const long long slot = L.slot_base + (long long)t.grp * L.chunks + t.chunk;
+    const long long slot = (MOE ? (long long)t.slice * a.moe.units_per_slice : L.slot_base) +
+                           (long long)t.grp * L.chunks + t.chunk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
-      if (m < a.M) {
+      if (m < t.m) {
         if (L.chunks == 1) {
-          if (row < L.N) L.y[(size_t)m * L.N + row] = (__bf16)acc[i];
+          const int yr = MOE ? tb.yrow[t.slice * kMoeMaxCap + m] : m;
+          if (row < L.N) L.y[(size_t)yr * L.N + row] = (__bf16)acc[i];
         } else {
           a.slots[((size_t)slot * a.M + m) * kGroupRows + wv * kTileRows + n] = acc[i];
         }
@@ -613,13 +772,13 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     return 1;
   };
   long long u = blockIdx.x;
-  if (u >= a.S) return;
+  if (u >= S) return;
   TileSeg<DT> s0, s1;
   TileUnit cur = decode(u);
   load(s0, cur, cur.j0);
   int in_b = 0;                                         // the current unit's first segment is in s1
   for (;;) {
-    const bool has_next = u + a.G < a.S;
+    const bool has_next = u + a.G < S;
     const TileUnit nx = has_next ? decode(u + a.G) : cur;
     stage(cur);
     const int flip = in_b ? run_unit(s1, s0, cur, nx, has_next)
@@ -660,6 +819,38 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchAr
     for (int r = 0; r < kCombineRows; ++r) sum[r] += v[r];
   }
   __bf16* y = L.y + (size_t)m * L.N + row;
+#pragma unroll
+  for (int r = 0; r < kCombineRows; ++r)
+    if (row + r < L.N) y[r] = (__bf16)sum[r];
+}
+
+// Second pass of a split MoE launch: grid row y is a slice, the table the
+// first workgroup of the main kernel left in the workspace names its routes.
+__global__ __launch_bounds__(kCombineThreads) void skinny_moe_combine(const LaunchArgs a) {
+  const LinDesc& L = a.lin[0];
+  const int* tb = a.moe.table;
+  const int sl = blockIdx.y;
+  if (sl >= tb[0]) return;
+  const int M = tb[1 + sl];
+  const int R = a.band_rows;
+  const int quads = (L.N + kCombineRows - 1) / kCombineRows;
+  const int i = blockIdx.x * kCombineThreads + threadIdx.x;
+  if (i >= M * quads) return;
+  const int m = i / quads;
+  const int row = (i - m * quads) * kCombineRows;
+  const int grp = row / R;
+  const int rr = row - grp * R;
+  const long long slot0 = (long long)sl * a.moe.units_per_slice + (long long)grp * L.chunks;
+  const f32x4* p =
+      reinterpret_cast<const f32x4*>(a.slots + ((size_t)slot0 * a.M + m) * R + rr);
+  const size_t stride = (size_t)a.M * R / kCombineRows;
+  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < L.chunks; ++c) {
+    const f32x4 v = p[c * stride];
+#pragma unroll
+    for (int r = 0; r < kCombineRows; ++r) sum[r] += v[r];
+  }
+  __bf16* y = L.y + (size_t)tb[1 + a.moe.max_slices + sl * kMoeMaxCap + m] * L.N + row;
 #pragma unroll
   for (int r = 0; r < kCombineRows; ++r)
     if (row + r < L.N) y[r] = (__bf16)sum[r];
@@ -904,19 +1095,19 @@ bool rows_supported(const skinny_linear& L, int M) {
 // skinny_tiles: fewest K-chunks of a linear whose x window fits the LDS
 // budget (token rows padded by one chunk), or -1 if not even one segment fits.
 constexpr int kTilesMinSegs = 4;          // segments per chunk when splitting for parallelism
-int tiles_lds_chunks(int dtype, int M, int K) {
+int tiles_lds_chunks(int dtype, int M, int K, int budget = kTilesXBudget) {
   const int xc = dtype == SKINNY_BF16 ? 1 : 2;
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  const int max_spc = (kTilesXBudget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
+  const int max_spc = (budget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
   if (max_spc < 1) return -1;
   return (spt + max_spc - 1) / max_spc;
 }
 
-int tiles_chunks(int dtype, int M, int K, long long par) {
+int tiles_chunks(int dtype, int M, int K, long long par, int budget = kTilesXBudget) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  return chunk_count(spt, tiles_lds_chunks(dtype, M, K), par, kTilesMinSegs);
+  return chunk_count(spt, tiles_lds_chunks(dtype, M, K, budget), par, kTilesMinSegs);
 }
 
 int tiles_max_chunks(int dtype, int M, int K) { return tiles_chunks(dtype, M, K, 1LL << 40); }
@@ -972,7 +1163,7 @@ KernelChoice tiles_kernel() {
   static_assert(kScaleBlock % (kTileRows * WPB) == 0, "a row group must sit in one scale block");
   static_assert((kTileRows * WPB) % kCombineRows == 0, "second-pass quads");
   KernelChoice k;
-  k.fn = skinny_tiles<DT, WPB>;
+  k.fn = skinny_tiles<DT, WPB, false>;
   k.band_rows = kTileRows * WPB;
   k.wpb = WPB;
   k.tiles = true;
@@ -1366,6 +1557,159 @@ size_t mlp_workspace(const skinny_mlp& P, int M) {
   return mlp_gu_bytes(P, M) + (a > b ? a : b);
 }
 
+// ---------------------------------------------------------------------------
+// Mixture-of-experts launches (skinny_tiles in its MoE form).
+
+struct MoePlan {
+  int cap;               // routes per slice: the token count
+  int routes;
+  int active;            // experts the routes can reach: min(E, routes)
+  int max_slices;
+  int groups;            // row groups per expert
+  int table_lds;         // LDS bytes of the slice table
+  int x_budget;          // LDS bytes left for x
+  size_t table_bytes;    // workspace bytes of the table copy (256-aligned)
+};
+
+// Slices: an expert with c routes makes ceil(c / cap) of them, so n active
+// experts over `routes` routes make at most n + (routes - n) / cap, which
+// grows with n (<= min(E, routes)).
+MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
+  MoePlan p;
+  p.cap = T;
+  p.routes = T * topk;
+  p.active = ex.E < p.routes ? ex.E : p.routes;
+  p.max_slices = p.active + (p.routes - p.active) / p.cap;
+  p.groups = (ex.N + kTileRows * kTilesWavesPerBlock - 1) / (kTileRows * kTilesWavesPerBlock);
+  const int tb = 2 * 4 + p.max_slices * (2 * 4 + 2 * kMoeMaxCap) + p.routes;
+  p.table_lds = (tb + 15) / 16 * 16;
+  p.x_budget = kTilesXBudget - p.table_lds;
+  const size_t tg = (size_t)(1 + p.max_slices * (1 + kMoeMaxCap)) * sizeof(int);
+  p.table_bytes = (tg + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+  return p;
+}
+
+size_t moe_workspace(const skinny_experts& ex, const MoePlan& p) {
+  const int c = tiles_chunks(ex.dtype, p.cap, ex.K, 1LL << 40, p.x_budget);
+  const size_t slots = c > 1 ? (size_t)p.max_slices * p.groups * c * p.cap *
+                                   (kTileRows * kTilesWavesPerBlock) * sizeof(float)
+                             : 0;
+  const size_t b = p.table_bytes + slots;
+  return b > SKINNY_MIN_WORKSPACE_BYTES ? b : SKINNY_MIN_WORKSPACE_BYTES;
+}
+
+skinny_status check_experts(const skinny_experts* ex, int T, int topk, int flags) {
+  if (!ex) return SKINNY_ERR_INVALID_ARG;
+  if (ex->dtype != SKINNY_BF16 && ex->dtype != SKINNY_FP8_BS128) return SKINNY_ERR_INVALID_ARG;
+  if (ex->E < 1 || ex->N < 1 || ex->K < 1 || !ex->w) return SKINNY_ERR_INVALID_ARG;
+  if ((ex->dtype == SKINNY_FP8_BS128) != (ex->w_scale != nullptr)) return SKINNY_ERR_INVALID_ARG;
+  if (T < 1 || T > SKINNY_MAX_M || topk < 1 || topk > SKINNY_MAX_TOPK) return SKINNY_ERR_INVALID_ARG;
+  if (flags & ~(SKINNY_MOE_X_PER_ROUTE | SKINNY_MOE_SWIGLU)) return SKINNY_ERR_INVALID_ARG;
+  if (ex->K % (ex->dtype == SKINNY_BF16 ? 8 : 16) != 0) return SKINNY_ERR_UNSUPPORTED;
+  if (ex->N > (1 << 26) || ex->K > (1 << 28)) return SKINNY_ERR_UNSUPPORTED;
+  if (!aligned(ex->w, 16) || (ex->w_scale && !aligned(ex->w_scale, 4))) return SKINNY_ERR_UNSUPPORTED;
+  const MoePlan p = moe_plan(*ex, T, topk);
+  if (p.routes > kMoeMaxRoutes || p.cap > kMoeMaxCap) return SKINNY_ERR_UNSUPPORTED;
+  if (tiles_lds_chunks(ex->dtype, p.cap, ex->K, p.x_budget) < 1) return SKINNY_ERR_UNSUPPORTED;
+  return SKINNY_OK;
+}
+
+skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, int T, int topk,
+                      int flags, void* y, void* ws, size_t ws_bytes, void* stream,
+                      void* const* events) {
+  skinny_status st = check_experts(ex, T, topk, flags);
+  if (st != SKINNY_OK) return st;
+  if (!x || !ids || !y) return SKINNY_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4)) return SKINNY_ERR_UNSUPPORTED;
+  const MoePlan p = moe_plan(*ex, T, topk);
+  if (!ws) return SKINNY_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
+  if (ws_bytes < moe_workspace(*ex, p)) return SKINNY_ERR_WORKSPACE;
+  const int dtype = ex->dtype;
+  const size_t eb = dtype == SKINNY_BF16 ? 2 : 1;
+  const size_t nb = (size_t)((ex->N + 127) / 128) * ((ex->K + 127) / 128);
+  const int xrows = flags & SKINNY_MOE_X_PER_ROUTE ? p.routes : T;
+  const Range yr{(uintptr_t)y, (uintptr_t)y + (size_t)p.routes * ex->N * 2};
+  const Range xr{(uintptr_t)x,
+                 (uintptr_t)x + (size_t)xrows * ex->K * 2 * (flags & SKINNY_MOE_SWIGLU ? 2 : 1)};
+  const Range ir{(uintptr_t)ids, (uintptr_t)ids + (size_t)p.routes * 4};
+  const Range wr{(uintptr_t)ex->w, (uintptr_t)ex->w + (size_t)ex->E * ex->N * ex->K * eb};
+  const Range sr{(uintptr_t)ex->w_scale,
+                 (uintptr_t)ex->w_scale + (ex->w_scale ? (size_t)ex->E * nb * 4 : 0)};
+  const Range kr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
+  if (overlap(yr, xr) || overlap(yr, ir) || overlap(yr, wr) || overlap(yr, sr) ||
+      overlap(yr, kr) || overlap(kr, xr) || overlap(kr, ir) || overlap(kr, wr) || overlap(kr, sr))
+    return SKINNY_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != SKINNY_OK) return st;
+  if (!dev.gfx950) return SKINNY_ERR_UNSUPPORTED;
+
+  KernelChoice k;
+  k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesPerBlock, true>
+                              : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesPerBlock, true>;
+  k.band_rows = kTileRows * kTilesWavesPerBlock;
+  k.wpb = kTilesWavesPerBlock;
+  k.tiles = true;
+  st = ensure_lds(k.fn, kTilesLds);
+  if (st != SKINNY_OK) return st;
+  int G = 0;
+  st = auto_workers(dev, k, kTilesLds, &G);
+  if (st != SKINNY_OK) return st;
+
+  LaunchArgs a;
+  memset(&a, 0, sizeof a);
+  a.nlin = 1;
+  a.M = p.cap;
+  a.band_rows = k.band_rows;
+  a.x_lds_bytes = p.x_budget;
+  LinDesc& d = a.lin[0];
+  d.w = (const u32x4*)ex->w;
+  d.scale = ex->w_scale;
+  d.x = (const u32x4*)x;
+  d.y = (__bf16*)y;
+  d.N = ex->N;
+  d.K = ex->K;
+  d.cpr = ex->K / (dtype == SKINNY_BF16 ? 8 : 16);
+  d.spt = (d.cpr + kSegChunksT - 1) / kSegChunksT;
+  d.kblocks = (ex->K + kScaleBlock - 1) / kScaleBlock;
+  d.act = flags & SKINNY_MOE_SWIGLU ? kActSwiGLU : kActNone;
+  // K-chunks as for a launch of `active` linears of this shape.
+  const long long want = (long long)kTilesUnitsPerWorker * G;
+  const long long groups = (long long)p.active * p.groups;
+  d.chunks = tiles_chunks(dtype, p.cap, ex->K, (want + groups - 1) / groups, p.x_budget);
+  MoeArgs& mo = a.moe;
+  mo.ids = ids;
+  mo.table = d.chunks > 1 ? (int*)ws : nullptr;
+  mo.w_stride = (long long)ex->N * d.cpr;
+  mo.s_stride = dtype == SKINNY_BF16 ? 0 : (long long)nb;
+  mo.E = ex->E;
+  mo.routes = p.routes;
+  mo.topk = topk;
+  mo.cap = p.cap;
+  mo.per_route = flags & SKINNY_MOE_X_PER_ROUTE ? 1 : 0;
+  mo.max_slices = p.max_slices;
+  mo.units_per_slice = p.groups * d.chunks;
+  mo.table_lds = p.x_budget + kTilesWBytes;
+  a.slots = (float*)((char*)ws + p.table_bytes);
+  a.S = (long long)p.max_slices * mo.units_per_slice;
+  if (G > a.S) G = (int)a.S;
+  a.G = G;
+  hipStream_t s = (hipStream_t)stream;
+  if (events && hipEventRecord((hipEvent_t)events[0], s) != hipSuccess) return SKINNY_ERR_HIP;
+  hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), kTilesLds, s, a);
+  if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+  if (events && hipEventRecord((hipEvent_t)events[1], s) != hipSuccess) return SKINNY_ERR_HIP;
+  if (d.chunks > 1) {
+    const long long quads = (long long)p.cap * ((ex->N + kCombineRows - 1) / kCombineRows);
+    const long long cblocks = (quads + kCombineThreads - 1) / kCombineThreads;
+    hipLaunchKernelGGL(skinny_moe_combine, dim3((unsigned)cblocks, p.max_slices),
+                       dim3(kCombineThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+  }
+  return SKINNY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1581,6 +1925,25 @@ skinny_status skinny_mlp_swiglu(const skinny_mlp* mlp, int M, void* workspace,
   st = run(&g, 1, M, nullptr, slots, workspace_bytes - gub, stream);
   if (st != SKINNY_OK) return st;
   return run(&d, 1, M, nullptr, slots, workspace_bytes - gub, stream, nullptr, 0, true);
+}
+
+size_t skinny_moe_workspace_bytes(const skinny_experts* experts, int T, int topk, int flags) {
+  if (check_experts(experts, T, topk, flags) != SKINNY_OK) return 0;
+  return moe_workspace(*experts, moe_plan(*experts, T, topk));
+}
+
+skinny_status skinny_moe_linear(const skinny_experts* experts, const void* x, const int* ids,
+                                int T, int topk, int flags, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return moe_run(experts, x, ids, T, topk, flags, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void* x,
+                                      const int* ids, int T, int topk, int flags, void* y,
+                                      void* const* events, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!events) return SKINNY_ERR_INVALID_ARG;
+  return moe_run(experts, x, ids, T, topk, flags, y, workspace, workspace_bytes, stream, events);
 }
 
 const char* skinny_status_string(int status) {

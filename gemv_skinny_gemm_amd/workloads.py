@@ -111,3 +111,37 @@ def algorithmic_bytes(specs, M: int) -> int:
 
 def flops(specs, M: int) -> int:
     return sum(s.flops(M) for s in specs)
+
+
+# Mixture-of-experts verify step.  The pages route tokens to the top 2 of 8
+# experts with hidden size 4096 and two favoured experts ("Multi-GPU Inference
+# and Serving at Scale", Example 8) and verify about six draft tokens per step
+# ("9% faster GLM-5.3-Flash prefill", section "TileLang: twice as fast, and no
+# faster").  They give no expert width; 1536 (a small expert, 3/8 of hidden)
+# is taken, a multiple of 128 so FP8 scale blocks never straddle experts.
+MOE_EXPERTS = 8
+MOE_TOPK = 2
+MOE_HIDDEN = 4096
+MOE_INTER = 1536
+MOE_TOKENS = 6
+
+
+def moe_experts(dtype: int = FP8_BS128) -> list[LinearSpec]:
+    """[gate_up, down] of the MoE layer's experts, each as one [E * N][K]
+    tensor (expert e = rows e N .. e N + N - 1, i.e. [E][N][K])."""
+    tag = "moe" + ("" if dtype == BF16 else "-fp8")
+    E, H, I = MOE_EXPERTS, MOE_HIDDEN, MOE_INTER
+    return [_spec(tag, 0, "experts_gate_up", E * 2 * I, H, dtype),
+            _spec(tag, 0, "experts_down", E * H, I, dtype)]
+
+
+def moe_algorithmic_bytes(spec: LinearSpec, ids, experts: int, x_rows: int,
+                          x_cols: int) -> int:
+    """One MoE linear call: the chosen experts' W and scales once each, x,
+    the routes' y and the ids."""
+    import numpy as np
+    ids = np.asarray(ids)
+    chosen = len(set(int(e) for e in ids.ravel() if 0 <= e < experts))
+    per_expert = (spec.weight_bytes() + spec.scale_bytes()) // experts
+    routes = ids.size
+    return chosen * per_expert + 2 * x_rows * x_cols + 2 * routes * (spec.N // experts) + 4 * routes

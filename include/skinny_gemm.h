@@ -219,6 +219,56 @@ size_t skinny_mlp_workspace_bytes(const skinny_mlp* mlp, int M);
 skinny_status skinny_mlp_swiglu(const skinny_mlp* mlp, int M, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* One linear of a mixture-of-experts layer over the routes of a decode or
+ * verify batch.  A router sends each of T tokens to topk experts, every
+ * expert being its own small network ("Multi-GPU Inference and Serving at
+ * Scale", Example 8); a verify step passes a handful of tokens through the
+ * weight-only FP8 expert matmuls ("9% faster GLM-5.3-Flash prefill with
+ * GPU-to-GPU IPC (and why TileLang didn't help)", section "TileLang: twice as
+ * fast, and no faster").  Route r = t * topk + j is token t's j-th choice,
+ * e = ids[r]:
+ *   y[r] = x_r . W_e^T, x_r = x[t] (default) or x[r] (SKINNY_MOE_X_PER_ROUTE),
+ *   y[r] = 0 for every r whose e is outside [0, E).
+ * With SKINNY_MOE_SWIGLU each x row holds [g | u] (2K values) and x_r is
+ * bf16(silu(g) * u) computed in fp32 as the input is staged: the experts'
+ * down projection reads their gate_up outputs directly.
+ *   experts->w        [E][N][K] bf16 or E4M3FN (expert e at e * N * K)
+ *   experts->w_scale  [E][ceil(N/128)][ceil(K/128)] fp32 (FP8), NULL (bf16)
+ *   x                 [T][K] bf16, or [T * topk][K]; 2K columns with SWIGLU
+ *   ids               [T][topk] int32, device, read by the kernel (no host
+ *                     synchronization); any values (duplicates included)
+ *   y                 [T * topk][N] bf16, written
+ * Each chosen expert's weights are streamed once for all of its routes, in
+ * one persistent launch that finds the routes per expert itself (plus a
+ * second pass when K is split).  Accumulation is fp32 with the single-linear
+ * bound per route.  Requirements as for a linear (K % 8 or % 16, 16-byte
+ * aligned x, y, w and workspace; 4-byte aligned ids and w_scale), plus
+ * 1 <= T <= SKINNY_MAX_M, 1 <= topk <= SKINNY_MAX_TOPK, E >= 1; y must not
+ * overlap x, ids, the weights, the scales or the workspace, and the
+ * workspace must not overlap x or ids.  Workspace:
+ * skinny_moe_workspace_bytes(experts, T, topk, flags), 0 for invalid
+ * arguments. */
+#define SKINNY_MAX_TOPK 16
+enum skinny_moe_flags { SKINNY_MOE_X_PER_ROUTE = 1, SKINNY_MOE_SWIGLU = 2 };
+typedef struct skinny_experts {
+  int dtype;            /* SKINNY_BF16 or SKINNY_FP8_BS128 */
+  int E;                /* experts                          */
+  int N;                /* rows of each expert's W          */
+  int K;                /* columns of each expert's W       */
+  const void* w;
+  const float* w_scale;
+} skinny_experts;
+size_t skinny_moe_workspace_bytes(const skinny_experts* experts, int T, int topk, int flags);
+skinny_status skinny_moe_linear(const skinny_experts* experts, const void* x, const int* ids,
+                                int T, int topk, int flags, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream);
+/* skinny_moe_linear recording events[0] / events[1] (hipEvent_t, created by
+ * the caller) just before and after its main launch, for benchmarks. */
+skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void* x,
+                                      const int* ids, int T, int topk, int flags, void* y,
+                                      void* const* events, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* skinny_status_string(int status);
 

@@ -211,3 +211,38 @@ def test_mlp_workspace_and_bad_arguments():
     assert call(sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, B, WS + 64)) == INVALID
     assert call(sg.Mlp(sg.BF16, 64, 32, 0, A, None, A + 0x10000, None, WS + 64, C)) == INVALID
     assert call(sg.Mlp(sg.FP8_BS128, 64, 32, 0, A, None, A + 0x10000, None, B, C)) == INVALID
+
+
+def test_moe_workspace_and_bad_arguments():
+    L = sg.lib()
+    ex = sg.Experts(sg.FP8_BS128, 8, 3072, 4096, A, A + 0x8000000)
+    wsb = sg.moe_workspace_bytes(ex, 6, 2)
+    assert wsb >= MIN_WORKSPACE and wsb % 16 == 0
+    assert sg.moe_workspace_bytes(ex, 0, 2) == 0 and sg.moe_workspace_bytes(ex, 17, 2) == 0
+    assert sg.moe_workspace_bytes(ex, 6, 0) == 0
+    assert sg.moe_workspace_bytes(ex, 6, sg.MAX_TOPK + 1) == 0
+    assert sg.moe_workspace_bytes(ex, 16, sg.MAX_TOPK) >= wsb          # more routes, more slices
+    assert sg.moe_workspace_bytes(sg.Experts(sg.BF16, 8, 64, 64, A, A), 1, 1) == 0  # bf16 + scales
+    assert sg.moe_workspace_bytes(sg.Experts(sg.FP8_BS128, 8, 64, 64, A, None), 1, 1) == 0
+    assert sg.moe_workspace_bytes(sg.Experts(sg.BF16, 0, 64, 64, A, None), 1, 1) == 0
+    X, IDS, Y = 0x20000000, 0x21000000, 0x22000000
+    big = 0x40000000                                                      # past the weights
+
+    def call(e=ex, x=X, ids=IDS, T=6, topk=2, flags=0, y=Y, ws=big, n=wsb):
+        return L.skinny_moe_linear(ctypes.byref(e) if e is not None else None, x, ids, T, topk,
+                                   flags, y, ws, n, None)
+    assert call(e=None) == INVALID
+    assert call(x=None) == INVALID and call(ids=None) == INVALID and call(y=None) == INVALID
+    assert call(T=0) == INVALID and call(T=17) == INVALID and call(topk=17) == INVALID
+    assert call(flags=4) == INVALID
+    assert call(ws=None) == WORKSPACE and call(n=wsb - 1) == WORKSPACE
+    assert call(x=X + 8) == UNSUPPORTED and call(ids=IDS + 2) == UNSUPPORTED
+    assert call(e=sg.Experts(sg.FP8_BS128, 8, 3072, 4088, A, A + 0x8000000)) == UNSUPPORTED
+    assert call(y=X) == INVALID                                          # y over x
+    assert call(y=IDS - 16) == INVALID                                   # y runs into ids
+    assert call(y=A + 0x1000) == INVALID                                 # y inside the weights
+    assert call(ws=X) == INVALID                                         # workspace over x
+    # x per route with SwiGLU: 12 routes x 2K bf16, so y just past 6 x K no longer clears it.
+    assert call(y=X + 6 * 4096 * 2, flags=sg.MOE_X_PER_ROUTE | sg.MOE_SWIGLU) == INVALID
+    assert L.skinny_moe_linear_timed(ctypes.byref(ex), X, IDS, 6, 2, 0, Y, None, big, wsb,
+                                     None) == INVALID
