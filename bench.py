@@ -44,6 +44,11 @@ WORKLOADS = {
     "qwen2.5-72b-tp1-mlp-swiglu-bf16": "one layer's gated MLP at TP=1: gate_up 59136x8192, silu(g)*u "
                                        "fused into down's input staging, down 8192x29568, bf16 W",
     "qwen2.5-72b-tp1-mlp-swiglu-fp8": "the same gated MLP with FP8-E4M3 W + 128x128 fp32 block scales",
+    "moe-verify-experts-fp8": "MoE verify step: M tokens (default 6) routed to the top 2 of 8 "
+                              "experts (two favoured), hidden 4096, expert width 1536: the "
+                              "chosen experts' gate_up [3072x4096] then down [4096x1536] with "
+                              "silu(g)*u fused, FP8-E4M3 W + 128x128 fp32 block scales",
+    "moe-verify-experts-bf16": "the same MoE verify step with bf16 expert weights",
 }
 
 
@@ -57,7 +62,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen2.5-72b-tp1-stack-bf16", choices=sorted(WORKLOADS))
-    p.add_argument("--m", type=int, default=1, help="tokens per step (1..16)")
+    p.add_argument("--m", type=int, default=None,
+                   help="tokens per step (1..16; default 1, the MoE verify step 6)")
     p.add_argument("--variant", default="auto", choices=["auto", "vector", "mfma"])
     p.add_argument("--waves", type=int, default=0, help="persistent waves (0 = automatic)")
     p.add_argument("--rotate-bytes", type=float, default=2.5e9,
@@ -88,7 +94,62 @@ def make_workload(name):
         return wl.mlp(1, wl.BF16)
     if name == "qwen2.5-72b-tp1-mlp-swiglu-fp8":
         return wl.mlp(1, wl.FP8_BS128)
+    if name == "moe-verify-experts-fp8":
+        return wl.moe_experts(wl.FP8_BS128)
+    if name == "moe-verify-experts-bf16":
+        return wl.moe_experts(wl.BF16)
     raise ValueError(name)
+
+
+def moe_routes(M):
+    """The verify step's seeded router choices (int32 [M][top k])."""
+    from gemv_skinny_gemm_amd import synth
+    from gemv_skinny_gemm_amd import workloads as wl
+    return synth.route_topk(0, synth.stream_id("moe-verify", M), M, wl.MOE_EXPERTS, wl.MOE_TOPK)
+
+
+def moe_bytes(specs, ids):
+    """(gate_up call, down call) algorithmic bytes: chosen experts' W once."""
+    from gemv_skinny_gemm_amd import workloads as wl
+    gu, dn = specs
+    E = wl.MOE_EXPERTS
+    a = wl.moe_algorithmic_bytes(gu, ids, E, ids.shape[0], gu.K)
+    b = wl.moe_algorithmic_bytes(dn, ids, E, ids.size, 2 * dn.K)
+    return a, b
+
+
+def moe_cpu_baseline(specs, ids, seed=0):
+    """The fp64 oracle over the whole MoE step (it is small): gate_up, then
+    down on the oracle's own bf16 gate_up outputs.  Returns seconds, bytes,
+    threads, (g_ref, g_a) and a description."""
+    import numpy as np
+
+    import oracle
+    from gemv_skinny_gemm_amd import synth
+    from gemv_skinny_gemm_amd import workloads as wl
+
+    E, T = wl.MOE_EXPERTS, ids.shape[0]
+    gu, dn = specs
+    x = synth.tensor_bf16(seed, gu.x_stream, T, gu.K, wl.X_SIGMA)
+    ws = []
+    for s in specs:
+        if s.dtype == wl.BF16:
+            ws.append((synth.tensor_bf16(seed, s.w_stream, s.N, s.K, wl.W_SIGMA)
+                       .reshape(E, s.N // E, s.K), None))
+        else:
+            q, sc, _ = synth.fp8_weight_bs128(seed, s.w_stream, s.N, s.K, wl.W_SIGMA)
+            ws.append((q.reshape(E, s.N // E, s.K), sc.reshape(E, -1, sc.shape[1])))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        g_ref, g_a = oracle.moe_linear(x, ids, ws[0][0], scales=ws[0][1])
+        h = oracle.bf16_encode(g_ref)
+        oracle.moe_linear(h, ids, ws[1][0], scales=ws[1][1], x_per_route=True, swiglu=True)
+        times.append(time.perf_counter() - t0)
+    secs = float(np.median(times))
+    desc = (f"the whole step ({T} tokens, {ids.size} routes, gate_up then down), compute only, "
+            "median of 3 runs")
+    return secs, sum(moe_bytes(specs, ids)), oracle.host_threads(), (g_ref, g_a), desc
 
 
 def measured_traffic(workload, M):
@@ -172,6 +233,9 @@ def main():
                                    "stack is measured at one GPU's share; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    moe = args.workload.startswith("moe-")
+    if args.m is None:
+        args.m = 6 if moe else 1
     if not 1 <= args.m <= 16:
         sys.exit("--m must be in 1..16")
 
@@ -192,6 +256,10 @@ def main():
     # counts its [M][2I] intermediate written and read.
     if mlp:
         step_bytes = wl.mlp_algorithmic_bytes(specs, M)
+    elif moe:
+        ids_host = moe_routes(M)
+        moe_gu_bytes, moe_dn_bytes = moe_bytes(specs, ids_host)
+        step_bytes = moe_gu_bytes + moe_dn_bytes
     else:
         step_bytes = wl.algorithmic_bytes(specs, M) + (4 * M if head else 0)
     step_flops = wl.flops(specs, M)
@@ -207,6 +275,21 @@ def main():
     if mlp:
         mlps = [sg.make_mlp(t[0][0], t[0][1], t[1][1], t[1][3], t[0][2], t[1][2]) for t in tensors]
         ws = torch.empty(sg.mlp_workspace_bytes(mlps[0], M), dtype=torch.uint8, device="cuda")
+    elif moe:
+        E = wl.MOE_EXPERTS
+        ids = torch.from_numpy(ids_host).cuda()
+
+        def experts(t):
+            w, sc = t[1], t[2]
+            return sg.make_experts(w.view(E, w.shape[0] // E, w.shape[1]),
+                                   None if sc is None else sc.view(E, -1, sc.shape[1]))
+        moe_ex = [(experts(t[0]), experts(t[1])) for t in tensors]
+        routes = ids_host.size
+        moe_gu = torch.empty((routes, specs[0].N // E), dtype=torch.bfloat16, device="cuda")
+        moe_y = torch.empty((routes, specs[1].N // E), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(sg.moe_workspace_bytes(moe_ex[0][0], M, wl.MOE_TOPK),
+                             sg.moe_workspace_bytes(moe_ex[0][1], M, wl.MOE_TOPK, True, True)),
+                         dtype=torch.uint8, device="cuda")
     else:
         ws = torch.empty(sg.stack_workspace_bytes(sets[0], M), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -214,12 +297,23 @@ def main():
     # launch (two thirds of its bytes), timed through the same entry point.
     timed_sets = [st[:1] for st in sets] if mlp else sets
     timed_bytes = wl.algorithmic_bytes(specs[:1], M) if mlp else step_bytes
-    plan = sg.plan_query(timed_sets[0], M)
-    n_launch = sg.launch_count(timed_sets[0])
+    if moe:
+        # The MoE step's dominant kernel is its gate_up launch (two thirds of the bytes).
+        timed_bytes = moe_gu_bytes
+        plan = sg.Plan(sg.VARIANT_MFMA, 0)
+        n_launch = 1
+    else:
+        plan = sg.plan_query(timed_sets[0], M)
+        n_launch = sg.launch_count(timed_sets[0])
 
     tokens = [torch.zeros(M, dtype=torch.int32, device="cuda") for _ in range(copies)]
 
     def step(i):
+        if moe:
+            ex_gu, ex_dn = moe_ex[i % copies]
+            sg.moe_linear(ex_gu, tensors[i % copies][0][0], ids, moe_gu, ws)
+            sg.moe_linear(ex_dn, moe_gu, ids, moe_y, ws, x_per_route=True, swiglu=True)
+            return
         if head or mlp:
             if variant != sg.VARIANT_AUTO or args.waves:
                 sys.exit("the lm-head and MLP workloads run the automatic plan")
@@ -263,6 +357,10 @@ def main():
     prefill(args.steps * 0.1)
     for i in range(args.steps):
         handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
+        if moe:
+            c = (args.warmup + i) % copies
+            sg.moe_linear_timed(moe_ex[c][0], tensors[c][0][0], ids, moe_gu, ws, handles)
+            continue
         sg.linear_run_timed(timed_sets[(args.warmup + i) % copies], M, ws, handles,
                             variant=variant, waves=args.waves)
     torch.cuda.synchronize()
@@ -327,7 +425,26 @@ def main():
         result["config"]["calibration_copy_bytes"] = 2 * n
         del src, dst
 
-    if not args.no_cpu_baseline:
+    if moe:
+        result["config"].update({
+            "experts": wl.MOE_EXPERTS, "top_k": wl.MOE_TOPK, "routes": int(ids_host.size),
+            "experts_chosen": len(set(ids_host.ravel().tolist())),
+            "gate_up_bytes": moe_gu_bytes, "down_bytes": moe_dn_bytes})
+
+    if not args.no_cpu_baseline and moe:
+        import oracle
+        secs, sbytes, threads, (g_ref, g_a), desc = moe_cpu_baseline(specs, ids_host)
+        step(0)
+        torch.cuda.synchronize()
+        ok, worst, _ = oracle.check(moe_gu.float().cpu().double().numpy(), g_ref, g_a)
+        if not ok:
+            log(f"GPU gate_up output outside the bound (worst {worst:.3g})")
+        result["cpu_baseline"] = {
+            "value": round(sbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": desc, "us_per_step": round(secs * 1e6, 1),
+            "cpu": platform.processor() or platform.machine()}
+        result["config"]["sampled_outputs_worst_err_over_bound"] = round(worst, 4)
+    elif not args.no_cpu_baseline:
         import oracle
         secs, sbytes, threads, refs, desc = cpu_baseline(specs, M, args.cpu_sample_rows)
         cpu_gbps = sbytes / secs / 1e9
