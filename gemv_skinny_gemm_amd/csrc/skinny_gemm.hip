@@ -79,7 +79,8 @@ struct LinDesc {
   long long slot_base;   // first partial slot of a split linear
   int act;               // kActNone, or kActSwiGLU: x is [M][2K] = [gate | up], the
                          // linear's input is silu(gate) * up
-  int pad;
+  int sub;               // skinny_tiles: x windows per K-chunk, walked in turn by the
+                         // unit's workgroup with its sums kept in registers
 };
 
 constexpr int kActNone = 0;
@@ -461,6 +462,7 @@ struct TileUnit {
   int l;                 // linear
   int grp;               // row group
   int chunk;             // K-chunk
+  int sub;               // x window of the chunk
   int j0, j1;            // segments [j0, j1) of each row
   int spc;               // x window, in segments
   int slice;             // MoE: slice (else the linear)
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
   // empty (chunks <= spt) and none is longer than the window.
   int ldec = 0;
-  auto decode = [&](long long u) {
+  auto decode = [&](long long u, int sub) {
     TileUnit t;
     long long local;
     if constexpr (MOE) {
@@ -624,9 +626,14 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     const LinDesc& L = a.lin[t.l];
     t.grp = (int)(local / L.chunks);
     t.chunk = (int)(local - (long long)t.grp * L.chunks);
-    t.spc = (L.spt + L.chunks - 1) / L.chunks;
-    t.j0 = (int)((long long)t.chunk * L.spt / L.chunks);
-    t.j1 = (int)((long long)(t.chunk + 1) * L.spt / L.chunks);
+    // Window `sub` of chunk c: [c0 + sub len / L.sub, c0 + (sub + 1) len / L.sub)
+    // of the chunk's segments [c0, c0 + len).
+    const int c0 = (int)((long long)t.chunk * L.spt / L.chunks);
+    const int len = (int)((long long)(t.chunk + 1) * L.spt / L.chunks) - c0;
+    t.sub = sub;
+    t.spc = ((L.spt + L.chunks - 1) / L.chunks + L.sub - 1) / L.sub;
+    t.j0 = c0 + sub * len / L.sub;
+    t.j1 = c0 + (sub + 1) * len / L.sub;
     return t;
   };
   // Segment j of unit t into s.  Rows past N read row N - 1 (a B column only
@@ -703,16 +710,17 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   };
   // x[M][window] of unit t into LDS, between two barriers, if it is not
   // there already (the same decision in every wave).
-  int staged_l = -1, staged_c = -1;
+  int staged_l = -1, staged_c = -1, staged_s = -1;
   auto stage = [&](const TileUnit& t) {
     const LinDesc& L = a.lin[t.l];
     const int win = t.spc * kSegChunksT * XC;                    // x chunks per token in LDS
     xstride = win + 1;
     xw0 = t.j0 * kSegChunksT * XC;
     xrow = xs + (n < t.m ? n : t.m) * xstride;
-    if (t.slice == staged_l && t.chunk == staged_c) return;
+    if (t.slice == staged_l && t.chunk == staged_c && t.sub == staged_s) return;
     staged_l = t.slice;
     staged_c = t.chunk;
+    staged_s = t.sub;
     const int xcpr = L.K >> 3;                                   // x chunks per token
     __syncthreads();                                             // all done with the old window
     // Token rows 0..M-1, zeros past K, then a zero row that lanes of absent
@@ -774,20 +782,22 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   long long u = blockIdx.x;
   if (u >= S) return;
   TileSeg<DT> s0, s1;
-  TileUnit cur = decode(u);
+  TileUnit cur = decode(u, 0);
   load(s0, cur, cur.j0);
   int in_b = 0;                                         // the current unit's first segment is in s1
   for (;;) {
-    const bool has_next = u + a.G < S;
-    const TileUnit nx = has_next ? decode(u + a.G) : cur;
+    // A unit's x windows in turn (its sums stay in acc), then the next unit.
+    const bool last = cur.sub + 1 == a.lin[cur.l].sub;
+    const bool has_next = !last || u + a.G < S;
+    const TileUnit nx = !last ? decode(u, cur.sub + 1) : has_next ? decode(u + a.G, 0) : cur;
     stage(cur);
     const int flip = in_b ? run_unit(s1, s0, cur, nx, has_next)
                           : run_unit(s0, s1, cur, nx, has_next);
-    epilogue(cur);
+    if (last) epilogue(cur);
     if (!has_next) break;
     in_b ^= flip;
     cur = nx;
-    u += a.G;
+    if (last) u += a.G;
   }
 }
 
@@ -1095,11 +1105,16 @@ bool rows_supported(const skinny_linear& L, int M) {
 // skinny_tiles: fewest K-chunks of a linear whose x window fits the LDS
 // budget (token rows padded by one chunk), or -1 if not even one segment fits.
 constexpr int kTilesMinSegs = 4;          // segments per chunk when splitting for parallelism
-int tiles_lds_chunks(int dtype, int M, int K, int budget = kTilesXBudget) {
+// Most segments an x window of M tokens may span within the budget.
+int tiles_max_spc(int dtype, int M, int budget) {
   const int xc = dtype == SKINNY_BF16 ? 1 : 2;
+  return (budget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
+}
+
+int tiles_lds_chunks(int dtype, int M, int K, int budget = kTilesXBudget) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  const int max_spc = (budget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
+  const int max_spc = tiles_max_spc(dtype, M, budget);
   if (max_spc < 1) return -1;
   return (spt + max_spc - 1) / max_spc;
 }
@@ -1111,6 +1126,27 @@ int tiles_chunks(int dtype, int M, int K, long long par, int budget = kTilesXBud
 }
 
 int tiles_max_chunks(int dtype, int M, int K) { return tiles_chunks(dtype, M, K, 1LL << 40); }
+
+// skinny_tiles split of one linear: K-chunks, each a unit with its own
+// partial slot (enough for the x window to fit the budget, more for a small
+// launch's parallelism) or, with `windows` and when parallelism asks for no
+// split, one chunk whose x windows the unit's workgroup walks in turn with its
+// sums kept in registers: no partial sums and no second pass, but x restaged
+// per unit.  Measured on MI355X: the walk costs 1.8% on the FP8 TP=1 stack at
+// M = 1 (every unit restages where a split workgroup keeps one window per
+// linear), so dense launches split and MoE launches walk.
+void tiles_split(int dtype, int M, int K, long long par, int budget, bool windows, int* chunks,
+                 int* sub) {
+  const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
+  const int c_lds = tiles_lds_chunks(dtype, M, K, budget);
+  *chunks = chunk_count(spt, c_lds, par, kTilesMinSegs);
+  *sub = 1;
+  if (windows && c_lds > 1 && chunk_count(spt, 1, par, kTilesMinSegs) == 1) {
+    *chunks = 1;
+    *sub = c_lds;                          // windows of <= spt / c_lds segments each
+  }
+}
 
 bool tiles_supported(const skinny_linear& L, int M) {
   return tiles_lds_chunks(L.dtype, M, L.K) > 0;
@@ -1303,8 +1339,11 @@ void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
   long long slots = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
-    const int c = tiles ? tiles_chunks(dtype, a.M, d.K, par) : rows_chunks(dtype, a.M, d.K, par);
+    int c, w = 1;
+    if (tiles) tiles_split(dtype, a.M, d.K, par, kTilesXBudget, false, &c, &w);
+    else c = rows_chunks(dtype, a.M, d.K, par);
     d.chunks = c;
+    d.sub = w;
     d.slot_base = slots;
     if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
   }
@@ -1347,6 +1386,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
                     : (d.cpr + kSegChunks - 1) / kSegChunks;
     d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
     d.chunks = 1;
+    d.sub = 1;
     d.act = L.reserved;
   }
   int G = workers;
@@ -1560,6 +1600,13 @@ size_t mlp_workspace(const skinny_mlp& P, int M) {
 // ---------------------------------------------------------------------------
 // Mixture-of-experts launches (skinny_tiles in its MoE form).
 
+// An MoE launch whose unsplit units would keep fewer than 1/kMoeSplitBelow of
+// the workers busy is cut into K-chunks for parallelism; otherwise each unit
+// walks its x windows in turn and no second pass runs.  Measured on MI355X
+// (verify step, 8 experts, top 2): splitting K for parallelism as the dense
+// planner does cost 1-9% at 1, 6 and 16 tokens, the second pass included.
+constexpr int kMoeSplitBelow = 8;
+
 struct MoePlan {
   int cap;               // routes per slice: the token count
   int routes;
@@ -1674,10 +1721,9 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   d.spt = (d.cpr + kSegChunksT - 1) / kSegChunksT;
   d.kblocks = (ex->K + kScaleBlock - 1) / kScaleBlock;
   d.act = flags & SKINNY_MOE_SWIGLU ? kActSwiGLU : kActNone;
-  // K-chunks as for a launch of `active` linears of this shape.
-  const long long want = (long long)kTilesUnitsPerWorker * G;
-  const long long groups = (long long)p.active * p.groups;
-  d.chunks = tiles_chunks(dtype, p.cap, ex->K, (want + groups - 1) / groups, p.x_budget);
+  // K-chunks and x windows, planned for `active` experts' row groups.
+  const long long units = (long long)kMoeSplitBelow * p.active * p.groups;
+  tiles_split(dtype, p.cap, ex->K, (G + units - 1) / units, p.x_budget, true, &d.chunks, &d.sub);
   MoeArgs& mo = a.moe;
   mo.ids = ids;
   mo.table = d.chunks > 1 ? (int*)ws : nullptr;

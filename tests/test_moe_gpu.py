@@ -127,8 +127,8 @@ def test_every_route_without_an_expert_gives_zeros():
 
 @pytest.mark.parametrize("dtype", [sg.BF16, sg.FP8_BS128])
 def test_split_k_second_pass(dtype):
-    """Few row groups and a long K: the planner splits K and the slices go
-    through the MoE second pass."""
+    """Three row groups and a long K: too few units to occupy the workers,
+    so the planner splits K and the slices go through the MoE second pass."""
     E, N, K = 3, 64, 16384
     ids = np.array([[0, 2], [2, 1], [1, 0]], np.int32)
     if dtype == sg.BF16:
@@ -157,7 +157,9 @@ def test_most_routes_many_experts():
 def test_verify_step_experts_full_size(dtype, T):
     """The synthetic verify-step MoE at full size: gate_up then down (the
     down reading gate_up's bf16 outputs through the SwiGLU), every route
-    against the oracle, against the stated bound."""
+    against the oracle, against the stated bound.  At 6 and 16 tokens the
+    gate_up's x window does not fit the LDS budget in one piece, so each unit
+    walks its windows in turn (no K split, no second pass)."""
     (gu_spec, dn_spec) = wl.moe_experts(dtype)
     ids = synth.route_topk(0, synth.stream_id("moe-full", T), T, wl.MOE_EXPERTS, wl.MOE_TOPK)
     E = wl.MOE_EXPERTS
