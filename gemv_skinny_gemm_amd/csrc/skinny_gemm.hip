@@ -226,7 +226,7 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
 // at any moment all workgroups read neighbouring rows - measured on MI355X
 // this compact moving window streams faster than giving each workgroup its
 // own contiguous share.  As in skinny_tiles, units are row-group-major and
-// the chunk count a power of two, so a workgroup keeps one K-chunk per
+// the chunk count divides the grid, so a workgroup keeps one K-chunk per
 // linear.  LDS holds x[M][window] of the current (linear, chunk), restaged
 // between two barriers when it changes, and per wave the FP8 scale row of
 // the current 128-row block, prefetched one unit ahead.  One x read from LDS
@@ -600,8 +600,8 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     S = (long long)slices * mo.units_per_slice;
   }
 
-  // Units are row-group-major: with a power-of-two chunk count dividing the
-  // grid, workgroup b keeps K-chunk (b - base) % chunks all linear long.
+  // Units are row-group-major: with the chunk count dividing the grid,
+  // workgroup b keeps K-chunk (b - base) % chunks all linear long.
   // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks): none is
   // empty (chunks <= spt) and none is longer than the window.
   int ldec = 0;
@@ -1070,12 +1070,14 @@ int rows_lds_chunks(int dtype, int M, int K) {
   return (spt + max_spc - 1) / max_spc;
 }
 
-// Most K-chunks the planner may give a linear (LDS need, or a small launch's
-// parallelism with >= U segments per chunk): bounds the workspace slots.
 // K-chunks of a linear with spt segments: at least c_lds (LDS) and, up to
-// spt / min_segs, par (parallelism of a small launch); rounded up to a power
-// of two, which divides the persistent grid, so every workgroup keeps one
-// K-chunk - one x window - for the whole linear.
+// spt / min_segs, par (parallelism of a small launch), rounded up to a power
+// of two or, when the x window sets the count, to 3 x a power of two if that
+// is closer (fewer partial sums, longer runs per row: +1.3-2.4% on the TP=1
+// stacks at FP8 M = 1 and 6 and bf16 M = 8, measured on MI355X; parallelism
+// splits keep powers of two, which measured better on the TP=8 layer).  The
+// grid is then trimmed to a multiple of every count (grid_for_chunks), so
+// every workgroup keeps one K-chunk - one x window - for the whole linear.
 int chunk_count(int spt, int c_lds, long long par, int min_segs) {
   int c_par = spt / min_segs;
   if (c_par < 1) c_par = 1;
@@ -1083,7 +1085,23 @@ int chunk_count(int spt, int c_lds, long long par, int min_segs) {
   const int need = c_par > c_lds ? c_par : c_lds;
   int c = 1;
   while (c < need) c *= 2;
+  if (c_lds >= c_par && c > 3 && 3 * (c / 4) >= need) c = 3 * (c / 4);
   return c <= spt ? c : need;
+}
+
+int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+
+// The persistent grid trimmed to a multiple of every K-chunk count of the
+// launch (3 x 2^k at most: at most a few percent of the workgroups), so each
+// workgroup keeps one chunk per linear; unchanged if no such multiple fits.
+int grid_for_chunks(int G, const LaunchArgs& a) {
+  int l = 1;
+  for (int i = 0; i < a.nlin; ++i) {
+    const int c = a.lin[i].chunks;
+    l = l / gcd(l, c) * c;
+    if (l > G) return G;
+  }
+  return G / l * l;
 }
 
 int rows_chunks(int dtype, int M, int K, long long par) {
@@ -1397,6 +1415,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
   plan_chunks(a, count, G, dtype, k.tiles);
+  G = grid_for_chunks(G, a);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
@@ -1739,6 +1758,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   mo.table_lds = p.x_budget + kTilesWBytes;
   a.slots = (float*)((char*)ws + p.table_bytes);
   a.S = (long long)p.max_slices * mo.units_per_slice;
+  G = grid_for_chunks(G, a);
   if (G > a.S) G = (int)a.S;
   a.G = G;
   hipStream_t s = (hipStream_t)stream;

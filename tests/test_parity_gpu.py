@@ -190,6 +190,21 @@ def test_bitwise_repeatable_and_splits_agree(M):
             assert_matches_oracle(y, y_ref, a, f"waves={waves}")
 
 
+@pytest.mark.parametrize("K,waves", [(8192, 4), (8192, 12), (29568, 4), (29568, 48)])
+def test_fp8_window_set_chunk_counts(K, waves):
+    """M = 6: the x window sets 3 K-chunks at K = 8192 and 12 at K = 29568 (3 x
+    2^k counts) once a small forced grid asks for little parallelism; grids of
+    1, 3 and 12 workgroups, the first not divisible by the count (its units
+    then change K-chunk, and x window, every time)."""
+    M, N = 6, 200
+    x = synth.tensor_bf16(0, synth.stream_id("w3", K, "x"), M, K, 1.0)
+    w = synth.tensor_bf16(0, synth.stream_id("w3", K, "w"), N, K, 0.02)
+    q, s = synth.quantize_bs128(w)
+    y_ref, a, _ = oracle.linear_fp8_bs128(x, q, s)
+    y = run_fp8(x, q, s, M, N, variant=sg.VARIANT_MFMA, waves=waves)
+    assert_matches_oracle(y, y_ref, a, f"fp8 M={M} K={K} waves={waves}")
+
+
 # --- configurations at their real sizes ----------------------------------------
 
 def test_qkv_tp8_gemv_seed0():
