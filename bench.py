@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--rotate-bytes", type=float, default=2.5e9,
                    help="small workloads cycle weight copies totalling at least this many bytes "
                         "so every step reads HBM, not the 256 MB last-level cache")
+    p.add_argument("--batches", type=int, default=7,
+                   help="event-bracketed batches inside the timed region (median / min / max)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=2048)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -336,18 +338,41 @@ def main():
     def prefill(expected_ms):
         torch.cuda._sleep(int(spin_cycles * (expected_ms + 5.0)))
 
-    # Timed region: K whole steps between two events on the library's stream.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps between two events on the library's stream,
+    # with events between batches of steps (up to 7) for the spread.
+    nb = max(1, min(args.batches, args.steps))
+    bounds = [b * args.steps // nb for b in range(nb + 1)]
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
     prefill(args.steps * 0.05)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
+    bev[0].record(stream)
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            step(args.warmup + i)
+        bev[b + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = bev[0].elapsed_time(bev[nb]) / args.steps
+    batch_us = [bev[b].elapsed_time(bev[b + 1]) / (bounds[b + 1] - bounds[b]) * 1e3
+                for b in range(nb)]
     log(f"{ms_per_step * 1e3:.1f} us/step")
+
+    # Hot-cache figure (labelled, never the value): the same steps on weight
+    # copy 0 only, so a workload smaller than the 256 MB last-level cache can
+    # be served from it.
+    hot_us = None
+    if copies > 1:
+        h0 = torch.cuda.Event(enable_timing=True)
+        h1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            step(0)
+        torch.cuda.synchronize()
+        prefill(args.steps * 0.05)
+        h0.record(stream)
+        for _ in range(args.steps):
+            step(0)
+        h1.record(stream)
+        torch.cuda.synchronize()
+        hot_us = h0.elapsed_time(h1) / args.steps * 1e3
 
     # Dominant kernel: events recorded by the library around every main launch.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launch * args.steps)]
@@ -392,6 +417,9 @@ def main():
             "algorithmic_bytes_per_step": step_bytes,
             "flops_per_step": step_flops,
             "us_per_step": round(ms_per_step * 1e3, 2),
+            "us_per_step_batches": {"batches": nb, "median": round(float(np.median(batch_us)), 2),
+                                    "min": round(min(batch_us), 2), "max": round(max(batch_us), 2)},
+            "hot_cache_us_per_step": None if hot_us is None else round(hot_us, 2),
             "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
             "weight_copies_rotated": copies,
             "variant": {0: "auto", 1: "vector", 2: "mfma"}[variant],
