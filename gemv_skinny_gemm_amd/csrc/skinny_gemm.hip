@@ -446,10 +446,14 @@ constexpr int kLanesPerRowT = kSegChunksT;            // lanes of a load on one 
 constexpr int kRowsPerLoadT = 64 / kLanesPerRowT;
 constexpr int kStepsT = kSegChunksT / 4;              // k-steps per segment
 constexpr int kSegBlocksT = kSegBytesT / kScaleBlock; // FP8 scale blocks per segment
-constexpr int kTilesWavesPerBlock = 4;
-constexpr int kTilesLds = 80 * 1024;                  // two workgroups per 160 KB CU
-constexpr int kTilesWBytes = kTilesWavesPerBlock * kTileRows * kRowStrideT;
-constexpr int kTilesXBudget = kTilesLds - kTilesWBytes;
+// Two workgroup shapes: 4 waves with 80 KB of LDS (two per CU) or 8 waves
+// with all 160 KB (one per CU, twice the x window).
+constexpr int kTilesWavesSmall = 4;
+constexpr int kTilesWavesLarge = 8;
+constexpr int tiles_lds(int wpb) { return wpb == kTilesWavesLarge ? 160 * 1024 : 80 * 1024; }
+constexpr int tiles_w_bytes(int wpb) { return wpb * kTileRows * kRowStrideT; }
+constexpr int tiles_x_budget(int wpb) { return tiles_lds(wpb) - tiles_w_bytes(wpb); }
+constexpr int kTilesXBudget = tiles_x_budget(kTilesWavesSmall);
 
 template <int DT>
 struct TileSeg {
@@ -1171,14 +1175,17 @@ bool tiles_supported(const skinny_linear& L, int M) {
 }
 
 // Workspace slots of one launch group: every linear at the most K-chunks the
-// planner may give it, for the kernel of this variant (rows per row group).
-size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int variant) {
-  const int rows = variant == SKINNY_VARIANT_MFMA ? kTileRows * kTilesWavesPerBlock
+// planner may give it, for the kernel of this variant (rows per row group) and,
+// for the tile kernel, workgroup shape.
+size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int variant,
+                         int wpb = kTilesWavesSmall) {
+  const int rows = variant == SKINNY_VARIANT_MFMA ? kTileRows * wpb
                                                   : kRowsWavesPerBlock * rows_r(M);
   long long slots = 0;
   for (int i = 0; i < count; ++i) {
-    const int c = variant == SKINNY_VARIANT_MFMA ? tiles_max_chunks(lin[i]->dtype, M, lin[i]->K)
-                                                 : rows_max_chunks(lin[i]->dtype, M, lin[i]->K);
+    const int c = variant == SKINNY_VARIANT_MFMA
+                      ? tiles_chunks(lin[i]->dtype, M, lin[i]->K, 1LL << 40, tiles_x_budget(wpb))
+                      : rows_max_chunks(lin[i]->dtype, M, lin[i]->K);
     if (c > 1) slots += (long long)((lin[i]->N + rows - 1) / rows) * c;
   }
   return (size_t)slots * M * rows * sizeof(float);
@@ -1211,9 +1218,8 @@ struct KernelChoice {
   bool tiles = false;          // skinny_tiles (else skinny_rows)
 };
 
-template <int DT>
+template <int DT, int WPB>
 KernelChoice tiles_kernel() {
-  constexpr int WPB = kTilesWavesPerBlock;
   static_assert(kScaleBlock % (kTileRows * WPB) == 0, "a row group must sit in one scale block");
   static_assert((kTileRows * WPB) % kCombineRows == 0, "second-pass quads");
   KernelChoice k;
@@ -1239,7 +1245,7 @@ KernelChoice rows_kernel() {
 
 template <int DT>
 KernelChoice pick_dt(int variant, int M) {
-  if (variant == SKINNY_VARIANT_MFMA) return tiles_kernel<DT>();
+  if (variant == SKINNY_VARIANT_MFMA) return tiles_kernel<DT, kTilesWavesSmall>();
   switch (M) {
     case 1: return rows_kernel<DT, 1>();
     case 2: return rows_kernel<DT, 2>();
@@ -1339,9 +1345,25 @@ skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, 
 // FP8 scale row per wave; the occupancy query uses the full budget so the grid
 // does not depend on the shapes of the launch.
 int kernel_lds(const KernelChoice& k, int dtype) {
-  if (k.tiles) return kTilesLds;
+  if (k.tiles) return tiles_lds(k.wpb);
   return kRowsXBudget +
          (dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
+}
+
+// The 8-wave tile workgroup (one per CU, twice the x window: fewer K-chunks,
+// one x copy per CU) for FP8 launches of M >= 2 tokens with at least 8 of its
+// 128-row groups per CU.  Measured on MI355X against the 4-wave shape: FP8
+// TP=1 stack (8-layer launches) +3 / +2 / +6 / +7 / +7% at M = 2 / 4 / 6 / 8 /
+// 16 but -3% at M = 1; a single FP8 gate_up (462 groups) -11% at M = 6, the
+// fewer, larger units leaving a tail; bf16 stacks within +-3%, the TP=8 layer
+// -4 to -6%.
+constexpr int kTilesLargeGroupsPerCU = 8;
+bool tiles_large(const skinny_linear* const* lin, int count, int M, int cus) {
+  if (lin[0]->dtype != SKINNY_FP8_BS128 || M < 2) return false;
+  long long groups = 0;
+  for (int i = 0; i < count; ++i)
+    groups += (lin[i]->N + kTileRows * kTilesWavesLarge - 1) / (kTileRows * kTilesWavesLarge);
+  return groups >= (long long)kTilesLargeGroupsPerCU * cus;
 }
 
 // K-chunks per linear (either kernel): enough for the x window to fit the LDS
@@ -1358,7 +1380,7 @@ void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
     int c, w = 1;
-    if (tiles) tiles_split(dtype, a.M, d.K, par, kTilesXBudget, false, &c, &w);
+    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, false, &c, &w);
     else c = rows_chunks(dtype, a.M, d.K, par);
     d.chunks = c;
     d.sub = w;
@@ -1375,8 +1397,11 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
                            hipEvent_t ev_before, hipEvent_t ev_after) {
   const int dtype = lin[0]->dtype;
   if (variant == SKINNY_VARIANT_AUTO) variant = auto_variant(lin, count, M);
-  const KernelChoice k = pick(dtype, variant, M);
+  KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
+  if (k.tiles && tiles_large(lin, count, M, dev.cus))
+    k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
+                             : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
   LaunchArgs a;
   memset(&a, 0, sizeof a);
   a.nlin = count;
@@ -1387,7 +1412,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     if (!(k.tiles ? tiles_supported(*lin[i], M) : rows_supported(*lin[i], M)))
       return SKINNY_ERR_UNSUPPORTED;
   const int lds = kernel_lds(k, dtype);
-  a.x_lds_bytes = k.tiles ? kTilesXBudget : kRowsXBudget;
+  a.x_lds_bytes = k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
   skinny_status st = ensure_lds(k.fn, lds);
   if (st != SKINNY_OK) return st;
   for (int i = 0; i < count; ++i) {
@@ -1489,6 +1514,8 @@ size_t required_workspace(const skinny_linear* lin, int count, int M) {
       const size_t b = group_slots_bytes(g, n, M, v);
       if (b > need) need = b;
     }
+    const size_t b = group_slots_bytes(g, n, M, SKINNY_VARIANT_MFMA, kTilesWavesLarge);
+    if (b > need) need = b;
     return SKINNY_OK;
   });
   return need;
@@ -1632,6 +1659,7 @@ struct MoePlan {
   int active;            // experts the routes can reach: min(E, routes)
   int max_slices;
   int groups;            // row groups per expert
+  int wpb;               // tile workgroup shape (waves)
   int table_lds;         // LDS bytes of the slice table
   int x_budget;          // LDS bytes left for x
   size_t table_bytes;    // workspace bytes of the table copy (256-aligned)
@@ -1640,25 +1668,39 @@ struct MoePlan {
 // Slices: an expert with c routes makes ceil(c / cap) of them, so n active
 // experts over `routes` routes make at most n + (routes - n) / cap, which
 // grows with n (<= min(E, routes)).
-MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
+MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb) {
   MoePlan p;
   p.cap = T;
   p.routes = T * topk;
   p.active = ex.E < p.routes ? ex.E : p.routes;
   p.max_slices = p.active + (p.routes - p.active) / p.cap;
-  p.groups = (ex.N + kTileRows * kTilesWavesPerBlock - 1) / (kTileRows * kTilesWavesPerBlock);
+  p.wpb = wpb;
+  p.groups = (ex.N + kTileRows * wpb - 1) / (kTileRows * wpb);
   const int tb = 2 * 4 + p.max_slices * (2 * 4 + 2 * kMoeMaxCap) + p.routes;
   p.table_lds = (tb + 15) / 16 * 16;
-  p.x_budget = kTilesXBudget - p.table_lds;
+  p.x_budget = tiles_x_budget(wpb) - p.table_lds;
   const size_t tg = (size_t)(1 + p.max_slices * (1 + kMoeMaxCap)) * sizeof(int);
   p.table_bytes = (tg + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+  return p;
+}
+
+// The 8-wave workgroup (twice the x window) when the 4-wave one would walk at
+// least kMoeLargeWindows x windows per unit.  Measured on MI355X (verify step,
+// 8 experts, top 2): 16 tokens +13% (FP8) and +4% (bf16); 6 tokens even; one
+// token 27-37% slower (its few units leave most of the half-as-many
+// workgroups idle).
+constexpr int kMoeLargeWindows = 4;
+MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
+  const MoePlan p = moe_plan_for(ex, T, topk, kTilesWavesSmall);
+  if (tiles_lds_chunks(ex.dtype, p.cap, ex.K, p.x_budget) >= kMoeLargeWindows)
+    return moe_plan_for(ex, T, topk, kTilesWavesLarge);
   return p;
 }
 
 size_t moe_workspace(const skinny_experts& ex, const MoePlan& p) {
   const int c = tiles_chunks(ex.dtype, p.cap, ex.K, 1LL << 40, p.x_budget);
   const size_t slots = c > 1 ? (size_t)p.max_slices * p.groups * c * p.cap *
-                                   (kTileRows * kTilesWavesPerBlock) * sizeof(float)
+                                   (kTileRows * p.wpb) * sizeof(float)
                              : 0;
   const size_t b = p.table_bytes + slots;
   return b > SKINNY_MIN_WORKSPACE_BYTES ? b : SKINNY_MIN_WORKSPACE_BYTES;
@@ -1712,15 +1754,20 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   if (!dev.gfx950) return SKINNY_ERR_UNSUPPORTED;
 
   KernelChoice k;
-  k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesPerBlock, true>
-                              : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesPerBlock, true>;
-  k.band_rows = kTileRows * kTilesWavesPerBlock;
-  k.wpb = kTilesWavesPerBlock;
+  if (p.wpb == kTilesWavesLarge)
+    k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesLarge, true>
+                                : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesLarge, true>;
+  else
+    k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesSmall, true>
+                                : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesSmall, true>;
+  k.band_rows = kTileRows * p.wpb;
+  k.wpb = p.wpb;
   k.tiles = true;
-  st = ensure_lds(k.fn, kTilesLds);
+  const int lds = tiles_lds(p.wpb);
+  st = ensure_lds(k.fn, lds);
   if (st != SKINNY_OK) return st;
   int G = 0;
-  st = auto_workers(dev, k, kTilesLds, &G);
+  st = auto_workers(dev, k, lds, &G);
   if (st != SKINNY_OK) return st;
 
   LaunchArgs a;
@@ -1755,7 +1802,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   mo.per_route = flags & SKINNY_MOE_X_PER_ROUTE ? 1 : 0;
   mo.max_slices = p.max_slices;
   mo.units_per_slice = p.groups * d.chunks;
-  mo.table_lds = p.x_budget + kTilesWBytes;
+  mo.table_lds = p.x_budget + tiles_w_bytes(p.wpb);
   a.slots = (float*)((char*)ws + p.table_bytes);
   a.S = (long long)p.max_slices * mo.units_per_slice;
   G = grid_for_chunks(G, a);
@@ -1763,7 +1810,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   a.G = G;
   hipStream_t s = (hipStream_t)stream;
   if (events && hipEventRecord((hipEvent_t)events[0], s) != hipSuccess) return SKINNY_ERR_HIP;
-  hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), kTilesLds, s, a);
+  hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), lds, s, a);
   if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
   if (events && hipEventRecord((hipEvent_t)events[1], s) != hipSuccess) return SKINNY_ERR_HIP;
   if (d.chunks > 1) {

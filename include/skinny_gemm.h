@@ -147,7 +147,9 @@ skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, i
 
 /* Rows of W in one row group of the main kernel of this dtype, variant
  * (VECTOR or MFMA; 0 for AUTO, whose choice depends on the shapes) and M; 0 if
- * invalid.  The split-K workspace holds fp32 partial sums laid out
+ * invalid.  For MFMA this is the 4-wave workgroup's 64; FP8 launches of M >= 2
+ * tokens with at least 8 row groups of 128 rows per compute unit run 8-wave
+ * workgroups with 128-row groups instead.  The split-K workspace holds fp32 partial sums laid out
  * [slot][M][band rows]: one slot per K-chunk of each row group of a linear the
  * launch splits; linears in order, then row groups, then K-chunks in K order. */
 int skinny_band_rows(int dtype, int variant, int M);

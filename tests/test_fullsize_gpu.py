@@ -98,3 +98,28 @@ def test_tp1_stack_fp8_sampled(M):
     assert worst < 0.5
     del tensors
 
+
+
+@pytest.mark.parametrize("M", [2, 16])
+def test_fp8_large_workgroup_sampled(M):
+    """One FP8 linear of 262144 x 8192 (2 GB): enough 128-row groups per CU for
+    the 8-wave tile workgroup, K-chunks from parallelism (M = 2) and from the
+    x window (M = 16, with the second pass); sampled rows as above."""
+    spec = wl.LinearSpec("wide-fp8", 262144, 8192, wl.FP8_BS128,
+                         synth.stream_id("wide-fp8", "w"), synth.stream_id("wide-fp8", M, "x"))
+    tensors = _run_stack([spec], M)
+    x_dev, q_dev, s_dev, y_dev = tensors[0]
+    x = synth.tensor_bf16(0, spec.x_stream, M, spec.K, wl.X_SIGMA)
+    assert np.array_equal(host_codes(x_dev), x)
+    rng = np.random.default_rng(M)
+    worst = 0.0
+    for band in sorted(set([0, 2047] + list(rng.choice(2048, 6, replace=False)))):
+        q, sc, r0 = synth.fp8_weight_bs128(0, spec.w_stream, spec.N, spec.K, wl.W_SIGMA, band, 1)
+        assert np.array_equal(q_dev[r0:r0 + 128].cpu().numpy(), q)
+        assert np.array_equal(s_dev[band:band + 1].cpu().numpy(), sc)
+        y_ref, a, _ = oracle.linear_fp8_bs128(x, q, sc)
+        ok, wr, idx = oracle.check(y_dev[:, r0:r0 + 128].float().cpu().double().numpy(), y_ref, a)
+        assert ok, f"band {band}: worst err/bound {wr:.3g} at {idx}"
+        worst = max(worst, wr)
+    assert worst < 0.5
+    del tensors
