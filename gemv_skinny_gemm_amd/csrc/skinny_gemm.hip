@@ -216,6 +216,21 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
   }
 }
 
+template <int THREADS>
+__device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
+                                               u32x4* dst, int stride) {
+  const int lane = threadIdx.x & 63;
+  const int pieces = (wlen + 63) / 64;
+  for (int p = threadIdx.x >> 6; p < M * pieces; p += THREADS / 64) {
+    const int m = p / pieces;
+    const int c0 = (p - m * pieces) * 64;
+    if (c0 + lane < wlen)
+      __builtin_amdgcn_global_load_lds(
+          L.x + (size_t)m * xcpr + xw0 + c0 + lane,
+          (__attribute__((address_space(3))) void*)(dst + m * stride + c0), 16, 0, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
 // wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
@@ -236,8 +251,12 @@ struct RowBatch {
   u32x4 w[U][R];
 };
 
+// The bf16 M = 1 instance keeps 16 waves per CU (<= 128 VGPRs); the others
+// have the registers they need.
 template <int DT, int MT, int U, int R, int WPB>
-__global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
+__global__ __launch_bounds__(64 * WPB)
+__attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT == 1) ? 4 : 1))) void skinny_rows(
+    const LaunchArgs a) {
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = WPB * R;
   constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
@@ -354,7 +373,13 @@ __global__ __launch_bounds__(64 * WPB) void skinny_rows(const LaunchArgs a) {
     if (nb > 0) load(b0, j0);
     if (l != staged_l || chunk != staged_c) {                    // same for all waves
       __syncthreads();                                           // all done with the old window
-      stage_x<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
+      if (L.act == kActNone) {
+        // Straight into LDS, no registers; the wait also covers the batch.
+        stage_x_direct<kThreads>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win);
+        __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        stage_x<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
+      }
       __syncthreads();
       staged_l = l;
       staged_c = chunk;
