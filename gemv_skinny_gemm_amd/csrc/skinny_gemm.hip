@@ -216,17 +216,18 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
   }
 }
 
-template <int THREADS>
+template <int THREADS, bool GATHER>
 __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
-                                               u32x4* dst, int stride) {
+                                               u32x4* dst, int stride, const unsigned char* rows) {
   const int lane = threadIdx.x & 63;
   const int pieces = (wlen + 63) / 64;
   for (int p = threadIdx.x >> 6; p < M * pieces; p += THREADS / 64) {
     const int m = p / pieces;
     const int c0 = (p - m * pieces) * 64;
+    const int src = GATHER ? rows[m] : m;
     if (c0 + lane < wlen)
       __builtin_amdgcn_global_load_lds(
-          L.x + (size_t)m * xcpr + xw0 + c0 + lane,
+          L.x + (size_t)src * xcpr + xw0 + c0 + lane,
           (__attribute__((address_space(3))) void*)(dst + m * stride + c0), 16, 0, 0);
   }
 }
@@ -375,7 +376,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT == 1) ? 4 : 1))) voi
       __syncthreads();                                           // all done with the old window
       if (L.act == kActNone) {
         // Straight into LDS, no registers; the wait also covers the batch.
-        stage_x_direct<kThreads>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win);
+        stage_x_direct<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
         __builtin_amdgcn_s_waitcnt(0);
       } else {
         stage_x<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
@@ -755,14 +756,18 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     // Token rows 0..M-1, zeros past K, then a zero row that lanes of absent
     // tokens read.
     const int wlen = min(win, xcpr - xw0);
-    stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride,
-                           MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr);
+    const unsigned char* rows = MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr;
+    if (L.act == kActNone)
+      stage_x_direct<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
+    else
+      stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
     const int pad = win - wlen;
     for (int i = threadIdx.x; i < t.m * pad; i += kThreads) {
       const int m = i / pad;
       xs[m * xstride + wlen + (i - m * pad)] = zero4();
     }
     for (int c = threadIdx.x; c < win; c += kThreads) xs[t.m * xstride + c] = zero4();
+    __builtin_amdgcn_s_waitcnt(0);                               // direct loads landed
     __syncthreads();
   };
   auto epilogue = [&](const TileUnit& t) {
