@@ -71,6 +71,10 @@ def parse():
                         "so every step reads HBM, not the 256 MB last-level cache")
     p.add_argument("--batches", type=int, default=7,
                    help="event-bracketed batches inside the timed region (median / min / max)")
+    p.add_argument("--read-reference-gib", type=int, default=8,
+                   help="after timing, time PyTorch's sum over an int64 tensor of this many GiB: "
+                        "a plain streaming read by a library kernel, reported as context "
+                        "(0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=2048)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -442,6 +446,25 @@ def main():
             "main_us_per_step": round(main_total_ms * 1e3, 2),
         },
     }
+
+    if args.read_reference_gib:
+        n = args.read_reference_gib << 30
+        t = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+        for _ in range(3):
+            t.sum()
+        torch.cuda.synchronize()
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(10):
+            t.sum()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        result["config"]["read_reference"] = {
+            "what": "torch.sum over an int64 tensor (PyTorch's reduction kernel: a plain "
+                    "streaming read), context for the HBM ceiling, not this library",
+            "bytes": n, "gbps": round(n / (r0.elapsed_time(r1) / 10 * 1e-3) / 1e9, 1)}
+        del t
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 19                 # bf16 elements
