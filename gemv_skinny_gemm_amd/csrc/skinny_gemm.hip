@@ -30,11 +30,15 @@
 //     through a private LDS tile into the B-operand layout of
 //     v_mfma_f32_16x16x32_bf16, and reads the A operand (x, token = lane % 16)
 //     from LDS.  The matrix cores make the arithmetic per weight independent
-//     of M, which the vector path's is not.
+//     of M, which the vector path's is not.  Workgroups of 4 waves (two per
+//     CU) or, for large FP8 launches, 8 waves with all of the CU's LDS.  Its
+//     MoE form takes the units of each chosen expert's slice of routes.
 //
-//   A linear cut into K-chunks has each unit write fp32 partial sums to its
-//   own workspace slot; skinny_combine adds a row's slots in chunk order.
-//   The second pass is deterministic and uses no atomics.
+//   x windows are copied from global memory straight into LDS (no
+//   registers) while a unit's first weights load.  A linear cut into
+//   K-chunks has each unit write fp32 partial sums to its own workspace
+//   slot; skinny_combine adds a row's slots in chunk order.  The second pass
+//   is deterministic and uses no atomics.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
