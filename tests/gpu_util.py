@@ -5,7 +5,6 @@ import torch
 
 import gemv_skinny_gemm_amd as sg
 import oracle
-from gemv_skinny_gemm_amd import synth
 
 
 def need_gpu():

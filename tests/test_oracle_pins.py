@@ -6,7 +6,6 @@ routine (torch's fp64 matmul and its bf16 / float8_e4m3fn decoders), closed
 forms and special cases (identity, permutation, constants)."""
 import json
 import os
-import random
 from fractions import Fraction
 
 import numpy as np

@@ -11,7 +11,7 @@ import torch
 import gemv_skinny_gemm_amd as sg
 import oracle
 from gemv_skinny_gemm_amd import synth
-from tests.gpu_util import (assert_matches_oracle, dev_bf16, dev_f32, dev_u8, host_codes,
+from tests.gpu_util import (assert_matches_oracle, dev_bf16, host_codes,
                             host_values, need_gpu, out, run_bf16, run_fp8, variants_for,
                             workspace)
 
