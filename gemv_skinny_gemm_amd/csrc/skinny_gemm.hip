@@ -1181,7 +1181,6 @@ int tiles_chunks(int dtype, int M, int K, long long par, int budget = kTilesXBud
   return chunk_count(spt, tiles_lds_chunks(dtype, M, K, budget), par, kTilesMinSegs);
 }
 
-int tiles_max_chunks(int dtype, int M, int K) { return tiles_chunks(dtype, M, K, 1LL << 40); }
 
 // skinny_tiles split of one linear: K-chunks, each a unit with its own
 // partial slot (enough for the x window to fit the budget, more for a small
