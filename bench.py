@@ -306,7 +306,7 @@ def main():
     if moe:
         # The MoE step's dominant kernel is its gate_up launch (two thirds of the bytes).
         timed_bytes = moe_gu_bytes
-        plan = sg.Plan(sg.VARIANT_MFMA, 0)
+        plan = sg.moe_plan_query(moe_ex[0][0], M, wl.MOE_TOPK)
         n_launch = 1
     else:
         plan = sg.plan_query(timed_sets[0], M)

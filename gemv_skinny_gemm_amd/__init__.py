@@ -19,6 +19,7 @@ __all__ = [
     "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
     "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
     "Experts", "make_experts", "moe_workspace_bytes", "moe_linear", "moe_linear_timed",
+    "moe_plan_query",
     "MOE_X_PER_ROUTE", "MOE_SWIGLU", "MAX_TOPK",
 ]
 
@@ -127,6 +128,8 @@ def _bind(path: str):
     L.skinny_moe_linear.argtypes = [ep, vp, vp, i, i, i, vp, vp, sz, vp]
     L.skinny_moe_linear_timed.restype = i
     L.skinny_moe_linear_timed.argtypes = [ep, vp, vp, i, i, i, vp, ctypes.POINTER(vp), vp, sz, vp]
+    L.skinny_moe_plan_query.restype = i
+    L.skinny_moe_plan_query.argtypes = [ep, i, i, i, ctypes.POINTER(Plan)]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_status_string.argtypes = [i]
     L.skinny_abi_version.restype = i
@@ -378,3 +381,14 @@ def moe_linear_timed(experts: Experts, x, ids, y, workspace, events, x_per_route
                                          _moe_flags(x_per_route, swiglu), _ptr(y), ev, wp, wb,
                                          _stream(stream)), "skinny_moe_linear_timed")
     return y
+
+
+def moe_plan_query(experts: Experts, T: int, topk: int, x_per_route: bool = False,
+                   swiglu: bool = False) -> Plan:
+    """The main kernel moe_linear takes for these experts and T x topk routes
+    (variant VARIANT_VECTOR or VARIANT_MFMA)."""
+    plan = Plan()
+    _check(lib().skinny_moe_plan_query(ctypes.byref(experts), T, topk,
+                                       _moe_flags(x_per_route, swiglu), ctypes.byref(plan)),
+           "skinny_moe_plan_query")
+    return plan

@@ -237,274 +237,6 @@ __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr
 }
 
 // ---------------------------------------------------------------------------
-// skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
-// wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
-// along K: lane l reads bytes [16 l, 16 l + 16) of each 1 KB segment of a
-// row, so each wave reads its rows front to back in 1 KB coalesced loads, U
-// segments per batch and two batches in flight.  Work units (row group,
-// K-chunk) are dealt round robin: workgroup b takes units b, b + G, ..., so
-// at any moment all workgroups read neighbouring rows - measured on MI355X
-// this compact moving window streams faster than giving each workgroup its
-// own contiguous share.  As in skinny_tiles, units are row-group-major and
-// the chunk count divides the grid, so a workgroup keeps one K-chunk per
-// linear.  LDS holds x[M][window] of the current (linear, chunk), restaged
-// between two barriers when it changes, and per wave the FP8 scale row of
-// the current 128-row block, prefetched one unit ahead.  One x read from LDS
-// serves the wave's R rows.
-template <int DT, int R, int U>
-struct RowBatch {
-  u32x4 w[U][R];
-};
-
-// The bf16 M = 1 instance keeps 16 waves per CU (<= 128 VGPRs); the others
-// have the registers they need.
-template <int DT, int MT, int U, int R, int WPB>
-__global__ __launch_bounds__(64 * WPB)
-__attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT == 1) ? 4 : 1))) void skinny_rows(
-    const LaunchArgs a) {
-  constexpr int kThreads = 64 * WPB;
-  constexpr int kGroupRows = WPB * R;
-  constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  u32x4* xs = reinterpret_cast<u32x4*>(lds);
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  float* ss = reinterpret_cast<float*>(lds + a.x_lds_bytes) + wv * kRowsMaxKBlocks;
-  float spre[kRowsMaxKBlocks / 64];
-  auto unit_of = [&](long long u, int& l, int& grp, int& chunk) {
-    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
-    const LinDesc& L = a.lin[l];
-    const long long local = u - L.unit_base;
-    grp = (int)(local / L.chunks);
-    chunk = (int)(local - (long long)grp * L.chunks);
-  };
-  auto prefetch_scales = [&](long long u, int l) {
-    if (DT == SKINNY_FP8_BS128 && u < a.S) {
-      int grp, chunk;
-      unit_of(u, l, grp, chunk);
-      const LinDesc& L = a.lin[l];
-      // The row group lies in one 128-row scale block (kGroupRows divides 128).
-      const float* src = L.scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks;
-#pragma unroll
-      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) {
-        const int k = 64 * i + lane;
-        spre[i] = k < L.kblocks ? src[k] : 0.0f;
-      }
-    }
-  };
-  auto store_scales = [&]() {
-    if (DT == SKINNY_FP8_BS128) {
-#pragma unroll
-      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) ss[64 * i + lane] = spre[i];
-    }
-  };
-  int l = 0;
-  int staged_l = -1;
-  int staged_c = -1;
-  long long u = blockIdx.x;
-  prefetch_scales(u, 0);
-  store_scales();
-  for (; u < a.S; u += a.G) {
-    int grp, chunk;
-    unit_of(u, l, grp, chunk);
-    const LinDesc& L = a.lin[l];
-    // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks).
-    const int spc = (L.spt + L.chunks - 1) / L.chunks;          // window, in segments
-    const int j0 = (int)((long long)chunk * L.spt / L.chunks);
-    const int j1 = (int)((long long)(chunk + 1) * L.spt / L.chunks);
-    const int xcpr = L.K >> 3;                                   // x chunks per token row
-    const int win = spc * kSegChunks * XC;                       // x chunks per token in LDS
-    const int xw0 = j0 * kSegChunks * XC;                        // first x chunk of the window
-    const int row0 = grp * kGroupRows + wv * R;
-    // Rows past N read row N - 1 instead; their sums are not written.
-    const u32x4* wrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) wrow[r] = L.w + (size_t)min(row0 + r, L.N - 1) * (size_t)L.cpr;
-    float acc[R][MT];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-    // A batch of U whole segments: plain loads (no selects, so the compiler
-    // keeps them unconditional and the waits exact) ...
-    auto load = [&](RowBatch<DT, R, U>& b, int j) {
-#pragma unroll
-      for (int v = 0; v < U; ++v)
-#pragma unroll
-        for (int r = 0; r < R; ++r) b.w[v][r] = wrow[r][(j + v) * kSegChunks + lane];
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // ... and its products.  OK marks the chunks inside the row (a ragged end).
-    auto consume = [&](const RowBatch<DT, R, U>& b, int j, auto masked) {
-      constexpr bool kMasked = decltype(masked)::value;
-#pragma unroll
-      for (int v = 0; v < U; ++v) {
-        const int cw = (j + v) * kSegChunks + lane;
-        const bool ok = !kMasked || ((j + v < j1) && cw < L.cpr);
-        const int xl = cw * XC - xw0;                            // chunk index in the window
-        if (DT == SKINNY_BF16) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const u32x4 xv = ok ? xs[m * win + xl] : zero4();
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][m] = dot8(xv, b.w[v][r], acc[r][m]);
-          }
-        } else {
-          // W chunk cw holds k in [16 cw, 16 cw + 16): scale block cw / 8.
-          const float sc = ok ? ss[cw >> 3] : 0.0f;
-          u32x4 b0[R], b1[R];
-#pragma unroll
-          for (int r = 0; r < R; ++r) e4m3x16_to_bf16(b.w[v][r], b0[r], b1[r]);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const u32x4 x0 = ok ? xs[m * win + xl] : zero4();
-            const u32x4 x1 = ok ? xs[m * win + xl + 1] : zero4();
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-              acc[r][m] = __builtin_fmaf(sc, dot8(x1, b1[r], dot8(x0, b0[r], 0.0f)), acc[r][m]);
-          }
-        }
-      }
-    };
-    using Plain = std::false_type;
-    using Masked = std::true_type;
-    // Whole batches [j0, jb) run two deep; the rest of the chunk (a short
-    // batch or the row's ragged end) takes the masked path.  The first
-    // batch's loads go out before x is staged, so the two fetches overlap.
-    const int jf = (j1 == L.spt && L.cpr % kSegChunks != 0) ? j1 - 1 : j1;   // whole segments
-    const int nb = (jf - j0) / U;
-    const int jb = j0 + nb * U;
-    RowBatch<DT, R, U> b0, b1;
-    if (nb > 0) load(b0, j0);
-    if (l != staged_l || chunk != staged_c) {                    // same for all waves
-      __syncthreads();                                           // all done with the old window
-      if (L.act == kActNone) {
-        // Straight into LDS, no registers; the wait also covers the batch.
-        stage_x_direct<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
-        __builtin_amdgcn_s_waitcnt(0);
-      } else {
-        stage_x<kThreads, false>(L, MT, xcpr, xw0, min(win, xcpr - xw0), xs, win, nullptr);
-      }
-      __syncthreads();
-      staged_l = l;
-      staged_c = chunk;
-    }
-    prefetch_scales(u + a.G, l);
-    if (nb > 0) {
-      int b = 0;
-      for (; b + 2 < nb; b += 2) {
-        load(b1, j0 + (b + 1) * U);
-        consume(b0, j0 + b * U, Plain{});
-        load(b0, j0 + (b + 2) * U);
-        consume(b1, j0 + (b + 1) * U, Plain{});
-      }
-      if (b + 2 == nb) {
-        load(b1, j0 + (b + 1) * U);
-        consume(b0, j0 + b * U, Plain{});
-        consume(b1, j0 + (b + 1) * U, Plain{});
-      } else {
-        consume(b0, j0 + b * U, Plain{});
-      }
-    }
-    for (int j = jb; j < j1; j += U) {
-#pragma unroll
-      for (int v = 0; v < U; ++v) {
-        const int cw = (j + v) * kSegChunks + lane;
-        const bool ok = (j + v < j1) && cw < L.cpr;
-#pragma unroll
-        for (int r = 0; r < R; ++r) b1.w[v][r] = ok ? wrow[r][ok ? cw : 0] : zero4();
-      }
-      consume(b1, j, Masked{});
-    }
-    // This wave's reads of the current scales are done: install the next unit's.
-    store_scales();
-    // 64-lane butterflies; lane 0's sums have a fixed order.
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc[r][m] += __shfl_xor(acc[r][m], off);
-    if (lane == 0) {
-      const long long slot = L.slot_base + (long long)grp * L.chunks + chunk;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (L.chunks == 1) {
-            if (row0 + r < L.N) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
-          } else {
-            a.slots[((size_t)slot * MT + m) * kGroupRows + wv * R + r] = acc[r][m];
-          }
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// skinny_tiles: matrix cores fed by rows streamed front to back.
-//
-// The MFMA B operand wants lane l to hold 16 bytes of W row (l % 16), so
-// loading it straight from HBM gives 64-byte pieces of 16 rows per wave
-// instruction: half cache lines, measured on MI355X to stream at most
-// ~5.8 TB/s.  Here every global load covers whole lines of two rows (lanes
-// 0-31 one row, 32-63 the next, 512 contiguous bytes each) and each wave
-// turns its 16 rows around through a private LDS tile, skewed by 16 bytes
-// per row so the operand reads hit 16 different bank groups.
-//
-// A workgroup of WPB waves handles a row group of 16 WPB rows (inside one
-// 128-row FP8 scale block); wave i owns the 16 rows from 16 i.  Work units
-// (row group, K-chunk) are dealt round robin over the workgroups as in
-// skinny_rows, with x[M][window] of the current (linear, K-chunk) in LDS
-// (token rows padded by one chunk, then a zero row for absent tokens).  A
-// segment is 512 bytes of each of the wave's rows: 8 loads, 8 LDS writes,
-// then 8 k-steps of one operand read each; bf16 needs one MFMA per k-step,
-// FP8 two (its 16-byte chunk holds 16 k) and the block scale is applied in
-// fp32 to each 128-k partial sum.  Loads run one segment ahead of the
-// products, across unit boundaries too: the last segment of a unit is
-// consumed after the next unit's first loads are out, so the stream never
-// drains between units and the x staging hides under those loads.
-//
-// Shape measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers and the
-// TP=8 layer, M = 1..16): 512-byte segments, 4 waves per workgroup and two
-// workgroups per CU beat 256- or 1024-byte segments and 8-wave workgroups.
-constexpr int kSegBytesT = 512;                       // bytes of one row per segment
-constexpr int kSegChunksT = kSegBytesT / 16;          // chunks
-constexpr int kRowStrideT = kSegBytesT + 16;          // LDS bytes per staged row
-constexpr int kLoadsT = kTileRows * kSegChunksT / 64; // wave loads per segment
-constexpr int kLanesPerRowT = kSegChunksT;            // lanes of a load on one row
-constexpr int kRowsPerLoadT = 64 / kLanesPerRowT;
-constexpr int kStepsT = kSegChunksT / 4;              // k-steps per segment
-constexpr int kSegBlocksT = kSegBytesT / kScaleBlock; // FP8 scale blocks per segment
-// Two workgroup shapes: 4 waves with 80 KB of LDS (two per CU) or 8 waves
-// with all 160 KB (one per CU, twice the x window).
-constexpr int kTilesWavesSmall = 4;
-constexpr int kTilesWavesLarge = 8;
-constexpr int tiles_lds(int wpb) { return wpb == kTilesWavesLarge ? 160 * 1024 : 80 * 1024; }
-constexpr int tiles_w_bytes(int wpb) { return wpb * kTileRows * kRowStrideT; }
-constexpr int tiles_x_budget(int wpb) { return tiles_lds(wpb) - tiles_w_bytes(wpb); }
-constexpr int kTilesXBudget = tiles_x_budget(kTilesWavesSmall);
-
-template <int DT>
-struct TileSeg {
-  u32x4 w[kLoadsT];
-  float sc;              // FP8: lane i holds the scale of the segment's block i % kSegBlocksT
-};
-
-// One work unit as every wave of the workgroup sees it (uniform values).
-struct TileUnit {
-  int l;                 // linear
-  int grp;               // row group
-  int chunk;             // K-chunk
-  int sub;               // x window of the chunk
-  int j0, j1;            // segments [j0, j1) of each row
-  int spc;               // x window, in segments
-  int slice;             // MoE: slice (else the linear)
-  int e;                 // MoE: expert
-  int m;                 // tokens (MoE: routes of the slice)
-};
-
-// ---------------------------------------------------------------------------
 // Mixture-of-experts slices.  A router sends token t to topk experts; route r
 // = t * topk + j goes to expert ids[r] ("Multi-GPU Inference and Serving at
 // Scale", Example 8).  The routes of one expert share its weights, so the
@@ -593,6 +325,314 @@ __device__ void moe_setup(const MoeArgs& mo, const MoeTable& tb, int* scratch) {
   }
   __syncthreads();
 }
+
+// ---------------------------------------------------------------------------
+// skinny_rows: a workgroup of WPB waves streams row groups of WPB x R rows;
+// wave i takes the R adjacent rows starting at row (WPB g + i) R.  Lanes run
+// along K: lane l reads bytes [16 l, 16 l + 16) of each 1 KB segment of a
+// row, so each wave reads its rows front to back in 1 KB coalesced loads, U
+// segments per batch and two batches in flight.  Work units (row group,
+// K-chunk) are dealt round robin: workgroup b takes units b, b + G, ..., so
+// at any moment all workgroups read neighbouring rows - measured on MI355X
+// this compact moving window streams faster than giving each workgroup its
+// own contiguous share.  As in skinny_tiles, units are row-group-major and
+// the chunk count divides the grid, so a workgroup keeps one K-chunk per
+// linear.  LDS holds x[M][window] of the current (linear, chunk), restaged
+// between two barriers when it changes, and per wave the FP8 scale row of
+// the current 128-row block, prefetched one unit ahead.  One x read from LDS
+// serves the wave's R rows.
+template <int DT, int R, int U>
+struct RowBatch {
+  u32x4 w[U][R];
+};
+
+// The bf16 M = 1 instances keep 16 waves per CU (<= 128 VGPRs); the others
+// have the registers they need.
+//
+// MoE form (MOE): lin[0] describes one expert as in skinny_tiles; units are
+// (slice, row group) with the K dimension unsplit, and a slice's x rows are
+// gathered into LDS by the slice table, which sits at a.moe.table_lds inside
+// the x budget.
+template <int DT, int MT, int U, int R, int WPB, bool MOE = false>
+__global__ __launch_bounds__(64 * WPB)
+__attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT == 1) ? 4 : 1))) void skinny_rows(
+    const LaunchArgs a) {
+  constexpr int kThreads = 64 * WPB;
+  constexpr int kGroupRows = WPB * R;
+  constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  float* ss = reinterpret_cast<float*>(lds + a.x_lds_bytes) + wv * kRowsMaxKBlocks;
+  float spre[kRowsMaxKBlocks / 64];
+  long long S = a.S;
+  MoeTable tb{};
+  if constexpr (MOE) {
+    // The slice table (built in the x region, free until the first staging),
+    // then this workgroup's share of the zero rows.
+    const MoeArgs& mo = a.moe;
+    const LinDesc& L = a.lin[0];
+    tb = moe_table(lds + mo.table_lds, mo.max_slices);
+    moe_setup<kThreads>(mo, tb, reinterpret_cast<int*>(lds));
+    const long long zeros = (long long)tb.head[1] * L.N;
+    for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < zeros;
+         i += (long long)a.G * kThreads) {
+      const int q = (int)(i / L.N);
+      L.y[(size_t)tb.inv[q] * L.N + (i - (long long)q * L.N)] = (__bf16)0.0f;
+    }
+    S = (long long)tb.head[0] * mo.units_per_slice;
+  }
+  // MoE: l is the unit's slice and e its expert; the linear is lin[0].
+  auto unit_of = [&](long long u, int& l, int& grp, int& chunk, int& e) {
+    long long local;
+    if constexpr (MOE) {
+      l = (int)(u / a.moe.units_per_slice);
+      local = u - (long long)l * a.moe.units_per_slice;
+      e = __builtin_amdgcn_readfirstlane(tb.expert[l]);
+    } else {
+      while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
+      local = u - a.lin[l].unit_base;
+      e = 0;
+    }
+    const LinDesc& L = a.lin[MOE ? 0 : l];
+    grp = (int)(local / L.chunks);
+    chunk = (int)(local - (long long)grp * L.chunks);
+  };
+  auto prefetch_scales = [&](long long u, int l) {
+    if (DT == SKINNY_FP8_BS128 && u < S) {
+      int grp, chunk, e;
+      unit_of(u, l, grp, chunk, e);
+      const LinDesc& L = a.lin[MOE ? 0 : l];
+      // The row group lies in one 128-row scale block (kGroupRows divides 128).
+      const float* scale = MOE ? L.scale + (size_t)e * a.moe.s_stride : L.scale;
+      const float* src = scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks;
+#pragma unroll
+      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) {
+        const int k = 64 * i + lane;
+        spre[i] = k < L.kblocks ? src[k] : 0.0f;
+      }
+    }
+  };
+  auto store_scales = [&]() {
+    if (DT == SKINNY_FP8_BS128) {
+#pragma unroll
+      for (int i = 0; i < kRowsMaxKBlocks / 64; ++i) ss[64 * i + lane] = spre[i];
+    }
+  };
+  int l = 0;
+  int staged_l = -1;
+  int staged_c = -1;
+  long long u = blockIdx.x;
+  prefetch_scales(u, 0);
+  store_scales();
+  for (; u < S; u += a.G) {
+    int grp, chunk, e;
+    unit_of(u, l, grp, chunk, e);
+    const LinDesc& L = a.lin[MOE ? 0 : l];
+    const int mt = MOE ? __builtin_amdgcn_readfirstlane(tb.rows[l]) : MT;   // tokens of the unit
+    // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks).
+    const int spc = (L.spt + L.chunks - 1) / L.chunks;          // window, in segments
+    const int j0 = (int)((long long)chunk * L.spt / L.chunks);
+    const int j1 = (int)((long long)(chunk + 1) * L.spt / L.chunks);
+    const int xcpr = L.K >> 3;                                   // x chunks per token row
+    const int win = spc * kSegChunks * XC;                       // x chunks per token in LDS
+    const int xw0 = j0 * kSegChunks * XC;                        // first x chunk of the window
+    const int row0 = grp * kGroupRows + wv * R;
+    // Rows past N read row N - 1 instead; their sums are not written.
+    const u32x4* w = MOE ? L.w + (size_t)e * a.moe.w_stride : L.w;
+    const u32x4* wrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wrow[r] = w + (size_t)min(row0 + r, L.N - 1) * (size_t)L.cpr;
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+    // A batch of U whole segments: plain loads (no selects, so the compiler
+    // keeps them unconditional and the waits exact) ...
+    auto load = [&](RowBatch<DT, R, U>& b, int j) {
+#pragma unroll
+      for (int v = 0; v < U; ++v)
+#pragma unroll
+        for (int r = 0; r < R; ++r) b.w[v][r] = wrow[r][(j + v) * kSegChunks + lane];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // ... and its products.  OK marks the chunks inside the row (a ragged end).
+    auto consume = [&](const RowBatch<DT, R, U>& b, int j, auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int cw = (j + v) * kSegChunks + lane;
+        const bool ok = !kMasked || ((j + v < j1) && cw < L.cpr);
+        const int xl = cw * XC - xw0;                            // chunk index in the window
+        if (DT == SKINNY_BF16) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 xv = ok ? xs[m * win + xl] : zero4();
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r][m] = dot8(xv, b.w[v][r], acc[r][m]);
+          }
+        } else {
+          // W chunk cw holds k in [16 cw, 16 cw + 16): scale block cw / 8.
+          const float sc = ok ? ss[cw >> 3] : 0.0f;
+          u32x4 b0[R], b1[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) e4m3x16_to_bf16(b.w[v][r], b0[r], b1[r]);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4 x0 = ok ? xs[m * win + xl] : zero4();
+            const u32x4 x1 = ok ? xs[m * win + xl + 1] : zero4();
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              acc[r][m] = __builtin_fmaf(sc, dot8(x1, b1[r], dot8(x0, b0[r], 0.0f)), acc[r][m]);
+          }
+        }
+      }
+    };
+    using Plain = std::false_type;
+    using Masked = std::true_type;
+    // Whole batches [j0, jb) run two deep; the rest of the chunk (a short
+    // batch or the row's ragged end) takes the masked path.  The first
+    // batch's loads go out before x is staged, so the two fetches overlap.
+    const int jf = (j1 == L.spt && L.cpr % kSegChunks != 0) ? j1 - 1 : j1;   // whole segments
+    const int nb = (jf - j0) / U;
+    const int jb = j0 + nb * U;
+    RowBatch<DT, R, U> b0, b1;
+    if (nb > 0) load(b0, j0);
+    if (l != staged_l || chunk != staged_c) {                    // same for all waves
+      __syncthreads();                                           // all done with the old window
+      // MoE: the slice's rows of x (rows past mt keep stale values; their
+      // sums are not written).
+      const unsigned char* rows = MOE ? tb.xrow + l * kMoeMaxCap : nullptr;
+      if (L.act == kActNone) {
+        // Straight into LDS, no registers; the wait also covers the batch.
+        stage_x_direct<kThreads, MOE>(L, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
+        __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        stage_x<kThreads, MOE>(L, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
+      }
+      __syncthreads();
+      staged_l = l;
+      staged_c = chunk;
+    }
+    prefetch_scales(u + a.G, l);
+    if (nb > 0) {
+      int b = 0;
+      for (; b + 2 < nb; b += 2) {
+        load(b1, j0 + (b + 1) * U);
+        consume(b0, j0 + b * U, Plain{});
+        load(b0, j0 + (b + 2) * U);
+        consume(b1, j0 + (b + 1) * U, Plain{});
+      }
+      if (b + 2 == nb) {
+        load(b1, j0 + (b + 1) * U);
+        consume(b0, j0 + b * U, Plain{});
+        consume(b1, j0 + (b + 1) * U, Plain{});
+      } else {
+        consume(b0, j0 + b * U, Plain{});
+      }
+    }
+    for (int j = jb; j < j1; j += U) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int cw = (j + v) * kSegChunks + lane;
+        const bool ok = (j + v < j1) && cw < L.cpr;
+#pragma unroll
+        for (int r = 0; r < R; ++r) b1.w[v][r] = ok ? wrow[r][ok ? cw : 0] : zero4();
+      }
+      consume(b1, j, Masked{});
+    }
+    // This wave's reads of the current scales are done: install the next unit's.
+    store_scales();
+    // 64-lane butterflies; lane 0's sums have a fixed order.
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc[r][m] += __shfl_xor(acc[r][m], off);
+    if (lane == 0) {
+      const long long slot = L.slot_base + (long long)grp * L.chunks + chunk;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if constexpr (MOE) {                                   // unsplit: chunks == 1
+            if (m < mt && row0 + r < L.N)
+              L.y[(size_t)tb.yrow[l * kMoeMaxCap + m] * L.N + row0 + r] = (__bf16)acc[r][m];
+          } else if (L.chunks == 1) {
+            if (row0 + r < L.N) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
+          } else {
+            a.slots[((size_t)slot * MT + m) * kGroupRows + wv * R + r] = acc[r][m];
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// skinny_tiles: matrix cores fed by rows streamed front to back.
+//
+// The MFMA B operand wants lane l to hold 16 bytes of W row (l % 16), so
+// loading it straight from HBM gives 64-byte pieces of 16 rows per wave
+// instruction: half cache lines, measured on MI355X to stream at most
+// ~5.8 TB/s.  Here every global load covers whole lines of two rows (lanes
+// 0-31 one row, 32-63 the next, 512 contiguous bytes each) and each wave
+// turns its 16 rows around through a private LDS tile, skewed by 16 bytes
+// per row so the operand reads hit 16 different bank groups.
+//
+// A workgroup of WPB waves handles a row group of 16 WPB rows (inside one
+// 128-row FP8 scale block); wave i owns the 16 rows from 16 i.  Work units
+// (row group, K-chunk) are dealt round robin over the workgroups as in
+// skinny_rows, with x[M][window] of the current (linear, K-chunk) in LDS
+// (token rows padded by one chunk, then a zero row for absent tokens).  A
+// segment is 512 bytes of each of the wave's rows: 8 loads, 8 LDS writes,
+// then 8 k-steps of one operand read each; bf16 needs one MFMA per k-step,
+// FP8 two (its 16-byte chunk holds 16 k) and the block scale is applied in
+// fp32 to each 128-k partial sum.  Loads run one segment ahead of the
+// products, across unit boundaries too: the last segment of a unit is
+// consumed after the next unit's first loads are out, so the stream never
+// drains between units and the x staging hides under those loads.
+//
+// Shape measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers and the
+// TP=8 layer, M = 1..16): 512-byte segments, 4 waves per workgroup and two
+// workgroups per CU beat 256- or 1024-byte segments and 8-wave workgroups.
+constexpr int kSegBytesT = 512;                       // bytes of one row per segment
+constexpr int kSegChunksT = kSegBytesT / 16;          // chunks
+constexpr int kRowStrideT = kSegBytesT + 16;          // LDS bytes per staged row
+constexpr int kLoadsT = kTileRows * kSegChunksT / 64; // wave loads per segment
+constexpr int kLanesPerRowT = kSegChunksT;            // lanes of a load on one row
+constexpr int kRowsPerLoadT = 64 / kLanesPerRowT;
+constexpr int kStepsT = kSegChunksT / 4;              // k-steps per segment
+constexpr int kSegBlocksT = kSegBytesT / kScaleBlock; // FP8 scale blocks per segment
+// Two workgroup shapes: 4 waves with 80 KB of LDS (two per CU) or 8 waves
+// with all 160 KB (one per CU, twice the x window).
+constexpr int kTilesWavesSmall = 4;
+constexpr int kTilesWavesLarge = 8;
+constexpr int tiles_lds(int wpb) { return wpb == kTilesWavesLarge ? 160 * 1024 : 80 * 1024; }
+constexpr int tiles_w_bytes(int wpb) { return wpb * kTileRows * kRowStrideT; }
+constexpr int tiles_x_budget(int wpb) { return tiles_lds(wpb) - tiles_w_bytes(wpb); }
+constexpr int kTilesXBudget = tiles_x_budget(kTilesWavesSmall);
+
+template <int DT>
+struct TileSeg {
+  u32x4 w[kLoadsT];
+  float sc;              // FP8: lane i holds the scale of the segment's block i % kSegBlocksT
+};
+
+// One work unit as every wave of the workgroup sees it (uniform values).
+struct TileUnit {
+  int l;                 // linear
+  int grp;               // row group
+  int chunk;             // K-chunk
+  int sub;               // x window of the chunk
+  int j0, j1;            // segments [j0, j1) of each row
+  int spc;               // x window, in segments
+  int slice;             // MoE: slice (else the linear)
+  int e;                 // MoE: expert
+  int m;                 // tokens (MoE: routes of the slice)
+};
 
 template <int DT, int WPB, bool MOE>
 __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
@@ -1098,12 +1138,12 @@ constexpr int kRowsUnitsPerWorker = 0;
 constexpr int kTilesUnitsPerWorker = 16;
 
 // Fewest K-chunks of a linear whose x window (M tokens x chunk) fits the budget.
-int rows_lds_chunks(int dtype, int M, int K) {
+int rows_lds_chunks(int dtype, int M, int K, int budget = kRowsXBudget) {
   const int xc = dtype == SKINNY_BF16 ? 1 : 2;
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunks - 1) / kSegChunks;
   const long long seg_bytes = (long long)M * kSegChunks * xc * 16;   // x bytes per segment
-  const int max_spc = (int)(kRowsXBudget / seg_bytes);
+  const int max_spc = (int)(budget / seg_bytes);
   if (max_spc < 1) return -1;
   return (spt + max_spc - 1) / max_spc;
 }
@@ -1273,6 +1313,13 @@ KernelChoice rows_kernel() {
   k.fn = skinny_rows<DT, MT, rows_u(MT, DT), R, WPB>;
   k.band_rows = WPB * R;
   k.wpb = WPB;
+  return k;
+}
+
+template <int DT, int MT>
+KernelChoice moe_rows_kernel() {
+  KernelChoice k = rows_kernel<DT, MT>();
+  k.fn = skinny_rows<DT, MT, rows_u(MT, DT), rows_r(MT), kRowsWavesPerBlock, true>;
   return k;
 }
 
@@ -1677,7 +1724,7 @@ size_t mlp_workspace(const skinny_mlp& P, int M) {
 }
 
 // ---------------------------------------------------------------------------
-// Mixture-of-experts launches (skinny_tiles in its MoE form).
+// Mixture-of-experts launches (skinny_tiles or skinny_rows in its MoE form).
 
 // An MoE launch whose unsplit units would keep fewer than 1/kMoeSplitBelow of
 // the workers busy is cut into K-chunks for parallelism; otherwise each unit
@@ -1692,28 +1739,54 @@ struct MoePlan {
   int active;            // experts the routes can reach: min(E, routes)
   int max_slices;
   int groups;            // row groups per expert
-  int wpb;               // tile workgroup shape (waves)
+  bool rows;             // skinny_rows (unsplit K), else skinny_tiles
+  int wpb;               // workgroup shape (waves)
   int table_lds;         // LDS bytes of the slice table
-  int x_budget;          // LDS bytes left for x
+  int x_budget;          // LDS bytes left for x; the table follows them
   size_t table_bytes;    // workspace bytes of the table copy (256-aligned)
 };
 
 // Slices: an expert with c routes makes ceil(c / cap) of them, so n active
 // experts over `routes` routes make at most n + (routes - n) / cap, which
 // grows with n (<= min(E, routes)).
-MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb) {
+MoePlan moe_plan_base(const skinny_experts& ex, int T, int topk) {
   MoePlan p;
   p.cap = T;
   p.routes = T * topk;
   p.active = ex.E < p.routes ? ex.E : p.routes;
   p.max_slices = p.active + (p.routes - p.active) / p.cap;
-  p.wpb = wpb;
-  p.groups = (ex.N + kTileRows * wpb - 1) / (kTileRows * wpb);
   const int tb = 2 * 4 + p.max_slices * (2 * 4 + 2 * kMoeMaxCap) + p.routes;
   p.table_lds = (tb + 15) / 16 * 16;
-  p.x_budget = tiles_x_budget(wpb) - p.table_lds;
   const size_t tg = (size_t)(1 + p.max_slices * (1 + kMoeMaxCap)) * sizeof(int);
   p.table_bytes = (tg + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+  return p;
+}
+
+MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb) {
+  MoePlan p = moe_plan_base(ex, T, topk);
+  p.rows = false;
+  p.wpb = wpb;
+  p.groups = (ex.N + kTileRows * wpb - 1) / (kTileRows * wpb);
+  p.x_budget = tiles_x_budget(wpb) - p.table_lds;
+  return p;
+}
+
+// The row kernel's plan: the table takes the top of its x region (the slice
+// setup's 2 KB of scratch at the bottom stays clear of it); usable only if the
+// whole of K fits the rest and a row spans at least kMoeRowsMinSegs 1 KB
+// segments (a wave's whole unit is one row: shorter rows leave too few loads
+// in flight per unit).
+constexpr int kMoeRowsMinSegs = 4;
+MoePlan moe_plan_rows(const skinny_experts& ex, int T, int topk) {
+  MoePlan p = moe_plan_base(ex, T, topk);
+  p.wpb = kRowsWavesPerBlock;
+  p.groups = (ex.N + kRowsWavesPerBlock * rows_r(T) - 1) / (kRowsWavesPerBlock * rows_r(T));
+  p.x_budget = kRowsXBudget - p.table_lds;
+  const int cpr = ex.K / (ex.dtype == SKINNY_BF16 ? 8 : 16);
+  p.rows = T <= kRowsMaxM && p.x_budget >= 2 * kMoeMaxRoutes * (int)sizeof(int) &&
+           (cpr + kSegChunks - 1) / kSegChunks >= kMoeRowsMinSegs &&
+           (ex.dtype == SKINNY_BF16 || (ex.K + kScaleBlock - 1) / kScaleBlock <= kRowsMaxKBlocks) &&
+           rows_lds_chunks(ex.dtype, T, ex.K, p.x_budget) == 1;
   return p;
 }
 
@@ -1723,7 +1796,19 @@ MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb) {
 // token 27-37% slower (its few units leave most of the half-as-many
 // workgroups idle).
 constexpr int kMoeLargeWindows = 4;
+// The row kernel for one-token slices: its 8-row units give the few chosen
+// experts' rows to many more workgroups than the tile kernel's 64-row units.
+// Measured on MI355X (verify step, 8 experts, top 2, one token): gate_up
+// (K = 4096) 11.8 -> 11.0 us FP8 and 15.9 -> 13.3 us bf16; the down linear
+// (K = 1536: 1.5 or 3 KB rows) 8.7 -> 13.3 and 10.1 -> 12.0 us, hence the
+// minimum row length; two-token slices 15.2 -> 23.0 and 23.2 -> 24.6 us on
+// gate_up (the two-token row instance's registers leave one workgroup per CU).
+constexpr int kMoeRowsMaxCap = 1;
 MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
+  if (T <= kMoeRowsMaxCap) {
+    const MoePlan r = moe_plan_rows(ex, T, topk);
+    if (r.rows) return r;
+  }
   const MoePlan p = moe_plan_for(ex, T, topk, kTilesWavesSmall);
   if (tiles_lds_chunks(ex.dtype, p.cap, ex.K, p.x_budget) >= kMoeLargeWindows)
     return moe_plan_for(ex, T, topk, kTilesWavesLarge);
@@ -1731,7 +1816,7 @@ MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
 }
 
 size_t moe_workspace(const skinny_experts& ex, const MoePlan& p) {
-  const int c = tiles_chunks(ex.dtype, p.cap, ex.K, 1LL << 40, p.x_budget);
+  const int c = p.rows ? 1 : tiles_chunks(ex.dtype, p.cap, ex.K, 1LL << 40, p.x_budget);
   const size_t slots = c > 1 ? (size_t)p.max_slices * p.groups * c * p.cap *
                                    (kTileRows * p.wpb) * sizeof(float)
                              : 0;
@@ -1751,7 +1836,8 @@ skinny_status check_experts(const skinny_experts* ex, int T, int topk, int flags
   if (!aligned(ex->w, 16) || (ex->w_scale && !aligned(ex->w_scale, 4))) return SKINNY_ERR_UNSUPPORTED;
   const MoePlan p = moe_plan(*ex, T, topk);
   if (p.routes > kMoeMaxRoutes || p.cap > kMoeMaxCap) return SKINNY_ERR_UNSUPPORTED;
-  if (tiles_lds_chunks(ex->dtype, p.cap, ex->K, p.x_budget) < 1) return SKINNY_ERR_UNSUPPORTED;
+  if (!p.rows && tiles_lds_chunks(ex->dtype, p.cap, ex->K, p.x_budget) < 1)
+    return SKINNY_ERR_UNSUPPORTED;
   return SKINNY_OK;
 }
 
@@ -1787,16 +1873,22 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   if (!dev.gfx950) return SKINNY_ERR_UNSUPPORTED;
 
   KernelChoice k;
-  if (p.wpb == kTilesWavesLarge)
-    k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesLarge, true>
-                                : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesLarge, true>;
-  else
-    k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesSmall, true>
-                                : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesSmall, true>;
-  k.band_rows = kTileRows * p.wpb;
-  k.wpb = p.wpb;
-  k.tiles = true;
-  const int lds = tiles_lds(p.wpb);
+  if (p.rows) {
+    static_assert(kMoeRowsMaxCap == 1, "row-kernel MoE instances");
+    k = dtype == SKINNY_BF16 ? moe_rows_kernel<SKINNY_BF16, 1>()
+                             : moe_rows_kernel<SKINNY_FP8_BS128, 1>();
+  } else {
+    if (p.wpb == kTilesWavesLarge)
+      k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesLarge, true>
+                                  : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesLarge, true>;
+    else
+      k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesSmall, true>
+                                  : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesSmall, true>;
+    k.band_rows = kTileRows * p.wpb;
+    k.wpb = p.wpb;
+    k.tiles = true;
+  }
+  const int lds = kernel_lds(k, dtype);
   st = ensure_lds(k.fn, lds);
   if (st != SKINNY_OK) return st;
   int G = 0;
@@ -1808,7 +1900,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   a.nlin = 1;
   a.M = p.cap;
   a.band_rows = k.band_rows;
-  a.x_lds_bytes = p.x_budget;
+  a.x_lds_bytes = p.rows ? kRowsXBudget : p.x_budget;
   LinDesc& d = a.lin[0];
   d.w = (const u32x4*)ex->w;
   d.scale = ex->w_scale;
@@ -1817,12 +1909,15 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   d.N = ex->N;
   d.K = ex->K;
   d.cpr = ex->K / (dtype == SKINNY_BF16 ? 8 : 16);
-  d.spt = (d.cpr + kSegChunksT - 1) / kSegChunksT;
+  d.spt = p.rows ? (d.cpr + kSegChunks - 1) / kSegChunks : (d.cpr + kSegChunksT - 1) / kSegChunksT;
   d.kblocks = (ex->K + kScaleBlock - 1) / kScaleBlock;
   d.act = flags & SKINNY_MOE_SWIGLU ? kActSwiGLU : kActNone;
   // K-chunks and x windows, planned for `active` experts' row groups.
   const long long units = (long long)kMoeSplitBelow * p.active * p.groups;
-  tiles_split(dtype, p.cap, ex->K, (G + units - 1) / units, p.x_budget, true, &d.chunks, &d.sub);
+  d.chunks = 1;
+  d.sub = 1;
+  if (!p.rows)
+    tiles_split(dtype, p.cap, ex->K, (G + units - 1) / units, p.x_budget, true, &d.chunks, &d.sub);
   MoeArgs& mo = a.moe;
   mo.ids = ids;
   mo.table = d.chunks > 1 ? (int*)ws : nullptr;
@@ -1835,7 +1930,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   mo.per_route = flags & SKINNY_MOE_X_PER_ROUTE ? 1 : 0;
   mo.max_slices = p.max_slices;
   mo.units_per_slice = p.groups * d.chunks;
-  mo.table_lds = p.x_budget + tiles_w_bytes(p.wpb);
+  mo.table_lds = p.rows ? p.x_budget : p.x_budget + tiles_w_bytes(p.wpb);
   a.slots = (float*)((char*)ws + p.table_bytes);
   a.S = (long long)p.max_slices * mo.units_per_slice;
   G = grid_for_chunks(G, a);
@@ -2090,6 +2185,16 @@ skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void*
                                       size_t workspace_bytes, void* stream) {
   if (!events) return SKINNY_ERR_INVALID_ARG;
   return moe_run(experts, x, ids, T, topk, flags, y, workspace, workspace_bytes, stream, events);
+}
+
+skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int topk, int flags,
+                                    skinny_plan* out) {
+  if (!out) return SKINNY_ERR_INVALID_ARG;
+  const skinny_status st = check_experts(experts, T, topk, flags);
+  if (st != SKINNY_OK) return st;
+  memset(out, 0, sizeof *out);
+  out->variant = moe_plan(*experts, T, topk).rows ? SKINNY_VARIANT_VECTOR : SKINNY_VARIANT_MFMA;
+  return SKINNY_OK;
 }
 
 const char* skinny_status_string(int status) {

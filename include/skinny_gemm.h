@@ -270,6 +270,15 @@ skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void*
                                       const int* ids, int T, int topk, int flags, void* y,
                                       void* const* events, void* workspace,
                                       size_t workspace_bytes, void* stream);
+/* The main kernel skinny_moe_linear takes for these experts and routes, for
+ * tests and benchmarks: out->variant is SKINNY_VARIANT_VECTOR (the row
+ * kernel, for one-token slices of rows long enough to keep its loads in
+ * flight) or SKINNY_VARIANT_MFMA (the tile kernel); out->waves and
+ * out->reserved are 0.  Host logic only (no device call).  Errors: the
+ * argument checks of skinny_moe_linear on experts, T, topk and flags, and
+ * SKINNY_ERR_INVALID_ARG for a NULL out. */
+skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int topk, int flags,
+                                    skinny_plan* out);
 
 /* Static text for a status code; never NULL. */
 const char* skinny_status_string(int status);

@@ -213,6 +213,36 @@ def test_mlp_workspace_and_bad_arguments():
     assert call(sg.Mlp(sg.FP8_BS128, 64, 32, 0, A, None, A + 0x10000, None, B, C)) == INVALID
 
 
+def test_moe_plan_query():
+    """One-token slices of rows of at least four 1 KB segments take the row
+    kernel (the verify step's gate_up, K = 4096); short rows (its down,
+    K = 1536), two or more tokens and a bf16 x row past the row kernel's
+    x window (about 63 KB beside the slice table) take the tile kernel."""
+    def variant(dtype, K, T, N=3072, flags=0):
+        ex = sg.Experts(dtype, 8, N, K, A, None if dtype == sg.BF16 else A + 0x8000000)
+        return sg.moe_plan_query(ex, T, 2, bool(flags & sg.MOE_X_PER_ROUTE),
+                                 bool(flags & sg.MOE_SWIGLU)).variant
+    for dt in (sg.BF16, sg.FP8_BS128):
+        assert variant(dt, 4096, 1) == sg.VARIANT_VECTOR
+        assert variant(dt, 4096, 1, flags=sg.MOE_X_PER_ROUTE | sg.MOE_SWIGLU) == sg.VARIANT_VECTOR
+        assert variant(dt, 1536, 1, N=4096) == sg.VARIANT_MFMA
+        assert variant(dt, 4096, 2) == sg.VARIANT_MFMA
+        assert variant(dt, 4096, 6) == sg.VARIANT_MFMA
+    assert variant(sg.BF16, 2048, 1) == sg.VARIANT_VECTOR                # 4 segments of 1 KB
+    assert variant(sg.BF16, 1536, 1) == sg.VARIANT_MFMA                  # 3
+    for dt in (sg.BF16, sg.FP8_BS128):
+        assert variant(dt, 31744, 1) == sg.VARIANT_VECTOR                # 62 KB of x
+        assert variant(dt, 32768, 1) == sg.VARIANT_MFMA                  # 64 KB: past the window
+    L = sg.lib()
+    plan = sg.Plan()
+    ex = sg.Experts(sg.BF16, 8, 64, 64, A, None)
+    assert L.skinny_moe_plan_query(ctypes.byref(ex), 1, 2, 0, None) == INVALID
+    assert L.skinny_moe_plan_query(ctypes.byref(ex), 0, 2, 0, ctypes.byref(plan)) == INVALID
+    assert L.skinny_moe_plan_query(ctypes.byref(ex), 1, 2, 4, ctypes.byref(plan)) == INVALID
+    bad = sg.Experts(sg.BF16, 8, 64, 60, A, None)
+    assert L.skinny_moe_plan_query(ctypes.byref(bad), 1, 2, 0, ctypes.byref(plan)) == UNSUPPORTED
+
+
 def test_moe_workspace_and_bad_arguments():
     L = sg.lib()
     ex = sg.Experts(sg.FP8_BS128, 8, 3072, 4096, A, A + 0x8000000)

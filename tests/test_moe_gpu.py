@@ -107,6 +107,53 @@ def test_swiglu_input_per_route(dtype):
     check(run_moe(gu, ids, w, s, x_per_route=True, swiglu=True), y_ref, a, f"swiglu {dtype}")
 
 
+# One- and two-token slices (one token: the row kernel's MoE form, two: the
+# tile kernel's): E = 5, so ids 5 and -1 have no expert; N = 200 and
+# K = 4112 end inside a row group, a 128 x 128 scale block and a row segment.
+ROW_IDS = {1: np.array([[3, 5, 0]], np.int32),
+           2: np.array([[2, -1, 4], [4, 2, 2]], np.int32)}
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("x_per_route", [False, True])
+@pytest.mark.parametrize("T", [1, 2])
+@pytest.mark.parametrize("dtype", [sg.BF16, sg.FP8_BS128])
+def test_one_and_two_token_slices(dtype, T, x_per_route, swiglu):
+    if swiglu and not x_per_route:
+        pytest.skip("the SwiGLU input is read per route")
+    E, N, K = 5, 200, 4112
+    ids = ROW_IDS[T]
+    tag = f"rows{T}{int(x_per_route)}{int(swiglu)}"
+    if dtype == sg.BF16:
+        w, s = experts_bf16(tag, E, N, K), None
+    else:
+        w, s = experts_fp8(tag, E, N, K)
+    x = x_for(tag, ids.size if x_per_route else T, 2 * K if swiglu else K)
+    y_ref, a = oracle.moe_linear(x, ids, w, scales=s, x_per_route=x_per_route, swiglu=swiglu)
+    y1, y2 = run_moe(x, ids, w, s, x_per_route=x_per_route, swiglu=swiglu, reps=2)
+    check(y1, y_ref, a, f"{dtype} T={T} per_route={x_per_route} swiglu={swiglu}")
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    dead = np.flatnonzero((ids.reshape(-1) < 0) | (ids.reshape(-1) >= E))
+    assert torch.all(y1[torch.from_numpy(dead).cuda()].float() == 0)
+
+
+@pytest.mark.parametrize("dtype", [sg.BF16, sg.FP8_BS128])
+def test_one_token_short_and_long_rows(dtype):
+    """One token with rows too short for the row kernel (K = 1536, the verify
+    step's down shape) and an x row too long for its x window (K = 33024:
+    66 KB of bf16): the tile kernel takes both."""
+    E, N = 3, 96
+    ids = np.array([[2, 0]], np.int32)
+    for K in (1536, 33024):
+        if dtype == sg.BF16:
+            w, s = experts_bf16(f"k{K}", E, N, K, 0.02), None
+        else:
+            w, s = experts_fp8(f"k{K}", E, N, K, 0.02)
+        x = x_for(f"k{K}", 1, K)
+        y_ref, a = oracle.moe_linear(x, ids, w, scales=s)
+        check(run_moe(x, ids, w, s), y_ref, a, f"K={K} {dtype}")
+
+
 def test_one_expert_takes_more_routes_than_tokens():
     """Duplicates: 8 routes of 2 tokens to expert 1 make 4 slices of it."""
     E, N, K = 3, 128, 512
