@@ -23,7 +23,9 @@
 //     [16 l, 16 l + 16) of each 1 KB segment; x of the current K-chunk sits in
 //     LDS, shared by the workgroup.  v_dot2_f32_bf16 accumulates in fp32 and
 //     a 64-lane butterfly ends each row.  Measured on MI355X, one contiguous
-//     stream per wave sustains ~6.3 TB/s.
+//     stream per wave sustains ~6.3 TB/s.  Its MoE form serves one-token
+//     slices, whose few chosen experts' rows its 8-row units spread over
+//     more workgroups than the tile kernel's.
 //
 //   skinny_tiles (MFMA variant): each wave streams 16 rows in whole cache
 //     lines (512 contiguous bytes per row per load), turns them around
