@@ -348,7 +348,7 @@ struct RowBatch {
   u32x4 w[U][R];
 };
 
-// The bf16 M = 1 instances keep 16 waves per CU (<= 128 VGPRs); the others
+// The bf16 M <= 2 instances keep 16 waves per CU (<= 128 VGPRs); the others
 // have the registers they need.
 //
 // MoE form (MOE): lin[0] describes one expert as in skinny_tiles; units are
@@ -357,7 +357,7 @@ struct RowBatch {
 // the x budget.
 template <int DT, int MT, int U, int R, int WPB, bool MOE = false>
 __global__ __launch_bounds__(64 * WPB)
-__attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT == 1) ? 4 : 1))) void skinny_rows(
+__attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) void skinny_rows(
     const LaunchArgs a) {
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = WPB * R;
@@ -1126,9 +1126,14 @@ skinny_status check_outputs(const skinny_linear* lin, int count, int M, const vo
 // skinny_rows shape per M: R rows per wave (one LDS read of x serves R weight
 // loads, so LDS traffic stays at <= 2 x reads per weight load up to M = 8) and
 // U segments per batch, R x U = 8 loads (bf16) or 4 (FP8, whose conversion
-// needs the registers) per batch, two batches in flight.
+// needs the registers) per batch, two batches in flight.  bf16 at M = 2 takes
+// half batches, which fit the 128 VGPRs of two workgroups per CU: as many
+// loads in flight per CU as one workgroup of full batches, and measured on
+// MI355X 42.0 against 47.4 us on the TP=8 layer (TP=1 stacks within +-1.5%).
 constexpr int rows_r(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : 4; }
-constexpr int rows_u(int M, int dtype) { return (dtype == SKINNY_BF16 ? 8 : 4) / rows_r(M); }
+constexpr int rows_u(int M, int dtype) {
+  return (dtype == SKINNY_BF16 ? (M == 2 ? 4 : 8) : 4) / rows_r(M);
+}
 constexpr int kRowsXBudget = 64 * 1024;   // LDS for x per workgroup: two workgroups per CU
 constexpr int kRowsMaxM = 8;
 // Units per workgroup below which a launch cuts K into more chunks for
@@ -1267,17 +1272,28 @@ size_t group_slots_bytes(const skinny_linear* const* lin, int count, int M, int 
 }
 
 // Variant choice, measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers
-// and stacks, the TP=8 layer).  Row streaming keeps one contiguous stream per
-// wave, but its vector work per weight grows with M (and FP8 adds a half-rate
-// conversion); the matrix-core kernel's does not.  bf16 TP=1 layer, rows vs
-// tiles: 6.10 / 5.92 TB/s at M = 1, 5.81 / 5.82 at M = 2, 5.37 / 5.42 at
-// M = 4; TP=8 layer at M = 2: 53.8 / 45.7 us (the row kernel's registers
-// leave one workgroup per CU there); FP8 TP=1 stack at M = 1: 5.85 / 5.93.
-constexpr int kRowsMaxAutoMBf16 = 1;
+// and stacks of 1-8 layers per launch, the TP=8 layer, single linears).  Row
+// streaming keeps one contiguous stream per wave, but its vector work per
+// weight grows with M (and FP8 adds a half-rate conversion); the matrix-core
+// kernel's does not.  bf16, rows vs tiles: M = 1 and 2 rows everywhere (TP=1
+// stacks +2-10% at M = 2, TP=8 layer 42.0 / 44.7 us) but for short rows
+// (8192 x 1024: 8.3 / 7.6 us); M = 3 and 4 rows only for launches of >= 2
+// TP=1 layers (+2-7%; one layer, 1.76 GB, -1%, the TP=8 layer -3 to -7%:
+// above two resident workgroups per CU the row kernel's fixed cost per launch
+// is larger); M = 5 and 6 within a few percent either way, M = 8 tiles.  FP8
+// at every M tiles (TP=1 stack at M = 1: 5.85 / 5.93 TB/s).
+constexpr int kRowsMaxAutoMBf16 = 2;
+constexpr int kRowsMaxAutoMBf16Large = 4;
+constexpr double kRowsLargeLaunchBytes = 2.5e9;   // weight bytes of one launch
 constexpr int kRowsMaxAutoMFp8 = 0;
 
 int auto_variant(const skinny_linear* const* lin, int count, int M) {
-  const int cap = lin[0]->dtype == SKINNY_BF16 ? kRowsMaxAutoMBf16 : kRowsMaxAutoMFp8;
+  int cap = kRowsMaxAutoMFp8;
+  if (lin[0]->dtype == SKINNY_BF16) {
+    double bytes = 0;
+    for (int i = 0; i < count; ++i) bytes += 2.0 * lin[i]->N * lin[i]->K;
+    cap = bytes >= kRowsLargeLaunchBytes ? kRowsMaxAutoMBf16Large : kRowsMaxAutoMBf16;
+  }
   if (M > cap) return SKINNY_VARIANT_MFMA;
   for (int i = 0; i < count; ++i)
     if (!rows_supported(*lin[i], M)) return SKINNY_VARIANT_MFMA;

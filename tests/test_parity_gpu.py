@@ -240,3 +240,21 @@ def test_tp8_layer_stack(M):
         torch.cuda.synchronize()
         for L, (xd, wd, yd), (y_ref, a, _) in zip(lins, dev, refs):
             assert_matches_oracle(yd, y_ref, a, f"{L.name} M={M} var={var}")
+
+
+def test_automatic_variant():
+    """bf16 takes the row kernel at M <= 2, and at M = 3-4 for launches of at
+    least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise, and
+    for FP8 at every M.  The stack's launches hold up to 32 linears."""
+    V, T = sg.VARIANT_VECTOR, sg.VARIANT_MFMA
+
+    def variant(shapes, M, dt=sg.BF16):
+        scale = None if dt == sg.BF16 else 0x300000
+        lins = [sg.Linear(dt, N, K, 0, 0x100000, scale, 0x2000000, 0x4000000) for N, K in shapes]
+        return sg.plan_query(lins, M).variant
+    tp8 = [(1280, 8192), (8192, 1024), (7392, 8192), (8192, 3696)]
+    tp1 = [(10240, 8192), (8192, 8192), (59136, 8192), (8192, 29568)]
+    assert [variant(tp8, M) for M in (1, 2, 3, 4, 5, 8, 16)] == [V, V, T, T, T, T, T]
+    assert [variant(tp1, M) for M in (1, 2, 3, 4)] == [V, V, T, T]                  # 1.76 GB
+    assert [variant(tp1 * 2, M) for M in (1, 2, 3, 4, 5, 6, 8)] == [V, V, V, V, T, T, T]
+    assert [variant(tp1 * 2, M, sg.FP8_BS128) for M in (1, 2, 4)] == [T, T, T]
