@@ -1234,9 +1234,10 @@ int tiles_chunks(int dtype, int M, int K, long long par, int budget = kTilesXBud
 // launch's parallelism) or, with `windows` and when parallelism asks for no
 // split, one chunk whose x windows the unit's workgroup walks in turn with its
 // sums kept in registers: no partial sums and no second pass, but x restaged
-// per unit.  Measured on MI355X: the walk costs 1.8% on the FP8 TP=1 stack at
-// M = 1 (every unit restages where a split workgroup keeps one window per
-// linear), so dense launches split and MoE launches walk.
+// per unit.  The split's partial sums grow with M (M + 1) per weight byte (M
+// outputs, a window of M + 1 rows), the walk's restaging with M, so the walk
+// wins at large M: MoE launches always walk, dense launches from
+// kTilesWalkMinM* tokens on (below).
 void tiles_split(int dtype, int M, int K, long long par, int budget, bool windows, int* chunks,
                  int* sub) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
@@ -1464,6 +1465,14 @@ bool tiles_large(const skinny_linear* const* lin, int count, int M, int cus) {
   return groups >= (long long)kTilesLargeGroupsPerCU * cus;
 }
 
+// Dense tile launches walk their x windows instead of splitting K for them
+// from these token counts on.  Measured on MI355X (8-layer TP=1 stack
+// launches, walk vs split): bf16 +0.8 / +2.8 / +1.7 / +5.7 / +10.5% at M = 5 /
+// 6 / 8 / 10 / 16; FP8 (8-wave) -3.0 / -0.8% at M = 5 / 6, even at 7 and 8,
+// +2.4 / +10.4 / +7.0% at 10 / 12 / 16 (the walk costs 1.8% at M = 1).
+constexpr int kTilesWalkMinMBf16 = 5;
+constexpr int kTilesWalkMinMFp8 = 9;
+
 // K-chunks per linear (either kernel): enough for the x window to fit the LDS
 // budget and, when the launch is too small to give every workgroup the
 // kernel's units per worker, more - but never fewer segments per chunk than
@@ -1478,7 +1487,8 @@ void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
   for (int i = 0; i < count; ++i) {
     LinDesc& d = a.lin[i];
     int c, w = 1;
-    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, false, &c, &w);
+    const bool walk = a.M >= (dtype == SKINNY_BF16 ? kTilesWalkMinMBf16 : kTilesWalkMinMFp8);
+    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, walk, &c, &w);
     else c = rows_chunks(dtype, a.M, d.K, par);
     d.chunks = c;
     d.sub = w;

@@ -123,3 +123,41 @@ def test_fp8_large_workgroup_sampled(M):
         worst = max(worst, wr)
     assert worst < 0.5
     del tensors
+
+
+@pytest.mark.parametrize("dtype,M,K", [(wl.BF16, 6, 4096), (wl.BF16, 16, 2048),
+                                       (wl.FP8_BS128, 16, 4096)])
+def test_window_walk_sampled(dtype, M, K):
+    """One linear of 524288 rows: its row groups alone give every tile
+    workgroup 16 units (no K split for parallelism), and the x window of
+    M + 1 token rows holds half of K, so from M = 5 (bf16) or 9 (FP8) tokens
+    on each unit walks its two x windows with the sums in registers (no
+    partial sums, no second pass); FP8 on the 8-wave workgroup.  Sampled rows
+    against the oracle as above."""
+    N = 524288
+    tag = f"walk-{dtype}-{M}-{K}"
+    spec = wl.LinearSpec(tag, N, K, dtype, synth.stream_id(tag, "w"), synth.stream_id(tag, "x"))
+    tensors = _run_stack([spec], M)
+    x_dev, w_dev, s_dev, y_dev = tensors[0]
+    x = synth.tensor_bf16(0, spec.x_stream, M, K, wl.X_SIGMA)
+    assert np.array_equal(host_codes(x_dev), x)
+    rng = np.random.default_rng(M)
+    worst = 0.0
+    if dtype == wl.BF16:
+        rows = sorted(set([0, 63, 64, N - 1] + list(rng.choice(N, 60, replace=False))))
+        w = synth.tensor_rows_bf16(0, spec.w_stream, rows, K, wl.W_SIGMA)
+        assert np.array_equal(host_codes(w_dev[rows]), w)
+        y_ref, a, _ = oracle.linear_bf16(x, w)
+        ok, worst, idx = oracle.check(y_dev[:, rows].float().cpu().double().numpy(), y_ref, a)
+        assert ok, f"worst err/bound {worst:.3g} at {idx}"
+    else:
+        for band in sorted(set([0, N // 128 - 1] + list(rng.choice(N // 128, 4, replace=False)))):
+            q, sc, r0 = synth.fp8_weight_bs128(0, spec.w_stream, N, K, wl.W_SIGMA, band, 1)
+            assert np.array_equal(w_dev[r0:r0 + 128].cpu().numpy(), q)
+            assert np.array_equal(s_dev[band:band + 1].cpu().numpy(), sc)
+            y_ref, a, _ = oracle.linear_fp8_bs128(x, q, sc)
+            ok, wr, idx = oracle.check(y_dev[:, r0:r0 + 128].float().cpu().double().numpy(), y_ref, a)
+            assert ok, f"band {band}: worst err/bound {wr:.3g} at {idx}"
+            worst = max(worst, wr)
+    assert worst < 0.5
+    del tensors
