@@ -71,13 +71,17 @@ def test_mlp_graph():
     _check_replays(lambda: sg.mlp_swiglu(mlp, M, ws), [t[0][0]], [t[1][3]])
 
 
-def test_moe_graph():
-    """MoE: the routing is read on the device, so new router choices written
-    between replays are honoured by the captured launch."""
-    E, N, K, T, topk = 8, 512, 1024, 6, 2
+@pytest.mark.parametrize("T", [1, 6])
+def test_moe_graph(T):
+    """MoE (one token: the row kernel's form; six: the tile kernel's): the
+    routing is read on the device, so new router choices written between
+    replays are honoured by the captured launch."""
+    E, N, K, topk = 8, 512, 2048, 2
     w = synth.tensor_bf16(0, 901, E * N, K, 0.02)
     wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda().view(E, N, K)
     ex = sg.make_experts(wd)
+    want = sg.VARIANT_VECTOR if T == 1 else sg.VARIANT_MFMA
+    assert sg.moe_plan_query(ex, T, topk).variant == want
     x = torch.zeros((T, K), dtype=torch.bfloat16, device="cuda")
     ids = torch.from_numpy(synth.route_topk(0, 902, T, E, topk)).cuda()
     y = torch.empty((T * topk, N), dtype=torch.bfloat16, device="cuda")
