@@ -42,7 +42,10 @@
  *   work on `stream` (a hipStream_t; NULL is the default stream) and return
  *   without waiting for it; execution faults surface at the caller's next
  *   synchronization.  Calls on different streams need separate workspaces.
- *   Workspace contents are undefined after a call.
+ *   Workspace contents are undefined after a call.  Entry points may be
+ *   called from several host threads at once: the library's only shared
+ *   state is a per-device cache of device properties, occupancy results and
+ *   granted LDS sizes, filled on first use under a lock.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
