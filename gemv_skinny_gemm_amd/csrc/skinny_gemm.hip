@@ -598,8 +598,9 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 // drains between units and the x staging hides under those loads.
 //
 // Shape measured on MI355X over the Qwen2.5-72B shapes (TP=1 layers and the
-// TP=8 layer, M = 1..16): 512-byte segments, 4 waves per workgroup and two
-// workgroups per CU beat 256- or 1024-byte segments and 8-wave workgroups.
+// TP=8 layer, M = 1..16): 512-byte segments beat 256- and 1024-byte ones, and
+// 4 waves per workgroup, two workgroups per CU, beat 8-wave workgroups on a
+// single layer; large FP8 launches take the 8-wave shape (tiles_large).
 constexpr int kSegBytesT = 512;                       // bytes of one row per segment
 constexpr int kSegChunksT = kSegBytesT / 16;          // chunks
 constexpr int kRowStrideT = kSegBytesT + 16;          // LDS bytes per staged row

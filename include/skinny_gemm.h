@@ -157,7 +157,10 @@ skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, i
  * launch splits; linears in order, then row groups, then K-chunks in K order. */
 int skinny_band_rows(int dtype, int variant, int M);
 
-/* The plan the library would use on the current device (fills *out). */
+/* The automatic plan (fills *out) of the first launch of linears[0]'s dtype
+ * on the current device: a call launches its linears grouped by dtype, at
+ * most SKINNY_MAX_LINEARS_PER_LAUNCH per launch, and each launch chooses its
+ * own variant (it can depend on the launch's size). */
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);
 
