@@ -886,9 +886,28 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
 // Second pass: for every output of a split linear, the sum of its K-chunks'
 // partial results in chunk order.  blockIdx.y is the linear; thread t of
 // the grid row takes four adjacent rows (one 16-byte slot read per chunk; a
-// row group's height is a multiple of four) of one token, so the chunks'
-// loads of a thread are all in flight together.
+// row group's height is a multiple of four) of one token.
 constexpr int kCombineRows = 4;
+constexpr int kCombineBatch = 8;
+
+// p[0] + p[stride] + ... + p[(n - 1) stride], added in that order.  Loads go
+// out kCombineBatch at a time (the last batch's past n re-read chunk n - 1
+// and are not added), so a thread waits once per batch instead of once per
+// chunk.
+__device__ __forceinline__ f32x4 sum_chunks(const f32x4* p, size_t stride, int n) {
+  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < n; c += kCombineBatch) {
+    f32x4 v[kCombineBatch];
+#pragma unroll
+    for (int q = 0; q < kCombineBatch; ++q) v[q] = p[(size_t)min(c + q, n - 1) * stride];
+#pragma unroll
+    for (int q = 0; q < kCombineBatch; ++q)
+      if (c + q < n)
+#pragma unroll
+        for (int r = 0; r < kCombineRows; ++r) sum[r] += v[q][r];
+  }
+  return sum;
+}
 __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchArgs a) {
   const LinDesc& L = a.lin[blockIdx.y];
   if (L.chunks == 1) return;
@@ -903,12 +922,7 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchAr
   const f32x4* p = reinterpret_cast<const f32x4*>(
       a.slots + ((size_t)(L.slot_base + (long long)grp * L.chunks) * a.M + m) * R + rr);
   const size_t stride = (size_t)a.M * R / kCombineRows;        // one chunk's slot, in f32x4
-  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = 0; c < L.chunks; ++c) {
-    const f32x4 v = p[c * stride];
-#pragma unroll
-    for (int r = 0; r < kCombineRows; ++r) sum[r] += v[r];
-  }
+  const f32x4 sum = sum_chunks(p, stride, L.chunks);
   __bf16* y = L.y + (size_t)m * L.N + row;
 #pragma unroll
   for (int r = 0; r < kCombineRows; ++r)
@@ -935,12 +949,7 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_moe_combine(const Laun
   const f32x4* p =
       reinterpret_cast<const f32x4*>(a.slots + ((size_t)slot0 * a.M + m) * R + rr);
   const size_t stride = (size_t)a.M * R / kCombineRows;
-  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = 0; c < L.chunks; ++c) {
-    const f32x4 v = p[c * stride];
-#pragma unroll
-    for (int r = 0; r < kCombineRows; ++r) sum[r] += v[r];
-  }
+  const f32x4 sum = sum_chunks(p, stride, L.chunks);
   __bf16* y = L.y + (size_t)tb[1 + a.moe.max_slices + sl * kMoeMaxCap + m] * L.N + row;
 #pragma unroll
   for (int r = 0; r < kCombineRows; ++r)
