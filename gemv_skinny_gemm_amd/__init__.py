@@ -152,11 +152,17 @@ def lib():
 
 
 def _ptr(t) -> int | None:
-    """Device address of a torch tensor, or an int address as given (None = NULL)."""
+    """Device address of a torch tensor, or an int address as given (None = NULL).
+    The library reads and writes dense row-major device memory, so a tensor must
+    be contiguous and on the GPU."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous (row-major)")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensors passed to the library must be on the GPU, not {t.device}")
     return t.data_ptr()
 
 
@@ -211,7 +217,7 @@ def _ws(workspace):
         return None, 0
     if isinstance(workspace, tuple):
         return workspace
-    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def skinny_gemm_bf16(x, w, y, workspace, stream=None):

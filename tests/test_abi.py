@@ -213,6 +213,21 @@ def test_mlp_workspace_and_bad_arguments():
     assert call(sg.Mlp(sg.FP8_BS128, 64, 32, 0, A, None, A + 0x10000, None, B, C)) == INVALID
 
 
+def test_binding_rejects_host_and_strided_tensors():
+    """The binding refuses tensors the kernels cannot address as dense device
+    memory, before anything reaches the C library."""
+    import torch
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    w = torch.zeros((32, 64), dtype=torch.bfloat16)
+    y = torch.zeros((2, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        sg.make_linear(x, w, y)
+    with pytest.raises(ValueError, match="contiguous"):
+        sg.make_linear(x, torch.zeros((64, 32), dtype=torch.bfloat16).t(), y)
+    with pytest.raises(ValueError, match="on the GPU"):
+        sg.skinny_gemm_bf16(x, w, y, torch.zeros(1024, dtype=torch.uint8))
+
+
 def test_moe_plan_query():
     """One-token slices of rows of at least four 1 KB segments take the row
     kernel (the verify step's gate_up, K = 4096); short rows (its down,
