@@ -86,3 +86,42 @@ def test_some_moe_pin_catches_mutant(mutant, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(name)
     assert caught, f"no pin catches the mutant {mutant}"
+
+
+# Mistakes in the oracle's Python helpers and the gated MLP chain: each planted
+# in a copy of the one function must make some pin fail (pins reach the
+# function through the module, so the copy replaces it for all of them).
+HELPER_MUTANTS = {
+    "silu_wrong_sign": ("silu", "np.exp(-v)", "np.exp(v)"),
+    "silu_is_sigmoid": ("silu", "return v / (1.0 + np.exp(-v))", "return 1.0 / (1.0 + np.exp(-v))"),
+    "bf16_truncates": ("bf16_encode", "sig = np.rint(f * 256.0)", "sig = np.floor(f * 256.0)"),
+    "bf16_rounds_half_up": ("bf16_encode", "sig = np.rint(f * 256.0)", "sig = np.floor(f * 256.0 + 0.5)"),
+    "bf16_nan_as_infinity": ("bf16_encode", "np.uint16(0x7FC0)", "np.uint16(0x7F80)"),
+    "mlp_gate_up_swapped": ("mlp_swiglu", "h = bf16_encode(silu(g) * u)", "h = bf16_encode(silu(u) * g)"),
+    "mlp_gate_not_rounded": ("mlp_swiglu", "g = bf16_decode(bf16_encode(gu[:, :I]))", "g = gu[:, :I]"),
+    "mlp_wrong_half_for_gate": ("mlp_swiglu", "g = bf16_decode(bf16_encode(gu[:, :I]))",
+                                "g = bf16_decode(bf16_encode(gu[:, I:]))"),
+    "argmax_last_of_ties": ("argmax_first", "if not np.isnan(x) and x > best_v:",
+                            "if not np.isnan(x) and x >= best_v:"),
+    "argmax_nan_first_kept": ("argmax_first", "best_v = -np.inf if np.isnan(v[m, 0]) else v[m, 0]",
+                              "best_v = v[m, 0]"),
+    "greedy_bound_sign": ("greedy_valid", "(y_ref[rows, idx] + b[rows, idx]) >= lo",
+                          "(y_ref[rows, idx] - b[rows, idx]) >= lo"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(HELPER_MUTANTS))
+def test_some_pin_catches_helper_mutant(mutant, monkeypatch):
+    fname, old, new = HELPER_MUTANTS[mutant]
+    src = inspect.getsource(getattr(oracle, fname))
+    assert src.count(old) == 1, "mutation site moved; update the mutant"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), "<helper_mutant>", "exec"), ns)
+    monkeypatch.setattr(oracle, fname, ns[fname])
+    caught = []
+    for name, fn in _pin_functions():
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(name)
+    assert caught, f"no pin catches the mutant {mutant}"

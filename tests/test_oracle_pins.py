@@ -369,6 +369,21 @@ def test_mlp_swiglu_matches_a_direct_computation():
     assert np.allclose(a, np.abs(hb) @ np.abs(wdv).T, rtol=1e-14, atol=1e-14)
 
 
+def test_mlp_rounds_gate_and_up_to_bf16():
+    """g and u are bf16 activations before the SiLU gate: with g = 1 + 2^-9
+    exactly (x = [1, 2^-9] against a gate row [1, 1]) and u = 1, bf16(g) = 1
+    and h = bf16(silu(1)) = 0.73046875, where an unrounded g would give
+    bf16(silu(1 + 2^-9)) = 0.734375; swapping the roles (u = 1 + 2^-9, g = 1)
+    pins the rounding of u the same way (bf16(silu(1) (1 + 2^-9)) = 0.734375)."""
+    x = bf16_codes_of(np.array([[1.0, 2.0 ** -9]]))
+    wd = bf16_codes_of(np.array([[1.0], [2.0]]))                 # H = 2, I = 1
+    for gate, up in (([1.0, 1.0], [1.0, 0.0]), ([1.0, 0.0], [1.0, 1.0])):
+        wg = bf16_codes_of(np.array([gate, up]))                 # [2I][H]: gate row, then up
+        y, a, h = oracle.mlp_swiglu(x, wg, wd)
+        assert torch_bf16_values(h).numpy().tolist() == [[0.73046875]]
+        assert y.tolist() == [[0.73046875, 1.4609375]]
+
+
 # --- mixture-of-experts linear ---------------------------------------------
 
 def _moe_exact(xv, ids, wv, x_per_route):
