@@ -107,6 +107,17 @@ HELPER_MUTANTS = {
                               "best_v = v[m, 0]"),
     "greedy_bound_sign": ("greedy_valid", "(y_ref[rows, idx] + b[rows, idx]) >= lo",
                           "(y_ref[rows, idx] - b[rows, idx]) >= lo"),
+    "greedy_without_output_rounding": ("greedy_valid", "b = bound(a, y_ref)", "b = bound(a)"),
+    "greedy_max_over_rows": ("greedy_valid", "np.max(y_ref - b, axis=1)", "np.max(y_ref - b)"),
+    "bound_without_absolute_term": ("bound", "REL_TOL * np.asarray(a, np.float64) + ABS_TOL",
+                                    "REL_TOL * np.asarray(a, np.float64)"),
+    "bound_without_half_ulp": ("bound", "b = b + bf16_half_ulp(y_ref)", "b = b"),
+    "half_ulp_a_bit_wide": ("bf16_half_ulp", "np.ldexp(1.0, e - 9)", "np.ldexp(1.0, e - 8)"),
+    "half_ulp_a_bit_narrow": ("bf16_half_ulp", "np.ldexp(1.0, e - 9)", "np.ldexp(1.0, e - 10)"),
+    "check_signed_error": ("check", "err = np.abs(np.asarray(y_gpu, np.float64) - y_ref)",
+                           "err = np.asarray(y_gpu, np.float64) - y_ref"),
+    "check_rejects_at_bound": ("check", "np.all(ratio <= 1.0)", "np.all(ratio < 1.0)"),
+    "bf16_decode_wrong_shift": ("bf16_decode", "astype(np.uint32) << 16", "astype(np.uint32) << 15"),
 }
 
 

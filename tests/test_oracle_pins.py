@@ -256,6 +256,11 @@ def test_check_accepts_inside_and_rejects_outside_bound():
     assert ok and worst < 1.0
     ok, worst, idx = oracle.check(y_ref + np.array([[0.0, 0.0211, 0.0]]), y_ref, a)
     assert not ok and idx == (0, 1)
+    ok, worst, idx = oracle.check(y_ref + np.array([[-0.0211, 0.0, 0.0]]), y_ref, a)
+    assert not ok and idx == (0, 0)                 # an error below y_ref counts as much
+    # Exactly at the bound is inside: A = 0 leaves the absolute term, 1e-6.
+    ok, worst, _ = oracle.check(np.array([[1e-6, -1e-6]]), np.zeros((1, 2)), np.zeros((1, 2)))
+    assert ok and worst == 1.0
 
 
 def test_threads_do_not_change_results():
@@ -317,6 +322,13 @@ def test_greedy_valid_admits_only_the_winner_when_the_gap_is_wide():
     wide = np.array([[1.0, 5000.0, 5000.0, 1.0]])     # bounds of 10: 4.9 is within reach
     assert oracle.greedy_valid(np.array([2]), y_ref, wide).tolist() == [True]
     assert oracle.greedy_valid(np.array([3]), y_ref, wide).tolist() == [False]
+    # 5.0 and 4.99 round to the same bf16 output (spacing 1/32 there), so the
+    # runner-up is admissible: the bound carries half an ulp of each.
+    close = np.array([[5.0, 4.99]])
+    assert oracle.greedy_valid(np.array([1]), close, np.ones((1, 2))).tolist() == [True]
+    two = np.array([[5.0, 1.0], [1.0, 2.0]])          # each row takes its own maximum
+    assert oracle.greedy_valid(np.array([0, 1]), two, np.ones((2, 2))).tolist() == [True, True]
+    assert oracle.greedy_valid(np.array([1, 0]), two, np.ones((2, 2))).tolist() == [False, False]
 
 
 # --- the gated MLP's activation ---------------------------------------------
