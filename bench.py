@@ -124,6 +124,22 @@ def moe_bytes(specs, ids):
     return a, b
 
 
+def step_work(specs, M, ids=None):
+    """(flops, weight bytes) of one step: 2 M N K per linear and every weight
+    and scale byte once; for a mixture-of-experts step (ids = the routes'
+    experts), 2 flops per (route, output, k) and only the chosen experts'
+    weights."""
+    from gemv_skinny_gemm_amd import workloads as wl
+    if ids is None:
+        return wl.flops(specs, M), sum(s.weight_bytes() + s.scale_bytes() for s in specs)
+    E = wl.MOE_EXPERTS
+    flat = [int(e) for e in ids.ravel()]
+    chosen = len({e for e in flat if 0 <= e < E})
+    routes = sum(1 for e in flat if 0 <= e < E)
+    flops = sum(2 * routes * (s.N // E) * s.K for s in specs)
+    return flops, sum(chosen * ((s.weight_bytes() + s.scale_bytes()) // E) for s in specs)
+
+
 def moe_cpu_baseline(specs, ids, seed=0):
     """The fp64 oracle over the whole MoE step (it is small): gate_up, then
     down on the oracle's own bf16 gate_up outputs.  Returns seconds, bytes,
@@ -268,7 +284,7 @@ def main():
         step_bytes = moe_gu_bytes + moe_dn_bytes
     else:
         step_bytes = wl.algorithmic_bytes(specs, M) + (4 * M if head else 0)
-    step_flops = wl.flops(specs, M)
+    step_flops, step_weight_bytes = step_work(specs, M, ids_host if moe else None)
     copies = 1 if step_bytes >= args.rotate_bytes else int(np.ceil(args.rotate_bytes / step_bytes))
     log(f"workload {args.workload}: {len(specs)} linears, M={M}, {step_bytes / 1e9:.3f} GB/step, "
         f"{copies} rotating cop{'y' if copies == 1 else 'ies'}")
@@ -425,6 +441,12 @@ def main():
                                     "min": round(min(batch_us), 2), "max": round(max(batch_us), 2)},
             "hot_cache_us_per_step": None if hot_us is None else round(hot_us, 2),
             "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            # Weight-only MBU: weight (and scale) bytes per second over the peak,
+            # the decode figure of "Developing a custom Qwen2.5 72B inference
+            # engine from scratch", section 6.1.
+            "weight_only_mbu_pct": round(
+                100 * step_weight_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
             "weight_copies_rotated": copies,
             "variant": {0: "auto", 1: "vector", 2: "mfma"}[variant],
             "auto_plan": {"variant": {1: "vector", 2: "mfma"}.get(plan.variant, plan.variant),
