@@ -35,11 +35,8 @@ def run_mlp(x, wg, wd, M, sg_=None, sd=None):
     return y
 
 
-def check(y, y_ref, a, what, strict=True):
-    """strict: the stated bound.  Otherwise (down's K < 1000: outputs with little
-    cancellation) half a bf16 ulp of y_ref on top, as for any small-K linear."""
-    ok, worst, idx = oracle.check(y.float().cpu().double().numpy(), y_ref, a,
-                                  bf16_rounding=not strict)
+def check(y, y_ref, a, what):
+    ok, worst, idx = oracle.check(y.float().cpu().double().numpy(), y_ref, a)
     assert ok, f"{what}: worst err/bound {worst:.3g} at {idx}"
     return worst
 
@@ -51,7 +48,7 @@ def test_small_mlp_bf16(M, H, I):
     wg = synth.tensor_bf16(0, synth.stream_id("mlp", H, I, "wg"), 2 * I, H, 0.05)
     wd = synth.tensor_bf16(0, synth.stream_id("mlp", H, I, "wd"), H, I, 0.05)
     y_ref, a, _ = oracle.mlp_swiglu(x, wg, wd)
-    check(run_mlp(x, wg, wd, M), y_ref, a, f"bf16 M={M} H={H} I={I}", strict=I >= 1000)
+    check(run_mlp(x, wg, wd, M), y_ref, a, f"bf16 M={M} H={H} I={I}")
 
 
 @pytest.mark.parametrize("M", [1, 6])

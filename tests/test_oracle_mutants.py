@@ -101,21 +101,31 @@ HELPER_MUTANTS = {
     "mlp_gate_not_rounded": ("mlp_swiglu", "g = bf16_decode(bf16_encode(gu[:, :I]))", "g = gu[:, :I]"),
     "mlp_wrong_half_for_gate": ("mlp_swiglu", "g = bf16_decode(bf16_encode(gu[:, :I]))",
                                 "g = bf16_decode(bf16_encode(gu[:, I:]))"),
-    "argmax_last_of_ties": ("argmax_first", "if not np.isnan(x) and x > best_v:",
-                            "if not np.isnan(x) and x >= best_v:"),
-    "argmax_nan_first_kept": ("argmax_first", "best_v = -np.inf if np.isnan(v[m, 0]) else v[m, 0]",
-                              "best_v = v[m, 0]"),
-    "greedy_bound_sign": ("greedy_valid", "(y_ref[rows, idx] + b[rows, idx]) >= lo",
-                          "(y_ref[rows, idx] - b[rows, idx]) >= lo"),
-    "greedy_without_output_rounding": ("greedy_valid", "b = bound(a, y_ref)", "b = bound(a)"),
-    "greedy_max_over_rows": ("greedy_valid", "np.max(y_ref - b, axis=1)", "np.max(y_ref - b)"),
+    "argmax_last_of_ties": ("argmax_first", "if best_i is None or x > v[m, best_i]:",
+                            "if best_i is None or x >= v[m, best_i]:"),
+    # The reading before NaN ranked below -inf: a leading NaN held index 0.
+    "argmax_nan_first_kept": ("argmax_first", "best_i = None                              # no number seen yet",
+                              "best_i = 0"),
+    "argmax_nan_not_skipped": ("argmax_first", "if np.isnan(x):\n                continue",
+                               "if np.isnan(x):\n                pass"),
+    "greedy_bound_sign": ("greedy_valid", "hi[rows, idx] >= np.max(lo, axis=1)",
+                          "lo[rows, idx] >= np.max(lo, axis=1)"),
+    "greedy_without_output_rounding": ("greedy_valid", "lo, hi = accepted(y_ref, a)",
+                                       "lo, hi = y_ref - bound(a), y_ref + bound(a)"),
+    "greedy_max_over_rows": ("greedy_valid", "np.max(lo, axis=1)", "np.max(lo)"),
     "bound_without_absolute_term": ("bound", "REL_TOL * np.asarray(a, np.float64) + ABS_TOL",
                                     "REL_TOL * np.asarray(a, np.float64)"),
-    "bound_without_half_ulp": ("bound", "b = b + bf16_half_ulp(y_ref)", "b = b"),
-    "half_ulp_a_bit_wide": ("bf16_half_ulp", "np.ldexp(1.0, e - 9)", "np.ldexp(1.0, e - 8)"),
-    "half_ulp_a_bit_narrow": ("bf16_half_ulp", "np.ldexp(1.0, e - 9)", "np.ldexp(1.0, e - 10)"),
-    "check_signed_error": ("check", "err = np.abs(np.asarray(y_gpu, np.float64) - y_ref)",
-                           "err = np.asarray(y_gpu, np.float64) - y_ref"),
+    "accepted_without_bracket": ("accepted", "return np.minimum(y_ref - b, lo_b), np.maximum(y_ref + b, hi_b)",
+                                 "return y_ref - b, y_ref + b"),
+    "accepted_rounded_not_bracketed": ("accepted", "lo_b, hi_b = bf16_bracket(y_ref)",
+                                       "lo_b = hi_b = bf16_decode(bf16_encode(y_ref))"),
+    "bracket_a_step_wide": ("bf16_bracket", "np.maximum(c - 1, 0)", "np.maximum(c - 2, 0)"),
+    "bracket_sign_not_mirrored": ("bf16_bracket",
+                                  "return np.where(v < 0, -above, below), np.where(v < 0, -below, above)",
+                                  "return np.where(v < 0, -below, below), np.where(v < 0, -above, above)"),
+    "check_signed_error": ("check", "err = np.abs(y - y_ref)", "err = y - y_ref"),
+    "check_wrong_side": ("check", "np.where(y >= y_ref, hi - y_ref, y_ref - lo)",
+                         "np.where(y >= y_ref, y_ref - lo, hi - y_ref)"),
     "check_rejects_at_bound": ("check", "np.all(ratio <= 1.0)", "np.all(ratio < 1.0)"),
     "bf16_decode_wrong_shift": ("bf16_decode", "astype(np.uint32) << 16", "astype(np.uint32) << 15"),
 }

@@ -277,20 +277,49 @@ def test_empty_shapes():
     assert y.shape == (2, 3) and np.all(y == 0) and np.all(a == 0)
 
 
-def test_bf16_half_ulp_covers_exact_rounding():
-    # Every bf16 rounding of a random real lies within the half ulp the check allows.
+def _all_finite_bf16():
+    """Every finite bf16 value, sorted (decoded by torch, not the oracle)."""
+    codes = np.arange(0x10000, dtype=np.uint32)
+    v = torch.from_numpy((codes << 16).astype(np.uint32).view(np.int32)).view(torch.float32)
+    v = v.double().numpy()
+    return np.unique(v[np.isfinite(v)])
+
+
+def test_bf16_bracket_is_the_pair_of_neighbours():
+    """Brute force against the sorted table of every finite bf16 value: lo is
+    the largest value <= v, hi the smallest >= v; torch's round-to-nearest
+    result is one of them."""
+    table = _all_finite_bf16()
     rng = np.random.default_rng(2)
-    v = rng.standard_normal(20000) * 2.0 ** rng.integers(-20, 20, 20000)
+    v = rng.standard_normal(20000) * 2.0 ** rng.integers(-130, 120, 20000)
+    v = np.concatenate([v, table[rng.integers(0, len(table), 2000)], [0.0, -0.0, 1.0, -1.0]])
+    lo, hi = oracle.bf16_bracket(v)
+    want_hi = table[np.searchsorted(table, v, side="left")]
+    want_lo = table[np.searchsorted(table, v, side="right") - 1]
+    assert np.array_equal(lo, want_lo) and np.array_equal(hi, want_hi)
     r = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
-    assert np.all(np.abs(r - v) <= oracle.bf16_half_ulp(v))
-    assert oracle.bf16_half_ulp(np.array([1.0]))[0] == 2.0 ** -8
-    assert oracle.bf16_half_ulp(np.array([0.75]))[0] == 2.0 ** -9
-    ok, _, _ = oracle.check(np.array([[0.0751953125]]), np.array([[0.07497585]]),
-                            np.array([[0.09527504]]))
-    assert not ok                                   # stated bound alone: too tight here
-    ok, _, _ = oracle.check(np.array([[0.0751953125]]), np.array([[0.07497585]]),
-                            np.array([[0.09527504]]), bf16_rounding=True)
-    assert ok
+    assert np.all((r == lo) | (r == hi))
+
+
+def test_check_accepts_the_bf16_neighbours_and_nothing_further():
+    """y_ref = 0.07497585 with A = 0.09527504: the stated bound (1.92e-4) is
+    below the distance to either bf16 neighbour (0.07470703125 below,
+    0.0751953125 above, step 2^-11 there), so exactly those two pass, the
+    values one step further do not, and the same holds mirrored."""
+    step = 2.0 ** -11
+    lo_v, hi_v = 0.07470703125, 0.0751953125
+    for sign in (1.0, -1.0):
+        y_ref = np.array([[sign * 0.07497585]])
+        a = np.array([[0.09527504]])
+        for y, want in ((hi_v, True), (lo_v, True), (hi_v + step, False), (lo_v - step, False)):
+            ok, _, _ = oracle.check(np.array([[sign * y]]), y_ref, a)
+            assert ok == want, (sign, y)
+    # A bf16-valued y_ref: only itself, when the bound is below the step.
+    y_ref = np.array([[hi_v, -hi_v]])
+    a = np.full((1, 2), 0.05)
+    assert oracle.check(y_ref, y_ref, a)[0]
+    assert not oracle.check(y_ref + np.array([[step, 0.0]]), y_ref, a)[0]
+    assert not oracle.check(y_ref - np.array([[0.0, step]]), y_ref, a)[0]
 
 
 # --- greedy next token ------------------------------------------------------
@@ -299,6 +328,9 @@ def test_argmax_first_fixed_cases():
     inf, nan = np.inf, np.nan
     cases = [([[1.0, 3.0, 3.0, 2.0]], [1]),            # ties: the first
              ([[nan, -inf, -5.0]], [2]),                # NaN below every number
+             ([[nan, -inf]], [1]),                      # ... -inf included
+             ([[nan, nan, -inf, -inf]], [2]),
+             ([[-inf, nan, -inf]], [0]),
              ([[nan, nan]], [0]),                       # a row of NaNs
              ([[-inf, -inf, -inf]], [0]),
              ([[0.0, -0.0]], [0]),                      # -0 == +0: the first

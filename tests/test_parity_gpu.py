@@ -40,8 +40,7 @@ def test_bf16_random_vs_oracle(M, N, K):
     for var in variants_for(M):
         for waves in (0, 4, 28):           # forced grids: whole workgroups, at least one
             y = run_bf16(x, w, M, N, variant=var, waves=waves)
-            assert_matches_oracle(y, y_ref, a, f"bf16 M={M} N={N} K={K} var={var} waves={waves}",
-                                  strict=K >= 1000)
+            assert_matches_oracle(y, y_ref, a, f"bf16 M={M} N={N} K={K} var={var} waves={waves}")
 
 
 FP8_SHAPES = [(1, 16), (130, 272), (300, 1024), (257, 3696)]
@@ -56,8 +55,7 @@ def test_fp8_random_vs_oracle(M, N, K):
     for var in variants_for(M):
         for waves in (0, 4, 20):
             y = run_fp8(x, q, s, M, N, variant=var, waves=waves)
-            assert_matches_oracle(y, y_ref, a, f"fp8 M={M} N={N} K={K} var={var} waves={waves}",
-                                  strict=K >= 1000)
+            assert_matches_oracle(y, y_ref, a, f"fp8 M={M} N={N} K={K} var={var} waves={waves}")
 
 
 # --- pins through the GPU: exact results --------------------------------------

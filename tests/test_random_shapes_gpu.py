@@ -55,7 +55,7 @@ def test_random_dense(case):
         w = synth.tensor_bf16(0, synth.stream_id("rnd-w", i, N, K), N, K, 0.02)
         y_ref, a, _ = oracle.linear_bf16(x, w)
         y = run_bf16(x, w, M, N, variant=var, waves=waves)
-    assert_matches_oracle(y, y_ref, a, what, strict=K >= 1000)
+    assert_matches_oracle(y, y_ref, a, what)
 
 
 def _moe_cases(n=40, seed=77):
@@ -75,7 +75,25 @@ def _moe_cases(n=40, seed=77):
     return cases
 
 
-@pytest.mark.parametrize("case", _moe_cases(), ids=lambda c: "m%d" % c[0])
+def _moe_cases_swiglu_shared(n=10, seed=78):
+    """The SwiGLU input read from a shared row per token ([T][2K], not per
+    route), which the cases above never draw."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        fp8 = bool(rng.integers(2))
+        E = int(rng.integers(1, 13))
+        T = int(rng.integers(1, 17))
+        topk = int(rng.integers(1, 5))
+        step = 16 if fp8 else 8
+        K = int(np.exp(rng.uniform(np.log(64), np.log(9000)))) // step * step
+        N = int(rng.integers(16, 700))
+        cases.append((100 + i, fp8, E, T, topk, N, K, False, True))
+    return cases
+
+
+@pytest.mark.parametrize("case", _moe_cases() + _moe_cases_swiglu_shared(),
+                         ids=lambda c: "m%d" % c[0])
 def test_random_moe(case):
     i, fp8, E, T, topk, N, K, per_route, swiglu = case
     rng = np.random.default_rng(1000 + i)
@@ -89,6 +107,6 @@ def test_random_moe(case):
                           2 * K if swiglu else K, 1.0)
     y_ref, a = oracle.moe_linear(x, ids, w, scales=s, x_per_route=per_route, swiglu=swiglu)
     y = run_moe(x, ids, w, s, x_per_route=per_route, swiglu=swiglu)
-    ok, worst, idx = oracle.check(y.float().cpu().double().numpy(), y_ref, a, bf16_rounding=K < 1000)
+    ok, worst, idx = oracle.check(y.float().cpu().double().numpy(), y_ref, a)
     assert ok, (f"case {i}: {'fp8' if fp8 else 'bf16'} E={E} T={T} topk={topk} N={N} K={K} "
                 f"per_route={per_route} swiglu={swiglu}: worst err/bound {worst:.3g} at {idx}")
