@@ -52,6 +52,18 @@ WORKLOADS = {
 }
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -515,7 +527,7 @@ def main():
         result["cpu_baseline"] = {
             "value": round(sbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "sample": desc, "us_per_step": round(secs * 1e6, 1),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model()}
         result["config"]["sampled_outputs_worst_err_over_bound"] = round(worst, 4)
     elif not args.no_cpu_baseline:
         import oracle
@@ -539,7 +551,7 @@ def main():
             "kind": "oracle",
             "sample": desc,
             "us_per_step_extrapolated": round(step_bytes / (cpu_gbps * 1e9) * 1e6, 1),
-            "cpu": platform.processor() or platform.machine(),
+            "cpu": cpu_model(),
         }
         result["config"]["sampled_outputs_worst_err_over_bound"] = round(worst, 4)
     print(json.dumps(result), flush=True)

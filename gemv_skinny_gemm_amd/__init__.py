@@ -212,6 +212,32 @@ def _shape2(t):
     return int(t.shape[0]), int(t.shape[1])
 
 
+def _dtype_name(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _need(t, shape, dtypes, what):
+    """Refuse a tensor whose shape or dtype does not match what the C entry
+    point will read or write: the library sees only pointers, so a short or
+    mistyped buffer would be read or written past its end."""
+    if isinstance(t, int) or t is None:
+        return
+    if tuple(int(v) for v in t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if _dtype_name(t) not in dtypes:
+        raise ValueError(f"{what}: dtype {_dtype_name(t)}, expected one of {sorted(dtypes)}")
+
+
+_BF16 = {"bfloat16"}
+_FP8 = {"uint8", "float8_e4m3fn"}
+_F32 = {"float32"}
+_I32 = {"int32"}
+
+
+def _scale_shape(N: int, K: int):
+    return ((N + 127) // 128, (K + 127) // 128)
+
+
 def _ws(workspace):
     if workspace is None:
         return None, 0
@@ -224,6 +250,9 @@ def skinny_gemm_bf16(x, w, y, workspace, stream=None):
     """y[M][N] = x[M][K] . w[N][K]^T (bf16 tensors on the GPU; y written in place)."""
     M, K = _shape2(x)
     N, _ = _shape2(w)
+    _need(x, (M, K), _BF16, "x")
+    _need(w, (N, K), _BF16, "w")
+    _need(y, (M, N), _BF16, "y")
     wp, wb = _ws(workspace)
     _check(lib().skinny_gemm_bf16(_ptr(x), _ptr(w), _ptr(y), M, N, K, wp, wb, _stream(stream)),
            "skinny_gemm_bf16")
@@ -235,6 +264,10 @@ def skinny_gemm_fp8_bs128(x, w_fp8, w_scale, y, workspace, stream=None):
     w_scale [ceil(N/128)][ceil(K/128)] float32."""
     M, K = _shape2(x)
     N, _ = _shape2(w_fp8)
+    _need(x, (M, K), _BF16, "x")
+    _need(w_fp8, (N, K), _FP8, "w_fp8")
+    _need(w_scale, _scale_shape(N, K), _F32, "w_scale")
+    _need(y, (M, N), _BF16, "y")
     wp, wb = _ws(workspace)
     _check(lib().skinny_gemm_fp8_bs128(_ptr(x), _ptr(w_fp8), _ptr(w_scale), _ptr(y), M, N, K,
                                         wp, wb, _stream(stream)), "skinny_gemm_fp8_bs128")
@@ -242,15 +275,36 @@ def skinny_gemm_fp8_bs128(x, w_fp8, w_scale, y, workspace, stream=None):
 
 
 def make_linear(x, w, y, w_scale=None, dtype=None) -> Linear:
-    """A skinny_linear from GPU tensors x [M][K], w [N][K], y [M][N] (w_scale for FP8)."""
+    """A skinny_linear from GPU tensors x [M][K], w [N][K], y [M][N] (w_scale for FP8).
+
+    Shapes and dtypes are checked here; the Linear remembers M (as ``rows``)
+    so that a call with another M is refused before it reaches the library."""
     N, K = _shape2(w)
     if dtype is None:
         dtype = FP8_BS128 if w_scale is not None else BF16
-    return Linear(dtype, N, K, 0, _ptr(w), _ptr(w_scale), _ptr(x), _ptr(y))
+    M = None
+    if not isinstance(x, int):
+        M, _ = _shape2(x)
+        _need(x, (M, K), _BF16, "x")
+        _need(y, (M, N), _BF16, "y")
+    _need(w, (N, K), _BF16 if dtype == BF16 else _FP8, "w")
+    if dtype == FP8_BS128:
+        _need(w_scale, _scale_shape(N, K), _F32, "w_scale")
+    lin = Linear(dtype, N, K, 0, _ptr(w), _ptr(w_scale), _ptr(x), _ptr(y))
+    lin.rows = M
+    return lin
+
+
+def _check_rows(linears, M: int):
+    for L in linears:
+        rows = getattr(L, "rows", None)
+        if rows is not None and rows != M:
+            raise ValueError(f"a linear made for M = {rows} called with M = {M}")
 
 
 def decode_linear_stack(linears, M: int, workspace, stream=None):
     """Run independent linears (a list of Linear) that share M."""
+    _check_rows(linears, M)
     arr = _linear_array(linears)
     wp, wb = _ws(workspace)
     _check(lib().decode_linear_stack(arr, len(linears), M, wp, wb, _stream(stream)),
@@ -260,6 +314,7 @@ def decode_linear_stack(linears, M: int, workspace, stream=None):
 def linear_run(linears, M: int, workspace, variant: int = VARIANT_AUTO, waves: int = 0,
                stream=None):
     """decode_linear_stack with a forced variant and/or persistent wave count."""
+    _check_rows(linears, M)
     arr = _linear_array(linears)
     plan = Plan(variant, waves)
     wp, wb = _ws(workspace)
@@ -281,6 +336,7 @@ def linear_run_timed(linears, M: int, workspace, events, variant: int = VARIANT_
                      waves: int = 0, stream=None):
     """linear_run recording events[2g] / events[2g+1] (hipEvent_t addresses) around
     main-kernel launch g."""
+    _check_rows(linears, M)
     arr = _linear_array(linears)
     plan = Plan(variant, waves)
     ev = (ctypes.c_void_p * len(events))(*events)
@@ -304,6 +360,8 @@ def argmax_bf16(y, idx, workspace, stream=None):
     """idx[m] = smallest index of the largest value of y[m] (bf16 [M][N] and
     int32 [M] tensors on the GPU; idx written in place)."""
     M, N = _shape2(y)
+    _need(y, (M, N), _BF16, "y")
+    _need(idx, (M,), _I32, "idx")
     wp, wb = _ws(workspace)
     _check(lib().skinny_argmax_bf16(_ptr(y), M, N, _ptr(idx), wp, wb, _stream(stream)),
            "skinny_argmax_bf16")
@@ -317,6 +375,8 @@ def lm_head_workspace_bytes(head: Linear, M: int) -> int:
 def lm_head_argmax(head: Linear, M: int, next_token, workspace, stream=None):
     """Run the vocabulary projection `head` (its y = logits) and write the
     greedy token of each of the M rows into next_token (int32 [M] on the GPU)."""
+    _check_rows([head], M)
+    _need(next_token, (M,), _I32, "next_token")
     arr = _linear_array([head])
     wp, wb = _ws(workspace)
     _check(lib().skinny_lm_head_argmax(arr, M, _ptr(next_token), wp, wb, _stream(stream)),
@@ -329,8 +389,21 @@ def make_mlp(x, w_gate_up, w_down, y, s_gate_up=None, s_down=None) -> Mlp:
     first), w_down [H][I], y [M][H] (scales for FP8)."""
     H, I = _shape2(w_down)
     dtype = FP8_BS128 if s_gate_up is not None else BF16
-    return Mlp(dtype, H, I, 0, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down), _ptr(s_down),
-               _ptr(x), _ptr(y))
+    wd = _BF16 if dtype == BF16 else _FP8
+    _need(w_gate_up, (2 * I, H), wd, "w_gate_up")
+    _need(w_down, (H, I), wd, "w_down")
+    if dtype == FP8_BS128:
+        _need(s_gate_up, _scale_shape(2 * I, H), _F32, "s_gate_up")
+        _need(s_down, _scale_shape(H, I), _F32, "s_down")
+    M = None
+    if not isinstance(x, int):
+        M, _ = _shape2(x)
+        _need(x, (M, H), _BF16, "x")
+        _need(y, (M, H), _BF16, "y")
+    mlp = Mlp(dtype, H, I, 0, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down), _ptr(s_down),
+              _ptr(x), _ptr(y))
+    mlp.rows = M
+    return mlp
 
 
 def mlp_workspace_bytes(mlp: Mlp, M: int) -> int:
@@ -339,6 +412,7 @@ def mlp_workspace_bytes(mlp: Mlp, M: int) -> int:
 
 def mlp_swiglu(mlp: Mlp, M: int, workspace, stream=None):
     """y = down(silu(gate) * up) with [gate | up] = x . W_gate_up^T."""
+    _check_rows([mlp], M)
     wp, wb = _ws(workspace)
     _check(lib().skinny_mlp_swiglu(ctypes.byref(mlp), M, wp, wb, _stream(stream)),
            "skinny_mlp_swiglu")
@@ -350,11 +424,22 @@ def make_experts(w, w_scale=None) -> Experts:
     if isinstance(w, int) or w.dim() != 3:
         raise ValueError("w must be a 3-D tensor [E][N][K]")
     E, N, K = (int(v) for v in w.shape)
+    _need(w, (E, N, K), _BF16 if w_scale is None else _FP8, "w")
+    if w_scale is not None:
+        _need(w_scale, (E, *_scale_shape(N, K)), _F32, "w_scale")
     return Experts(FP8_BS128 if w_scale is not None else BF16, E, N, K, _ptr(w), _ptr(w_scale))
 
 
 def _moe_flags(x_per_route: bool, swiglu: bool) -> int:
     return (MOE_X_PER_ROUTE if x_per_route else 0) | (MOE_SWIGLU if swiglu else 0)
+
+
+def _check_moe(experts: Experts, x, ids, y, x_per_route: bool, swiglu: bool):
+    T, topk = _shape2(ids)
+    _need(ids, (T, topk), _I32, "ids")
+    _need(x, ((T * topk if x_per_route else T), (2 if swiglu else 1) * experts.K), _BF16, "x")
+    _need(y, (T * topk, experts.N), _BF16, "y")
+    return T, topk
 
 
 def moe_workspace_bytes(experts: Experts, T: int, topk: int, x_per_route: bool = False,
@@ -368,7 +453,7 @@ def moe_linear(experts: Experts, x, ids, y, workspace, x_per_route: bool = False
     """y[t * topk + j] = x_r . W_{ids[t][j]}^T for the T x topk routes of ids
     (int32 [T][topk] on the GPU); x_r = x[t], or x[r] with x_per_route, or
     silu(g) * u of that row [g | u] with swiglu."""
-    T, topk = _shape2(ids)
+    T, topk = _check_moe(experts, x, ids, y, x_per_route, swiglu)
     wp, wb = _ws(workspace)
     _check(lib().skinny_moe_linear(ctypes.byref(experts), _ptr(x), _ptr(ids), T, topk,
                                    _moe_flags(x_per_route, swiglu), _ptr(y), wp, wb,
@@ -380,7 +465,7 @@ def moe_linear_timed(experts: Experts, x, ids, y, workspace, events, x_per_route
                      swiglu: bool = False, stream=None):
     """moe_linear recording the two hipEvent_t handles in `events` around its
     main launch."""
-    T, topk = _shape2(ids)
+    T, topk = _check_moe(experts, x, ids, y, x_per_route, swiglu)
     wp, wb = _ws(workspace)
     ev = (ctypes.c_void_p * 2)(*events)
     _check(lib().skinny_moe_linear_timed(ctypes.byref(experts), _ptr(x), _ptr(ids), T, topk,

@@ -964,14 +964,16 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_moe_combine(const Laun
 // workgroup (b, m) of the first reduces slice b of row m (kArgmaxSlice
 // logits) to one (value, index) pair in the workspace; the second reduces
 // each row's pairs.  Pairs are ordered by value, then by lower index, so
-// the result does not depend on the reduction order.  NaN compares below
-// every number.
+// the result does not depend on the reduction order.  NaN ranks below every
+// number, -inf included: a NaN is never taken, and a pair that has seen no
+// number keeps the index N, which loses to every real index; a row of NaNs
+// ends with N and gives 0.
 constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxSlice = 4096;                    // logits per first-pass workgroup
 constexpr int kArgmaxMaxSlices = 1 << 20;
 
 __device__ __forceinline__ void argmax_take(float v, int i, float& bv, int& bi) {
-  if (v != v) v = -__builtin_inff();
+  if (v != v) return;
   if (v > bv || (v == bv && i < bi)) {
     bv = v;
     bi = i;
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void skinny_argmax_rows(const Argma
     argmax_take(p.v, p.i, bv, bi);
   }
   argmax_block(bv, bi);
-  if (threadIdx.x == 0) idx[m] = bi;
+  if (threadIdx.x == 0) idx[m] = bi < N ? bi : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1105,13 +1107,27 @@ struct Range {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// The buffers a call writes (every y and the workspace) must not overlap
+// anything else it reads or writes.
 skinny_status check_outputs(const skinny_linear* lin, int count, int M, const void* ws,
                             size_t ws_bytes) {
+  const Range wsr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = lin[i];
     Range y{(uintptr_t)L.y, (uintptr_t)L.y + (size_t)M * L.N * 2};
-    Range wsr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
     if (overlap(y, wsr)) return SKINNY_ERR_INVALID_ARG;
+    {
+      const size_t wbytes = (size_t)L.N * L.K * (L.dtype == SKINNY_BF16 ? 2 : 1);
+      const size_t xbytes = (size_t)M * L.K * 2 * (L.reserved == kActSwiGLU ? 2 : 1);
+      if (overlap(wsr, Range{(uintptr_t)L.x, (uintptr_t)L.x + xbytes}) ||
+          overlap(wsr, Range{(uintptr_t)L.w, (uintptr_t)L.w + wbytes}))
+        return SKINNY_ERR_INVALID_ARG;
+      if (L.w_scale) {
+        const size_t sb = (size_t)((L.N + 127) / 128) * ((L.K + 127) / 128) * 4;
+        if (overlap(wsr, Range{(uintptr_t)L.w_scale, (uintptr_t)L.w_scale + sb}))
+          return SKINNY_ERR_INVALID_ARG;
+      }
+    }
     for (int j = 0; j < count; ++j) {
       const skinny_linear& O = lin[j];
       const size_t wbytes = (size_t)O.N * O.K * (O.dtype == SKINNY_BF16 ? 2 : 1);

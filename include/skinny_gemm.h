@@ -38,10 +38,11 @@
  *   alive until the work on `stream` has finished.  The library allocates
  *   nothing and keeps no pointer after a call returns.  Host arrays passed in
  *   (the `linears` of a stack) are read during the call only.  y must not
- *   overlap x, W, w_scale, the workspace or another call's y.  Calls enqueue
- *   work on `stream` (a hipStream_t; NULL is the default stream) and return
- *   without waiting for it; execution faults surface at the caller's next
- *   synchronization.  Calls on different streams need separate workspaces.
+ *   overlap x, W, w_scale, the workspace or another linear's y, and the
+ *   workspace must not overlap x, W or w_scale (checked:
+ *   SKINNY_ERR_INVALID_ARG).  Calls enqueue work on `stream` (a hipStream_t;
+ *   NULL is the default stream) and return without waiting for it; execution
+ *   faults surface at the caller's next synchronization.  Calls on different streams need separate workspaces.
  *   Workspace contents are undefined after a call.  Entry points may be
  *   called from several host threads at once: the library's only shared
  *   state is a per-device cache of device properties, occupancy results and
@@ -105,7 +106,12 @@ typedef struct skinny_plan {
  * The workspace holds the fp32 partial sums of K-chunks that the second pass
  * adds: for every row group of a linear that the launch splits into C > 1
  * K-chunks, C slots of [M][band rows] floats.  The value covers the largest
- * split either variant may choose. */
+ * split either variant may choose.  The split is the long dimension cut
+ * across workgroups so that a skinny launch still streams on the whole chip
+ * ("9% faster GLM-5.3-Flash prefill with GPU-to-GPU IPC (and why TileLang
+ * didn't help)", section "TileLang: twice as fast, and no faster"); a
+ * K-split's partial results add up to the product ("Multi-GPU Inference and
+ * Serving at Scale", Example 3, the row-split second linear). */
 size_t skinny_workspace_bytes(int dtype, int M, int N, int K);
 
 /* Bytes of workspace decode_linear_stack needs for these linears at this M. */
@@ -121,11 +127,21 @@ skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const floa
                                     size_t workspace_bytes, void* stream);
 
 /* Runs `count` independent linears that share M, e.g. the QKV, O, gate_up
- * and down projections of every decoder layer.  Each linear reads its own x
- * and writes its own y; no y may overlap any x, W, w_scale or other y (checked).
- * The linears are streamed by one persistent launch per
- * SKINNY_MAX_LINEARS_PER_LAUNCH group and each group's split-K partial sums
- * are combined by a second, deterministic pass. */
+ * and down projections of every decoder layer: the decode step streams every
+ * layer's weights once per generated token ("Developing a custom Qwen2.5 72B
+ * inference engine from scratch - what is the real bottleneck?", section 1
+ * (80 layers, each with attention and MLP projections) and section 2 "The
+ * two-phase reality" (decode reads the whole model from HBM per token)).
+ *   linears    host array of `count` >= 1 skinny_linear, read during the call
+ *   M          tokens, 1..SKINNY_MAX_M, the rows of every x and y
+ *   workspace  device, 16-byte aligned, >= skinny_stack_workspace_bytes(linears,
+ *              count, M); contents undefined afterwards
+ * Each linear reads its own x and writes its own y; no y may overlap any x,
+ * W, w_scale, other y or the workspace (checked).  Linears are grouped by
+ * dtype in call order and streamed by one persistent launch per
+ * SKINNY_MAX_LINEARS_PER_LAUNCH group; each group's split-K partial sums are
+ * combined by a second, deterministic pass.  Errors (any linear failing the
+ * checks of a single linear) are returned before anything is enqueued. */
 skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
@@ -165,8 +181,8 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);
 
 /* Greedy next token: idx[m] = the smallest n such that y[m][n] is the largest
- * of y[m][0..N), comparing the bf16 values (NaN compares below every number,
- * so a row of NaNs gives 0).  This is the decode step's on-device argmax
+ * of y[m][0..N), comparing the bf16 values (NaN ranks below every number,
+ * -inf included, so a row of NaNs gives 0).  This is the decode step's on-device argmax
  * ("Developing a custom Qwen2.5 72B inference engine from scratch - what is
  * the real bottleneck?", section 5, third lever: pick the next token on the
  * GPU rather than copying the logits back to the host).

@@ -96,6 +96,8 @@ def fp8_call(x=B, w=A, s=0x300000, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
     (dict(y=B), INVALID),                       # y overlaps x
     (dict(y=A + 64), INVALID),                  # y inside W
     (dict(y=WS + 128), INVALID),                # y inside the workspace
+    (dict(x=WS + 128), INVALID),                # x inside the workspace
+    (dict(w=WS - 64), INVALID),                 # W runs into the workspace
 ])
 def test_bf16_rejects_bad_arguments(kw, status):
     assert bf16_call(**kw) == status
@@ -104,6 +106,7 @@ def test_bf16_rejects_bad_arguments(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(s=None), INVALID), (dict(K=24), UNSUPPORTED), (dict(s=0x300002), UNSUPPORTED),
     (dict(M=17), INVALID), (dict(wsb=0), WORKSPACE),
+    (dict(s=WS + 64), INVALID),                 # scales inside the workspace
 ])
 def test_fp8_rejects_bad_arguments(kw, status):
     assert fp8_call(**kw) == status
@@ -226,6 +229,71 @@ def test_binding_rejects_host_and_strided_tensors():
         sg.make_linear(x, torch.zeros((64, 32), dtype=torch.bfloat16).t(), y)
     with pytest.raises(ValueError, match="on the GPU"):
         sg.skinny_gemm_bf16(x, w, y, torch.zeros(1024, dtype=torch.uint8))
+
+
+def test_binding_rejects_mismatched_shapes_and_dtypes():
+    """The library sees only pointers, so the binding compares every tensor's
+    shape and dtype with what the entry point will read or write, before
+    anything reaches the C library (CPU tensors: the shape check comes first)."""
+    import torch
+    bf, u8, f32, i32 = torch.bfloat16, torch.uint8, torch.float32, torch.int32
+    x = torch.zeros((2, 64), dtype=bf)
+    w = torch.zeros((32, 64), dtype=bf)
+    y = torch.zeros((2, 32), dtype=bf)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    bad_linears = [
+        dict(x=torch.zeros((2, 48), dtype=bf)),                  # K of x != K of w
+        dict(y=torch.zeros((1, 32), dtype=bf)),                  # too few rows of y
+        dict(y=torch.zeros((2, 31), dtype=bf)),                  # y narrower than N
+        dict(x=torch.zeros((2, 64), dtype=torch.float16)),
+        dict(y=torch.zeros((2, 32), dtype=f32)),
+        dict(w=torch.zeros((32, 64), dtype=f32)),
+    ]
+    for kw in bad_linears:
+        a = {**dict(x=x, w=w, y=y), **kw}
+        with pytest.raises(ValueError, match="shape|dtype"):
+            sg.make_linear(a["x"], a["w"], a["y"])
+        with pytest.raises(ValueError, match="shape|dtype"):
+            sg.skinny_gemm_bf16(a["x"], a["w"], a["y"], ws)
+    q = torch.zeros((32, 64), dtype=u8)
+    with pytest.raises(ValueError, match="w_scale: shape"):
+        sg.make_linear(x, q, y, w_scale=torch.zeros((1, 2), dtype=f32))
+    with pytest.raises(ValueError, match="w_scale: dtype"):
+        sg.skinny_gemm_fp8_bs128(x, q, torch.zeros((1, 1), dtype=torch.float64), y, ws)
+    with pytest.raises(ValueError, match="w: dtype"):
+        sg.make_linear(x, w, y, w_scale=torch.zeros((1, 1), dtype=f32))   # bf16 codes as FP8
+    # A linear remembers its M: another M is refused.
+    lin = sg.Linear(sg.BF16, 32, 64, 0, A, None, B, C)
+    lin.rows = 2
+    with pytest.raises(ValueError, match="M = 2 called with M = 3"):
+        sg.decode_linear_stack([lin], 3, (WS, 1 << 20))
+    with pytest.raises(ValueError, match="idx: shape"):
+        sg.argmax_bf16(y, torch.zeros(3, dtype=i32), ws)
+    with pytest.raises(ValueError, match="idx: dtype"):
+        sg.argmax_bf16(y, torch.zeros(2, dtype=torch.int64), ws)
+    # Gated MLP: x [M][H], y [M][H], w_gate_up [2I][H], w_down [H][I].
+    H, I = 64, 32
+    wg, wd = torch.zeros((2 * I, H), dtype=bf), torch.zeros((H, I), dtype=bf)
+    xm, ym = torch.zeros((2, H), dtype=bf), torch.zeros((2, H), dtype=bf)
+    with pytest.raises(ValueError, match="w_gate_up: shape"):
+        sg.make_mlp(xm, torch.zeros((I, H), dtype=bf), wd, ym)
+    with pytest.raises(ValueError, match="y: shape"):
+        sg.make_mlp(xm, wg, wd, torch.zeros((2, I), dtype=bf))
+    # MoE: x [T or T*topk][K or 2K], ids int32 [T][topk], y [T*topk][N].
+    E, N, K = 3, 32, 64
+    ex = sg.Experts(sg.BF16, E, N, K, A, None)
+    ids = torch.zeros((2, 2), dtype=i32)
+    xs, yr = torch.zeros((2, K), dtype=bf), torch.zeros((4, N), dtype=bf)
+    for kw, what in ((dict(x=torch.zeros((4, K), dtype=bf)), "x: shape"),          # per-route rows, shared flag
+                     (dict(y=torch.zeros((2, N), dtype=bf)), "y: shape"),           # a row per token, not per route
+                     (dict(ids=torch.zeros((2, 2), dtype=torch.int64)), "ids: dtype")):
+        a = {**dict(x=xs, ids=ids, y=yr), **kw}
+        with pytest.raises(ValueError, match=what):
+            sg.moe_linear(ex, a["x"], a["ids"], a["y"], ws)
+    with pytest.raises(ValueError, match="x: shape"):
+        sg.moe_linear(ex, xs, ids, yr, ws, swiglu=True)                              # needs 2K columns
+    with pytest.raises(ValueError, match="w: shape|w: dtype"):
+        sg.make_experts(torch.zeros((E, N, K), dtype=u8))                            # FP8 codes without scales
 
 
 def test_moe_plan_query():

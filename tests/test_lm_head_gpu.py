@@ -58,6 +58,42 @@ def test_argmax_matches_oracle_exactly(M, N, aligned):
     assert idx.cpu().numpy().tolist() == want.tolist()
 
 
+NAN, NEG_INF = 0x7FC0, 0xFF80
+
+
+@pytest.mark.parametrize("aligned", [True, False])
+def test_argmax_nan_ranks_below_minus_infinity(aligned):
+    """NaN loses to every number, -inf included, inside a slice of the first
+    pass and across slices (a slice of NaNs against a later slice's -inf); a
+    row of NaNs gives 0."""
+    N = 9000                                                # three 4096-logit slices
+    rows = []
+    for head in ([NAN, NEG_INF], [NAN, NAN, NEG_INF, NEG_INF], [NEG_INF, NAN, NEG_INF], []):
+        r = np.full(N, NAN, np.uint16)
+        r[:len(head)] = head
+        rows.append(r)
+    r = np.full(N, NAN, np.uint16)
+    r[5000] = NEG_INF                                       # the first number is in slice 1
+    r[8999] = NEG_INF
+    rows.append(r)
+    r = np.full(N, NEG_INF, np.uint16)
+    r[:4096] = NAN                                          # slice 0 all NaN
+    rows.append(r)
+    codes = np.stack(rows)
+    M = codes.shape[0]
+    want = oracle.argmax_first(bf16_values(codes))
+    assert want.tolist() == [1, 2, 0, 0, 5000, 4096]
+    flat = np.zeros(M * N + 8, np.uint16)
+    off = 0 if aligned else 1
+    flat[off:off + M * N] = codes.reshape(-1)
+    y = dev_bf16(flat)[off:off + M * N].view(M, N)
+    idx = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(sg.argmax_workspace_bytes(M, N), dtype=torch.uint8, device="cuda")
+    sg.argmax_bf16(y, idx, ws)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().tolist() == want.tolist()
+
+
 def test_lm_head_one_hot_rows_pick_exactly():
     """W row n = one-hot at column perm[n]: the logits are x[:, perm] exactly,
     so the greedy token is decided exactly."""
