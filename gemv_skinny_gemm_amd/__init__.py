@@ -15,7 +15,7 @@ __all__ = [
     "BF16", "FP8_BS128", "VARIANT_AUTO", "VARIANT_VECTOR", "VARIANT_MFMA", "MAX_M",
     "SkinnyError", "Linear", "Plan", "lib", "lib_path",
     "workspace_bytes", "stack_workspace_bytes", "skinny_gemm_bf16", "skinny_gemm_fp8_bs128",
-    "decode_linear_stack", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
+    "decode_linear_stack", "decode_linear_stack_noalloc", "STATIC_SCRATCH_BYTES", "linear_run", "linear_run_timed", "launch_count", "band_rows", "plan_query",
     "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
     "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
     "Experts", "make_experts", "moe_workspace_bytes", "moe_linear", "moe_linear_timed",
@@ -34,6 +34,7 @@ MAX_TOPK = 16
 MOE_X_PER_ROUTE = 1
 MOE_SWIGLU = 2
 ABI_VERSION = 1
+STATIC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libskinny_gemm.so"
@@ -97,6 +98,8 @@ def _bind(path: str):
     L.skinny_gemm_fp8_bs128.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     L.decode_linear_stack.restype = i
     L.decode_linear_stack.argtypes = [lp, i, i, vp, sz, vp]
+    L.decode_linear_stack_noalloc.restype = i
+    L.decode_linear_stack_noalloc.argtypes = [lp, i, i, vp]
     L.skinny_linear_run.restype = i
     L.skinny_linear_run.argtypes = [lp, i, i, ctypes.POINTER(Plan), vp, sz, vp]
     L.skinny_launch_count.restype = i
@@ -309,6 +312,16 @@ def decode_linear_stack(linears, M: int, workspace, stream=None):
     wp, wb = _ws(workspace)
     _check(lib().decode_linear_stack(arr, len(linears), M, wp, wb, _stream(stream)),
            "decode_linear_stack")
+
+
+def decode_linear_stack_noalloc(linears, M: int, stream=None):
+    """decode_linear_stack without a workspace: the partial sums go to the
+    library's static device buffer (STATIC_SCRATCH_BYTES per GPU), shared by
+    every call on that GPU, so calls that may overlap on one GPU race."""
+    _check_rows(linears, M)
+    arr = _linear_array(linears)
+    _check(lib().decode_linear_stack_noalloc(arr, len(linears), M, _stream(stream)),
+           "decode_linear_stack_noalloc")
 
 
 def linear_run(linears, M: int, workspace, variant: int = VARIANT_AUTO, waves: int = 0,

@@ -2005,6 +2005,33 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   return SKINNY_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Split-K partial sums without a caller's workspace: a static device buffer
+// of SKINNY_STATIC_SCRATCH_BYTES that every GPU the library runs on holds
+// from the code object's load until the process ends.  In host code the
+// array's name is not a device address: its address on a device comes from
+// hipGetSymbolAddress with that device current, resolved on the first call
+// on the device and kept per device; only that address is passed to kernels.
+// The partial-sum slots are written before the second pass reads them, so
+// the buffer needs no clearing between calls.
+static __device__ __align__(256) unsigned char scratch[SKINNY_STATIC_SCRATCH_BYTES];
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+skinny_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SKINNY_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SKINNY_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SKINNY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2062,6 +2089,26 @@ skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const floa
 skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M,
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return run(linears, count, M, nullptr, workspace, workspace_bytes, stream);
+}
+
+skinny_status decode_linear_stack_noalloc(const skinny_linear* linears, int count, int M,
+                                          void* stream) {
+  // Argument and size errors are returned before any device call.
+  if (!linears || count < 1 || M < 1 || M > SKINNY_MAX_M) return SKINNY_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    skinny_status st = check_linear(linears[i], M);
+    if (st != SKINNY_OK) return st;
+  }
+  if (required_workspace(linears, count, M) > (size_t)SKINNY_STATIC_SCRATCH_BYTES)
+    return SKINNY_ERR_WORKSPACE;
+  DeviceInfo d;
+  skinny_status st = device_info(&d);
+  if (st != SKINNY_OK) return st;
+  if (!d.gfx950) return SKINNY_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SKINNY_OK) return st;
+  return run(linears, count, M, nullptr, ws, SKINNY_STATIC_SCRATCH_BYTES, stream);
 }
 
 skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,

@@ -145,6 +145,25 @@ skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const floa
 skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* decode_linear_stack for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the split-K partial sums go to a static
+ * device buffer of SKINNY_STATIC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends.  Nothing is allocated on the call
+ * path (the first call on a device only looks up the buffer's address there).
+ *   A call is accepted only if skinny_stack_workspace_bytes(linears, count, M)
+ *   <= SKINNY_STATIC_SCRATCH_BYTES (a bound from the shapes alone, so the
+ *   same call is accepted on every device); otherwise SKINNY_ERR_WORKSPACE,
+ *   returned before anything is enqueued.  Every other argument rule and
+ *   error is that of decode_linear_stack.
+ *   All calls on one GPU share its buffer, which keeps the last call's
+ *   contents: calls on one stream are ordered and safe, but calls that may
+ *   overlap on one GPU (other streams, other host threads) race on it and
+ *   give wrong results.  No part of the buffer needs to start at zero. */
+#define SKINNY_STATIC_SCRATCH_BYTES (64u << 20)
+skinny_status decode_linear_stack_noalloc(const skinny_linear* linears, int count, int M,
+                                          void* stream);
+
 /* decode_linear_stack with an explicit plan (plan may be NULL = automatic). */
 skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
                                 const skinny_plan* plan, void* workspace,

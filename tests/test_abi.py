@@ -136,6 +136,29 @@ def test_stack_rejects_bad_arguments():
     assert L.skinny_linear_run(one, 1, 1, ctypes.byref(plan), WS, wsb, None) == INVALID
 
 
+def test_noalloc_stack_rejects_before_any_device_call():
+    """The allocation-free stack accepts a call only if its workspace bound
+    fits the static buffer; argument and size errors come back before any
+    device call (these fake addresses are never used)."""
+    L = sg.lib()
+    m = re.search(r"#define\s+SKINNY_STATIC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == sg.STATIC_SCRATCH_BYTES
+    shapes = [(10240, 8192), (8192, 8192), (59136, 8192), (8192, 29568)] * 8   # 8 TP=1 layers
+    big = [sg.Linear(sg.BF16, N, K, 0, A, None, B, C) for N, K in shapes]
+    assert sg.stack_workspace_bytes(big, 16) > sg.STATIC_SCRATCH_BYTES
+    assert sg.stack_workspace_bytes(big, 1) <= sg.STATIC_SCRATCH_BYTES
+    arr = (sg.Linear * len(big))(*big)
+    assert L.decode_linear_stack_noalloc(arr, len(big), 16, None) == WORKSPACE
+    with pytest.raises(sg.SkinnyError, match="WORKSPACE"):
+        sg.decode_linear_stack_noalloc(big, 16, stream=0)
+    one = (sg.Linear * 1)(sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C))
+    assert L.decode_linear_stack_noalloc(one, 1, 0, None) == INVALID
+    assert L.decode_linear_stack_noalloc(one, 0, 1, None) == INVALID
+    assert L.decode_linear_stack_noalloc(None, 1, 1, None) == INVALID
+    bad = (sg.Linear * 1)(sg.Linear(sg.BF16, 64, 12, 0, A, None, B, C))
+    assert L.decode_linear_stack_noalloc(bad, 1, 1, None) == UNSUPPORTED
+
+
 def test_band_rows_and_launch_counts():
     for dt in (sg.BF16, sg.FP8_BS128):
         for M in (1, 2, 6, 16):
