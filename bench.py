@@ -84,9 +84,12 @@ def parse():
     p.add_argument("--batches", type=int, default=7,
                    help="event-bracketed batches inside the timed region (median / min / max)")
     p.add_argument("--read-reference-gib", type=int, default=8,
-                   help="after timing, time PyTorch's sum over an int64 tensor of this many GiB: "
-                        "a plain streaming read by a library kernel, reported as context "
-                        "(0 = skip)")
+                   help="after timing, measure the HBM read ceiling on a buffer of this many "
+                        "GiB: the streaming-read probe's patterns and PyTorch's int64 sum, "
+                        "reported as context (0 = skip)")
+    p.add_argument("--probe-only", action="store_true",
+                   help="only measure the HBM read ceiling (the arithmetic-free streaming-read "
+                        "probe and PyTorch's sum over the same buffer) and print it as JSON")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=2048)
     p.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -259,6 +262,51 @@ def cpu_baseline(specs, M, rows, seed=0, repeats=5):
     return total_s, total_b, threads, refs, desc
 
 
+# The streaming-read probe's configurations (gemv_skinny_gemm_amd/probe):
+# (label, order, row bytes, KB per batch, waves per CU).  Measured on MI355X
+# over orders, row sizes, batch depths and grid sizes, reads stream fastest
+# with about 32 KB in flight per CU in a compact window of addresses; the
+# last line is the pattern of a deep row-streaming kernel (16 waves per CU,
+# 8 KB batches), for contrast.
+PROBE_CONFIGS = [
+    ("32 KB rows to 4-wave workgroups, waves interleaving 2 KB batches, 8 waves/CU",
+     1, 32 << 10, 2, 8),
+    ("8 KB rows to waves, 2 KB batches, 8 waves/CU", 0, 8 << 10, 2, 8),
+    ("16 KB rows to waves, 8 KB batches, 16 waves/CU", 0, 16 << 10, 8, 16),
+]
+
+
+def read_ceiling(gib: int, stream) -> dict:
+    """The HBM read ceiling on this GPU: the probe's configurations and
+    PyTorch's reduction kernel, each streaming the same buffer of `gib` GiB
+    (10 timed passes after 2 untimed ones)."""
+    import torch
+    from gemv_skinny_gemm_amd import probe
+    n = gib << 30
+    t = torch.ones(n // 8, dtype=torch.int64, device="cuda")
+    out = {"bytes": n, "probe": []}
+    for label, order, row, u, wpc in PROBE_CONFIGS:
+        gbps = probe.measure(t, row, order, u, wpc, reps=10)
+        out["probe"].append({"pattern": label, "gbps": round(gbps, 1)})
+    out["probe_best_gbps"] = max(p["gbps"] for p in out["probe"])
+    for _ in range(3):
+        t.sum()
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(10):
+        t.sum()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    out["torch_sum_gbps"] = round(n / (r0.elapsed_time(r1) / 10 * 1e-3) / 1e9, 1)
+    out["what"] = ("arithmetic-free streaming reads (gemv_skinny_gemm_amd/probe) and PyTorch's "
+                   "int64 sum over the same buffer: the HBM read ceiling this library is held "
+                   "against, not this library")
+    del t
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -281,6 +329,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.probe_only:
+        gib = args.read_reference_gib or 8
+        print(json.dumps({"read_ceiling": read_ceiling(gib, torch.cuda.current_stream()),
+                          "gpu": torch.cuda.get_device_name(0)}), flush=True)
+        return
     sg.lib()
     M = args.m
     specs = make_workload(args.workload)
@@ -482,23 +535,9 @@ def main():
     }
 
     if args.read_reference_gib:
-        n = args.read_reference_gib << 30
-        t = torch.ones(n // 8, dtype=torch.int64, device="cuda")
-        for _ in range(3):
-            t.sum()
-        torch.cuda.synchronize()
-        r0 = torch.cuda.Event(enable_timing=True)
-        r1 = torch.cuda.Event(enable_timing=True)
-        r0.record(stream)
-        for _ in range(10):
-            t.sum()
-        r1.record(stream)
-        torch.cuda.synchronize()
-        result["config"]["read_reference"] = {
-            "what": "torch.sum over an int64 tensor (PyTorch's reduction kernel: a plain "
-                    "streaming read), context for the HBM ceiling, not this library",
-            "bytes": n, "gbps": round(n / (r0.elapsed_time(r1) / 10 * 1e-3) / 1e9, 1)}
-        del t
+        rc = read_ceiling(args.read_reference_gib, stream)
+        result["config"]["read_ceiling"] = rc
+        result["config"]["pct_of_read_ceiling"] = round(100 * gbps / rc["probe_best_gbps"], 1)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib << 19                 # bf16 elements

@@ -3,6 +3,8 @@
 libskinny_gemm.so          the C-ABI library (kernels + host entry points)
 synth/libskinny_synth.so   the GPU twin of the seeded input generator (test and
                            benchmark data only; shares no code with the library)
+probe/libskinny_probe.so   an arithmetic-free streaming read, the HBM read
+                           ceiling bench.py reports beside the library's rate
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ COMMON = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
 LIBS = {
     "libskinny_gemm.so": [os.path.join(CSRC, "skinny_gemm.hip")],
     os.path.join("synth", "libskinny_synth.so"): [os.path.join(PKG, "synth", "synth_gpu.hip")],
+    os.path.join("probe", "libskinny_probe.so"): [os.path.join(PKG, "probe", "stream_read.hip")],
 }
 
 

@@ -1160,6 +1160,19 @@ constexpr int rows_r(int M) { return M <= 2 ? 1 : M <= 4 ? 2 : 4; }
 constexpr int rows_u(int M, int dtype) {
   return (dtype == SKINNY_BF16 ? (M == 2 ? 4 : 8) : 4) / rows_r(M);
 }
+// The lean instance for large bf16 launches: 2 KB batches (2 / R segments
+// of R rows) and one 8-wave workgroup per CU, so about 32 KB of loads are in
+// flight per CU instead of ~6x that.  Measured on MI355X with an
+// arithmetic-free read probe, HBM reads stream fastest (6.5 TB/s) with about
+// 32 KB in flight per CU: less leaves latency exposed, more loses ~5% (the
+// memory system serves a wider window of addresses at once).  On an 8-layer
+// TP=1 launch the lean instance streams 6.49 against 6.20 TB/s (M = 1) and
+// 6.38 against 6.09 (M = 2); a launch too small to fill the chip needs the
+// deeper instance to cover latency (TP=8 layer at M = 1: 48.0 against 40.9
+// us), hence a minimum launch size.
+constexpr int rows_u_lean(int M) { return M <= 2 ? 2 : M <= 4 ? 1 : 0; }
+constexpr int kRowsLeanWavesPerCU = 8;
+constexpr double kRowsLeanLaunchBytes = 0.4e9;     // weight bytes of one launch
 constexpr int kRowsXBudget = 64 * 1024;   // LDS for x per workgroup: two workgroups per CU
 constexpr int kRowsMaxM = 8;
 // Units per workgroup below which a launch cuts K into more chunks for
@@ -1334,6 +1347,7 @@ struct KernelChoice {
   int band_rows = 0;           // rows per row group
   int wpb = 0;                 // waves per workgroup
   bool tiles = false;          // skinny_tiles (else skinny_rows)
+  int waves_per_cu = kTargetRowsWavesPerCU;   // cap on the persistent grid
 };
 
 template <int DT, int WPB>
@@ -1359,6 +1373,34 @@ KernelChoice rows_kernel() {
   k.band_rows = WPB * R;
   k.wpb = WPB;
   return k;
+}
+
+template <int MT>
+KernelChoice rows_kernel_lean() {
+  static_assert(rows_u_lean(MT) > 0, "lean instances exist for M <= 4");
+  KernelChoice k = rows_kernel<SKINNY_BF16, MT>();
+  k.fn = skinny_rows<SKINNY_BF16, MT, rows_u_lean(MT), rows_r(MT), kRowsWavesPerBlock>;
+  k.waves_per_cu = kRowsLeanWavesPerCU;
+  return k;
+}
+
+// bf16 row-kernel launches of at least kRowsLeanLaunchBytes of weights at
+// M <= 4 take the lean instance.
+bool rows_lean(const skinny_linear* const* lin, int count, int M) {
+  if (lin[0]->dtype != SKINNY_BF16 || rows_u_lean(M) == 0) return false;
+  double bytes = 0;
+  for (int i = 0; i < count; ++i) bytes += 2.0 * lin[i]->N * lin[i]->K;
+  return bytes >= kRowsLeanLaunchBytes;
+}
+
+KernelChoice pick_lean(int M) {
+  switch (M) {
+    case 1: return rows_kernel_lean<1>();
+    case 2: return rows_kernel_lean<2>();
+    case 3: return rows_kernel_lean<3>();
+    case 4: return rows_kernel_lean<4>();
+    default: return KernelChoice{};
+  }
 }
 
 template <int DT, int MT>
@@ -1458,8 +1500,7 @@ skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, 
   if (st != SKINNY_OK) return st;
   if (bpc < 1) return SKINNY_ERR_UNSUPPORTED;
   int waves_per_cu = bpc * k.wpb;
-  if (waves_per_cu > kTargetRowsWavesPerCU)
-    waves_per_cu = kTargetRowsWavesPerCU < k.wpb ? k.wpb : kTargetRowsWavesPerCU;
+  if (waves_per_cu > k.waves_per_cu) waves_per_cu = k.waves_per_cu < k.wpb ? k.wpb : k.waves_per_cu;
   long long g = (long long)d.cus * waves_per_cu;
   if (g > kMaxWaves) g = kMaxWaves;
   *workers = (int)(g / k.wpb);
@@ -1533,6 +1574,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   if (variant == SKINNY_VARIANT_AUTO) variant = auto_variant(lin, count, M);
   KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
+  if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
   if (k.tiles && tiles_large(lin, count, M, dev.cus))
     k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
                              : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
@@ -2156,8 +2198,9 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   if (st != SKINNY_OK) return st;
   memset(out, 0, sizeof *out);
   out->variant = auto_variant(group, n, M);
-  const KernelChoice k = pick(linears[0].dtype, out->variant, M);
+  KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
+  if (!k.tiles && rows_lean(group, n, M)) k = pick_lean(M);
   const int lds = kernel_lds(k, linears[0].dtype);
   st = ensure_lds(k.fn, lds);
   if (st != SKINNY_OK) return st;

@@ -1,0 +1,93 @@
+"""ctypes binding of the streaming-read probe (stream_read.hip): the HBM read
+ceiling that bench.py reports beside the library's own rate.  Measurement
+only; the skinny-GEMM library does not use it."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+ORDER_WAVES = 0
+ORDER_WORKGROUPS = 1
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.path.join(_HERE, "libskinny_probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        L.skinny_probe_stream_read.restype = ctypes.c_int
+        L.skinny_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
+                                               ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.skinny_probe_stream_read_tiles.restype = ctypes.c_int
+        L.skinny_probe_stream_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
+                                                     ctypes.c_longlong, ctypes.c_int,
+                                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                     ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu: int,
+                  reps: int = 5) -> float:
+    """GB/s of the matrix-core kernel's read pattern over the whole of buf."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    nbytes -= nbytes % (16 * wpb * row_bytes)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    workgroups = cus * workgroups_per_cu
+    sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
+    stream = torch.cuda.current_stream()
+
+    def go():
+        rc = lib().skinny_probe_stream_read_tiles(buf.data_ptr(), nbytes, row_bytes, wpb,
+                                                  int(ksplit), workgroups, sink.data_ptr(),
+                                                  stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"skinny_probe_stream_read_tiles failed ({rc})")
+    for _ in range(2):
+        go()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        go()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def stream_read(buf, nbytes: int, row_bytes: int, order: int, u: int, workgroups: int, sink,
+                stream: int):
+    """Enqueue one read of the first nbytes of the device tensor buf."""
+    rc = lib().skinny_probe_stream_read(buf.data_ptr(), nbytes, row_bytes, order, u, workgroups,
+                                        sink.data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError(f"skinny_probe_stream_read failed ({rc})")
+
+
+def measure(buf, row_bytes: int, order: int, u: int, waves_per_cu: int, reps: int = 5,
+            cus: int | None = None) -> float:
+    """GB/s of `reps` back-to-back reads of the whole of buf (HIP events on
+    the current stream, after two untimed reads)."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    nbytes -= nbytes % row_bytes
+    if cus is None:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+    workgroups = cus * waves_per_cu // 4
+    sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9

@@ -1,0 +1,192 @@
+// stream_read.hip - arithmetic-free streaming reads of a device buffer, the
+// HBM read ceiling the decode-phase linear layer is measured against.
+//
+// Decode streams every weight byte once per step and is bound by HBM
+// bandwidth ("Developing a custom Qwen2.5 72B inference engine from scratch
+// - what is the real bottleneck?", section 6.1 "Decode GEMV: already near
+// the roofline"); this kernel does nothing but those reads, so its rate is
+// what a weight-streaming kernel can reach on this GPU at best.  Measurement
+// only: the skinny-GEMM library neither links nor calls it.
+//
+// The buffer is cut into rows of `row_chunks` 16-byte chunks (a multiple of
+// 64 * 2 * U, i.e. whole pairs of batches).  A wave reads a row front to
+// back in 1 KB wave loads (lane l takes chunk 64 s + l of segment s), U
+// segments per batch and two batches in flight.  Rows are dealt to the
+// waves in one of two orders:
+//   ORDER_WAVES      wave w of the grid takes rows w, w + W, ... (every wave
+//                    its own stream, all waves within a moving window),
+//   ORDER_WORKGROUPS workgroup b takes rows b, b + G, ... and its waves
+//                    split each row's batches between them.
+// Every loaded word is XOR-folded into a value that is written out only if
+// it equals a sentinel the data never produces, so no load can be dropped.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;                 // 4 waves per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int ORDER_WAVES = 0;
+constexpr int ORDER_WORKGROUPS = 1;
+
+template <int U, int ORDER>
+__global__ __launch_bounds__(kThreads) void stream_read(const u32x4* buf, long long rows,
+                                                         int row_chunks, unsigned* sink) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int batches = row_chunks / (64 * U);   // batches per row, even
+  long long first, step;
+  int b0, bstep;                               // batches of a row this wave reads
+  if (ORDER == ORDER_WAVES) {
+    first = (long long)blockIdx.x * kWaves + wv;
+    step = (long long)gridDim.x * kWaves;
+    b0 = 0;
+    bstep = 1;
+  } else {
+    first = blockIdx.x;
+    step = gridDim.x;
+    b0 = wv;
+    bstep = kWaves;
+  }
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (long long r = first; r < rows; r += step) {
+    const u32x4* row = buf + r * (long long)row_chunks + lane;
+    u32x4 a[U], b[U];
+    int k = b0;
+    if (k >= batches) continue;
+#pragma unroll
+    for (int v = 0; v < U; ++v) a[v] = row[(k * U + v) * 64];
+    for (; k + bstep < batches; k += 2 * bstep) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) b[v] = row[((k + bstep) * U + v) * 64];
+#pragma unroll
+      for (int v = 0; v < U; ++v) acc ^= a[v];
+      if (k + 2 * bstep < batches) {
+#pragma unroll
+        for (int v = 0; v < U; ++v) a[v] = row[((k + 2 * bstep) * U + v) * 64];
+      }
+#pragma unroll
+      for (int v = 0; v < U; ++v) acc ^= b[v];
+    }
+    if (k < batches) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) acc ^= a[v];
+    }
+  }
+  const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+// The matrix-core kernel's access pattern: units of 16 WPB rows of
+// `row_chunks` chunks, dealt round robin to the workgroups.  A wave load
+// covers 512 bytes of each of two rows (lanes 0-31 one row, 32-63 the
+// next), a segment 512 bytes of each of 16 rows (8 loads), one segment in
+// flight ahead of the one being folded.  KSPLIT = false: wave i takes rows
+// 16 i .. 16 i + 15 of the unit, all of K; KSPLIT = true: the unit is 16
+// rows and wave i takes segments i, i + WPB, ... of them (the waves split K).
+template <int WPB, bool KSPLIT>
+__global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, long long rows,
+                                                              int row_chunks, unsigned* sink) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  constexpr int kUnitRows = KSPLIT ? 16 : 16 * WPB;
+  const int segs = row_chunks / 32;            // 512-byte segments per row
+  const long long units = rows / kUnitRows;
+  const int lrow = lane >> 5, lchunk = lane & 31;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    const long long row0 = u * kUnitRows + (KSPLIT ? 0 : 16 * wv);
+    const u32x4* base = buf + (row0 + lrow) * (long long)row_chunks + lchunk;
+    const int s0 = KSPLIT ? wv : 0;
+    const int sstep = KSPLIT ? WPB : 1;
+    if (s0 >= segs) continue;
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = base[2 * q * (long long)row_chunks + s0 * 32];
+    int s = s0;
+    for (; s + sstep < segs; s += 2 * sstep) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) b[q] = base[2 * q * (long long)row_chunks + (s + sstep) * 32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= a[q];
+      if (s + 2 * sstep < segs) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = base[2 * q * (long long)row_chunks + (s + 2 * sstep) * 32];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= b[q];
+    }
+    if (s < segs) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= a[q];
+    }
+  }
+  const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+typedef void (*probe_fn)(const u32x4*, long long, int, unsigned*);
+
+template <int ORDER>
+probe_fn pick(int u) {
+  switch (u) {
+    case 1: return stream_read<1, ORDER>;
+    case 2: return stream_read<2, ORDER>;
+    case 4: return stream_read<4, ORDER>;
+    case 8: return stream_read<8, ORDER>;
+    case 16: return stream_read<16, ORDER>;
+    default: return nullptr;
+  }
+}
+
+constexpr int kMaxProbeThreads = 512;
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` of `buf` (16-byte aligned device memory) once: rows of
+// row_bytes, dealt in `order` (0 = to waves, 1 = to workgroups), U KB per
+// batch, `workgroups` workgroups of 4 waves.  Requirements: u in {1, 2, 4,
+// 8, 16}; row_bytes a multiple of 2 U KB; bytes a multiple of row_bytes; sink
+// device memory of >= 4 * workgroups bytes (written only on the sentinel).
+// Returns 0, or -1 for invalid arguments (nothing enqueued), or -2 if the
+// launch failed.
+int skinny_probe_stream_read(const void* buf, long long bytes, long long row_bytes, int order,
+                             int u, int workgroups, unsigned* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
+  if (((uintptr_t)buf & 15) != 0) return -1;
+  const probe_fn fn = order == ORDER_WAVES ? pick<ORDER_WAVES>(u)
+                      : order == ORDER_WORKGROUPS ? pick<ORDER_WORKGROUPS>(u)
+                                                  : nullptr;
+  if (!fn) return -1;
+  if (row_bytes % (2LL * u * 1024) != 0 || bytes % row_bytes != 0) return -1;
+  if (row_bytes / 16 > (1LL << 30)) return -1;
+  hipLaunchKernelGGL(fn, dim3(workgroups), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// The matrix-core kernel's pattern (stream_read_tiles): `bytes` of buf read
+// as rows of row_bytes (a multiple of 512; bytes a multiple of 16 * wpb *
+// row_bytes), wpb in {4, 8} waves per workgroup, ksplit 0 or 1.  Same
+// returns and sink rule as skinny_probe_stream_read.
+int skinny_probe_stream_read_tiles(const void* buf, long long bytes, long long row_bytes,
+                                   int wpb, int ksplit, int workgroups, unsigned* sink,
+                                   void* stream) {
+  if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
+  if (((uintptr_t)buf & 15) != 0 || row_bytes % 512 != 0) return -1;
+  if (bytes % (16LL * wpb * row_bytes) != 0 || row_bytes / 16 > (1LL << 30)) return -1;
+  probe_fn fn = nullptr;
+  if (wpb == 4) fn = ksplit ? stream_read_tiles<4, true> : stream_read_tiles<4, false>;
+  if (wpb == 8) fn = ksplit ? stream_read_tiles<8, true> : stream_read_tiles<8, false>;
+  if (!fn || 64 * wpb > kMaxProbeThreads) return -1;
+  hipLaunchKernelGGL(fn, dim3(workgroups), dim3(64 * wpb), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+}  // extern "C"
