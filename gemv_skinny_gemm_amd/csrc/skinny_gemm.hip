@@ -617,6 +617,10 @@ constexpr int tiles_lds(int wpb) { return wpb == kTilesWavesLarge ? 160 * 1024 :
 constexpr int tiles_w_bytes(int wpb) { return wpb * kTileRows * kRowStrideT; }
 constexpr int tiles_x_budget(int wpb) { return tiles_lds(wpb) - tiles_w_bytes(wpb); }
 constexpr int kTilesXBudget = tiles_x_budget(kTilesWavesSmall);
+// The K-split form keeps its waves' partial tiles, two halves of WPB x 64
+// lanes x 16 bytes, between the W tiles and the end of its LDS.
+constexpr int tiles_red_bytes(int wpb) { return 2 * wpb * 64 * 16; }
+constexpr int tiles_x_budget_ks(int wpb) { return tiles_x_budget(wpb) - tiles_red_bytes(wpb); }
 
 template <int DT>
 struct TileSeg {
@@ -637,16 +641,28 @@ struct TileUnit {
   int m;                 // tokens (MoE: routes of the slice)
 };
 
-template <int DT, int WPB, bool MOE>
+// KS (K split inside the workgroup): a unit is one 16-row tile, and the
+// workgroup's waves take its segments round robin (wave i: segments j0 + i,
+// j0 + i + WPB, ...), so every wave of the workgroup loads at once even
+// where a row has only a few segments.  A window may then hold no segment
+// for some waves.  The waves' partial tiles are added in LDS in wave order
+// at the end of the unit (deterministic).
+template <int DT, int WPB, bool MOE, bool KS = false>
 __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   constexpr int kThreads = 64 * WPB;
-  constexpr int kGroupRows = kTileRows * WPB;
+  constexpr int kGroupRows = KS ? kTileRows : kTileRows * WPB;
+  constexpr int kSegStep = KS ? WPB : 1;               // between a wave's segments
   constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   u32x4* xs = reinterpret_cast<u32x4*>(lds);
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int seg_off = KS ? wv : 0;                     // this wave's first segment of a window
+  const int wrow = KS ? 0 : wv * kTileRows;            // this wave's first row of the group
   unsigned char* wt = lds + a.x_lds_bytes + wv * (kTileRows * kRowStrideT);
+  // KS: partial tiles [2][WPB][64 lanes], alternate halves on alternate units.
+  f32x4* red = reinterpret_cast<f32x4*>(lds + a.x_lds_bytes + WPB * kTileRows * kRowStrideT);
+  int red_half = 0;
   const int n = lane & 15;                             // operand row: token (A) / W row (B)
   const int g = lane >> 4;                             // operand k-group
   const int lrow = lane / kLanesPerRowT;               // load q: row q kRowsPerLoadT + lrow
@@ -719,7 +735,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   // unconditional and in bounds and the compiler's waits stay exact.
   auto load = [&](TileSeg<DT>& s, const TileUnit& t, int j) {
     const LinDesc& L = a.lin[t.l];
-    const int row0 = t.grp * kGroupRows + wv * kTileRows;
+    const int row0 = t.grp * kGroupRows + wrow;
     const int c = min(j * kSegChunksT + lchunk, L.cpr - 1);
     const u32x4* w = MOE ? L.w + (size_t)t.e * a.moe.w_stride : L.w;
 #pragma unroll
@@ -818,9 +834,27 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     __syncthreads();
   };
   auto epilogue = [&](const TileUnit& t) {
+    if constexpr (KS) {
+      // The waves' partial tiles, added by wave 0 in wave order.  The other
+      // half of `red` takes the next unit's, so one barrier per unit
+      // suffices: a wave writes this half again only after passing the next
+      // unit's barrier, which wave 0 reaches after these reads.
+      f32x4* r = red + red_half * (WPB * 64);
+      red_half ^= 1;
+      r[wv * 64 + lane] = acc;
+      __syncthreads();
+      if (wv != 0) {
+        acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        return;
+      }
+      f32x4 sum = r[lane];
+#pragma unroll
+      for (int w = 1; w < WPB; ++w) sum += r[w * 64 + lane];
+      acc = sum;
+    }
     // Lane (n, g) holds D[4 g + i][n]: token 4 g + i, row row0 + n.
     const LinDesc& L = a.lin[t.l];
-    const int row = t.grp * kGroupRows + wv * kTileRows + n;
+    const int row = t.grp * kGroupRows + wrow + n;
     const long long slot = (MOE ? (long long)t.slice * a.moe.units_per_slice : L.slot_base) +
                            (long long)t.grp * L.chunks + t.chunk;
 #pragma unroll
@@ -831,7 +865,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
           const int yr = MOE ? tb.yrow[t.slice * kMoeMaxCap + m] : m;
           if (row < L.N) L.y[(size_t)yr * L.N + row] = (__bf16)acc[i];
         } else {
-          a.slots[((size_t)slot * a.M + m) * kGroupRows + wv * kTileRows + n] = acc[i];
+          a.slots[((size_t)slot * a.M + m) * kGroupRows + wrow + n] = acc[i];
         }
       }
     }
@@ -840,23 +874,31 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   // The segments of unit t, the first of which is already loading into A.
   // Ends with the first segment of unit nx (if has_next) loading into A when
   // t has an even number of segments, into B when odd; returns which.
+  // This wave's segments of t are j0 + seg_off, then every kSegStep-th; in
+  // the K-split form a window may hold none for this wave, and then nothing
+  // was loaded for it.
   auto run_unit = [&](TileSeg<DT>& A, TileSeg<DT>& B, const TileUnit& t, const TileUnit& nx,
                       bool has_next) {
-    int j = t.j0;
-    for (; j + 2 < t.j1; j += 2) {
-      load(B, t, j + 1);
-      consume(A, t, j);
-      load(A, t, j + 2);
-      consume(B, t, j + 1);
-    }
-    if (j + 2 == t.j1) {
-      load(B, t, j + 1);
-      consume(A, t, j);
-      if (has_next) load(A, nx, nx.j0);
-      consume(B, t, j + 1);
+    const bool next = has_next && nx.j0 + seg_off < nx.j1;
+    int j = t.j0 + seg_off;
+    if (KS && j >= t.j1) {
+      if (next) load(A, nx, nx.j0 + seg_off);
       return 0;
     }
-    if (has_next) load(B, nx, nx.j0);
+    for (; j + 2 * kSegStep < t.j1; j += 2 * kSegStep) {
+      load(B, t, j + kSegStep);
+      consume(A, t, j);
+      load(A, t, j + 2 * kSegStep);
+      consume(B, t, j + kSegStep);
+    }
+    if (j + kSegStep < t.j1) {
+      load(B, t, j + kSegStep);
+      consume(A, t, j);
+      if (next) load(A, nx, nx.j0 + seg_off);
+      consume(B, t, j + kSegStep);
+      return 0;
+    }
+    if (next) load(B, nx, nx.j0 + seg_off);
     consume(A, t, j);
     return 1;
   };
@@ -864,7 +906,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   if (u >= S) return;
   TileSeg<DT> s0, s1;
   TileUnit cur = decode(u, 0);
-  load(s0, cur, cur.j0);
+  if (cur.j0 + seg_off < cur.j1) load(s0, cur, cur.j0 + seg_off);
   int in_b = 0;                                         // the current unit's first segment is in s1
   for (;;) {
     // A unit's x windows in turn (its sums stay in acc), then the next unit.
@@ -1840,6 +1882,8 @@ struct MoePlan {
   int table_lds;         // LDS bytes of the slice table
   int x_budget;          // LDS bytes left for x; the table follows them
   size_t table_bytes;    // workspace bytes of the table copy (256-aligned)
+  bool ks = false;       // skinny_tiles' K-split form (16-row groups)
+  int band = 0;          // rows per row group
 };
 
 // Slices: an expert with c routes makes ceil(c / cap) of them, so n active
@@ -1858,12 +1902,14 @@ MoePlan moe_plan_base(const skinny_experts& ex, int T, int topk) {
   return p;
 }
 
-MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb) {
+MoePlan moe_plan_for(const skinny_experts& ex, int T, int topk, int wpb, bool ks = false) {
   MoePlan p = moe_plan_base(ex, T, topk);
   p.rows = false;
   p.wpb = wpb;
-  p.groups = (ex.N + kTileRows * wpb - 1) / (kTileRows * wpb);
-  p.x_budget = tiles_x_budget(wpb) - p.table_lds;
+  p.ks = ks;
+  p.band = ks ? kTileRows : kTileRows * wpb;
+  p.groups = (ex.N + p.band - 1) / p.band;
+  p.x_budget = (ks ? tiles_x_budget_ks(wpb) : tiles_x_budget(wpb)) - p.table_lds;
   return p;
 }
 
@@ -1876,7 +1922,8 @@ constexpr int kMoeRowsMinSegs = 4;
 MoePlan moe_plan_rows(const skinny_experts& ex, int T, int topk) {
   MoePlan p = moe_plan_base(ex, T, topk);
   p.wpb = kRowsWavesPerBlock;
-  p.groups = (ex.N + kRowsWavesPerBlock * rows_r(T) - 1) / (kRowsWavesPerBlock * rows_r(T));
+  p.band = kRowsWavesPerBlock * rows_r(T);
+  p.groups = (ex.N + p.band - 1) / p.band;
   p.x_budget = kRowsXBudget - p.table_lds;
   const int cpr = ex.K / (ex.dtype == SKINNY_BF16 ? 8 : 16);
   p.rows = T <= kRowsMaxM && p.x_budget >= 2 * kMoeMaxRoutes * (int)sizeof(int) &&
@@ -1900,11 +1947,20 @@ constexpr int kMoeLargeWindows = 4;
 // minimum row length; two-token slices 15.2 -> 23.0 and 23.2 -> 24.6 us on
 // gate_up (the two-token row instance's registers leave one workgroup per CU).
 constexpr int kMoeRowsMaxCap = 1;
+// One-token slices whose rows are too short for the row kernel take the tile
+// kernel's K-split form: 16-row units (four times as many as 64-row ones,
+// every workgroup busy) whose few segments all waves load at once.  Measured
+// on MI355X (verify step, 8 experts, top 2, one token, down: K = 1536):
+// 7.87 -> 7.68 us FP8, 10.09 -> 9.13 us bf16.  For gate_up (K = 4096) it was
+// no faster than the row kernel (FP8 11.07 -> 10.95, bf16 13.33 -> 13.74 us),
+// and at two or more tokens no faster than one tile per wave.
+constexpr int kMoeKsMaxCap = 1;
 MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
   if (T <= kMoeRowsMaxCap) {
     const MoePlan r = moe_plan_rows(ex, T, topk);
     if (r.rows) return r;
   }
+  if (T <= kMoeKsMaxCap) return moe_plan_for(ex, T, topk, kTilesWavesSmall, true);
   const MoePlan p = moe_plan_for(ex, T, topk, kTilesWavesSmall);
   if (tiles_lds_chunks(ex.dtype, p.cap, ex.K, p.x_budget) >= kMoeLargeWindows)
     return moe_plan_for(ex, T, topk, kTilesWavesLarge);
@@ -1913,8 +1969,7 @@ MoePlan moe_plan(const skinny_experts& ex, int T, int topk) {
 
 size_t moe_workspace(const skinny_experts& ex, const MoePlan& p) {
   const int c = p.rows ? 1 : tiles_chunks(ex.dtype, p.cap, ex.K, 1LL << 40, p.x_budget);
-  const size_t slots = c > 1 ? (size_t)p.max_slices * p.groups * c * p.cap *
-                                   (kTileRows * p.wpb) * sizeof(float)
+  const size_t slots = c > 1 ? (size_t)p.max_slices * p.groups * c * p.cap * p.band * sizeof(float)
                              : 0;
   const size_t b = p.table_bytes + slots;
   return b > SKINNY_MIN_WORKSPACE_BYTES ? b : SKINNY_MIN_WORKSPACE_BYTES;
@@ -1974,13 +2029,16 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
     k = dtype == SKINNY_BF16 ? moe_rows_kernel<SKINNY_BF16, 1>()
                              : moe_rows_kernel<SKINNY_FP8_BS128, 1>();
   } else {
-    if (p.wpb == kTilesWavesLarge)
+    if (p.ks)
+      k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesSmall, true, true>
+                                  : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesSmall, true, true>;
+    else if (p.wpb == kTilesWavesLarge)
       k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesLarge, true>
                                   : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesLarge, true>;
     else
       k.fn = dtype == SKINNY_BF16 ? skinny_tiles<SKINNY_BF16, kTilesWavesSmall, true>
                                   : skinny_tiles<SKINNY_FP8_BS128, kTilesWavesSmall, true>;
-    k.band_rows = kTileRows * p.wpb;
+    k.band_rows = p.band;
     k.wpb = p.wpb;
     k.tiles = true;
   }
@@ -2026,7 +2084,10 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
   mo.per_route = flags & SKINNY_MOE_X_PER_ROUTE ? 1 : 0;
   mo.max_slices = p.max_slices;
   mo.units_per_slice = p.groups * d.chunks;
-  mo.table_lds = p.rows ? p.x_budget : p.x_budget + tiles_w_bytes(p.wpb);
+  // The tile kernel's LDS: x, the W tiles, (K-split: the partial tiles,)
+  // then the table.
+  mo.table_lds = p.rows ? p.x_budget
+                        : p.x_budget + tiles_w_bytes(p.wpb) + (p.ks ? tiles_red_bytes(p.wpb) : 0);
   a.slots = (float*)((char*)ws + p.table_bytes);
   a.S = (long long)p.max_slices * mo.units_per_slice;
   G = grid_for_chunks(G, a);

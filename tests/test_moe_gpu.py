@@ -151,6 +151,30 @@ def test_one_token_short_and_long_rows(dtype):
         check(run_moe(x, ids, w, s), y_ref, a, f"K={K} {dtype}")
 
 
+@pytest.mark.parametrize("swiglu,x_per_route", [(False, False), (False, True), (True, False),
+                                                  (True, True)])
+@pytest.mark.parametrize("dtype,K", [(sg.BF16, 520), (sg.BF16, 1024), (sg.FP8_BS128, 1040),
+                                     (sg.FP8_BS128, 2048)])
+def test_one_token_k_split_tiles(dtype, K, swiglu, x_per_route):
+    """One token with rows of 2-4 segments of 512 bytes: the tile kernel's
+    K-split form, where the workgroup's four waves share each 16-row tile's
+    segments (some waves get none) and add their partial tiles in LDS.  N =
+    200 ends inside a tile; id 4 names no expert."""
+    E, N = 4, 200
+    ids = np.array([[3, 4, 1]], np.int32)
+    tag = f"ks{K}{int(swiglu)}{int(x_per_route)}"
+    if dtype == sg.BF16:
+        w, s = experts_bf16(tag, E, N, K), None
+    else:
+        w, s = experts_fp8(tag, E, N, K)
+    x = x_for(tag, ids.size if x_per_route else 1, 2 * K if swiglu else K)
+    y_ref, a = oracle.moe_linear(x, ids, w, scales=s, x_per_route=x_per_route, swiglu=swiglu)
+    y1, y2 = run_moe(x, ids, w, s, x_per_route=x_per_route, swiglu=swiglu, reps=2)
+    check(y1, y_ref, a, f"{dtype} K={K} swiglu={swiglu} per_route={x_per_route}")
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.all(y1[1].float() == 0)
+
+
 def test_one_expert_takes_more_routes_than_tokens():
     """Duplicates: 8 routes of 2 tokens to expert 1 make 4 slices of it."""
     E, N, K = 3, 128, 512
