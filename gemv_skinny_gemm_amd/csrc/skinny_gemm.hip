@@ -111,6 +111,25 @@ struct MoeArgs {
   int table_lds;         // LDS offset of the slice table
 };
 
+// Greedy-token reduction ("Developing a custom Qwen2.5 72B inference engine
+// from scratch - what is the real bottleneck?", section 5, third lever):
+// pairs (value, index) ordered by value, then by lower index, so the result
+// does not depend on the reduction order.  NaN ranks below every number,
+// -inf included: a NaN is never taken, and a pair that has seen no number
+// keeps the index N, which loses to every real index.
+struct ArgmaxPair {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ void argmax_take(float v, int i, float& bv, int& bi) {
+  if (v != v) return;
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
 struct LaunchArgs {
   int nlin;
   int M;
@@ -120,6 +139,7 @@ struct LaunchArgs {
   float* slots;          // fp32 partial sums [slot][M][band_rows], one slot per split unit
   int x_lds_bytes;       // LDS bytes for x; the kernel's other LDS follows
   int pad;
+  ArgmaxPair* pairs;     // skinny_rows, one unsplit linear: [M][G] greedy pairs, or NULL
   MoeArgs moe;
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
@@ -426,6 +446,15 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
   int staged_l = -1;
   int staged_c = -1;
   long long u = blockIdx.x;
+  // Greedy token of the rows this wave writes (a.pairs: one unsplit linear):
+  // the best bf16 output per token, kept by lane 0.
+  float gbv[MT];
+  int gbi[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    gbv[m] = -__builtin_inff();
+    gbi[m] = a.lin[0].N;
+  }
   prefetch_scales(u, 0);
   store_scales();
   for (; u < S; u += a.G) {
@@ -564,11 +593,32 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
             if (m < mt && row0 + r < L.N)
               L.y[(size_t)tb.yrow[l * kMoeMaxCap + m] * L.N + row0 + r] = (__bf16)acc[r][m];
           } else if (L.chunks == 1) {
-            if (row0 + r < L.N) L.y[(size_t)m * L.N + row0 + r] = (__bf16)acc[r][m];
+            if (row0 + r < L.N) {
+              const __bf16 yv = (__bf16)acc[r][m];
+              L.y[(size_t)m * L.N + row0 + r] = yv;
+              if (a.pairs) argmax_take((float)yv, row0 + r, gbv[m], gbi[m]);
+            }
           } else {
             a.slots[((size_t)slot * MT + m) * kGroupRows + wv * R + r] = acc[r][m];
           }
         }
+    }
+  }
+  if (!MOE && a.pairs) {
+    // The workgroup's pair per token, from its waves' in wave order (the
+    // order does not change the result), into pairs[m][workgroup].
+    __syncthreads();                                             // every wave is done with x
+    ArgmaxPair* red = reinterpret_cast<ArgmaxPair*>(lds);
+    if (lane == 0)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wv * MT + m] = ArgmaxPair{gbv[m], gbi[m]};
+    __syncthreads();
+    if (threadIdx.x < MT) {
+      const int m = threadIdx.x;
+      float bv = -__builtin_inff();
+      int bi = a.lin[0].N;
+      for (int w = 0; w < WPB; ++w) argmax_take(red[w * MT + m].v, red[w * MT + m].i, bv, bi);
+      a.pairs[(size_t)m * a.G + blockIdx.x] = ArgmaxPair{bv, bi};
     }
   }
 }
@@ -1014,13 +1064,6 @@ constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxSlice = 4096;                    // logits per first-pass workgroup
 constexpr int kArgmaxMaxSlices = 1 << 20;
 
-__device__ __forceinline__ void argmax_take(float v, int i, float& bv, int& bi) {
-  if (v != v) return;
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
 
 // (value, index) of the workgroup into lane 0 of wave 0.
 __device__ __forceinline__ void argmax_block(float& bv, int& bi) {
@@ -1042,11 +1085,6 @@ __device__ __forceinline__ void argmax_block(float& bv, int& bi) {
   if (threadIdx.x == 0)
     for (int w = 1; w < kArgmaxThreads / 64; ++w) argmax_take(sv[w], si[w], bv, bi);
 }
-
-struct ArgmaxPair {
-  float v;
-  int i;
-};
 
 // VEC: N % 8 == 0 and 16-byte aligned rows, 8 logits per load.
 template <bool VEC>
@@ -1609,9 +1647,14 @@ void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
 // Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
 // workers = 0 sizes the persistent grid from occupancy; otherwise it is the
 // number of waves to run (rounded down to whole workgroups, at least one).
+//
+// pairs (optional): for a launch of one linear on the row kernel with K
+// unsplit, the kernel also writes each workgroup's greedy pair per token to
+// pairs[M][grid] and *pairs_grid is set to the grid; otherwise 0.
 skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* lin, int count,
                            int M, int variant, int workers, float* slots, hipStream_t stream,
-                           hipEvent_t ev_before, hipEvent_t ev_after) {
+                           hipEvent_t ev_before, hipEvent_t ev_after,
+                           ArgmaxPair* pairs = nullptr, int* pairs_grid = nullptr) {
   const int dtype = lin[0]->dtype;
   if (variant == SKINNY_VARIANT_AUTO) variant = auto_variant(lin, count, M);
   KernelChoice k = pick(dtype, variant, M);
@@ -1669,6 +1712,11 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   if (G > S) G = (int)S;
   if (G < 1) G = 1;
   a.G = G;
+  if (pairs_grid) *pairs_grid = 0;
+  if (pairs && !k.tiles && count == 1 && a.lin[0].chunks == 1) {
+    a.pairs = pairs;
+    if (pairs_grid) *pairs_grid = G;
+  }
   if (ev_before && hipEventRecord(ev_before, stream) != hipSuccess) return SKINNY_ERR_HIP;
   hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), lds, stream, a);
   if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
@@ -1741,7 +1789,8 @@ size_t required_workspace(const skinny_linear* lin, int count, int M) {
 
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
                   void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr,
-                  int event_count = 0, bool allow_act = false) {
+                  int event_count = 0, bool allow_act = false, ArgmaxPair* pairs = nullptr,
+                  int* pairs_grid = nullptr) {
   if (!lin || count < 1) return SKINNY_ERR_INVALID_ARG;
   if (M < 1 || M > SKINNY_MAX_M) return SKINNY_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
@@ -1783,7 +1832,7 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
     hipEvent_t after = events ? (hipEvent_t)events[2 * launch + 1] : nullptr;
     ++launch;
     return launch_group(d, g, n, M, variant, waves, (float*)ws, (hipStream_t)stream, before,
-                        after);
+                        after, pairs, pairs_grid);
   });
 }
 
@@ -1792,6 +1841,11 @@ int argmax_slices(int N) { return (N + kArgmaxSlice - 1) / kArgmaxSlice; }
 size_t argmax_workspace(int M, int N) {
   const size_t b = (size_t)M * argmax_slices(N) * sizeof(ArgmaxPair);
   return b > SKINNY_MIN_WORKSPACE_BYTES ? b : SKINNY_MIN_WORKSPACE_BYTES;
+}
+
+// The greedy pairs the row kernel's epilogue writes: one per workgroup and token.
+size_t argmax_fused_workspace(int M) {
+  return (size_t)M * (kMaxWaves / kRowsWavesPerBlock) * sizeof(ArgmaxPair);
 }
 
 skinny_status launch_argmax(const void* y, int M, int N, int* idx, void* ws, hipStream_t stream) {
@@ -2291,7 +2345,8 @@ size_t skinny_lm_head_workspace_bytes(const skinny_linear* head, int M) {
   if (!head || M < 1 || M > SKINNY_MAX_M) return 0;
   const size_t lin = skinny_stack_workspace_bytes(head, 1, M);
   if (lin == 0) return 0;
-  const size_t am = argmax_workspace(M, head->N);
+  size_t am = argmax_workspace(M, head->N);
+  if (argmax_fused_workspace(M) > am) am = argmax_fused_workspace(M);
   return lin > am ? lin : am;
 }
 
@@ -2315,11 +2370,20 @@ skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_
     if (overlap(ir, Range{(uintptr_t)head->w_scale, (uintptr_t)head->w_scale + sb}))
       return SKINNY_ERR_INVALID_ARG;
   }
-  // The workspace serves the linear's partial sums, then (stream order: the
-  // linear is done with them) the argmax pairs.
-  st = run(head, 1, M, nullptr, workspace, workspace_bytes, stream);
+  if (workspace_bytes < argmax_fused_workspace(M)) return SKINNY_ERR_WORKSPACE;
+  // On the row kernel with K unsplit, the linear's launch also leaves each
+  // workgroup's greedy pair per token at the start of the workspace (it needs
+  // no partial sums then), and one pass reduces them.  Otherwise the
+  // workspace serves the linear's partial sums, then (stream order: the
+  // linear is done with them) the two argmax passes over the logits.
+  int grid = 0;
+  st = run(head, 1, M, nullptr, workspace, workspace_bytes, stream, nullptr, 0, false,
+           (ArgmaxPair*)workspace, &grid);
   if (st != SKINNY_OK) return st;
-  return launch_argmax(head->y, M, head->N, next_token, workspace, (hipStream_t)stream);
+  if (grid == 0) return launch_argmax(head->y, M, head->N, next_token, workspace, (hipStream_t)stream);
+  hipLaunchKernelGGL(skinny_argmax_rows, dim3(M), dim3(kArgmaxThreads), 0, (hipStream_t)stream,
+                     (const ArgmaxPair*)workspace, grid, head->N, next_token);
+  return hipGetLastError() == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP;
 }
 
 size_t skinny_mlp_workspace_bytes(const skinny_mlp* mlp, int M) {

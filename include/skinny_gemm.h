@@ -220,10 +220,14 @@ skinny_status skinny_argmax_bf16(const void* y, int M, int N, int* idx, void* wo
 /* The vocabulary projection and its greedy token in one call (same section
  * and lever): runs the one linear `head` (N = vocabulary size, K = hidden
  * size, head->y = the logits [M][N], written) exactly as decode_linear_stack
- * would, then skinny_argmax_bf16 over those logits into next_token[M] (device
- * int32).  next_token must not overlap x, W, w_scale, y or the workspace.  The
- * workspace serves the linear, then the argmax (stream order), so it needs
- * skinny_lm_head_workspace_bytes(head, M) bytes (0 for invalid arguments). */
+ * would, and writes into next_token[M] (device int32) what skinny_argmax_bf16
+ * over those logits gives.  Where the linear runs on the vector kernel with K
+ * unsplit, its launch also leaves one (value, index) pair per workgroup and
+ * token and a single pass reduces them; otherwise the two argmax passes run
+ * after the linear.  next_token must not overlap x, W, w_scale, y or the
+ * workspace.  The workspace serves the linear and the argmax (stream order),
+ * so it needs skinny_lm_head_workspace_bytes(head, M) bytes (0 for invalid
+ * arguments); less returns SKINNY_ERR_WORKSPACE before anything is enqueued. */
 size_t skinny_lm_head_workspace_bytes(const skinny_linear* head, int M);
 skinny_status skinny_lm_head_argmax(const skinny_linear* head, int M, int* next_token,
                                     void* workspace, size_t workspace_bytes, void* stream);

@@ -94,6 +94,32 @@ def test_argmax_nan_ranks_below_minus_infinity(aligned):
     assert idx.cpu().numpy().tolist() == want.tolist()
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_lm_head_fused_greedy_ties(M):
+    """A vocabulary projection large enough for the row kernel's lean
+    instance, whose epilogue leaves one greedy pair per workgroup and token
+    (then one pass over the pairs): W row n = one-hot at column perm[n], and
+    x drawn from a few values, so the logits x[:, perm] tie across many
+    workgroups and the smallest index of the largest value must win."""
+    N, K = 150000, 4096                                   # 1.2 GB of bf16 weights
+    rng = np.random.default_rng(40 + M)
+    perm = rng.integers(0, K, N)
+    vals = torch.tensor(rng.normal(size=9), dtype=torch.float64).to(torch.bfloat16)
+    x = vals.view(torch.int16).numpy().view(np.uint16)[rng.integers(0, 9, (M, K))]
+    wd = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    wd[torch.arange(N, device="cuda"), torch.from_numpy(perm).cuda()] = 1.0
+    xd, yd = dev_bf16(x), out(M, N)
+    tok = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    lin = sg.make_linear(xd, wd, yd)
+    ws = torch.empty(sg.lm_head_workspace_bytes(lin, M), dtype=torch.uint8, device="cuda")
+    sg.lm_head_argmax(lin, M, tok, ws)
+    torch.cuda.synchronize()
+    logits = bf16_values(x[:, perm])
+    assert np.array_equal(host_values(yd), logits)
+    assert tok.cpu().numpy().tolist() == oracle.argmax_first(logits).tolist()
+    del wd
+
+
 def test_lm_head_one_hot_rows_pick_exactly():
     """W row n = one-hot at column perm[n]: the logits are x[:, perm] exactly,
     so the greedy token is decided exactly."""
