@@ -22,8 +22,9 @@ def lib():
         L = ctypes.CDLL(path)
         L.skinny_probe_stream_read.restype = ctypes.c_int
         L.skinny_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
-                                               ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
-                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                               ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                               ctypes.c_void_p]
         L.skinny_probe_stream_read_tiles.restype = ctypes.c_int
         L.skinny_probe_stream_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
                                                      ctypes.c_longlong, ctypes.c_int,
@@ -62,32 +63,34 @@ def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu
 
 
 def stream_read(buf, nbytes: int, row_bytes: int, order: int, u: int, workgroups: int, sink,
-                stream: int):
-    """Enqueue one read of the first nbytes of the device tensor buf."""
-    rc = lib().skinny_probe_stream_read(buf.data_ptr(), nbytes, row_bytes, order, u, workgroups,
-                                        sink.data_ptr(), stream)
+                stream: int, read_bytes: int | None = None):
+    """Enqueue one read of the first nbytes of the device tensor buf (of each
+    row, its first read_bytes; default the whole row)."""
+    rc = lib().skinny_probe_stream_read(buf.data_ptr(), nbytes, row_bytes, read_bytes or row_bytes,
+                                        order, u, workgroups, sink.data_ptr(), stream)
     if rc != 0:
         raise RuntimeError(f"skinny_probe_stream_read failed ({rc})")
 
 
 def measure(buf, row_bytes: int, order: int, u: int, waves_per_cu: int, reps: int = 5,
-            cus: int | None = None) -> float:
-    """GB/s of `reps` back-to-back reads of the whole of buf (HIP events on
-    the current stream, after two untimed reads)."""
+            cus: int | None = None, read_bytes: int | None = None) -> float:
+    """GB/s read by `reps` back-to-back reads of buf (of each row, its first
+    read_bytes; HIP events on the current stream, after two untimed reads)."""
     import torch
     nbytes = buf.numel() * buf.element_size()
     nbytes -= nbytes % row_bytes
+    read = read_bytes or row_bytes
     if cus is None:
         cus = torch.cuda.get_device_properties(0).multi_processor_count
     workgroups = cus * waves_per_cu // 4
     sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
     stream = torch.cuda.current_stream()
     for _ in range(2):
-        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream)
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream)
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read)
     e1.record(stream)
     torch.cuda.synchronize()
-    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return nbytes // row_bytes * read * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9

@@ -1,0 +1,77 @@
+"""Sweeps of the streaming-read probe on one GPU; prints one table per sweep.
+
+    python -m gemv_skinny_gemm_amd.probe depth    order x row size x batch x waves per CU
+    python -m gemv_skinny_gemm_amd.probe stride   1-2 KB read from the start of every row of a
+                                                  given stride (32 GiB buffer)
+    python -m gemv_skinny_gemm_amd.probe tiles    the matrix-core kernel's read pattern
+
+Every figure is GB/s read from an 8 GiB buffer (GiB = 2^30 bytes), best of
+three measurements of five passes each.  Measurement only.
+"""
+import sys
+
+import torch
+
+from gemv_skinny_gemm_amd import probe
+
+GIB = 1 << 30
+
+
+def best(fn, n=3):
+    return max(fn() for _ in range(n))
+
+
+def depth(buf):
+    print("| order | row | KB per batch | waves/CU | GB/s |")
+    print("|---|---|---|---|---|")
+    for order, rows in ((probe.ORDER_WAVES, (2, 4, 8, 16, 64, 1024)),
+                        (probe.ORDER_WORKGROUPS, (16, 32, 128, 512, 2048))):
+        for row_kb in rows:
+            for u in (1, 2, 4, 8):
+                if row_kb % (2 * u):
+                    continue
+                for wpc in (4, 8, 12, 16, 32):
+                    g = best(lambda: probe.measure(buf, row_kb << 10, order, u, wpc))
+                    name = "to waves" if order == probe.ORDER_WAVES else "to workgroups"
+                    print(f"| {name} | {row_kb} KB | {u} | {wpc} | {g:.0f} |", flush=True)
+
+
+def stride(buf):
+    """1 or 2 KB read from the start of every row of `stride` bytes, rows
+    dealt to waves: the requests in flight sit `stride` apart (a 32 GiB
+    buffer, so even the widest stride reads 128 MB per pass)."""
+    del buf
+    big = torch.ones(32 * GIB // 8, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    print("| stride | read per row | waves/CU | GB/s |")
+    print("|---|---|---|---|")
+    for sk in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        for read_kb, u in ((1, 1), (2, 2)):
+            if read_kb > sk:
+                continue
+            for wpc in (8, 16):
+                g = best(lambda: probe.measure(big, sk << 10, probe.ORDER_WAVES, u, wpc,
+                                               read_bytes=read_kb << 10))
+                print(f"| {sk} KB | {read_kb} KB | {wpc} | {g:.0f} |", flush=True)
+
+
+def tiles(buf):
+    print("| row | waves/workgroup | K split | workgroups/CU | GB/s |")
+    print("|---|---|---|---|---|")
+    for rb in (8192, 16384, 57344):
+        for wpb, wgpc in ((4, 1), (4, 2), (8, 1)):
+            for ks in (False, True):
+                g = best(lambda: probe.measure_tiles(buf, rb, wpb, ks, wgpc))
+                print(f"| {rb >> 10} KB | {wpb} | {int(ks)} | {wgpc} | {g:.0f} |", flush=True)
+
+
+def main():
+    what = sys.argv[1] if len(sys.argv) > 1 else "depth"
+    buf = torch.ones(8 * GIB // 8, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    print(f"# {what} sweep, {torch.cuda.get_device_name(0)}", flush=True)
+    {"depth": depth, "stride": stride, "tiles": tiles}[what](buf)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,9 +8,10 @@
 // what a weight-streaming kernel can reach on this GPU at best.  Measurement
 // only: the skinny-GEMM library neither links nor calls it.
 //
-// The buffer is cut into rows of `row_chunks` 16-byte chunks (a multiple of
-// 64 * 2 * U, i.e. whole pairs of batches).  A wave reads a row front to
-// back in 1 KB wave loads (lane l takes chunk 64 s + l of segment s), U
+// The buffer is cut into rows of `row_chunks` 16-byte chunks, of which the
+// first `read_chunks` (a multiple of 64 U: whole batches) are read; reading
+// less than the whole row gives a strided pattern.  A wave reads a row front
+// to back in 1 KB wave loads (lane l takes chunk 64 s + l of segment s), U
 // segments per batch and two batches in flight.  Rows are dealt to the
 // waves in one of two orders:
 //   ORDER_WAVES      wave w of the grid takes rows w, w + W, ... (every wave
@@ -34,10 +35,11 @@ constexpr int ORDER_WORKGROUPS = 1;
 
 template <int U, int ORDER>
 __global__ __launch_bounds__(kThreads) void stream_read(const u32x4* buf, long long rows,
-                                                         int row_chunks, unsigned* sink) {
+                                                         int row_chunks, int read_chunks,
+                                                         unsigned* sink) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int batches = row_chunks / (64 * U);   // batches per row, even
+  const int batches = read_chunks / (64 * U);  // batches read per row
   long long first, step;
   int b0, bstep;                               // batches of a row this wave reads
   if (ORDER == ORDER_WAVES) {
@@ -128,7 +130,8 @@ __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, 
   if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
 }
 
-typedef void (*probe_fn)(const u32x4*, long long, int, unsigned*);
+typedef void (*probe_fn)(const u32x4*, long long, int, int, unsigned*);
+typedef void (*tiles_fn)(const u32x4*, long long, int, unsigned*);
 
 template <int ORDER>
 probe_fn pick(int u) {
@@ -148,25 +151,29 @@ constexpr int kMaxProbeThreads = 512;
 
 extern "C" {
 
-// Reads `bytes` of `buf` (16-byte aligned device memory) once: rows of
-// row_bytes, dealt in `order` (0 = to waves, 1 = to workgroups), U KB per
-// batch, `workgroups` workgroups of 4 waves.  Requirements: u in {1, 2, 4,
-// 8, 16}; row_bytes a multiple of 2 U KB; bytes a multiple of row_bytes; sink
-// device memory of >= 4 * workgroups bytes (written only on the sentinel).
-// Returns 0, or -1 for invalid arguments (nothing enqueued), or -2 if the
-// launch failed.
-int skinny_probe_stream_read(const void* buf, long long bytes, long long row_bytes, int order,
-                             int u, int workgroups, unsigned* sink, void* stream) {
-  if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
+// Reads the first read_bytes of every row_bytes of the first `bytes` of `buf`
+// (16-byte aligned device memory) once: rows dealt in `order` (0 = to waves,
+// 1 = to workgroups), U KB per batch, `workgroups` workgroups of 4 waves.
+// Requirements: u in {1, 2, 4, 8, 16}; read_bytes a multiple of U KB and at
+// most row_bytes; bytes a multiple of row_bytes; sink device memory of
+// >= 4 * workgroups bytes (written only on the sentinel).  Returns 0, or -1
+// for invalid arguments (nothing enqueued), or -2 if the launch failed.
+int skinny_probe_stream_read(const void* buf, long long bytes, long long row_bytes,
+                             long long read_bytes, int order, int u, int workgroups,
+                             unsigned* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || read_bytes <= 0 || workgroups < 1)
+    return -1;
   if (((uintptr_t)buf & 15) != 0) return -1;
   const probe_fn fn = order == ORDER_WAVES ? pick<ORDER_WAVES>(u)
                       : order == ORDER_WORKGROUPS ? pick<ORDER_WORKGROUPS>(u)
                                                   : nullptr;
   if (!fn) return -1;
-  if (row_bytes % (2LL * u * 1024) != 0 || bytes % row_bytes != 0) return -1;
-  if (row_bytes / 16 > (1LL << 30)) return -1;
+  if (read_bytes % (u * 1024LL) != 0 || read_bytes > row_bytes || bytes % row_bytes != 0)
+    return -1;
+  if (row_bytes % 16 != 0 || row_bytes / 16 > (1LL << 30)) return -1;
   hipLaunchKernelGGL(fn, dim3(workgroups), dim3(kThreads), 0, (hipStream_t)stream,
-                     (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16), sink);
+                     (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16),
+                     (int)(read_bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
@@ -180,7 +187,7 @@ int skinny_probe_stream_read_tiles(const void* buf, long long bytes, long long r
   if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
   if (((uintptr_t)buf & 15) != 0 || row_bytes % 512 != 0) return -1;
   if (bytes % (16LL * wpb * row_bytes) != 0 || row_bytes / 16 > (1LL << 30)) return -1;
-  probe_fn fn = nullptr;
+  tiles_fn fn = nullptr;
   if (wpb == 4) fn = ksplit ? stream_read_tiles<4, true> : stream_read_tiles<4, false>;
   if (wpb == 8) fn = ksplit ? stream_read_tiles<8, true> : stream_read_tiles<8, false>;
   if (!fn || 64 * wpb > kMaxProbeThreads) return -1;
