@@ -515,13 +515,13 @@ def main():
             "weight_copies_rotated": copies,
             "variant": {0: "auto", 1: "vector", 2: "mfma"}[variant],
             "auto_plan": {"variant": {1: "vector", 2: "mfma"}.get(plan.variant, plan.variant),
-                          "waves": plan.waves},
+                          "waves": plan.waves, "kernel": sg.KERNEL_NAMES.get(plan.kernel)},
             "main_launches_per_step": n_launch,
             "gpu": torch.cuda.get_device_name(0),
         },
         "roofline": {
-            "kernel": {1: "skinny_rows", 2: "skinny_tiles"}.get(
-                plan.variant if variant == sg.VARIANT_AUTO else variant, "skinny_main"),
+            "kernel": (sg.KERNEL_NAMES.get(plan.kernel, "skinny_main") if variant == sg.VARIANT_AUTO
+                       else {1: "skinny_rows", 2: "skinny_tiles"}.get(variant, "skinny_main")),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

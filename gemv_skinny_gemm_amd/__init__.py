@@ -20,7 +20,7 @@ __all__ = [
     "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
     "Experts", "make_experts", "moe_workspace_bytes", "moe_linear", "moe_linear_timed",
     "moe_plan_query",
-    "MOE_X_PER_ROUTE", "MOE_SWIGLU", "MAX_TOPK",
+    "MOE_X_PER_ROUTE", "MOE_SWIGLU", "MAX_TOPK", "KERNEL_NAMES",
 ]
 
 BF16 = 0
@@ -33,7 +33,11 @@ MAX_LINEARS_PER_LAUNCH = 32
 MAX_TOPK = 16
 MOE_X_PER_ROUTE = 1
 MOE_SWIGLU = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
+# enum skinny_kernel (skinny_plan.kernel): the main kernel's form, by the name
+# of its HIP function (and instance).
+KERNEL_NAMES = {1: "skinny_rows", 2: "skinny_rows (lean)", 3: "skinny_rows_flat",
+                4: "skinny_tiles", 5: "skinny_tiles (8-wave)", 6: "skinny_tiles (K-split)"}
 STATIC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,8 +76,8 @@ class Experts(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     """struct skinny_plan"""
-    _fields_ = [("variant", ctypes.c_int), ("waves", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6)]
+    _fields_ = [("variant", ctypes.c_int), ("waves", ctypes.c_int), ("kernel", ctypes.c_int),
+                ("reserved", ctypes.c_int * 5)]
 
 
 _lib = None

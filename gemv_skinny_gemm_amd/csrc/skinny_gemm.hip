@@ -624,6 +624,254 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// skinny_rows_flat: the row kernel for one token (M = 1) with every wave's
+// loads running as one stream across its units.  In skinny_rows a wave's
+// pipeline fills at the start of each unit and drains at its end, so a short
+// row (8 KB of FP8 at K = 8192) leaves the wave with little in flight for a
+// good part of its time; here the wave keeps P slots of U 1 KB row segments
+// in flight and, near the end of a unit, the loads already reach into its
+// next unit (the next row group of the same or a later linear).  An FP8 scale
+// travels with each load (the lane's 16 weights lie in one 128 x 128 block),
+// so no scale row has to be staged between units.  Units are (row group of 8
+// rows, whole K), dealt round robin as in skinny_rows; wave i takes row
+// 8 g + i.  x of the current linear sits whole in LDS and is restaged between
+// two barriers when the consumed unit moves to the next linear (all waves of
+// a workgroup walk the same units, so they meet there).
+//
+// Every load is issued unconditionally, so the waits between a load and its
+// products stay exact: loads past a ragged row end re-read the row's last
+// chunk (those lanes do not add their products) and loads past the last unit
+// re-read its last segment (never consumed).  Outputs are collected in LDS
+// and written when x is restaged, when the buffer is full and at the end:
+// loads and stores may complete out of order with each other, so a store in
+// flight among the loads would turn the next wait into a full drain.  The
+// per-lane arithmetic is that of skinny_rows at M = 1; the lane sum has its
+// own fixed order (wave_sum_rows).
+constexpr int kFlatYUnits = 1024;       // units whose outputs the LDS buffer holds
+constexpr int kFlatYBytes = kFlatYUnits * kRowsWavesPerBlock * 2;
+
+// Sum over the 64 lanes in a fixed order, without a round trip through LDS:
+// each 16-lane row folds itself with rotations (DPP), then the four row sums
+// are read out and added as (r0 + r1) + (r2 + r3).  The result is in every
+// lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += dpp_f32<0x128>(v);                              // row_ror:8
+  v += dpp_f32<0x124>(v);                              // row_ror:4
+  v += dpp_f32<0x122>(v);                              // row_ror:2
+  v += dpp_f32<0x121>(v);                              // row_ror:1
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+template <int U>
+struct FlatSlot {
+  u32x4 w[U];            // 16 weight bytes of lane l in each of U segments of the row
+  float s[U];            // FP8: their block scales
+};
+
+template <int DT, int P, int U>
+__global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(const LaunchArgs a) {
+  constexpr int WPB = kRowsWavesPerBlock;
+  constexpr int kThreads = 64 * WPB;
+  constexpr bool kFp8 = DT == SKINNY_FP8_BS128;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  __bf16* ybuf = reinterpret_cast<__bf16*>(lds + a.x_lds_bytes);   // [unit][wave]
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long S = a.S;
+  if ((long long)blockIdx.x >= S) {
+    if (a.pairs && threadIdx.x == 0) a.pairs[blockIdx.x] = ArgmaxPair{-__builtin_inff(), a.lin[0].N};
+    return;
+  }
+  auto linear_of = [&](long long u, int l) {
+    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
+    return l;
+  };
+  // Load cursor: unit lu of linear ll, next segment lj of the wave's row.
+  long long lu = blockIdx.x;
+  int ll = linear_of(lu, 0);
+  int lj = 0;
+  const u32x4* lw = nullptr;
+  const float* ls = nullptr;
+  int lspt = 0, lcpr = 0;
+  auto enter_load = [&]() {
+    const LinDesc& L = a.lin[ll];
+    const int row = min((int)(lu - L.unit_base) * WPB + wv, L.N - 1);
+    lw = L.w + (size_t)row * L.cpr;
+    if (kFp8) ls = L.scale + (size_t)(row / kScaleBlock) * L.kblocks;
+    lspt = (L.spt + U - 1) / U;
+    lcpr = L.cpr;
+  };
+  auto load_next = [&](FlatSlot<U>& q) {
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      const int c = min((lj * U + v) * kSegChunks + lane, lcpr - 1);
+      q.w[v] = lw[c];
+      if (kFp8) q.s[v] = ls[c >> 3];              // chunk c: k in [16 c, 16 c + 16)
+    }
+    if (++lj == lspt) {
+      if (lu + a.G < S) {
+        lu += a.G;
+        ll = linear_of(lu, ll);
+        enter_load();
+        lj = 0;
+      } else {
+        lj = lspt - 1;
+      }
+    }
+  };
+  // Consume cursor: unit cu of linear cl, segment cj; rows of cfull whole
+  // segments end with a ragged one.  The outputs of the units yfirst,
+  // yfirst + G, ... (ny of them) wait in ybuf.
+  long long cu = blockIdx.x;
+  int cl = ll;
+  int cj = 0, crow = 0, cspt = 0, ccpr = 0, cfull = 0;
+  long long yfirst = cu;
+  int ny = 0;
+  float acc = 0.0f;
+  float gbv = -__builtin_inff();
+  int gbi = a.lin[0].N;
+  auto enter_consume = [&]() {
+    const LinDesc& L = a.lin[cl];
+    crow = (int)(cu - L.unit_base) * WPB + wv;
+    cspt = (L.spt + U - 1) / U;
+    ccpr = L.cpr;
+    cfull = L.cpr / (U * kSegChunks);
+  };
+  // Writes the buffered outputs of linear cl (after a barrier: every wave's
+  // entries are in).  The caller waits for the stores and barriers again
+  // before ybuf is reused.
+  auto flush_y = [&]() {
+    __syncthreads();
+    const LinDesc& L = a.lin[cl];
+    const bool vec = (reinterpret_cast<size_t>(L.y) & 15) == 0;
+    for (int i = threadIdx.x; i < ny; i += kThreads) {
+      const int row0 = (int)(yfirst + (long long)i * a.G - L.unit_base) * WPB;
+      const __bf16* src = ybuf + i * WPB;
+      if (vec && row0 + WPB <= L.N) {
+        *reinterpret_cast<u32x4*>(L.y + row0) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        for (int e = 0; e < WPB && row0 + e < L.N; ++e) L.y[row0 + e] = src[e];
+      }
+    }
+    ny = 0;
+  };
+  auto stage = [&]() {
+    __syncthreads();                                       // all done with the old x
+    const LinDesc& L = a.lin[cl];
+    const int xcpr = L.K >> 3;
+    stage_x_direct<kThreads, false>(L, 1, xcpr, 0, xcpr, xs, xcpr, nullptr);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // Products of one slot; true when the wave has no unit left.
+  auto consume = [&](const FlatSlot<U>& q) -> bool {
+    if (cj < cfull) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int c = (cj * U + v) * kSegChunks + lane;
+        if (kFp8) {
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(q.w[v], b0, b1);
+          acc = __builtin_fmaf(q.s[v], dot8(xs[2 * c + 1], b1, dot8(xs[2 * c], b0, 0.0f)), acc);
+        } else {
+          acc = dot8(xs[c], q.w[v], acc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int c = (cj * U + v) * kSegChunks + lane;
+        const bool ok = c < ccpr;
+        const int cx = ok ? c : 0;
+        float t;
+        if (kFp8) {
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(q.w[v], b0, b1);
+          t = __builtin_fmaf(q.s[v], dot8(xs[2 * cx + 1], b1, dot8(xs[2 * cx], b0, 0.0f)), acc);
+        } else {
+          t = dot8(xs[cx], q.w[v], acc);
+        }
+        acc = ok ? t : acc;
+      }
+    }
+    if (++cj < cspt) return false;
+    acc = wave_sum_rows(acc);
+    if (lane == 0) {
+      const __bf16 yv = (__bf16)acc;
+      ybuf[ny * WPB + wv] = yv;
+      if (a.pairs && crow < a.lin[cl].N) argmax_take((float)yv, crow, gbv, gbi);
+    }
+    acc = 0.0f;
+    cj = 0;
+    ++ny;
+    if (cu + a.G >= S) return true;
+    cu += a.G;
+    const int nl = linear_of(cu, cl);
+    if (nl != cl) {
+      flush_y();                                           // stage() waits and barriers
+      cl = nl;
+      yfirst = cu;
+      enter_consume();
+      stage();
+    } else {
+      if (ny == kFlatYUnits) {
+        flush_y();
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        yfirst = cu;
+      }
+      enter_consume();
+    }
+    return false;
+  };
+  FlatSlot<U> q[P];
+  enter_load();
+  enter_consume();
+#pragma unroll
+  for (int s = 0; s < P - 1; ++s) load_next(q[s]);
+  stage();
+  // P steps per pass: load the slot consumed last, consume the oldest.  Every
+  // pass issues the same loads in the same order, the last one included (a
+  // finished wave only skips its products), so each wait counts exactly the
+  // loads that may still be in flight.
+  bool done = false;
+  for (;;) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      load_next(q[(s + P - 1) % P]);
+      if (!done) done = consume(q[s]);
+    }
+    if (done) break;
+  }
+  flush_y();
+  if (a.pairs) {
+    // The workgroup's pair, from its waves' (M = 1: pairs[workgroup]).
+    __syncthreads();
+    ArgmaxPair* red = reinterpret_cast<ArgmaxPair*>(ybuf);
+    if (lane == 0) red[wv] = ArgmaxPair{gbv, gbi};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float bv = -__builtin_inff();
+      int bi = a.lin[0].N;
+      for (int w = 0; w < WPB; ++w) argmax_take(red[w].v, red[w].i, bv, bi);
+      a.pairs[blockIdx.x] = ArgmaxPair{bv, bi};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // skinny_tiles: matrix cores fed by rows streamed front to back.
 //
 // The MFMA B operand wants lane l to hold 16 bytes of W row (l % 16), so
@@ -1427,7 +1675,9 @@ struct KernelChoice {
   int band_rows = 0;           // rows per row group
   int wpb = 0;                 // waves per workgroup
   bool tiles = false;          // skinny_tiles (else skinny_rows)
+  bool flat = false;           // skinny_rows_flat
   int waves_per_cu = kTargetRowsWavesPerCU;   // cap on the persistent grid
+  int id = SKINNY_KERNEL_NONE; // enum skinny_kernel
 };
 
 template <int DT, int WPB>
@@ -1439,6 +1689,7 @@ KernelChoice tiles_kernel() {
   k.band_rows = kTileRows * WPB;
   k.wpb = WPB;
   k.tiles = true;
+  k.id = WPB == kTilesWavesSmall ? SKINNY_KERNEL_TILES : SKINNY_KERNEL_TILES_WIDE;
   return k;
 }
 
@@ -1452,6 +1703,7 @@ KernelChoice rows_kernel() {
   k.fn = skinny_rows<DT, MT, rows_u(MT, DT), R, WPB>;
   k.band_rows = WPB * R;
   k.wpb = WPB;
+  k.id = SKINNY_KERNEL_ROWS;
   return k;
 }
 
@@ -1461,6 +1713,7 @@ KernelChoice rows_kernel_lean() {
   KernelChoice k = rows_kernel<SKINNY_BF16, MT>();
   k.fn = skinny_rows<SKINNY_BF16, MT, rows_u_lean(MT), rows_r(MT), kRowsWavesPerBlock>;
   k.waves_per_cu = kRowsLeanWavesPerCU;
+  k.id = SKINNY_KERNEL_ROWS_LEAN;
   return k;
 }
 
@@ -1481,6 +1734,68 @@ KernelChoice pick_lean(int M) {
     case 4: return rows_kernel_lean<4>();
     default: return KernelChoice{};
   }
+}
+
+// One-token launches on skinny_rows_flat, one 8-wave workgroup per CU: FP8
+// with 2 slots of 2 KB per wave, bf16 with 3 of 1 KB.  Measured on MI355X
+// against the kernels they replace (same process, interleaved): FP8 8-layer
+// TP=1 launch 6.22 -> 6.29-6.30 TB/s (tile kernel before), FP8 vocabulary
+// projection 225 -> 217 us, one FP8 TP=1 layer (0.87 GB) -0.6%, hence the
+// launch size; other shapes of the FP8 kernel (1 KB slots, 3-8 deep, 16 waves
+// per CU) 0.3-3% slower.  bf16 stacks are as fast on the lean skinny_rows
+// instance (8-layer launch 6.50 vs 6.51 TB/s), which they keep; the bf16
+// flat instance serves forced row-kernel calls at M = 1.  Neither leaving x
+// staged across linears nor dropping the FP8 scale loads (timing-only
+// builds) moved the FP8 rate, so it is not the staging drains or the extra
+// loads that hold it below the bf16 rate.
+constexpr int flat_depth(int dtype) { return dtype == SKINNY_BF16 ? 3 : 2; }
+constexpr int flat_segs(int dtype) { return dtype == SKINNY_BF16 ? 1 : 2; }
+constexpr bool kFlatAutoBf16 = false;
+constexpr int kFlatWavesPerCU = 8;
+constexpr double kFlatLaunchBytes = 1.0e9;     // weight bytes of one launch
+
+template <int DT>
+KernelChoice flat_kernel() {
+  KernelChoice k;
+  k.fn = skinny_rows_flat<DT, flat_depth(DT), flat_segs(DT)>;
+  k.band_rows = kRowsWavesPerBlock;
+  k.wpb = kRowsWavesPerBlock;
+  k.flat = true;
+  k.waves_per_cu = kFlatWavesPerCU;
+  k.id = SKINNY_KERNEL_ROWS_FLAT;
+  return k;
+}
+
+// The flat kernel takes a launch of one token whose linears all read a plain
+// x that fits whole in its LDS (every segment of the longest row included).
+bool flat_fits(const skinny_linear* const* lin, int count, int M) {
+  if (M != 1) return false;
+  for (int i = 0; i < count; ++i) {
+    const skinny_linear& L = *lin[i];
+    if (L.reserved != kActNone) return false;
+    const int xc = L.dtype == SKINNY_BF16 ? 1 : 2;
+    const int cpr = L.K / (L.dtype == SKINNY_BF16 ? 8 : 16);
+    const long long spt = (cpr + kSegChunks - 1) / kSegChunks;
+    if (spt * kSegChunks * xc * 16 > kRowsXBudget) return false;
+  }
+  return true;
+}
+
+// Automatic variant: FP8 launches of at least kFlatLaunchBytes of weights take
+// the flat kernel when it fits; a forced VECTOR variant takes it whenever it
+// fits.
+bool use_flat(const skinny_linear* const* lin, int count, int M, int requested) {
+  if (requested == SKINNY_VARIANT_MFMA || !flat_fits(lin, count, M)) return false;
+  if (requested == SKINNY_VARIANT_VECTOR) return true;
+  if (lin[0]->dtype == SKINNY_BF16 && !kFlatAutoBf16) return false;
+  double bytes = 0;
+  for (int i = 0; i < count; ++i)
+    bytes += (lin[i]->dtype == SKINNY_BF16 ? 2.0 : 1.0) * lin[i]->N * lin[i]->K;
+  return bytes >= kFlatLaunchBytes;
+}
+
+KernelChoice pick_flat(int dtype) {
+  return dtype == SKINNY_BF16 ? flat_kernel<SKINNY_BF16>() : flat_kernel<SKINNY_FP8_BS128>();
 }
 
 template <int DT, int MT>
@@ -1592,6 +1907,7 @@ skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, 
 // does not depend on the shapes of the launch.
 int kernel_lds(const KernelChoice& k, int dtype) {
   if (k.tiles) return tiles_lds(k.wpb);
+  if (k.flat) return kRowsXBudget + kFlatYBytes;
   return kRowsXBudget +
          (dtype == SKINNY_FP8_BS128 ? k.wpb * kRowsMaxKBlocks * (int)sizeof(float) : 0);
 }
@@ -1656,10 +1972,12 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
                            hipEvent_t ev_before, hipEvent_t ev_after,
                            ArgmaxPair* pairs = nullptr, int* pairs_grid = nullptr) {
   const int dtype = lin[0]->dtype;
+  const int requested = variant;
   if (variant == SKINNY_VARIANT_AUTO) variant = auto_variant(lin, count, M);
   KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
+  if (use_flat(lin, count, M, requested)) k = pick_flat(dtype);
   if (k.tiles && tiles_large(lin, count, M, dev.cus))
     k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
                              : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
@@ -1701,6 +2019,9 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
   plan_chunks(a, count, G, dtype, k.tiles);
+  if (k.flat)
+    for (int i = 0; i < count; ++i)
+      if (a.lin[i].chunks != 1) return SKINNY_ERR_UNSUPPORTED;   // x fits: never split
   G = grid_for_chunks(G, a);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
@@ -1800,7 +2121,7 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   int variant = SKINNY_VARIANT_AUTO;
   int waves = 0;
   if (plan) {
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (plan->reserved[i] != 0) return SKINNY_ERR_INVALID_ARG;
     variant = plan->variant;
     waves = plan->waves;
@@ -2316,6 +2637,14 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
   if (!k.tiles && rows_lean(group, n, M)) k = pick_lean(M);
+  if (use_flat(group, n, M, SKINNY_VARIANT_AUTO)) {
+    out->variant = SKINNY_VARIANT_VECTOR;
+    k = pick_flat(linears[0].dtype);
+  }
+  if (k.tiles && tiles_large(group, n, M, d.cus))
+    k = linears[0].dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
+                                        : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
+  out->kernel = k.id;
   const int lds = kernel_lds(k, linears[0].dtype);
   st = ensure_lds(k.fn, lds);
   if (st != SKINNY_OK) return st;
@@ -2462,7 +2791,11 @@ skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int to
   const skinny_status st = check_experts(experts, T, topk, flags);
   if (st != SKINNY_OK) return st;
   memset(out, 0, sizeof *out);
-  out->variant = moe_plan(*experts, T, topk).rows ? SKINNY_VARIANT_VECTOR : SKINNY_VARIANT_MFMA;
+  const MoePlan p = moe_plan(*experts, T, topk);
+  out->variant = p.rows ? SKINNY_VARIANT_VECTOR : SKINNY_VARIANT_MFMA;
+  out->kernel = p.rows ? SKINNY_KERNEL_ROWS
+                : p.ks ? SKINNY_KERNEL_TILES_KSPLIT
+                : p.wpb == kTilesWavesSmall ? SKINNY_KERNEL_TILES : SKINNY_KERNEL_TILES_WIDE;
   return SKINNY_OK;
 }
 

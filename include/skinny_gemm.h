@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SKINNY_ABI_VERSION 1
+#define SKINNY_ABI_VERSION 2
 #define SKINNY_MAX_M 16
 /* Linears one main-kernel launch carries; longer stacks use several launches. */
 #define SKINNY_MAX_LINEARS_PER_LAUNCH 32
@@ -94,11 +94,25 @@ typedef struct skinny_linear {
   void* y;              /* y[M][N] bf16                                     */
 } skinny_linear;
 
+/* Main kernel of a launch, as the plan queries report it. */
+enum skinny_kernel {
+  SKINNY_KERNEL_NONE = 0,
+  SKINNY_KERNEL_ROWS = 1,         /* skinny_rows (VECTOR), deep instance; MoE form      */
+  SKINNY_KERNEL_ROWS_LEAN = 2,    /* skinny_rows, lean instance (bf16 launches >= 0.4 GB) */
+  SKINNY_KERNEL_ROWS_FLAT = 3,    /* skinny_rows_flat (one token, loads streamed across
+                                     units; FP8 launches >= 1 GB)                       */
+  SKINNY_KERNEL_TILES = 4,        /* skinny_tiles (MFMA), 4-wave workgroups; MoE form  */
+  SKINNY_KERNEL_TILES_WIDE = 5,   /* skinny_tiles, 8-wave workgroups                    */
+  SKINNY_KERNEL_TILES_KSPLIT = 6  /* skinny_tiles' K-split form (one-token MoE slices)  */
+};
+
 /* Launch plan override, for tests and benchmarks.  Zero-initialised = automatic. */
 typedef struct skinny_plan {
   int variant;          /* enum skinny_variant                               */
   int waves;            /* persistent waves per main launch; 0 = automatic   */
-  int reserved[6];      /* must be 0                                         */
+  int kernel;           /* enum skinny_kernel, filled by the plan queries;
+                           ignored on input                                  */
+  int reserved[5];      /* must be 0                                         */
 } skinny_plan;
 
 /* Bytes of workspace a single linear needs: at least SKINNY_MIN_WORKSPACE_BYTES
@@ -195,7 +209,8 @@ int skinny_band_rows(int dtype, int variant, int M);
 /* The automatic plan (fills *out) of the first launch of linears[0]'s dtype
  * on the current device: a call launches its linears grouped by dtype, at
  * most SKINNY_MAX_LINEARS_PER_LAUNCH per launch, and each launch chooses its
- * own variant (it can depend on the launch's size). */
+ * own variant (it can depend on the launch's size).  out->variant, ->waves
+ * (persistent waves of the main launch) and ->kernel (its form) are set. */
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);
 
@@ -318,8 +333,8 @@ skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void*
 /* The main kernel skinny_moe_linear takes for these experts and routes, for
  * tests and benchmarks: out->variant is SKINNY_VARIANT_VECTOR (the row
  * kernel, for one-token slices of rows long enough to keep its loads in
- * flight) or SKINNY_VARIANT_MFMA (the tile kernel); out->waves and
- * out->reserved are 0.  Host logic only (no device call).  Errors: the
+ * flight) or SKINNY_VARIANT_MFMA (the tile kernel); out->kernel names the
+ * kernel's form; out->waves and out->reserved are 0.  Host logic only (no device call).  Errors: the
  * argument checks of skinny_moe_linear on experts, T, topk and flags, and
  * SKINNY_ERR_INVALID_ARG for a NULL out. */
 skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int topk, int flags,

@@ -339,6 +339,14 @@ def test_moe_plan_query():
     for dt in (sg.BF16, sg.FP8_BS128):
         assert variant(dt, 31744, 1) == sg.VARIANT_VECTOR                # 62 KB of x
         assert variant(dt, 32768, 1) == sg.VARIANT_MFMA                  # 64 KB: past the window
+
+    def kernel(dtype, K, T, N=3072):
+        ex = sg.Experts(dtype, 8, N, K, A, None if dtype == sg.BF16 else A + 0x8000000)
+        return sg.KERNEL_NAMES[sg.moe_plan_query(ex, T, 2).kernel]
+    for dt in (sg.BF16, sg.FP8_BS128):
+        assert kernel(dt, 4096, 1) == "skinny_rows"
+        assert kernel(dt, 1536, 1, N=4096) == "skinny_tiles (K-split)"     # the verify step's down
+        assert kernel(dt, 4096, 6) in ("skinny_tiles", "skinny_tiles (8-wave)")
     L = sg.lib()
     plan = sg.Plan()
     ex = sg.Experts(sg.BF16, 8, 64, 64, A, None)

@@ -242,8 +242,10 @@ def test_tp8_layer_stack(M):
 
 def test_automatic_variant():
     """bf16 takes the row kernel at M <= 2, and at M = 3-4 for launches of at
-    least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise, and
-    for FP8 at every M.  The stack's launches hold up to 32 linears."""
+    least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise.  FP8
+    takes the tile kernel but for one-token launches of at least 1 GB of
+    weights (the flat row kernel).  The stack's launches hold up to 32
+    linears."""
     V, T = sg.VARIANT_VECTOR, sg.VARIANT_MFMA
 
     def variant(shapes, M, dt=sg.BF16):
@@ -255,4 +257,15 @@ def test_automatic_variant():
     assert [variant(tp8, M) for M in (1, 2, 3, 4, 5, 8, 16)] == [V, V, T, T, T, T, T]
     assert [variant(tp1, M) for M in (1, 2, 3, 4)] == [V, V, T, T]                  # 1.76 GB
     assert [variant(tp1 * 2, M) for M in (1, 2, 3, 4, 5, 6, 8)] == [V, V, V, V, T, T, T]
-    assert [variant(tp1 * 2, M, sg.FP8_BS128) for M in (1, 2, 4)] == [T, T, T]
+    assert [variant(tp1 * 2, M, sg.FP8_BS128) for M in (1, 2, 4)] == [V, T, T]   # 1.76 GB
+    assert variant(tp1, 1, sg.FP8_BS128) == T                                     # 0.88 GB
+    assert variant([(152064, 8192)], 1, sg.FP8_BS128) == V                       # 1.25 GB
+
+    def kernel(shapes, M, dt=sg.BF16):
+        scale = None if dt == sg.BF16 else 0x300000
+        lins = [sg.Linear(dt, N, K, 0, 0x100000, scale, 0x2000000, 0x4000000) for N, K in shapes]
+        return sg.KERNEL_NAMES[sg.plan_query(lins, M).kernel]
+    assert kernel(tp1 * 2, 1, sg.FP8_BS128) == "skinny_rows_flat"
+    assert kernel(tp1 * 2, 1) == "skinny_rows (lean)"
+    assert kernel(tp8, 1) == "skinny_rows"
+    assert kernel(tp8, 8) == "skinny_tiles"
