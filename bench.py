@@ -158,7 +158,8 @@ def step_work(specs, M, ids=None):
 def moe_cpu_baseline(specs, ids, seed=0):
     """The fp64 oracle over the whole MoE step (it is small): gate_up, then
     down on the oracle's own bf16 gate_up outputs.  Returns seconds, bytes,
-    threads, (g_ref, g_a) and a description."""
+    threads, (g_ref, g_a, the down experts' weights and scales) and a
+    description."""
     import numpy as np
 
     import oracle
@@ -186,7 +187,7 @@ def moe_cpu_baseline(specs, ids, seed=0):
     secs = float(np.median(times))
     desc = (f"the whole step ({T} tokens, {ids.size} routes, gate_up then down), compute only, "
             "median of 3 runs")
-    return secs, sum(moe_bytes(specs, ids)), oracle.host_threads(), (g_ref, g_a), desc
+    return secs, sum(moe_bytes(specs, ids)), oracle.host_threads(), (g_ref, g_a, ws[1]), desc
 
 
 def measured_traffic(workload, M):
@@ -372,11 +373,22 @@ def main():
                                    None if sc is None else sc.view(E, -1, sc.shape[1]))
         moe_ex = [(experts(t[0]), experts(t[1])) for t in tensors]
         routes = ids_host.size
-        moe_gu = torch.empty((routes, specs[0].N // E), dtype=torch.bfloat16, device="cuda")
         moe_y = torch.empty((routes, specs[1].N // E), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(max(sg.moe_workspace_bytes(moe_ex[0][0], M, wl.MOE_TOPK),
-                             sg.moe_workspace_bytes(moe_ex[0][1], M, wl.MOE_TOPK, True, True)),
+        # Zeroed: the one-token launch keeps its counters at the workspace's
+        # start; the gate_up outputs follow them.
+        ws = torch.zeros(sg.moe_mlp_workspace_bytes(moe_ex[0][0], moe_ex[0][1], M, wl.MOE_TOPK),
                          dtype=torch.uint8, device="cuda")
+        n_gu = specs[0].N // E
+        c0 = sg.MOE_MLP_COUNTER_BYTES
+        one_launch = sg.moe_mlp_plan_query(moe_ex[0][0], moe_ex[0][1], M, wl.MOE_TOPK).kernel == 7
+
+        def moe_gate_up():
+            """The gate_up outputs the last call left in the workspace (one
+            launch: 64-bit words, a call number above two bf16 outputs)."""
+            if one_launch:
+                w = ws[c0:c0 + routes * n_gu * 4].view(torch.int32).view(routes, n_gu // 2, 2)
+                return w[:, :, 0].contiguous().view(torch.bfloat16).view(routes, n_gu)
+            return ws[c0:c0 + routes * n_gu * 2].view(torch.bfloat16).view(routes, n_gu)
     else:
         ws = torch.empty(sg.stack_workspace_bytes(sets[0], M), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -385,9 +397,11 @@ def main():
     timed_sets = [st[:1] for st in sets] if mlp else sets
     timed_bytes = wl.algorithmic_bytes(specs[:1], M) if mlp else step_bytes
     if moe:
-        # The MoE step's dominant kernel is its gate_up launch (two thirds of the bytes).
-        timed_bytes = moe_gu_bytes
-        plan = sg.moe_plan_query(moe_ex[0][0], M, wl.MOE_TOPK)
+        # The MoE step's dominant kernel: its one launch (one token), else its
+        # gate_up launch (two thirds of the bytes).
+        plan = sg.moe_mlp_plan_query(moe_ex[0][0], moe_ex[0][1], M, wl.MOE_TOPK)
+        timed_bytes = step_bytes if sg.KERNEL_NAMES.get(plan.kernel) == "skinny_moe_mlp1" \
+            else moe_gu_bytes
         n_launch = 1
     else:
         plan = sg.plan_query(timed_sets[0], M)
@@ -398,8 +412,7 @@ def main():
     def step(i):
         if moe:
             ex_gu, ex_dn = moe_ex[i % copies]
-            sg.moe_linear(ex_gu, tensors[i % copies][0][0], ids, moe_gu, ws)
-            sg.moe_linear(ex_dn, moe_gu, ids, moe_y, ws, x_per_route=True, swiglu=True)
+            sg.moe_mlp_swiglu(ex_gu, ex_dn, tensors[i % copies][0][0], ids, moe_y, ws)
             return
         if head or mlp:
             if variant != sg.VARIANT_AUTO or args.waves:
@@ -469,7 +482,8 @@ def main():
         handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
         if moe:
             c = (args.warmup + i) % copies
-            sg.moe_linear_timed(moe_ex[c][0], tensors[c][0][0], ids, moe_gu, ws, handles)
+            sg.moe_mlp_swiglu_timed(moe_ex[c][0], moe_ex[c][1], tensors[c][0][0], ids, moe_y, ws,
+                                    handles)
             continue
         sg.linear_run_timed(timed_sets[(args.warmup + i) % copies], M, ws, handles,
                             variant=variant, waves=args.waves)
@@ -557,12 +571,20 @@ def main():
 
     if not args.no_cpu_baseline and moe:
         import oracle
-        secs, sbytes, threads, (g_ref, g_a), desc = moe_cpu_baseline(specs, ids_host)
+        secs, sbytes, threads, (g_ref, g_a, (wd, sd)), desc = moe_cpu_baseline(specs, ids_host)
         step(0)
         torch.cuda.synchronize()
+        moe_gu = moe_gate_up()
         ok, worst, _ = oracle.check(moe_gu.float().cpu().double().numpy(), g_ref, g_a)
         if not ok:
             log(f"GPU gate_up output outside the bound (worst {worst:.3g})")
+        # down against the oracle on the GPU's own gate_up outputs.
+        h = moe_gu.cpu().view(torch.int16).numpy().view(np.uint16)
+        d_ref, d_a = oracle.moe_linear(h, ids_host, wd, scales=sd, x_per_route=True, swiglu=True)
+        ok_d, worst_d, _ = oracle.check(moe_y.float().cpu().double().numpy(), d_ref, d_a)
+        if not ok_d:
+            log(f"GPU down output outside the bound (worst {worst_d:.3g})")
+        worst = max(worst, worst_d)
         result["cpu_baseline"] = {
             "value": round(sbytes / secs / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "sample": desc, "us_per_step": round(secs * 1e6, 1),

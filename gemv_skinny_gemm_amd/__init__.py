@@ -19,7 +19,8 @@ __all__ = [
     "status_string", "abi_version", "argmax_bf16", "argmax_workspace_bytes", "lm_head_argmax",
     "lm_head_workspace_bytes", "Mlp", "make_mlp", "mlp_workspace_bytes", "mlp_swiglu",
     "Experts", "make_experts", "moe_workspace_bytes", "moe_linear", "moe_linear_timed",
-    "moe_plan_query",
+    "moe_plan_query", "moe_mlp_workspace_bytes", "moe_mlp_swiglu", "moe_mlp_swiglu_timed",
+    "moe_mlp_set_spin_limit", "moe_mlp_gave_up", "moe_mlp_plan_query", "MOE_MLP_COUNTER_BYTES",
     "MOE_X_PER_ROUTE", "MOE_SWIGLU", "MAX_TOPK", "KERNEL_NAMES",
 ]
 
@@ -37,8 +38,10 @@ ABI_VERSION = 2
 # enum skinny_kernel (skinny_plan.kernel): the main kernel's form, by the name
 # of its HIP function (and instance).
 KERNEL_NAMES = {1: "skinny_rows", 2: "skinny_rows (lean)", 3: "skinny_rows_flat",
-                4: "skinny_tiles", 5: "skinny_tiles (8-wave)", 6: "skinny_tiles (K-split)"}
+                4: "skinny_tiles", 5: "skinny_tiles (8-wave)", 6: "skinny_tiles (K-split)",
+                7: "skinny_moe_mlp1"}
 STATIC_SCRATCH_BYTES = 64 << 20
+MOE_MLP_COUNTER_BYTES = 256   # moe_mlp_swiglu's workspace: counter and flag, then gate_up outputs
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libskinny_gemm.so"
@@ -137,6 +140,17 @@ def _bind(path: str):
     L.skinny_moe_linear_timed.argtypes = [ep, vp, vp, i, i, i, vp, ctypes.POINTER(vp), vp, sz, vp]
     L.skinny_moe_plan_query.restype = i
     L.skinny_moe_plan_query.argtypes = [ep, i, i, i, ctypes.POINTER(Plan)]
+    L.skinny_moe_mlp_workspace_bytes.restype = sz
+    L.skinny_moe_mlp_workspace_bytes.argtypes = [ep, ep, i, i]
+    L.skinny_moe_mlp_swiglu.restype = i
+    L.skinny_moe_mlp_swiglu.argtypes = [ep, ep, vp, vp, i, i, vp, vp, sz, vp]
+    L.skinny_moe_mlp_swiglu_timed.restype = i
+    L.skinny_moe_mlp_swiglu_timed.argtypes = [ep, ep, vp, vp, i, i, vp, ctypes.POINTER(vp), vp,
+                                              sz, vp]
+    L.skinny_moe_mlp_plan_query.restype = i
+    L.skinny_moe_mlp_plan_query.argtypes = [ep, ep, i, i, ctypes.POINTER(Plan)]
+    L.skinny_moe_mlp_set_spin_limit.restype = None
+    L.skinny_moe_mlp_set_spin_limit.argtypes = [ctypes.c_longlong]
     L.skinny_status_string.restype = ctypes.c_char_p
     L.skinny_status_string.argtypes = [i]
     L.skinny_abi_version.restype = i
@@ -489,6 +503,66 @@ def moe_linear_timed(experts: Experts, x, ids, y, workspace, events, x_per_route
                                          _moe_flags(x_per_route, swiglu), _ptr(y), ev, wp, wb,
                                          _stream(stream)), "skinny_moe_linear_timed")
     return y
+
+
+def _check_moe_mlp(gate_up: Experts, down: Experts, x, ids, y):
+    T, topk = _shape2(ids)
+    _need(ids, (T, topk), _I32, "ids")
+    _need(x, (T, gate_up.K), _BF16, "x")
+    _need(y, (T * topk, down.N), _BF16, "y")
+    return T, topk
+
+
+def moe_mlp_workspace_bytes(gate_up: Experts, down: Experts, T: int, topk: int) -> int:
+    """Bytes of workspace moe_mlp_swiglu needs; allocate it zeroed (its first
+    256 bytes are counters that must start at zero)."""
+    return lib().skinny_moe_mlp_workspace_bytes(ctypes.byref(gate_up), ctypes.byref(down), T,
+                                                topk)
+
+
+def moe_mlp_swiglu(gate_up: Experts, down: Experts, x, ids, y, workspace, stream=None):
+    """y[r] = bf16(silu(g) * u) . Wdown_e^T with [g | u] = x[t] . Wgate_up_e^T
+    (bf16) for route r = t * topk + j, e = ids[t][j]; one launch for one token."""
+    T, topk = _check_moe_mlp(gate_up, down, x, ids, y)
+    wp, wb = _ws(workspace)
+    _check(lib().skinny_moe_mlp_swiglu(ctypes.byref(gate_up), ctypes.byref(down), _ptr(x),
+                                       _ptr(ids), T, topk, _ptr(y), wp, wb, _stream(stream)),
+           "skinny_moe_mlp_swiglu")
+    return y
+
+
+def moe_mlp_swiglu_timed(gate_up: Experts, down: Experts, x, ids, y, workspace, events,
+                         stream=None):
+    """moe_mlp_swiglu recording the two hipEvent_t handles in `events` around
+    its main launch (the one launch for one token, else gate_up's)."""
+    T, topk = _check_moe_mlp(gate_up, down, x, ids, y)
+    wp, wb = _ws(workspace)
+    ev = (ctypes.c_void_p * 2)(*events)
+    _check(lib().skinny_moe_mlp_swiglu_timed(ctypes.byref(gate_up), ctypes.byref(down), _ptr(x),
+                                             _ptr(ids), T, topk, _ptr(y), ev, wp, wb,
+                                             _stream(stream)), "skinny_moe_mlp_swiglu_timed")
+    return y
+
+
+def moe_mlp_plan_query(gate_up: Experts, down: Experts, T: int, topk: int) -> Plan:
+    """The main launch moe_mlp_swiglu makes (kernel 7 = the one launch)."""
+    plan = Plan()
+    _check(lib().skinny_moe_mlp_plan_query(ctypes.byref(gate_up), ctypes.byref(down), T, topk,
+                                           ctypes.byref(plan)), "skinny_moe_mlp_plan_query")
+    return plan
+
+
+def moe_mlp_set_spin_limit(polls: int) -> None:
+    """Polls before the one-token launch's wait gives up (< 0: it does not
+    wait); for tests of that path."""
+    lib().skinny_moe_mlp_set_spin_limit(int(polls))
+
+
+def moe_mlp_gave_up(workspace) -> bool:
+    """Whether a wait of the one-token launch on this workspace gave up (its
+    counter word 2; synchronizes with the device)."""
+    import torch
+    return bool(int(workspace[:16].view(torch.int32)[2].item()))
 
 
 def moe_plan_query(experts: Experts, T: int, topk: int, x_per_route: bool = False,

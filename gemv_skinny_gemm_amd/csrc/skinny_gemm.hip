@@ -46,6 +46,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -62,6 +63,7 @@ constexpr int kTileRows = 16;          // rows of one MFMA B operand
 constexpr int kSegChunks = 64;          // 16-byte chunks per 1 KB row segment (skinny_rows)
 constexpr int kCombineThreads = 256;
 constexpr int kMaxWaves = 8192;         // 256 CUs x 32 resident waves
+constexpr int kMaxLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kScaleBlock = 128;
 constexpr int kRowsMaxKBlocks = 256;    // skinny_rows FP8: K <= 32768
 // skinny_rows shape, measured on MI355X over the Qwen2.5-72B shapes: 8 waves
@@ -269,6 +271,7 @@ __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr
 // neither a host round trip nor a launch of its own.  Routes whose expert is
 // outside [0, E) belong to no slice; their y rows are zeroed.
 constexpr int kMoeMaxRoutes = 256;
+constexpr int kMoeMlpMaxRoutes = 16;      // routes of the one-token fused MLP (top-k)
 constexpr int kMoeMaxCap = 16;
 
 struct MoeTable {
@@ -1297,6 +1300,333 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_moe_combine(const Laun
 }
 
 // ---------------------------------------------------------------------------
+// The experts' gated MLP for one token in one launch: gate_up of each chosen
+// expert, the SiLU-gated product, then down ("Multi-GPU Inference and
+// Serving at Scale", Example 8: a router sends the token to its top-k
+// experts; Example 3: an MLP's activation sits between its two linears).
+// Route r uses expert ids[r]; routes whose id is outside [0, E) have zero
+// outputs.  With one token each expert is read for one route, and two
+// dependent launches cost more than their bytes (a launch's start, its first
+// loads and its tail, twice); here the workgroups pass gate_up's outputs to
+// each other within the launch.  Each output pair is written as one 64-bit
+// word carrying the call's number, and a workgroup that computes down rows
+// reads the words of its route until all carry this call's number: the data
+// is its own signal, with no counter to wait on between the linears.  The
+// call's number is the count of finished workgroups over all earlier calls
+// divided by G, plus one; each workgroup adds itself to that count as it
+// ends, and reads it at its start (at most G - 1 others of the same call can
+// have ended by then, which leaves the quotient unchanged).  The grid is the
+// resident one, so every workgroup whose outputs are waited for is running;
+// the wait gives up after `spin` polls and then sets a flag word, so it never
+// hangs.
+//
+// Units are 8 rows of one route (one row per wave): gate_up units dealt round
+// robin over the grid, down units of each route over a group of workgroups
+// (so each reads the outputs of one route).  A wave issues the loads of all
+// its gate_up rows at its start and of all its down rows once its gate_up
+// products are done (MA and MB slots of U 1 KB segments, unconditional, in a
+// straight line so the waits stay exact), so down's weights arrive while the
+// outputs of gate_up are passed on.
+struct MoeMlpArgs {
+  const u32x4* wg;       // gate_up experts [E][N1][K1], 16-byte chunks
+  const float* sg;       // their FP8 scales [E][ceil(N1/128)][ceil(K1/128)]
+  const u32x4* wd;       // down experts [E][N2][K2]
+  const float* sd;
+  long long wg_stride, sg_stride, wd_stride, sd_stride;   // per expert
+  int E, R;              // experts; routes (top-k of the one token)
+  int N1, K1, cpr1, spt1, kb1;   // gate_up: N1 = 2 K2 rows ([gate | up]) of K1
+  int N2, K2, cpr2, spt2, kb2;   // down: N2 rows of K2
+  const int* ids;        // [R]
+  const u32x4* x;        // [K1] bf16
+  unsigned long long* gu;         // [R][N1 / 2] gate_up outputs: call number << 32 | 2 x bf16
+  __bf16* y;             // [R][N2] bf16
+  unsigned long long* ended;      // workgroups finished, over all calls
+  int* gave_up;          // set when a wait gives up
+  long long spin;        // polls before a wait gives up; < 0: do not wait
+  int G;
+  int hs_off, ya_off, yb_off, tab_off;   // LDS: x at 0, h, the output buffers, the route table
+};
+
+// A workgroup's walk over its units of one linear: unit t is b + t G, in
+// route k (of the valid routes) at row group grp; slot item j.
+struct MlpCursor {
+  int t, j, k, grp;
+};
+
+__device__ __forceinline__ MlpCursor mlp_cursor(int u, int g) {
+  return MlpCursor{0, 0, u / g, u % g};
+}
+
+__device__ __forceinline__ void mlp_advance(MlpCursor& c, int items, int g, int G) {
+  if (++c.j < items) return;
+  c.j = 0;
+  ++c.t;
+  c.grp += G;
+  while (c.grp >= g) {
+    c.grp -= g;
+    ++c.k;
+  }
+}
+
+template <int DT, int MA, int MB, int U>
+__global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_moe_mlp1(const MoeMlpArgs a) {
+  constexpr int WPB = kRowsWavesPerBlock;
+  constexpr int kThreads = 64 * WPB;
+  constexpr bool kFp8 = DT == SKINNY_FP8_BS128;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  u32x4* hs = reinterpret_cast<u32x4*>(lds + a.hs_off);      // h of route kb: [K2 / 8]
+  __bf16* ya = reinterpret_cast<__bf16*>(lds + a.ya_off);    // [gate_up unit][wave]
+  __bf16* yb = reinterpret_cast<__bf16*>(lds + a.yb_off);    // [down unit][wave]
+  int* tab = reinterpret_cast<int*>(lds + a.tab_off);        // nv, route[16], expert[16], call
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int G = a.G;
+  // x into LDS and the router's choices, with one wait for both.
+  const int n1x = a.K1 >> 3;
+  for (int p = wv; p * 64 < n1x; p += WPB)
+    __builtin_amdgcn_global_load_lds(a.x + min(p * 64 + lane, n1x - 1),
+                                     (__attribute__((address_space(3))) void*)(xs + p * 64), 16,
+                                     0, 0);
+  int e = -1;
+  if (wv == 0 && lane < a.R) e = a.ids[lane];
+  unsigned long long ended = 0;
+  if (threadIdx.x == 0)
+    ended = __hip_atomic_load(a.ended, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (wv == 0) {                         // valid routes, in route order
+    const bool ok = lane < a.R && e >= 0 && e < a.E;
+    const unsigned long long m = __ballot(ok);
+    if (ok) {
+      const int pos = __popcll(m & ((1ull << lane) - 1));
+      tab[1 + pos] = lane;
+      tab[1 + kMoeMlpMaxRoutes + pos] = e;
+    }
+    if (lane == 0) {
+      tab[0] = __popcll(m);
+      tab[1 + 2 * kMoeMlpMaxRoutes] = (int)(unsigned)(ended / G + 1);
+    }
+  }
+  __syncthreads();
+  const int nv = __builtin_amdgcn_readfirstlane(tab[0]);
+  const int gA = (a.N1 + WPB - 1) / WPB, gB = (a.N2 + WPB - 1) / WPB;
+  const int UA = nv * gA;
+  const int nua = b < UA ? (UA - 1 - b) / G + 1 : 0;     // this workgroup's gate_up units
+  // down: the workgroups are split into one group per valid route, so each
+  // stages h of one route only (half the reads of the intermediate at top-2,
+  // which all workgroups read at once); workgroup b takes row groups
+  // lb, lb + Gk, ... of route kb.
+  const int kb = nv > 0 ? b * nv / G : 0;
+  const int wg0 = nv > 0 ? (kb * G + nv - 1) / nv : 0;
+  const int Gk = nv > 0 ? ((kb + 1) * G + nv - 1) / nv - wg0 : 1;
+  const int lb = b - wg0;
+  const int nub = nv > 0 && lb < gB ? (gB - 1 - lb) / Gk + 1 : 0;
+  const int ia = (a.spt1 + U - 1) / U, ib = (a.spt2 + U - 1) / U;   // slots per unit
+  const int k2c = a.K2 >> 3;                                          // h chunks per route
+
+  // Every slot is loaded, all at the start: the slots of a linear walk the
+  // workgroup's units item by item; slots past its units re-read its last
+  // item (or x, if it has none), and their products are skipped.
+  auto load_slot = [&](FlatSlot<U>& q, const MlpCursor& c, int n, bool down) {
+    const u32x4* w = a.x;
+    const float* sc = a.sg;
+    int cpr = 1, j = 0;
+    if (n > 0) {
+      MlpCursor d = c;
+      if (c.t >= n) {                    // the last unit's last item
+        if (down) {
+          d = MlpCursor{n - 1, ib - 1, kb, lb + (n - 1) * Gk};
+        } else {
+          d = mlp_cursor(b + (n - 1) * G, gA);
+          d.j = ia - 1;
+        }
+      }
+      j = d.j;
+      const int N = down ? a.N2 : a.N1;
+      const int row = min(d.grp * WPB + wv, N - 1);
+      const int ex = __builtin_amdgcn_readfirstlane(tab[1 + kMoeMlpMaxRoutes + d.k]);
+      cpr = down ? a.cpr2 : a.cpr1;
+      w = (down ? a.wd + (size_t)ex * a.wd_stride : a.wg + (size_t)ex * a.wg_stride) +
+          (size_t)row * cpr;
+      if (kFp8)
+        sc = (down ? a.sd + (size_t)ex * a.sd_stride : a.sg + (size_t)ex * a.sg_stride) +
+             (size_t)(row / kScaleBlock) * (down ? a.kb2 : a.kb1);
+    }
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      const int c = min((j * U + v) * kSegChunks + lane, cpr - 1);
+      q.w[v] = w[c];
+      if (kFp8) q.s[v] = sc[c >> 3];
+    }
+  };
+  FlatSlot<U> qa[MA], qb[MB];
+  {
+    MlpCursor c = mlp_cursor(b, gA);
+#pragma unroll
+    for (int s = 0; s < MA; ++s) {
+      load_slot(qa[s], c, nua, false);
+      mlp_advance(c, ia, gA, G);
+    }
+  }
+  auto down_cursor = [&]() { return MlpCursor{0, 0, kb, lb}; };
+  auto down_advance = [&](MlpCursor& c) {
+    if (++c.j < ib) return;
+    c.j = 0;
+    ++c.t;
+    c.grp += Gk;
+  };
+  auto load_down = [&]() {
+    MlpCursor c = down_cursor();
+#pragma unroll
+    for (int s = 0; s < MB; ++s) {
+      load_slot(qb[s], c, nub, true);
+      down_advance(c);
+    }
+  };
+
+  float acc = 0.0f;
+  // Products of one slot at cursor c, from src; at a unit's last item the
+  // row's sum goes to the LDS buffer.
+  auto consume = [&](const FlatSlot<U>& q, const MlpCursor& c, int n, bool down,
+                     const u32x4* src) {
+    if (c.t >= n) return;
+    const int cpr = down ? a.cpr2 : a.cpr1;
+    const int j = c.j;
+    if ((j + 1) * U * kSegChunks <= cpr) {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int ci = (j * U + v) * kSegChunks + lane;
+        if (kFp8) {
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(q.w[v], b0, b1);
+          acc = __builtin_fmaf(q.s[v], dot8(src[2 * ci + 1], b1, dot8(src[2 * ci], b0, 0.0f)),
+                               acc);
+        } else {
+          acc = dot8(src[ci], q.w[v], acc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        const int ci = (j * U + v) * kSegChunks + lane;
+        const bool ok = ci < cpr;
+        const int cx = ok ? ci : 0;
+        float tv;
+        if (kFp8) {
+          u32x4 b0, b1;
+          e4m3x16_to_bf16(q.w[v], b0, b1);
+          tv = __builtin_fmaf(q.s[v], dot8(src[2 * cx + 1], b1, dot8(src[2 * cx], b0, 0.0f)),
+                              acc);
+        } else {
+          tv = dot8(src[cx], q.w[v], acc);
+        }
+        acc = ok ? tv : acc;
+      }
+    }
+    if (j == (down ? ib : ia) - 1) {
+      acc = wave_sum_rows(acc);
+      if (lane == 0) (down ? yb : ya)[c.t * WPB + wv] = (__bf16)acc;
+      acc = 0.0f;
+    }
+  };
+  {
+    MlpCursor c = mlp_cursor(b, gA);
+#pragma unroll
+    for (int s = 0; s < MA; ++s) {
+      consume(qa[s], c, nua, false, xs);
+      mlp_advance(c, ia, gA, G);
+    }
+  }
+
+  // Wave 0 writes gate_up's outputs, tagged with the call's number, then every
+  // wave loads its down rows while the outputs are passed on (loading them
+  // earlier, before the outputs are out, measured slower: 15.6 against
+  // 14.5 us).  The words are relaxed device-scope atomic accesses, which the
+  // hardware keeps coherent across the chip without cache-wide write-backs or
+  // invalidations (release and acquire fences cost one of those per
+  // workgroup, measured at tens of microseconds over the grid).
+  __syncthreads();
+  const unsigned call = (unsigned)tab[1 + 2 * kMoeMlpMaxRoutes];
+  if (wv == 0) {
+    for (int i = lane; i < nua * (WPB / 2); i += 64) {
+      const int t = i / (WPB / 2), w = i - t * (WPB / 2);
+      const int u = b + t * G;
+      const int k = u / gA;
+      const unsigned lo = __builtin_bit_cast(unsigned short, ya[t * WPB + 2 * w]);
+      const unsigned hi = __builtin_bit_cast(unsigned short, ya[t * WPB + 2 * w + 1]);
+      __hip_atomic_store(a.gu + ((size_t)tab[1 + k] * a.N1 + (u - k * gA) * WPB) / 2 + w,
+                         ((unsigned long long)call << 32) | lo | (hi << 16), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  load_down();
+  // h of route kb: every word read until it carries this call's number.
+  // Each workgroup starts at a different chunk, so that the workgroups
+  // reading one route at once spread over its lines.
+  if (nub > 0) {
+    const unsigned long long* row = a.gu + (size_t)tab[1 + kb] * (a.N1 / 2);
+    const int rot = (int)(((long long)b * 67) % k2c);
+    bool gave_up = a.spin < 0;
+    for (int i = threadIdx.x; i < k2c; i += kThreads) {
+      const int c = i + rot < k2c ? i + rot : i + rot - k2c;
+      unsigned long long wd[8];
+      long long polls = 0;
+      for (;;) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          wd[q] = __hip_atomic_load(row + 4 * c + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          wd[4 + q] = __hip_atomic_load(row + 4 * (k2c + c) + q, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        }
+        bool ready = true;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ready = ready && (unsigned)(wd[q] >> 32) == call;
+        if (ready || gave_up) break;
+        if (++polls > a.spin) gave_up = true;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      u32x4 g, v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g[q] = (unsigned)wd[q];
+        v[q] = (unsigned)wd[4 + q];
+      }
+      hs[c] = swiglu8(g, v);
+    }
+    if (gave_up) __hip_atomic_store(a.gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  {
+    MlpCursor c = down_cursor();
+#pragma unroll
+    for (int s = 0; s < MB; ++s) {
+      consume(qb[s], c, nub, true, hs);
+      down_advance(c);
+    }
+  }
+
+  // Down outputs, then the zero rows of routes with no expert.
+  __syncthreads();
+  for (int i = threadIdx.x; i < nub * WPB; i += kThreads) {
+    const int row = (lb + (i / WPB) * Gk) * WPB + (i % WPB);
+    if (row < a.N2) a.y[(size_t)tab[1 + kb] * a.N2 + row] = yb[i];
+  }
+  if (nv < a.R) {
+    for (int r = 0, k = 0; r < a.R; ++r) {
+      if (k < nv && tab[1 + k] == r) {
+        ++k;
+        continue;
+      }
+      for (int i = b * kThreads + threadIdx.x; i < a.N2; i += G * kThreads)
+        a.y[(size_t)r * a.N2 + i] = (__bf16)0.0f;
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(a.ended, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Greedy next token: for each token, the smallest index of the largest logit
 // ("Developing a custom Qwen2.5 72B inference engine from scratch - what is
 // the real bottleneck?", section 5, third lever: pick the next token on the
@@ -1833,7 +2163,7 @@ KernelChoice pick(int dtype, int variant, int M) {
 constexpr int kOccCache = 256;
 struct OccEntry {
   int dev;
-  main_fn fn;
+  const void* fn;
   int lds;
   int blocks_per_cu;
 };
@@ -1841,7 +2171,7 @@ OccEntry g_occ[kOccCache];
 int g_occ_n = 0;
 std::mutex g_occ_mu;
 
-skinny_status blocks_per_cu(main_fn fn, int lds, int threads, int* out) {
+skinny_status blocks_per_cu(const void* fn, int lds, int threads, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
   {
@@ -1853,7 +2183,7 @@ skinny_status blocks_per_cu(main_fn fn, int lds, int threads, int* out) {
       }
   }
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, threads, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) !=
       hipSuccess)
     return SKINNY_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_occ_mu);
@@ -1866,13 +2196,13 @@ skinny_status blocks_per_cu(main_fn fn, int lds, int threads, int* out) {
 // largest size granted so far is remembered per (device, kernel).
 struct LdsEntry {
   int dev;
-  main_fn fn;
+  const void* fn;
   int bytes;
 };
 LdsEntry g_lds[kOccCache];
 int g_lds_n = 0;
 
-skinny_status ensure_lds(main_fn fn, int bytes) {
+skinny_status ensure_lds(const void* fn, int bytes) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_occ_mu);
@@ -1880,7 +2210,7 @@ skinny_status ensure_lds(main_fn fn, int bytes) {
   for (int i = 0; i < g_lds_n; ++i)
     if (g_lds[i].dev == dev && g_lds[i].fn == fn) slot = i;
   if (slot >= 0 && g_lds[slot].bytes >= bytes) return SKINNY_OK;
-  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
       hipSuccess)
     return SKINNY_ERR_HIP;
   if (slot >= 0) g_lds[slot].bytes = bytes;
@@ -1891,7 +2221,7 @@ skinny_status ensure_lds(main_fn fn, int bytes) {
 // Workgroups of the persistent grid: as many as are resident at once.
 skinny_status auto_workers(const DeviceInfo& d, const KernelChoice& k, int lds, int* workers) {
   int bpc = 0;
-  skinny_status st = blocks_per_cu(k.fn, lds, 64 * k.wpb, &bpc);
+  skinny_status st = blocks_per_cu((const void*)k.fn, lds, 64 * k.wpb, &bpc);
   if (st != SKINNY_OK) return st;
   if (bpc < 1) return SKINNY_ERR_UNSUPPORTED;
   int waves_per_cu = bpc * k.wpb;
@@ -1992,7 +2322,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
       return SKINNY_ERR_UNSUPPORTED;
   const int lds = kernel_lds(k, dtype);
   a.x_lds_bytes = k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
-  skinny_status st = ensure_lds(k.fn, lds);
+  skinny_status st = ensure_lds((const void*)k.fn, lds);
   if (st != SKINNY_OK) return st;
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = *lin[i];
@@ -2418,7 +2748,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
     k.tiles = true;
   }
   const int lds = kernel_lds(k, dtype);
-  st = ensure_lds(k.fn, lds);
+  st = ensure_lds((const void*)k.fn, lds);
   if (st != SKINNY_OK) return st;
   int G = 0;
   st = auto_workers(dev, k, lds, &G);
@@ -2646,7 +2976,7 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                         : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
   out->kernel = k.id;
   const int lds = kernel_lds(k, linears[0].dtype);
-  st = ensure_lds(k.fn, lds);
+  st = ensure_lds((const void*)k.fn, lds);
   if (st != SKINNY_OK) return st;
   int workers = 0;
   st = auto_workers(d, k, lds, &workers);
@@ -2783,6 +3113,258 @@ skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void*
                                       size_t workspace_bytes, void* stream) {
   if (!events) return SKINNY_ERR_INVALID_ARG;
   return moe_run(experts, x, ids, T, topk, flags, y, workspace, workspace_bytes, stream, events);
+}
+
+// ---------------------------------------------------------------------------
+// The experts' gated MLP (skinny_moe_mlp_swiglu).  Workspace: kMoeMlpCtrBytes
+// of counters (zero before the first call, left zero by every call), the
+// gate_up outputs [T * topk][2I] bf16, then what the two skinny_moe_linear
+// launches of the general path need.
+constexpr int kMoeMlpMaxGrid = 1 << 20;
+constexpr size_t kMoeMlpCtrBytes = 256;
+static_assert(kMoeMlpCtrBytes == SKINNY_MOE_MLP_COUNTER_BYTES, "the header's layout");
+constexpr int kMoeMlpSegs = 2;           // 1 KB segments per slot of the one-token kernel
+std::atomic<long long> g_moe_mlp_spin{1LL << 22};
+
+// The gate_up outputs: bf16, or (one launch) 64-bit words of two bf16 and a tag.
+size_t moe_mlp_gu_bytes(const skinny_experts& gu, int T, int topk) {
+  return ((size_t)T * topk * gu.N * 4 + 255) / 256 * 256;
+}
+
+skinny_status check_moe_mlp(const skinny_experts* gu, const skinny_experts* dn, int T, int topk) {
+  skinny_status st = check_experts(gu, T, topk, 0);
+  if (st != SKINNY_OK) return st;
+  st = check_experts(dn, T, topk, SKINNY_MOE_X_PER_ROUTE | SKINNY_MOE_SWIGLU);
+  if (st != SKINNY_OK) return st;
+  if (gu->E != dn->E || gu->N != 2 * dn->K) return SKINNY_ERR_INVALID_ARG;
+  return SKINNY_OK;
+}
+
+size_t moe_mlp_workspace(const skinny_experts& gu, const skinny_experts& dn, int T, int topk) {
+  const size_t a = moe_workspace(gu, moe_plan(gu, T, topk));
+  const size_t b = moe_workspace(dn, moe_plan(dn, T, topk));
+  return kMoeMlpCtrBytes + moe_mlp_gu_bytes(gu, T, topk) + (a > b ? a : b);
+}
+
+// LDS of the one-token kernel for G workgroups, or 0 if it does not apply.
+struct MoeMlpLds {
+  int hs_off, ya_off, yb_off, tab_off, bytes;
+};
+MoeMlpLds moe_mlp1_lds(const skinny_experts& gu, const skinny_experts& dn, int topk, int G) {
+  MoeMlpLds l{};
+  const long long xchunks = ((gu.K / 8 + 63) / 64) * 64;
+  const long long gA = (gu.N + kRowsWavesPerBlock - 1) / kRowsWavesPerBlock;
+  const long long gB = (dn.N + kRowsWavesPerBlock - 1) / kRowsWavesPerBlock;
+  const long long ua = (topk * gA + G - 1) / G, ub = (gB + G / topk - 1) / (G / topk);
+  long long off = xchunks * 16;
+  l.hs_off = (int)off;
+  off += (long long)(dn.K / 8) * 16;
+  l.ya_off = (int)off;
+  off += (ua * kRowsWavesPerBlock * 2 + 15) / 16 * 16;
+  l.yb_off = (int)off;
+  off += (ub * kRowsWavesPerBlock * 2 + 15) / 16 * 16;
+  l.tab_off = (int)off;
+  off += (2 + 2 * kMoeMlpMaxRoutes) * 4;
+  if (off > kMaxLdsBytes) return MoeMlpLds{};
+  l.bytes = (int)off;
+  return l;
+}
+
+// The one-token kernel's instances: slots per wave for gate_up and down.  A
+// call takes the first whose slots hold every workgroup's rows (units per
+// workgroup x slots per unit, for the most routes the call can have), with
+// one workgroup per CU: two per CU measured slower on the verify step (FP8
+// 18.7 against 16.2 us, bf16 24.0 against 22.0 us).
+struct MoeMlpInst {
+  int dtype, ma, mb;
+  void (*fn)(MoeMlpArgs);
+};
+const MoeMlpInst kMoeMlpInsts[] = {
+    {SKINNY_FP8_BS128, 4, 2, skinny_moe_mlp1<SKINNY_FP8_BS128, 4, 2, kMoeMlpSegs>},
+    {SKINNY_FP8_BS128, 6, 4, skinny_moe_mlp1<SKINNY_FP8_BS128, 6, 4, kMoeMlpSegs>},
+    {SKINNY_FP8_BS128, 8, 8, skinny_moe_mlp1<SKINNY_FP8_BS128, 8, 8, kMoeMlpSegs>},
+    {SKINNY_BF16, 8, 4, skinny_moe_mlp1<SKINNY_BF16, 8, 4, kMoeMlpSegs>},
+    {SKINNY_BF16, 12, 8, skinny_moe_mlp1<SKINNY_BF16, 12, 8, kMoeMlpSegs>},
+};
+
+// Slots a wave needs for one linear: gate_up units are dealt over all G
+// workgroups, down units of a route over its group of at least G / topk.
+long long moe_mlp1_slots(const skinny_experts& e, int topk, int G, bool down) {
+  const long long groups = (e.N + kRowsWavesPerBlock - 1) / kRowsWavesPerBlock;
+  const long long units = down ? (groups + G / topk - 1) / (G / topk)
+                               : (topk * groups + G - 1) / G;
+  const int cpr = e.K / (e.dtype == SKINNY_BF16 ? 8 : 16);
+  const int spt = (cpr + kSegChunks - 1) / kSegChunks;
+  return units * ((spt + kMoeMlpSegs - 1) / kMoeMlpSegs);
+}
+
+struct MoeMlpChoice {
+  const MoeMlpInst* inst = nullptr;
+  int G = 0;
+  MoeMlpLds lds{};
+};
+
+// The one-token kernel's instance and grid for this call, or none.
+skinny_status moe_mlp1_choose(const skinny_experts& gu, const skinny_experts& dn, int T, int topk,
+                              int cus, MoeMlpChoice* out) {
+  *out = MoeMlpChoice{};
+  if (T != 1 || topk > kMoeMlpMaxRoutes || gu.dtype != dn.dtype) return SKINNY_OK;
+  const int G = cus;
+  if (G < topk) return SKINNY_OK;
+  if (G > kMoeMlpMaxGrid) return SKINNY_OK;
+  const MoeMlpLds l = moe_mlp1_lds(gu, dn, topk, G);
+  if (l.bytes == 0) return SKINNY_OK;
+  for (const MoeMlpInst& in : kMoeMlpInsts) {
+    if (in.dtype != gu.dtype || moe_mlp1_slots(gu, topk, G, false) > in.ma ||
+        moe_mlp1_slots(dn, topk, G, true) > in.mb)
+      continue;
+    skinny_status st = ensure_lds((const void*)in.fn, l.bytes);
+    if (st != SKINNY_OK) return st;
+    int bpc = 0;
+    st = blocks_per_cu((const void*)in.fn, l.bytes, 64 * kRowsWavesPerBlock, &bpc);
+    if (st != SKINNY_OK) return st;
+    if (bpc < 1) continue;
+    *out = MoeMlpChoice{&in, G, l};
+    return SKINNY_OK;
+  }
+  return SKINNY_OK;
+}
+
+skinny_status moe_mlp_run(const skinny_experts* gu, const skinny_experts* dn, const void* x,
+                          const int* ids, int T, int topk, void* y, void* ws, size_t ws_bytes,
+                          void* stream, void* const* events) {
+  skinny_status st = check_moe_mlp(gu, dn, T, topk);
+  if (st != SKINNY_OK) return st;
+  if (!x || !ids || !y) return SKINNY_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4)) return SKINNY_ERR_UNSUPPORTED;
+  if (!ws) return SKINNY_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SKINNY_ERR_UNSUPPORTED;
+  if (ws_bytes < moe_mlp_workspace(*gu, *dn, T, topk)) return SKINNY_ERR_WORKSPACE;
+  const int routes = T * topk;
+  auto wrange = [](const skinny_experts* e) {
+    return Range{(uintptr_t)e->w, (uintptr_t)e->w + (size_t)e->E * e->N * e->K *
+                                                      (e->dtype == SKINNY_BF16 ? 2 : 1)};
+  };
+  auto srange = [](const skinny_experts* e) {
+    const size_t nb = (size_t)((e->N + 127) / 128) * ((e->K + 127) / 128);
+    return Range{(uintptr_t)e->w_scale,
+                 (uintptr_t)e->w_scale + (e->w_scale ? (size_t)e->E * nb * 4 : 0)};
+  };
+  const Range yr{(uintptr_t)y, (uintptr_t)y + (size_t)routes * dn->N * 2};
+  const Range xr{(uintptr_t)x, (uintptr_t)x + (size_t)T * gu->K * 2};
+  const Range ir{(uintptr_t)ids, (uintptr_t)ids + (size_t)routes * 4};
+  const Range kr{(uintptr_t)ws, (uintptr_t)ws + ws_bytes};
+  const Range in[] = {xr, ir, wrange(gu), srange(gu), wrange(dn), srange(dn)};
+  for (const Range& r : in)
+    if (overlap(yr, r) || overlap(kr, r)) return SKINNY_ERR_INVALID_ARG;
+  if (overlap(yr, kr)) return SKINNY_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != SKINNY_OK) return st;
+  if (!dev.gfx950) return SKINNY_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  __bf16* gub = (__bf16*)((char*)ws + kMoeMlpCtrBytes);
+  void* rest = (char*)ws + kMoeMlpCtrBytes + moe_mlp_gu_bytes(*gu, T, topk);
+  const size_t rest_bytes = ws_bytes - kMoeMlpCtrBytes - moe_mlp_gu_bytes(*gu, T, topk);
+
+  MoeMlpChoice ch;
+  st = moe_mlp1_choose(*gu, *dn, T, topk, dev.cus, &ch);
+  if (st != SKINNY_OK) return st;
+  if (ch.inst) {
+    const int dtype = gu->dtype;
+    const MoeMlpLds& l = ch.lds;
+    MoeMlpArgs a;
+    memset(&a, 0, sizeof a);
+    const int kpc = dtype == SKINNY_BF16 ? 8 : 16;       // K per 16-byte chunk
+    a.wg = (const u32x4*)gu->w;
+    a.sg = gu->w_scale;
+    a.wd = (const u32x4*)dn->w;
+    a.sd = dn->w_scale;
+    a.E = gu->E;
+    a.R = topk;
+    a.N1 = gu->N;
+    a.K1 = gu->K;
+    a.cpr1 = gu->K / kpc;
+    a.spt1 = (a.cpr1 + kSegChunks - 1) / kSegChunks;
+    a.kb1 = (gu->K + kScaleBlock - 1) / kScaleBlock;
+    a.N2 = dn->N;
+    a.K2 = dn->K;
+    a.cpr2 = dn->K / kpc;
+    a.spt2 = (a.cpr2 + kSegChunks - 1) / kSegChunks;
+    a.kb2 = (dn->K + kScaleBlock - 1) / kScaleBlock;
+    a.wg_stride = (long long)a.N1 * a.cpr1;
+    a.wd_stride = (long long)a.N2 * a.cpr2;
+    a.sg_stride = dtype == SKINNY_BF16 ? 0 : (long long)((a.N1 + 127) / 128) * a.kb1;
+    a.sd_stride = dtype == SKINNY_BF16 ? 0 : (long long)((a.N2 + 127) / 128) * a.kb2;
+    a.ids = ids;
+    a.x = (const u32x4*)x;
+    a.gu = (unsigned long long*)gub;
+    a.y = (__bf16*)y;
+    a.ended = (unsigned long long*)ws;
+    a.gave_up = (int*)((char*)ws + 8);
+    a.spin = g_moe_mlp_spin.load();
+    a.G = ch.G;
+    a.hs_off = l.hs_off;
+    a.ya_off = l.ya_off;
+    a.yb_off = l.yb_off;
+    a.tab_off = l.tab_off;
+    if (events && hipEventRecord((hipEvent_t)events[0], s) != hipSuccess) return SKINNY_ERR_HIP;
+    hipLaunchKernelGGL(ch.inst->fn, dim3(ch.G), dim3(64 * kRowsWavesPerBlock), l.bytes, s, a);
+    if (hipGetLastError() != hipSuccess) return SKINNY_ERR_HIP;
+    if (events && hipEventRecord((hipEvent_t)events[1], s) != hipSuccess) return SKINNY_ERR_HIP;
+    return SKINNY_OK;
+  }
+  // Two launches: gate_up into the workspace, then down through the SwiGLU.
+  st = moe_run(gu, x, ids, T, topk, 0, gub, rest, rest_bytes, stream, events);
+  if (st != SKINNY_OK) return st;
+  return moe_run(dn, gub, ids, T, topk, SKINNY_MOE_X_PER_ROUTE | SKINNY_MOE_SWIGLU, y, rest,
+                 rest_bytes, stream, nullptr);
+}
+
+size_t skinny_moe_mlp_workspace_bytes(const skinny_experts* gate_up, const skinny_experts* down,
+                                      int T, int topk) {
+  if (check_moe_mlp(gate_up, down, T, topk) != SKINNY_OK) return 0;
+  return moe_mlp_workspace(*gate_up, *down, T, topk);
+}
+
+skinny_status skinny_moe_mlp_swiglu(const skinny_experts* gate_up, const skinny_experts* down,
+                                    const void* x, const int* ids, int T, int topk, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_mlp_run(gate_up, down, x, ids, T, topk, y, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+skinny_status skinny_moe_mlp_swiglu_timed(const skinny_experts* gate_up,
+                                          const skinny_experts* down, const void* x,
+                                          const int* ids, int T, int topk, void* y,
+                                          void* const* events, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (!events) return SKINNY_ERR_INVALID_ARG;
+  return moe_mlp_run(gate_up, down, x, ids, T, topk, y, workspace, workspace_bytes, stream,
+                     events);
+}
+
+void skinny_moe_mlp_set_spin_limit(long long polls) { g_moe_mlp_spin.store(polls); }
+
+skinny_status skinny_moe_mlp_plan_query(const skinny_experts* gate_up, const skinny_experts* down,
+                                        int T, int topk, skinny_plan* out) {
+  if (!out) return SKINNY_ERR_INVALID_ARG;
+  skinny_status st = check_moe_mlp(gate_up, down, T, topk);
+  if (st != SKINNY_OK) return st;
+  DeviceInfo dev;
+  st = device_info(&dev);
+  if (st != SKINNY_OK) return st;
+  MoeMlpChoice ch;
+  st = moe_mlp1_choose(*gate_up, *down, T, topk, dev.cus, &ch);
+  if (st != SKINNY_OK) return st;
+  if (ch.inst) {
+    memset(out, 0, sizeof *out);
+    out->variant = SKINNY_VARIANT_VECTOR;
+    out->waves = ch.G * kRowsWavesPerBlock;
+    out->kernel = SKINNY_KERNEL_MOE_MLP1;
+    return SKINNY_OK;
+  }
+  return skinny_moe_plan_query(gate_up, T, topk, 0, out);
 }
 
 skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int topk, int flags,

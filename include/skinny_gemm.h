@@ -103,7 +103,8 @@ enum skinny_kernel {
                                      units; FP8 launches >= 1 GB)                       */
   SKINNY_KERNEL_TILES = 4,        /* skinny_tiles (MFMA), 4-wave workgroups; MoE form  */
   SKINNY_KERNEL_TILES_WIDE = 5,   /* skinny_tiles, 8-wave workgroups                    */
-  SKINNY_KERNEL_TILES_KSPLIT = 6  /* skinny_tiles' K-split form (one-token MoE slices)  */
+  SKINNY_KERNEL_TILES_KSPLIT = 6, /* skinny_tiles' K-split form (one-token MoE slices)  */
+  SKINNY_KERNEL_MOE_MLP1 = 7      /* skinny_moe_mlp1 (the experts' MLP in one launch)   */
 };
 
 /* Launch plan override, for tests and benchmarks.  Zero-initialised = automatic. */
@@ -339,6 +340,65 @@ skinny_status skinny_moe_linear_timed(const skinny_experts* experts, const void*
  * SKINNY_ERR_INVALID_ARG for a NULL out. */
 skinny_status skinny_moe_plan_query(const skinny_experts* experts, int T, int topk, int flags,
                                     skinny_plan* out);
+
+/* The experts' gated MLP over the routes of a batch (the same sources as
+ * skinny_moe_linear: the router's top-k experts, each its own small MLP whose
+ * SiLU-gated activation sits between its two linears, "Multi-GPU Inference
+ * and Serving at Scale", Examples 3 and 8).  For route r = t * topk + j,
+ * e = ids[r]:
+ *   [g | u] = bf16(x[t] . Wgu_e^T),  y[r] = bf16(silu(g) * u) . Wdn_e^T,
+ * exactly skinny_moe_linear(gate_up, x, ids, ..., flags 0) into a
+ * [T * topk][2I] buffer followed by skinny_moe_linear(down, that buffer, ids,
+ * ..., SKINNY_MOE_X_PER_ROUTE | SKINNY_MOE_SWIGLU, y).  y[r] = 0 for routes
+ * whose e is outside [0, E).
+ *   gate_up  E experts of N = 2I rows, K = H columns
+ *   down     the same E experts (same dtype or not) of N rows, K = I columns
+ *   x        [T][H] bf16;  ids [T][topk] int32, device;  y [T * topk][N] bf16
+ * One token (T = 1, topk <= 16, both linears of one dtype, and each
+ * workgroup's rows within the one-token kernel's registers) runs as one
+ * launch: every wave issues the loads of all its gate_up and down rows at its
+ * start, and the workgroups (one or two per CU, all resident) meet once
+ * between the linears through a counter in the workspace.  A wait there gives
+ * up after a bounded number of polls (skinny_moe_mlp_set_spin_limit) and then
+ * sets the flag word, leaving y invalid; it never hangs.  Other calls make the
+ * two launches.
+ *   Workspace: skinny_moe_mlp_workspace_bytes(gate_up, down, T, topk) bytes,
+ * 256-byte aligned; 0 for invalid arguments.  Its first
+ * SKINNY_MOE_MLP_COUNTER_BYTES hold a counter (bytes 0-7: workgroups of the
+ * one-launch form finished over all calls, a multiple of the grid between
+ * calls) and a flag (bytes 8-11, nonzero once a wait gave up; the caller
+ * clears it): zero them once before the first call on that workspace, do not
+ * hand the workspace to other calls in between, and do not run two calls on
+ * it at once.  The gate_up outputs follow: [T * topk][2I] bf16 (two launches),
+ * or [topk][I] 64-bit words, each this call's number (low 32 bits of the
+ * counter / grid + 1) above two bf16 values (one launch; rows of routes with
+ * no expert keep what they held). */
+#define SKINNY_MOE_MLP_COUNTER_BYTES 256
+/* Requirements and errors as for skinny_moe_linear on both linears, plus gate_up->E ==
+ * down->E and gate_up->N == 2 * down->K (else SKINNY_ERR_INVALID_ARG); y
+ * must not overlap x, ids, the weights, the scales or the workspace, and the
+ * workspace must not overlap x, ids, the weights or the scales. */
+size_t skinny_moe_mlp_workspace_bytes(const skinny_experts* gate_up, const skinny_experts* down,
+                                      int T, int topk);
+skinny_status skinny_moe_mlp_swiglu(const skinny_experts* gate_up, const skinny_experts* down,
+                                    const void* x, const int* ids, int T, int topk, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+/* skinny_moe_mlp_swiglu recording events[0] / events[1] just before and after
+ * its main launch (the one launch, or gate_up's), for benchmarks. */
+skinny_status skinny_moe_mlp_swiglu_timed(const skinny_experts* gate_up,
+                                          const skinny_experts* down, const void* x,
+                                          const int* ids, int T, int topk, void* y,
+                                          void* const* events, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+/* Polls before the one-token launch's wait gives up (default 4194304; a
+ * negative value makes it give up without waiting).  Process-wide; read when
+ * a call is enqueued.  For tests of that path. */
+void skinny_moe_mlp_set_spin_limit(long long polls);
+/* The plan of skinny_moe_mlp_swiglu's main launch on the current device:
+ * kernel SKINNY_KERNEL_MOE_MLP1 (variant VECTOR, waves of its grid) for the
+ * one launch, else skinny_moe_plan_query's answer for the gate_up launch. */
+skinny_status skinny_moe_mlp_plan_query(const skinny_experts* gate_up, const skinny_experts* down,
+                                        int T, int topk, skinny_plan* out);
 
 /* Static text for a status code; never NULL. */
 const char* skinny_status_string(int status);
