@@ -2066,23 +2066,28 @@ KernelChoice pick_lean(int M) {
   }
 }
 
-// One-token launches on skinny_rows_flat, one 8-wave workgroup per CU: FP8
-// with 2 slots of 2 KB per wave, bf16 with 3 of 1 KB.  Measured on MI355X
-// against the kernels they replace (same process, interleaved): FP8 8-layer
-// TP=1 launch 6.22 -> 6.29-6.30 TB/s (tile kernel before), FP8 vocabulary
-// projection 225 -> 217 us, one FP8 TP=1 layer (0.87 GB) -0.6%, hence the
-// launch size; other shapes of the FP8 kernel (1 KB slots, 3-8 deep, 16 waves
-// per CU) 0.3-3% slower.  bf16 stacks are as fast on the lean skinny_rows
-// instance (8-layer launch 6.50 vs 6.51 TB/s), which they keep; the bf16
-// flat instance serves forced row-kernel calls at M = 1.  Neither leaving x
-// staged across linears nor dropping the FP8 scale loads (timing-only
-// builds) moved the FP8 rate, so it is not the staging drains or the extra
-// loads that hold it below the bf16 rate.
-constexpr int flat_depth(int dtype) { return dtype == SKINNY_BF16 ? 3 : 2; }
+// One-token launches on skinny_rows_flat: FP8 with 2 slots of 2 KB per wave,
+// bf16 with 4 of 1 KB.  Measured on MI355X against the kernels they replace
+// (same process, interleaved):
+// - FP8 launches of at least kFlatLaunchBytes, one 8-wave workgroup per CU:
+//   8-layer TP=1 launch 6.22 -> 6.29-6.30 TB/s (tile kernel before), FP8
+//   vocabulary projection 225 -> 217 us; one FP8 TP=1 layer (0.87 GB) -0.6%,
+//   hence the launch size; other shapes (1 KB slots, 3-8 deep, 16 waves per
+//   CU) 0.3-3% slower.  bf16 launches of that size are as fast on the lean
+//   skinny_rows instance (8-layer launch 6.50 vs 6.51 TB/s), which they keep.
+// - Launches under kFlatSmallBytes (a TP=8 layer, its QKV GEMV), two
+//   workgroups per CU: TP=8 layer 39.8 -> 38.7 us (bf16) and 26.1 -> 24.2 us
+//   (FP8), QKV GEMV 7.4 -> 7.0 us, against the deep skinny_rows instance and
+//   the tile kernel; at one workgroup per CU they were 1-3% slower than those.
+// Neither leaving x staged across linears nor dropping the FP8 scale loads
+// (timing-only builds) moved the FP8 rate of the large launches, so it is not
+// the staging drains or the extra loads that hold it below the bf16 rate.
+constexpr int flat_depth(int dtype) { return dtype == SKINNY_BF16 ? 4 : 2; }
 constexpr int flat_segs(int dtype) { return dtype == SKINNY_BF16 ? 1 : 2; }
-constexpr bool kFlatAutoBf16 = false;
 constexpr int kFlatWavesPerCU = 8;
-constexpr double kFlatLaunchBytes = 1.0e9;     // weight bytes of one launch
+constexpr int kFlatWavesPerCUSmall = 16;
+constexpr double kFlatLaunchBytes = 1.0e9;     // FP8 launches of at least this: flat
+constexpr double kFlatSmallBytes = 0.4e9;      // launches under this: flat, 16 waves per CU
 
 template <int DT>
 KernelChoice flat_kernel() {
@@ -2111,21 +2116,25 @@ bool flat_fits(const skinny_linear* const* lin, int count, int M) {
   return true;
 }
 
-// Automatic variant: FP8 launches of at least kFlatLaunchBytes of weights take
-// the flat kernel when it fits; a forced VECTOR variant takes it whenever it
-// fits.
-bool use_flat(const skinny_linear* const* lin, int count, int M, int requested) {
-  if (requested == SKINNY_VARIANT_MFMA || !flat_fits(lin, count, M)) return false;
-  if (requested == SKINNY_VARIANT_VECTOR) return true;
-  if (lin[0]->dtype == SKINNY_BF16 && !kFlatAutoBf16) return false;
+// Waves per CU of the flat kernel for this launch, or 0 if it does not take
+// it.  Automatic variant: launches under kFlatSmallBytes of weights (16 waves
+// per CU) and FP8 launches of at least kFlatLaunchBytes (8); a forced VECTOR
+// variant takes it whenever it fits.
+int use_flat(const skinny_linear* const* lin, int count, int M, int requested) {
+  if (requested == SKINNY_VARIANT_MFMA || !flat_fits(lin, count, M)) return 0;
   double bytes = 0;
   for (int i = 0; i < count; ++i)
     bytes += (lin[i]->dtype == SKINNY_BF16 ? 2.0 : 1.0) * lin[i]->N * lin[i]->K;
-  return bytes >= kFlatLaunchBytes;
+  const int waves = bytes < kFlatSmallBytes ? kFlatWavesPerCUSmall : kFlatWavesPerCU;
+  if (requested == SKINNY_VARIANT_VECTOR || bytes < kFlatSmallBytes) return waves;
+  return lin[0]->dtype != SKINNY_BF16 && bytes >= kFlatLaunchBytes ? waves : 0;
 }
 
-KernelChoice pick_flat(int dtype) {
-  return dtype == SKINNY_BF16 ? flat_kernel<SKINNY_BF16>() : flat_kernel<SKINNY_FP8_BS128>();
+KernelChoice pick_flat(int dtype, int waves_per_cu) {
+  KernelChoice k =
+      dtype == SKINNY_BF16 ? flat_kernel<SKINNY_BF16>() : flat_kernel<SKINNY_FP8_BS128>();
+  k.waves_per_cu = waves_per_cu;
+  return k;
 }
 
 template <int DT, int MT>
@@ -2307,7 +2316,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
-  if (use_flat(lin, count, M, requested)) k = pick_flat(dtype);
+  if (const int fw = use_flat(lin, count, M, requested)) k = pick_flat(dtype, fw);
   if (k.tiles && tiles_large(lin, count, M, dev.cus))
     k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
                              : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
@@ -2967,9 +2976,9 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
   if (!k.tiles && rows_lean(group, n, M)) k = pick_lean(M);
-  if (use_flat(group, n, M, SKINNY_VARIANT_AUTO)) {
+  if (const int fw = use_flat(group, n, M, SKINNY_VARIANT_AUTO)) {
     out->variant = SKINNY_VARIANT_VECTOR;
-    k = pick_flat(linears[0].dtype);
+    k = pick_flat(linears[0].dtype, fw);
   }
   if (k.tiles && tiles_large(group, n, M, d.cus))
     k = linears[0].dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()

@@ -244,7 +244,8 @@ def test_automatic_variant():
     """bf16 takes the row kernel at M <= 2, and at M = 3-4 for launches of at
     least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise.  FP8
     takes the tile kernel but for one-token launches of at least 1 GB of
-    weights (the flat row kernel).  The stack's launches hold up to 32
+    weights.  One-token launches under 0.4 GB (both dtypes) and FP8 ones of at
+    least 1 GB run the flat row kernel.  The stack's launches hold up to 32
     linears."""
     V, T = sg.VARIANT_VECTOR, sg.VARIANT_MFMA
 
@@ -260,6 +261,7 @@ def test_automatic_variant():
     assert [variant(tp1 * 2, M, sg.FP8_BS128) for M in (1, 2, 4)] == [V, T, T]   # 1.76 GB
     assert variant(tp1, 1, sg.FP8_BS128) == T                                     # 0.88 GB
     assert variant([(152064, 8192)], 1, sg.FP8_BS128) == V                       # 1.25 GB
+    assert [variant(tp8, M, sg.FP8_BS128) for M in (1, 2)] == [V, T]             # 0.11 GB
 
     def kernel(shapes, M, dt=sg.BF16):
         scale = None if dt == sg.BF16 else 0x300000
@@ -267,5 +269,5 @@ def test_automatic_variant():
         return sg.KERNEL_NAMES[sg.plan_query(lins, M).kernel]
     assert kernel(tp1 * 2, 1, sg.FP8_BS128) == "skinny_rows_flat"
     assert kernel(tp1 * 2, 1) == "skinny_rows (lean)"
-    assert kernel(tp8, 1) == "skinny_rows"
+    assert kernel(tp8, 1) == "skinny_rows_flat"                                 # 0.22 GB
     assert kernel(tp8, 8) == "skinny_tiles"
