@@ -650,8 +650,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 // flight among the loads would turn the next wait into a full drain.  The
 // per-lane arithmetic is that of skinny_rows at M = 1; the lane sum has its
 // own fixed order (wave_sum_rows).
-constexpr int kFlatYUnits = 1024;       // units whose outputs the LDS buffer holds
-constexpr int kFlatYBytes = kFlatYUnits * kRowsWavesPerBlock * 2;
+constexpr int kFlatYBytes = 16 * 1024;  // LDS for outputs waiting to be written
 
 // Sum over the 64 lanes in a fixed order, without a round trip through LDS:
 // each 16-lane row folds itself with rotations (DPP), then the four row sums
@@ -682,19 +681,21 @@ struct FlatSlot {
   float s[U];            // FP8: their block scales
 };
 
-template <int DT, int P, int U>
+template <int DT, int MT, int P, int U>
 __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(const LaunchArgs a) {
   constexpr int WPB = kRowsWavesPerBlock;
   constexpr int kThreads = 64 * WPB;
   constexpr bool kFp8 = DT == SKINNY_FP8_BS128;
+  constexpr int kYUnits = kFlatYBytes / (MT * WPB * 2);         // units whose outputs ybuf holds
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  u32x4* xs = reinterpret_cast<u32x4*>(lds);
-  __bf16* ybuf = reinterpret_cast<__bf16*>(lds + a.x_lds_bytes);   // [unit][wave]
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);                  // [token][K / 8]
+  __bf16* ybuf = reinterpret_cast<__bf16*>(lds + a.x_lds_bytes);   // [unit][token][wave]
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const long long S = a.S;
   if ((long long)blockIdx.x >= S) {
-    if (a.pairs && threadIdx.x == 0) a.pairs[blockIdx.x] = ArgmaxPair{-__builtin_inff(), a.lin[0].N};
+    if (a.pairs && threadIdx.x < MT)
+      a.pairs[(size_t)threadIdx.x * a.G + blockIdx.x] = ArgmaxPair{-__builtin_inff(), a.lin[0].N};
     return;
   }
   auto linear_of = [&](long long u, int l) {
@@ -735,22 +736,29 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
     }
   };
   // Consume cursor: unit cu of linear cl, segment cj; rows of cfull whole
-  // segments end with a ragged one.  The outputs of the units yfirst,
-  // yfirst + G, ... (ny of them) wait in ybuf.
+  // segments end with a ragged one; x has cxs chunks per token.  The outputs
+  // of the units yfirst, yfirst + G, ... (ny of them) wait in ybuf.
   long long cu = blockIdx.x;
   int cl = ll;
-  int cj = 0, crow = 0, cspt = 0, ccpr = 0, cfull = 0;
+  int cj = 0, crow = 0, cspt = 0, ccpr = 0, cfull = 0, cxs = 0;
   long long yfirst = cu;
   int ny = 0;
-  float acc = 0.0f;
-  float gbv = -__builtin_inff();
-  int gbi = a.lin[0].N;
+  float acc[MT];
+  float gbv[MT];
+  int gbi[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    acc[m] = 0.0f;
+    gbv[m] = -__builtin_inff();
+    gbi[m] = a.lin[0].N;
+  }
   auto enter_consume = [&]() {
     const LinDesc& L = a.lin[cl];
     crow = (int)(cu - L.unit_base) * WPB + wv;
     cspt = (L.spt + U - 1) / U;
     ccpr = L.cpr;
     cfull = L.cpr / (U * kSegChunks);
+    cxs = L.K >> 3;
   };
   // Writes the buffered outputs of linear cl (after a barrier: every wave's
   // entries are in).  The caller waits for the stores and barriers again
@@ -758,14 +766,16 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   auto flush_y = [&]() {
     __syncthreads();
     const LinDesc& L = a.lin[cl];
-    const bool vec = (reinterpret_cast<size_t>(L.y) & 15) == 0;
-    for (int i = threadIdx.x; i < ny; i += kThreads) {
-      const int row0 = (int)(yfirst + (long long)i * a.G - L.unit_base) * WPB;
+    const bool vec = (reinterpret_cast<size_t>(L.y) & 15) == 0 && L.N % 8 == 0;
+    for (int i = threadIdx.x; i < ny * MT; i += kThreads) {
+      const int t = i / MT, m = i - t * MT;
+      const int row0 = (int)(yfirst + (long long)t * a.G - L.unit_base) * WPB;
       const __bf16* src = ybuf + i * WPB;
+      __bf16* dst = L.y + (size_t)m * L.N + row0;
       if (vec && row0 + WPB <= L.N) {
-        *reinterpret_cast<u32x4*>(L.y + row0) = *reinterpret_cast<const u32x4*>(src);
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
       } else {
-        for (int e = 0; e < WPB && row0 + e < L.N; ++e) L.y[row0 + e] = src[e];
+        for (int e = 0; e < WPB && row0 + e < L.N; ++e) dst[e] = src[e];
       }
     }
     ny = 0;
@@ -774,7 +784,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
     __syncthreads();                                       // all done with the old x
     const LinDesc& L = a.lin[cl];
     const int xcpr = L.K >> 3;
-    stage_x_direct<kThreads, false>(L, 1, xcpr, 0, xcpr, xs, xcpr, nullptr);
+    stage_x_direct<kThreads, false>(L, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -787,9 +797,15 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
         if (kFp8) {
           u32x4 b0, b1;
           e4m3x16_to_bf16(q.w[v], b0, b1);
-          acc = __builtin_fmaf(q.s[v], dot8(xs[2 * c + 1], b1, dot8(xs[2 * c], b0, 0.0f)), acc);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4* x = xs + m * cxs;
+            acc[m] = __builtin_fmaf(q.s[v], dot8(x[2 * c + 1], b1, dot8(x[2 * c], b0, 0.0f)),
+                                    acc[m]);
+          }
         } else {
-          acc = dot8(xs[c], q.w[v], acc);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[m] = dot8(xs[m * cxs + c], q.w[v], acc[m]);
         }
       }
     } else {
@@ -798,25 +814,36 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
         const int c = (cj * U + v) * kSegChunks + lane;
         const bool ok = c < ccpr;
         const int cx = ok ? c : 0;
-        float t;
         if (kFp8) {
           u32x4 b0, b1;
           e4m3x16_to_bf16(q.w[v], b0, b1);
-          t = __builtin_fmaf(q.s[v], dot8(xs[2 * cx + 1], b1, dot8(xs[2 * cx], b0, 0.0f)), acc);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const u32x4* x = xs + m * cxs;
+            const float t =
+                __builtin_fmaf(q.s[v], dot8(x[2 * cx + 1], b1, dot8(x[2 * cx], b0, 0.0f)), acc[m]);
+            acc[m] = ok ? t : acc[m];
+          }
         } else {
-          t = dot8(xs[cx], q.w[v], acc);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const float t = dot8(xs[m * cxs + cx], q.w[v], acc[m]);
+            acc[m] = ok ? t : acc[m];
+          }
         }
-        acc = ok ? t : acc;
       }
     }
     if (++cj < cspt) return false;
-    acc = wave_sum_rows(acc);
-    if (lane == 0) {
-      const __bf16 yv = (__bf16)acc;
-      ybuf[ny * WPB + wv] = yv;
-      if (a.pairs && crow < a.lin[cl].N) argmax_take((float)yv, crow, gbv, gbi);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc[m] = wave_sum_rows(acc[m]);
+      if (lane == 0) {
+        const __bf16 yv = (__bf16)acc[m];
+        ybuf[(ny * MT + m) * WPB + wv] = yv;
+        if (a.pairs && crow < a.lin[cl].N) argmax_take((float)yv, crow, gbv[m], gbi[m]);
+      }
+      acc[m] = 0.0f;
     }
-    acc = 0.0f;
     cj = 0;
     ++ny;
     if (cu + a.G >= S) return true;
@@ -829,7 +856,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
       enter_consume();
       stage();
     } else {
-      if (ny == kFlatYUnits) {
+      if (ny == kYUnits) {
         flush_y();
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -860,16 +887,20 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   }
   flush_y();
   if (a.pairs) {
-    // The workgroup's pair, from its waves' (M = 1: pairs[workgroup]).
+    // The workgroup's pair per token, from its waves' (in wave order; the
+    // order does not change the result), into pairs[m][workgroup].
     __syncthreads();
     ArgmaxPair* red = reinterpret_cast<ArgmaxPair*>(ybuf);
-    if (lane == 0) red[wv] = ArgmaxPair{gbv, gbi};
+    if (lane == 0)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wv * MT + m] = ArgmaxPair{gbv[m], gbi[m]};
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < MT) {
+      const int m = threadIdx.x;
       float bv = -__builtin_inff();
       int bi = a.lin[0].N;
-      for (int w = 0; w < WPB; ++w) argmax_take(red[w].v, red[w].i, bv, bi);
-      a.pairs[blockIdx.x] = ArgmaxPair{bv, bi};
+      for (int w = 0; w < WPB; ++w) argmax_take(red[w * MT + m].v, red[w * MT + m].i, bv, bi);
+      a.pairs[(size_t)m * a.G + blockIdx.x] = ArgmaxPair{bv, bi};
     }
   }
 }
@@ -2079,6 +2110,12 @@ KernelChoice pick_lean(int M) {
 //   workgroups per CU: TP=8 layer 39.8 -> 38.7 us (bf16) and 26.1 -> 24.2 us
 //   (FP8), QKV GEMV 7.4 -> 7.0 us, against the deep skinny_rows instance and
 //   the tile kernel; at one workgroup per CU they were 1-3% slower than those.
+//   With several tokens, against skinny_rows (M = 2) and the tile kernel: bf16
+//   TP=8 layer 42.6 / 44.2 / 44.5 -> 40.3 / 40.9 / 42.6 us at M = 2 / 3 / 4,
+//   QKV GEMV 8.1 / 11.3 -> 7.4 / 8.4 us at M = 2 / 4; FP8 TP=8 layer 26.8 ->
+//   26.2 us at M = 2 but 27.4 -> 32.5 us at M = 4, where each 16-byte weight
+//   chunk takes two x reads from LDS per token (LDS-bound), hence
+//   flat_max_m.  bf16 x of K = 8192 fits the LDS for up to 4 tokens.
 // Neither leaving x staged across linears nor dropping the FP8 scale loads
 // (timing-only builds) moved the FP8 rate of the large launches, so it is not
 // the staging drains or the extra loads that hold it below the bf16 rate.
@@ -2088,11 +2125,12 @@ constexpr int kFlatWavesPerCU = 8;
 constexpr int kFlatWavesPerCUSmall = 16;
 constexpr double kFlatLaunchBytes = 1.0e9;     // FP8 launches of at least this: flat
 constexpr double kFlatSmallBytes = 0.4e9;      // launches under this: flat, 16 waves per CU
+constexpr int flat_max_m(int dtype) { return dtype == SKINNY_BF16 ? 4 : 2; }
 
-template <int DT>
+template <int DT, int MT>
 KernelChoice flat_kernel() {
   KernelChoice k;
-  k.fn = skinny_rows_flat<DT, flat_depth(DT), flat_segs(DT)>;
+  k.fn = skinny_rows_flat<DT, MT, flat_depth(DT), flat_segs(DT)>;
   k.band_rows = kRowsWavesPerBlock;
   k.wpb = kRowsWavesPerBlock;
   k.flat = true;
@@ -2101,38 +2139,52 @@ KernelChoice flat_kernel() {
   return k;
 }
 
-// The flat kernel takes a launch of one token whose linears all read a plain
-// x that fits whole in its LDS (every segment of the longest row included).
+template <int DT>
+KernelChoice flat_kernel_m(int M) {
+  static_assert(flat_max_m(DT) == 2 || flat_max_m(DT) == 4, "instances for 2 or 4 tokens");
+  if (M == 1) return flat_kernel<DT, 1>();
+  if (M == 2) return flat_kernel<DT, 2>();
+  if constexpr (flat_max_m(DT) == 4) {
+    if (M == 3) return flat_kernel<DT, 3>();
+    if (M == 4) return flat_kernel<DT, 4>();
+  }
+  return KernelChoice{};
+}
+
+// The flat kernel takes a launch of up to flat_max_m tokens whose linears all
+// read a plain x that fits whole in its LDS (every segment of the longest row
+// included, for each token).
 bool flat_fits(const skinny_linear* const* lin, int count, int M) {
-  if (M != 1) return false;
+  if (M < 1 || M > flat_max_m(lin[0]->dtype)) return false;
   for (int i = 0; i < count; ++i) {
     const skinny_linear& L = *lin[i];
     if (L.reserved != kActNone) return false;
     const int xc = L.dtype == SKINNY_BF16 ? 1 : 2;
     const int cpr = L.K / (L.dtype == SKINNY_BF16 ? 8 : 16);
     const long long spt = (cpr + kSegChunks - 1) / kSegChunks;
-    if (spt * kSegChunks * xc * 16 > kRowsXBudget) return false;
+    if (spt * kSegChunks * xc * 16 * M > kRowsXBudget) return false;
   }
   return true;
 }
 
 // Waves per CU of the flat kernel for this launch, or 0 if it does not take
 // it.  Automatic variant: launches under kFlatSmallBytes of weights (16 waves
-// per CU) and FP8 launches of at least kFlatLaunchBytes (8); a forced VECTOR
-// variant takes it whenever it fits.
+// per CU) and one-token FP8 launches of at least kFlatLaunchBytes (8); a
+// forced VECTOR variant takes it for one token whenever it fits.
 int use_flat(const skinny_linear* const* lin, int count, int M, int requested) {
   if (requested == SKINNY_VARIANT_MFMA || !flat_fits(lin, count, M)) return 0;
   double bytes = 0;
   for (int i = 0; i < count; ++i)
     bytes += (lin[i]->dtype == SKINNY_BF16 ? 2.0 : 1.0) * lin[i]->N * lin[i]->K;
   const int waves = bytes < kFlatSmallBytes ? kFlatWavesPerCUSmall : kFlatWavesPerCU;
-  if (requested == SKINNY_VARIANT_VECTOR || bytes < kFlatSmallBytes) return waves;
-  return lin[0]->dtype != SKINNY_BF16 && bytes >= kFlatLaunchBytes ? waves : 0;
+  if (requested == SKINNY_VARIANT_VECTOR) return M == 1 ? waves : 0;
+  if (bytes < kFlatSmallBytes) return waves;
+  return M == 1 && lin[0]->dtype != SKINNY_BF16 && bytes >= kFlatLaunchBytes ? waves : 0;
 }
 
-KernelChoice pick_flat(int dtype, int waves_per_cu) {
-  KernelChoice k =
-      dtype == SKINNY_BF16 ? flat_kernel<SKINNY_BF16>() : flat_kernel<SKINNY_FP8_BS128>();
+KernelChoice pick_flat(int dtype, int M, int waves_per_cu) {
+  KernelChoice k = dtype == SKINNY_BF16 ? flat_kernel_m<SKINNY_BF16>(M)
+                                        : flat_kernel_m<SKINNY_FP8_BS128>(M);
   k.waves_per_cu = waves_per_cu;
   return k;
 }
@@ -2316,7 +2368,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
-  if (const int fw = use_flat(lin, count, M, requested)) k = pick_flat(dtype, fw);
+  if (const int fw = use_flat(lin, count, M, requested)) k = pick_flat(dtype, M, fw);
   if (k.tiles && tiles_large(lin, count, M, dev.cus))
     k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
                              : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
@@ -2978,7 +3030,7 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   if (!k.tiles && rows_lean(group, n, M)) k = pick_lean(M);
   if (const int fw = use_flat(group, n, M, SKINNY_VARIANT_AUTO)) {
     out->variant = SKINNY_VARIANT_VECTOR;
-    k = pick_flat(linears[0].dtype, fw);
+    k = pick_flat(linears[0].dtype, M, fw);
   }
   if (k.tiles && tiles_large(group, n, M, d.cus))
     k = linears[0].dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()

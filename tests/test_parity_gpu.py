@@ -244,9 +244,9 @@ def test_automatic_variant():
     """bf16 takes the row kernel at M <= 2, and at M = 3-4 for launches of at
     least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise.  FP8
     takes the tile kernel but for one-token launches of at least 1 GB of
-    weights.  One-token launches under 0.4 GB (both dtypes) and FP8 ones of at
-    least 1 GB run the flat row kernel.  The stack's launches hold up to 32
-    linears."""
+    weights.  Launches under 0.4 GB of up to 4 tokens (bf16) or 2 (FP8), and
+    one-token FP8 ones of at least 1 GB, run the flat row kernel.  The stack's
+    launches hold up to 32 linears."""
     V, T = sg.VARIANT_VECTOR, sg.VARIANT_MFMA
 
     def variant(shapes, M, dt=sg.BF16):
@@ -255,13 +255,13 @@ def test_automatic_variant():
         return sg.plan_query(lins, M).variant
     tp8 = [(1280, 8192), (8192, 1024), (7392, 8192), (8192, 3696)]
     tp1 = [(10240, 8192), (8192, 8192), (59136, 8192), (8192, 29568)]
-    assert [variant(tp8, M) for M in (1, 2, 3, 4, 5, 8, 16)] == [V, V, T, T, T, T, T]
+    assert [variant(tp8, M) for M in (1, 2, 3, 4, 5, 8, 16)] == [V, V, V, V, T, T, T]
     assert [variant(tp1, M) for M in (1, 2, 3, 4)] == [V, V, T, T]                  # 1.76 GB
     assert [variant(tp1 * 2, M) for M in (1, 2, 3, 4, 5, 6, 8)] == [V, V, V, V, T, T, T]
     assert [variant(tp1 * 2, M, sg.FP8_BS128) for M in (1, 2, 4)] == [V, T, T]   # 1.76 GB
     assert variant(tp1, 1, sg.FP8_BS128) == T                                     # 0.88 GB
     assert variant([(152064, 8192)], 1, sg.FP8_BS128) == V                       # 1.25 GB
-    assert [variant(tp8, M, sg.FP8_BS128) for M in (1, 2)] == [V, T]             # 0.11 GB
+    assert [variant(tp8, M, sg.FP8_BS128) for M in (1, 2, 3)] == [V, V, T]       # 0.11 GB
 
     def kernel(shapes, M, dt=sg.BF16):
         scale = None if dt == sg.BF16 else 0x300000
@@ -270,4 +270,7 @@ def test_automatic_variant():
     assert kernel(tp1 * 2, 1, sg.FP8_BS128) == "skinny_rows_flat"
     assert kernel(tp1 * 2, 1) == "skinny_rows (lean)"
     assert kernel(tp8, 1) == "skinny_rows_flat"                                 # 0.22 GB
+    assert kernel(tp8, 4) == "skinny_rows_flat"
+    assert kernel(tp8, 2, sg.FP8_BS128) == "skinny_rows_flat"
+    assert kernel(tp8, 3, sg.FP8_BS128) == "skinny_tiles"
     assert kernel(tp8, 8) == "skinny_tiles"
