@@ -2115,7 +2115,11 @@ KernelChoice pick_lean(int M) {
 //   QKV GEMV 8.1 / 11.3 -> 7.4 / 8.4 us at M = 2 / 4; FP8 TP=8 layer 26.8 ->
 //   26.2 us at M = 2 but 27.4 -> 32.5 us at M = 4, where each 16-byte weight
 //   chunk takes two x reads from LDS per token (LDS-bound), hence
-//   flat_max_m.  bf16 x of K = 8192 fits the LDS for up to 4 tokens.
+//   flat_max_m.  bf16 x of K = 8192 fits the LDS for up to 4 tokens; with a
+//   128 KB x budget (one workgroup, 8 waves per CU) it fits 5-8 tokens, but
+//   the TP=8 layer then took 50.1 / 54.5 / 64.8 us at M = 5 / 6 / 8 against
+//   the tile kernel's 45.1 / 45.3 / 45.6 (two waves per SIMD do not cover the
+//   LDS reads and products of 5-8 tokens), so the tile kernel keeps them.
 // Neither leaving x staged across linears nor dropping the FP8 scale loads
 // (timing-only builds) moved the FP8 rate of the large launches, so it is not
 // the staging drains or the extra loads that hold it below the bf16 rate.
