@@ -19,6 +19,7 @@ bounded sample on this host's cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import platform
@@ -433,6 +434,13 @@ def main():
     # and host launch overhead stays out of the figures.
     spin_cycles = calibrate_spin(stream)
 
+    # The host enqueues each timed region while a spin kernel holds the GPU;
+    # a garbage-collector pass in the middle (tens of ms in a process holding
+    # torch) could outlast that lead and show up as GPU idle time, so the
+    # collector stays off until the timed regions are done.
+    gc.collect()
+    gc.disable()
+
     def prefill(expected_ms):
         torch.cuda._sleep(int(spin_cycles * (expected_ms + 5.0)))
 
@@ -488,6 +496,7 @@ def main():
         sg.linear_run_timed(timed_sets[(args.warmup + i) % copies], M, ws, handles,
                             variant=variant, waves=args.waves)
     torch.cuda.synchronize()
+    gc.enable()
     main_ms = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(n_launch * args.steps)]
     main_avg_ms = float(np.mean(main_ms))
     bytes_per_launch = timed_bytes / n_launch
@@ -516,7 +525,8 @@ def main():
             "algorithmic_bytes_per_step": step_bytes,
             "flops_per_step": step_flops,
             "us_per_step": round(ms_per_step * 1e3, 2),
-            "us_per_step_batches": {"batches": nb, "median": round(float(np.median(batch_us)), 2),
+            "us_per_step_batches": {"batches": nb, "us": [round(b, 2) for b in batch_us],
+                                    "median": round(float(np.median(batch_us)), 2),
                                     "min": round(min(batch_us), 2), "max": round(max(batch_us), 2)},
             "hot_cache_us_per_step": None if hot_us is None else round(hot_us, 2),
             "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -568,6 +578,12 @@ def main():
             "experts": wl.MOE_EXPERTS, "top_k": wl.MOE_TOPK, "routes": int(ids_host.size),
             "experts_chosen": len(set(ids_host.ravel().tolist())),
             "gate_up_bytes": moe_gu_bytes, "down_bytes": moe_dn_bytes})
+        if one_launch:
+            # A wait that gave up leaves wrong outputs: the run is then invalid.
+            gave_up = sg.moe_mlp_gave_up(ws)
+            result["config"]["one_launch_wait_gave_up"] = gave_up
+            if gave_up:
+                log("a wait of the one-launch MoE MLP gave up: outputs of this run are invalid")
 
     if not args.no_cpu_baseline and moe:
         import oracle
