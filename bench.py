@@ -441,8 +441,32 @@ def main():
     gc.collect()
     gc.disable()
 
-    def prefill(expected_ms):
-        torch.cuda._sleep(int(spin_cycles * (expected_ms + 5.0)))
+    # The spin that leads a timed region is sized from the host's enqueue
+    # time and the GPU's time per step, both measured here on untimed steps:
+    # long enough for the host to stay ahead of the GPU, and no longer, since
+    # a GPU left near idle for many milliseconds runs the next steps at a
+    # transiently lower rate (measured on MI355X: the TP=8 layer at M = 4 on
+    # the flat row kernel took 44 us per step after a 1 ms lead but rose to
+    # 49 us within 5 ms of steps after a 15 ms one).
+    n_cal = max(5, min(50, args.steps))
+    t0 = time.perf_counter()
+    for i in range(n_cal):
+        step(args.warmup + i)
+    host_ms = (time.perf_counter() - t0) * 1e3 / n_cal
+    torch.cuda.synchronize()
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(spin_cycles * (1.0 + 2.0 * n_cal * host_ms)))
+    ca.record(stream)
+    for i in range(n_cal):
+        step(args.warmup + i)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    gpu_ms = ca.elapsed_time(cb) / n_cal
+
+    def prefill(n, host_factor=1.0):
+        """Spin ahead of n steps whose enqueue costs host_factor x host_ms each."""
+        lag = n * max(0.0, 1.5 * host_factor * host_ms - gpu_ms)
+        torch.cuda._sleep(int(spin_cycles * (1.0 + lag)))
 
     # Timed region: K whole steps between two events on the library's stream,
     # with events between batches of steps (up to 7) for the spread.
@@ -450,7 +474,7 @@ def main():
     bounds = [b * args.steps // nb for b in range(nb + 1)]
     bev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
-    prefill(args.steps * 0.05)
+    prefill(args.steps)
     bev[0].record(stream)
     for b in range(nb):
         for i in range(bounds[b], bounds[b + 1]):
@@ -472,7 +496,7 @@ def main():
         for _ in range(3):
             step(0)
         torch.cuda.synchronize()
-        prefill(args.steps * 0.05)
+        prefill(args.steps)
         h0.record(stream)
         for _ in range(args.steps):
             step(0)
@@ -485,7 +509,7 @@ def main():
     for e in evs:
         e.record(stream)                     # creates the underlying hipEvent_t
     torch.cuda.synchronize()
-    prefill(args.steps * 0.1)
+    prefill(args.steps, host_factor=2.0)
     for i in range(args.steps):
         handles = [e.cuda_event for e in evs[2 * n_launch * i: 2 * n_launch * (i + 1)]]
         if moe:
@@ -529,6 +553,8 @@ def main():
                                     "median": round(float(np.median(batch_us)), 2),
                                     "min": round(min(batch_us), 2), "max": round(max(batch_us), 2)},
             "hot_cache_us_per_step": None if hot_us is None else round(hot_us, 2),
+            "lead_in": {"host_us_per_step": round(host_ms * 1e3, 2),
+                        "gpu_us_per_step": round(gpu_ms * 1e3, 2)},
             "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
             # Weight-only MBU: weight (and scale) bytes per second over the peak,
             # the decode figure of "Developing a custom Qwen2.5 72B inference
