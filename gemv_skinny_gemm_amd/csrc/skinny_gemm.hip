@@ -2171,17 +2171,32 @@ bool flat_fits(const skinny_linear* const* lin, int count, int M) {
   return true;
 }
 
+// A workgroup of the flat kernel restages x, between two barriers that drain
+// its loads, each time its units move to another linear.  Many linears of
+// few rows each make that happen at nearly every unit.  With more than one
+// linear the automatic variant therefore asks for at least this many weight
+// bytes per workgroup and switch (count - 1 switches at most).  Measured on
+// MI355X, launches of eight equal linears against the next automatic
+// choice: FP8 4096 x 1536 (14 KB per switch) 21.3 us flat against 12.5 on
+// the tile kernel at M = 1 (23.4 against 12.6 at M = 2); bf16 4096 x 1536 at
+// M = 2 (28 KB) 26.2 flat against 30.4 on skinny_rows; FP8 3072 x 4096 at
+// M = 1 (28 KB) 22.1 flat against 24.4 tiles; the TP=8 layer (143 KB) gains.
+constexpr double kFlatMinBytesPerSwitch = 24 * 1024;
+
 // Waves per CU of the flat kernel for this launch, or 0 if it does not take
 // it.  Automatic variant: launches under kFlatSmallBytes of weights (16 waves
-// per CU) and one-token FP8 launches of at least kFlatLaunchBytes (8); a
-// forced VECTOR variant takes it for one token whenever it fits.
-int use_flat(const skinny_linear* const* lin, int count, int M, int requested) {
+// per CU) and one-token FP8 launches of at least kFlatLaunchBytes (8), given
+// kFlatMinBytesPerSwitch; a forced VECTOR variant takes it for one token
+// whenever it fits.
+int use_flat(const skinny_linear* const* lin, int count, int M, int requested, int cus) {
   if (requested == SKINNY_VARIANT_MFMA || !flat_fits(lin, count, M)) return 0;
   double bytes = 0;
   for (int i = 0; i < count; ++i)
     bytes += (lin[i]->dtype == SKINNY_BF16 ? 2.0 : 1.0) * lin[i]->N * lin[i]->K;
   const int waves = bytes < kFlatSmallBytes ? kFlatWavesPerCUSmall : kFlatWavesPerCU;
   if (requested == SKINNY_VARIANT_VECTOR) return M == 1 ? waves : 0;
+  const double workgroups = (double)cus * waves / kRowsWavesPerBlock;
+  if (count > 1 && bytes / (workgroups * (count - 1)) < kFlatMinBytesPerSwitch) return 0;
   if (bytes < kFlatSmallBytes) return waves;
   return M == 1 && lin[0]->dtype != SKINNY_BF16 && bytes >= kFlatLaunchBytes ? waves : 0;
 }
@@ -2372,7 +2387,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   KernelChoice k = pick(dtype, variant, M);
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
-  if (const int fw = use_flat(lin, count, M, requested)) k = pick_flat(dtype, M, fw);
+  if (const int fw = use_flat(lin, count, M, requested, dev.cus)) k = pick_flat(dtype, M, fw);
   if (k.tiles && tiles_large(lin, count, M, dev.cus))
     k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
                              : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
@@ -3032,7 +3047,7 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
   KernelChoice k = pick(linears[0].dtype, out->variant, M);
   if (!k.fn) return SKINNY_ERR_INVALID_ARG;
   if (!k.tiles && rows_lean(group, n, M)) k = pick_lean(M);
-  if (const int fw = use_flat(group, n, M, SKINNY_VARIANT_AUTO)) {
+  if (const int fw = use_flat(group, n, M, SKINNY_VARIANT_AUTO, d.cus)) {
     out->variant = SKINNY_VARIANT_VECTOR;
     k = pick_flat(linears[0].dtype, M, fw);
   }

@@ -90,23 +90,29 @@ def test_flat_stack_switches_linears(dtype):
     """Five linears of different K and ragged N in one launch, each with its
     own x: a workgroup's units cross from one linear to the next (its outputs
     written, the next x staged).  Rows of N not a multiple of 8 are written
-    value by value, the others 8 at a time."""
-    shapes = [(9, 272), (1000, 3696), (3, 16), (523, 1024), (64, 4096)]
+    value by value, the others 8 at a time.  The last linear is large enough
+    (about 0.1 GB) for the automatic plan to take the flat kernel with five
+    linears in the launch."""
+    N5 = 12000 if dtype == sg.BF16 else 24000
+    shapes = [(9, 272), (1000, 3696), (3, 16), (523, 1024), (N5, 4096)]
+    weights = []                                           # host weights and device copies
+    for i, (N, K) in enumerate(shapes):
+        if dtype == sg.BF16:
+            w = synth.tensor_bf16(0, synth.stream_id("flat-stack", i, "w"), N, K, 0.02)
+            weights.append(((w,), dev_bf16(w), None))
+        else:
+            q, s, _ = synth.fp8_weight_bs128(0, synth.stream_id("flat-stack", i, "q"), N, K)
+            weights.append(((q, s), dev_u8(q), dev_f32(s)))
     for M in range(1, MAX_M[dtype] + 1):
         assert _plan_is_flat(dtype, shapes, M)
         descs, refs, ys, keep = [], [], [], []
         for i, (N, K) in enumerate(shapes):
             x = synth.tensor_bf16(0, synth.stream_id("flat-stack", M, i, "x"), M, K, 1.0)
-            if dtype == sg.BF16:
-                w = synth.tensor_bf16(0, synth.stream_id("flat-stack", i, "w"), N, K, 0.02)
-                refs.append(oracle.linear_bf16(x, w))
-                wd, sd = dev_bf16(w), None
-            else:
-                q, s, _ = synth.fp8_weight_bs128(0, synth.stream_id("flat-stack", i, "q"), N, K)
-                refs.append(oracle.linear_fp8_bs128(x, q, s))
-                wd, sd = dev_u8(q), dev_f32(s)
+            host, wd, sd = weights[i]
+            refs.append(oracle.linear_bf16(x, *host) if dtype == sg.BF16
+                        else oracle.linear_fp8_bs128(x, *host))
             xd, yd = dev_bf16(x), out(M, N)
-            keep += [xd, wd, sd]
+            keep.append(xd)
             ys.append(yd)
             descs.append(sg.make_linear(xd, wd, yd, w_scale=sd))
         assert _kernel(descs, M) == FLAT
