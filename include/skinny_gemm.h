@@ -99,8 +99,9 @@ enum skinny_kernel {
   SKINNY_KERNEL_NONE = 0,
   SKINNY_KERNEL_ROWS = 1,         /* skinny_rows (VECTOR), deep instance; MoE form      */
   SKINNY_KERNEL_ROWS_LEAN = 2,    /* skinny_rows, lean instance (bf16 launches >= 0.4 GB) */
-  SKINNY_KERNEL_ROWS_FLAT = 3,    /* skinny_rows_flat (one token, loads streamed across
-                                     units; FP8 launches >= 1 GB)                       */
+  SKINNY_KERNEL_ROWS_FLAT = 3,    /* skinny_rows_flat (loads streamed across units):
+                                     launches < 0.4 GB of up to 4 (bf16) or 2 (FP8)
+                                     tokens, one-token FP8 launches >= 1 GB             */
   SKINNY_KERNEL_TILES = 4,        /* skinny_tiles (MFMA), 4-wave workgroups; MoE form  */
   SKINNY_KERNEL_TILES_WIDE = 5,   /* skinny_tiles, 8-wave workgroups                    */
   SKINNY_KERNEL_TILES_KSPLIT = 6, /* skinny_tiles' K-split form (one-token MoE slices)  */
