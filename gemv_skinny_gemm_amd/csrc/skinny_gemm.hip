@@ -869,9 +869,25 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   FlatSlot<U> q[P];
   enter_load();
   enter_consume();
+  {
+    // The first x goes out ahead of the first P - 1 slots, so one wait that
+    // leaves those slots' loads in flight (loads complete in issue order)
+    // covers it: the start does not drain the stream.
+    const LinDesc& L = a.lin[cl];
+    const int xcpr = L.K >> 3;
+    stage_x_direct<kThreads, false>(L, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s = 0; s < P - 1; ++s) load_next(q[s]);
-  stage();
+    for (int s = 0; s < P - 1; ++s) load_next(q[s]);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kSlotLoads = (P - 1) * U * (kFp8 ? 2 : 1);
+    static_assert(kSlotLoads < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((kSlotLoads & 0xF) | ((kSlotLoads >> 4) << 14) | 0x3F70);
+    // A plain barrier: the compiler would put a wait for every outstanding
+    // load in front of __syncthreads() here (the x copies write LDS), which
+    // the wait above already covers for x.
+    asm volatile("s_barrier" ::: "memory");
+  }
   // P steps per pass: load the slot consumed last, consume the oldest.  Every
   // pass issues the same loads in the same order, the last one included (a
   // finished wave only skips its products), so each wait counts exactly the
