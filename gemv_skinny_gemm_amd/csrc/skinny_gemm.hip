@@ -146,6 +146,12 @@ struct LaunchArgs {
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
 };
 
+// Weight loads are nontemporal: every weight byte is read once per call and
+// never again soon, and on MI355X the streaming-read probe reads 7.2 TB/s
+// with nontemporal 16-byte loads against 6.5 TB/s with plain ones (same
+// patterns, 8 GiB).  x, the FP8 scales and everything shared stay plain.
+__device__ __forceinline__ u32x4 ldw(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) {
   return __builtin_bit_cast(bf16x2, u);
 }
@@ -489,7 +495,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 #pragma unroll
       for (int v = 0; v < U; ++v)
 #pragma unroll
-        for (int r = 0; r < R; ++r) b.w[v][r] = wrow[r][(j + v) * kSegChunks + lane];
+        for (int r = 0; r < R; ++r) b.w[v][r] = ldw(wrow[r] + (j + v) * kSegChunks + lane);
       __builtin_amdgcn_sched_barrier(0);
     };
     // ... and its products.  OK marks the chunks inside the row (a ragged end).
@@ -573,7 +579,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
         const int cw = (j + v) * kSegChunks + lane;
         const bool ok = (j + v < j1) && cw < L.cpr;
 #pragma unroll
-        for (int r = 0; r < R; ++r) b1.w[v][r] = ok ? wrow[r][ok ? cw : 0] : zero4();
+        for (int r = 0; r < R; ++r) b1.w[v][r] = ok ? ldw(wrow[r] + (ok ? cw : 0)) : zero4();
       }
       consume(b1, j, Masked{});
     }
@@ -721,7 +727,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       const int c = min((lj * U + v) * kSegChunks + lane, lcpr - 1);
-      q.w[v] = lw[c];
+      q.w[v] = ldw(lw + c);
       if (kFp8) q.s[v] = ls[c >> 3];              // chunk c: k in [16 c, 16 c + 16)
     }
     if (++lj == lspt) {
@@ -1089,7 +1095,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
 #pragma unroll
     for (int q = 0; q < kLoadsT; ++q) {
       const int row = min(row0 + kRowsPerLoadT * q + lrow, L.N - 1);
-      s.w[q] = w[(size_t)row * L.cpr + c];
+      s.w[q] = ldw(w + (size_t)row * L.cpr + c);
     }
     if (DT == SKINNY_FP8_BS128) {
       // The row group lies in one 128-row scale block.  Blocks past K cover
@@ -1503,7 +1509,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_moe_mlp1(const
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       const int c = min((j * U + v) * kSegChunks + lane, cpr - 1);
-      q.w[v] = w[c];
+      q.w[v] = ldw(w + c);
       if (kFp8) q.s[v] = sc[c >> 3];
     }
   };
