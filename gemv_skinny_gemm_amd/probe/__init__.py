@@ -23,19 +23,19 @@ def lib():
         L.skinny_probe_stream_read.restype = ctypes.c_int
         L.skinny_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
                                                ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int,
-                                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                               ctypes.c_void_p]
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_void_p]
         L.skinny_probe_stream_read_tiles.restype = ctypes.c_int
         L.skinny_probe_stream_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
                                                      ctypes.c_longlong, ctypes.c_int,
-                                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                                     ctypes.c_void_p]
+                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
 
 def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu: int,
-                  reps: int = 5) -> float:
+                  reps: int = 5, nontemporal: bool = False) -> float:
     """GB/s of the matrix-core kernel's read pattern over the whole of buf."""
     import torch
     nbytes = buf.numel() * buf.element_size()
@@ -47,8 +47,8 @@ def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu
 
     def go():
         rc = lib().skinny_probe_stream_read_tiles(buf.data_ptr(), nbytes, row_bytes, wpb,
-                                                  int(ksplit), workgroups, sink.data_ptr(),
-                                                  stream.cuda_stream)
+                                                  int(ksplit), workgroups, int(nontemporal),
+                                                  sink.data_ptr(), stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"skinny_probe_stream_read_tiles failed ({rc})")
     for _ in range(2):
@@ -63,17 +63,19 @@ def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu
 
 
 def stream_read(buf, nbytes: int, row_bytes: int, order: int, u: int, workgroups: int, sink,
-                stream: int, read_bytes: int | None = None):
+                stream: int, read_bytes: int | None = None, nontemporal: bool = False):
     """Enqueue one read of the first nbytes of the device tensor buf (of each
     row, its first read_bytes; default the whole row)."""
     rc = lib().skinny_probe_stream_read(buf.data_ptr(), nbytes, row_bytes, read_bytes or row_bytes,
-                                        order, u, workgroups, sink.data_ptr(), stream)
+                                        order, u, workgroups, int(nontemporal), sink.data_ptr(),
+                                        stream)
     if rc != 0:
         raise RuntimeError(f"skinny_probe_stream_read failed ({rc})")
 
 
 def measure(buf, row_bytes: int, order: int, u: int, waves_per_cu: int, reps: int = 5,
-            cus: int | None = None, read_bytes: int | None = None) -> float:
+            cus: int | None = None, read_bytes: int | None = None,
+            nontemporal: bool = False) -> float:
     """GB/s read by `reps` back-to-back reads of buf (of each row, its first
     read_bytes; HIP events on the current stream, after two untimed reads)."""
     import torch
@@ -86,11 +88,13 @@ def measure(buf, row_bytes: int, order: int, u: int, waves_per_cu: int, reps: in
     sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
     stream = torch.cuda.current_stream()
     for _ in range(2):
-        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read)
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read,
+                    nontemporal)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read)
+        stream_read(buf, nbytes, row_bytes, order, u, workgroups, sink, stream.cuda_stream, read,
+                    nontemporal)
     e1.record(stream)
     torch.cuda.synchronize()
     return nbytes // row_bytes * read * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9

@@ -4,6 +4,8 @@
     python -m gemv_skinny_gemm_amd.probe stride   1-2 KB read from the start of every row of a
                                                   given stride (32 GiB buffer)
     python -m gemv_skinny_gemm_amd.probe tiles    the matrix-core kernel's read pattern
+    python -m gemv_skinny_gemm_amd.probe nt       plain against nontemporal loads, the fastest
+                                                  patterns of the sweeps above and the tiles one
 
 Every figure is GB/s read from an 8 GiB buffer (GiB = 2^30 bytes), best of
 three measurements of five passes each.  Measurement only.
@@ -65,12 +67,35 @@ def tiles(buf):
                 print(f"| {rb >> 10} KB | {wpb} | {int(ks)} | {wgpc} | {g:.0f} |", flush=True)
 
 
+def nontemporal(buf):
+    """The same patterns with plain and with nontemporal loads (the hint the
+    library's weight loads carry)."""
+    print("| pattern | plain GB/s | nontemporal GB/s |")
+    print("|---|---|---|")
+    for name, order, row_kb, u, wpc in (
+            ("8 KB rows to waves, 2 KB batches, 8 waves/CU", probe.ORDER_WAVES, 8, 2, 8),
+            ("32 KB rows to workgroups, 2 KB batches, 8 waves/CU", probe.ORDER_WORKGROUPS, 32, 2, 8),
+            ("16 KB rows to waves, 1 KB batches, 16 waves/CU", probe.ORDER_WAVES, 16, 1, 16),
+            ("16 KB rows to waves, 4 KB batches, 8 waves/CU", probe.ORDER_WAVES, 16, 4, 8),
+            ("16 KB rows to waves, 8 KB batches, 16 waves/CU", probe.ORDER_WAVES, 16, 8, 16),
+            ("8 KB rows to waves, 1 KB batches, 8 waves/CU", probe.ORDER_WAVES, 8, 1, 8)):
+        g = [best(lambda: probe.measure(buf, row_kb << 10, order, u, wpc, nontemporal=nt))
+             for nt in (False, True)]
+        print(f"| {name} | {g[0]:.0f} | {g[1]:.0f} |", flush=True)
+    for rb in (8192, 16384):
+        for wpb, wgpc in ((4, 2), (8, 1)):
+            g = [best(lambda: probe.measure_tiles(buf, rb, wpb, False, wgpc, nontemporal=nt))
+                 for nt in (False, True)]
+            print(f"| tiles: {rb >> 10} KB rows, {wpb}-wave workgroups x {wgpc} per CU | "
+                  f"{g[0]:.0f} | {g[1]:.0f} |", flush=True)
+
+
 def main():
     what = sys.argv[1] if len(sys.argv) > 1 else "depth"
     buf = torch.ones(8 * GIB // 8, dtype=torch.int64, device="cuda")
     torch.cuda.synchronize()
     print(f"# {what} sweep, {torch.cuda.get_device_name(0)}", flush=True)
-    {"depth": depth, "stride": stride, "tiles": tiles}[what](buf)
+    {"depth": depth, "stride": stride, "tiles": tiles, "nt": nontemporal}[what](buf)
 
 
 if __name__ == "__main__":

@@ -20,6 +20,8 @@
 //                    split each row's batches between them.
 // Every loaded word is XOR-folded into a value that is written out only if
 // it equals a sentinel the data never produces, so no load can be dropped.
+// NT: the loads carry the nontemporal hint (streamed data, not to be kept in
+// the caches), as the library's weight loads do.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -33,7 +35,13 @@ constexpr int kWaves = kThreads / 64;
 constexpr int ORDER_WAVES = 0;
 constexpr int ORDER_WORKGROUPS = 1;
 
-template <int U, int ORDER>
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int U, int ORDER, bool NT>
 __global__ __launch_bounds__(kThreads) void stream_read(const u32x4* buf, long long rows,
                                                          int row_chunks, int read_chunks,
                                                          unsigned* sink) {
@@ -60,15 +68,15 @@ __global__ __launch_bounds__(kThreads) void stream_read(const u32x4* buf, long l
     int k = b0;
     if (k >= batches) continue;
 #pragma unroll
-    for (int v = 0; v < U; ++v) a[v] = row[(k * U + v) * 64];
+    for (int v = 0; v < U; ++v) a[v] = ld<NT>(row + (k * U + v) * 64);
     for (; k + bstep < batches; k += 2 * bstep) {
 #pragma unroll
-      for (int v = 0; v < U; ++v) b[v] = row[((k + bstep) * U + v) * 64];
+      for (int v = 0; v < U; ++v) b[v] = ld<NT>(row + ((k + bstep) * U + v) * 64);
 #pragma unroll
       for (int v = 0; v < U; ++v) acc ^= a[v];
       if (k + 2 * bstep < batches) {
 #pragma unroll
-        for (int v = 0; v < U; ++v) a[v] = row[((k + 2 * bstep) * U + v) * 64];
+        for (int v = 0; v < U; ++v) a[v] = ld<NT>(row + ((k + 2 * bstep) * U + v) * 64);
       }
 #pragma unroll
       for (int v = 0; v < U; ++v) acc ^= b[v];
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void stream_read(const u32x4* buf, long l
 // flight ahead of the one being folded.  KSPLIT = false: wave i takes rows
 // 16 i .. 16 i + 15 of the unit, all of K; KSPLIT = true: the unit is 16
 // rows and wave i takes segments i, i + WPB, ... of them (the waves split K).
-template <int WPB, bool KSPLIT>
+template <int WPB, bool KSPLIT, bool NT>
 __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, long long rows,
                                                               int row_chunks, unsigned* sink) {
   const int lane = threadIdx.x & 63;
@@ -107,16 +115,18 @@ __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, 
     if (s0 >= segs) continue;
     u32x4 a[8], b[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) a[q] = base[2 * q * (long long)row_chunks + s0 * 32];
+    for (int q = 0; q < 8; ++q) a[q] = ld<NT>(base + 2 * q * (long long)row_chunks + s0 * 32);
     int s = s0;
     for (; s + sstep < segs; s += 2 * sstep) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) b[q] = base[2 * q * (long long)row_chunks + (s + sstep) * 32];
+      for (int q = 0; q < 8; ++q)
+        b[q] = ld<NT>(base + 2 * q * (long long)row_chunks + (s + sstep) * 32);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc ^= a[q];
       if (s + 2 * sstep < segs) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = base[2 * q * (long long)row_chunks + (s + 2 * sstep) * 32];
+        for (int q = 0; q < 8; ++q)
+          a[q] = ld<NT>(base + 2 * q * (long long)row_chunks + (s + 2 * sstep) * 32);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc ^= b[q];
@@ -133,16 +143,23 @@ __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, 
 typedef void (*probe_fn)(const u32x4*, long long, int, int, unsigned*);
 typedef void (*tiles_fn)(const u32x4*, long long, int, unsigned*);
 
-template <int ORDER>
+template <int ORDER, bool NT>
 probe_fn pick(int u) {
   switch (u) {
-    case 1: return stream_read<1, ORDER>;
-    case 2: return stream_read<2, ORDER>;
-    case 4: return stream_read<4, ORDER>;
-    case 8: return stream_read<8, ORDER>;
-    case 16: return stream_read<16, ORDER>;
+    case 1: return stream_read<1, ORDER, NT>;
+    case 2: return stream_read<2, ORDER, NT>;
+    case 4: return stream_read<4, ORDER, NT>;
+    case 8: return stream_read<8, ORDER, NT>;
+    case 16: return stream_read<16, ORDER, NT>;
     default: return nullptr;
   }
+}
+
+template <bool NT>
+probe_fn pick_order(int order, int u) {
+  return order == ORDER_WAVES ? pick<ORDER_WAVES, NT>(u)
+         : order == ORDER_WORKGROUPS ? pick<ORDER_WORKGROUPS, NT>(u)
+                                     : nullptr;
 }
 
 constexpr int kMaxProbeThreads = 512;
@@ -153,20 +170,19 @@ extern "C" {
 
 // Reads the first read_bytes of every row_bytes of the first `bytes` of `buf`
 // (16-byte aligned device memory) once: rows dealt in `order` (0 = to waves,
-// 1 = to workgroups), U KB per batch, `workgroups` workgroups of 4 waves.
-// Requirements: u in {1, 2, 4, 8, 16}; read_bytes a multiple of U KB and at
-// most row_bytes; bytes a multiple of row_bytes; sink device memory of
-// >= 4 * workgroups bytes (written only on the sentinel).  Returns 0, or -1
-// for invalid arguments (nothing enqueued), or -2 if the launch failed.
+// 1 = to workgroups), U KB per batch, `workgroups` workgroups of 4 waves,
+// nontemporal loads if `nontemporal` is nonzero.  Requirements: u in {1, 2,
+// 4, 8, 16}; read_bytes a multiple of U KB and at most row_bytes; bytes a
+// multiple of row_bytes; sink device memory of >= 4 * workgroups bytes
+// (written only on the sentinel).  Returns 0, or -1 for invalid arguments
+// (nothing enqueued), or -2 if the launch failed.
 int skinny_probe_stream_read(const void* buf, long long bytes, long long row_bytes,
                              long long read_bytes, int order, int u, int workgroups,
-                             unsigned* sink, void* stream) {
+                             int nontemporal, unsigned* sink, void* stream) {
   if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || read_bytes <= 0 || workgroups < 1)
     return -1;
   if (((uintptr_t)buf & 15) != 0) return -1;
-  const probe_fn fn = order == ORDER_WAVES ? pick<ORDER_WAVES>(u)
-                      : order == ORDER_WORKGROUPS ? pick<ORDER_WORKGROUPS>(u)
-                                                  : nullptr;
+  const probe_fn fn = nontemporal ? pick_order<true>(order, u) : pick_order<false>(order, u);
   if (!fn) return -1;
   if (read_bytes % (u * 1024LL) != 0 || read_bytes > row_bytes || bytes % row_bytes != 0)
     return -1;
@@ -179,17 +195,23 @@ int skinny_probe_stream_read(const void* buf, long long bytes, long long row_byt
 
 // The matrix-core kernel's pattern (stream_read_tiles): `bytes` of buf read
 // as rows of row_bytes (a multiple of 512; bytes a multiple of 16 * wpb *
-// row_bytes), wpb in {4, 8} waves per workgroup, ksplit 0 or 1.  Same
-// returns and sink rule as skinny_probe_stream_read.
+// row_bytes), wpb in {4, 8} waves per workgroup, ksplit 0 or 1, nontemporal
+// loads if `nontemporal` is nonzero.  Same returns and sink rule as
+// skinny_probe_stream_read.
 int skinny_probe_stream_read_tiles(const void* buf, long long bytes, long long row_bytes,
-                                   int wpb, int ksplit, int workgroups, unsigned* sink,
-                                   void* stream) {
+                                   int wpb, int ksplit, int workgroups, int nontemporal,
+                                   unsigned* sink, void* stream) {
   if (!buf || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
   if (((uintptr_t)buf & 15) != 0 || row_bytes % 512 != 0) return -1;
   if (bytes % (16LL * wpb * row_bytes) != 0 || row_bytes / 16 > (1LL << 30)) return -1;
   tiles_fn fn = nullptr;
-  if (wpb == 4) fn = ksplit ? stream_read_tiles<4, true> : stream_read_tiles<4, false>;
-  if (wpb == 8) fn = ksplit ? stream_read_tiles<8, true> : stream_read_tiles<8, false>;
+  if (nontemporal) {
+    if (wpb == 4) fn = ksplit ? stream_read_tiles<4, true, true> : stream_read_tiles<4, false, true>;
+    if (wpb == 8) fn = ksplit ? stream_read_tiles<8, true, true> : stream_read_tiles<8, false, true>;
+  } else {
+    if (wpb == 4) fn = ksplit ? stream_read_tiles<4, true, false> : stream_read_tiles<4, false, false>;
+    if (wpb == 8) fn = ksplit ? stream_read_tiles<8, true, false> : stream_read_tiles<8, false, false>;
+  }
   if (!fn || 64 * wpb > kMaxProbeThreads) return -1;
   hipLaunchKernelGGL(fn, dim3(workgroups), dim3(64 * wpb), 0, (hipStream_t)stream,
                      (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16), sink);

@@ -390,3 +390,17 @@ def test_moe_workspace_and_bad_arguments():
     assert call(y=X + 6 * 4096 * 2, flags=sg.MOE_X_PER_ROUTE | sg.MOE_SWIGLU) == INVALID
     assert L.skinny_moe_linear_timed(ctypes.byref(ex), X, IDS, 6, 2, 0, Y, None, big, wsb,
                                      None) == INVALID
+
+
+def test_read_probe_loads_and_rejects_bad_arguments():
+    """The streaming-read probe library (measurement only) loads and refuses
+    invalid arguments on the host, before any device call, in both load modes."""
+    from gemv_skinny_gemm_amd import probe
+    L = probe.lib()
+    for nt in (0, 1):
+        assert L.skinny_probe_stream_read(None, 1 << 20, 8192, 8192, 0, 2, 1, nt, 16, None) == -1
+        assert L.skinny_probe_stream_read(16, 1 << 20, 8192, 8192, 5, 2, 1, nt, 16, None) == -1
+        assert L.skinny_probe_stream_read(16, 1 << 20, 8192, 8192, 0, 3, 1, nt, 16, None) == -1
+        assert L.skinny_probe_stream_read_tiles(None, 1 << 20, 8192, 4, 0, 1, nt, 16, None) == -1
+        assert L.skinny_probe_stream_read_tiles(16, 1 << 20, 8000, 4, 0, 1, nt, 16, None) == -1
+        assert L.skinny_probe_stream_read_tiles(16, 1 << 20, 8192, 6, 0, 1, nt, 16, None) == -1
