@@ -633,7 +633,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// skinny_rows_flat: the row kernel for one token (M = 1) with every wave's
+// skinny_rows_flat: the row kernel for MT = 1-4 tokens with every wave's
 // loads running as one stream across its units.  In skinny_rows a wave's
 // pipeline fills at the start of each unit and drains at its end, so a short
 // row (8 KB of FP8 at K = 8192) leaves the wave with little in flight for a
@@ -653,9 +653,9 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 // re-read its last segment (never consumed).  Outputs are collected in LDS
 // and written when x is restaged, when the buffer is full and at the end:
 // loads and stores may complete out of order with each other, so a store in
-// flight among the loads would turn the next wait into a full drain.  The
-// per-lane arithmetic is that of skinny_rows at M = 1; the lane sum has its
-// own fixed order (wave_sum_rows).
+// flight among the loads would turn the next wait into a full drain.  A wave
+// keeps one sum per token; the per-lane arithmetic is that of skinny_rows,
+// and the lane sum has its own fixed order (wave_sum_rows).
 constexpr int kFlatYBytes = 16 * 1024;  // LDS for outputs waiting to be written
 
 // Sum over the 64 lanes in a fixed order, without a round trip through LDS:
