@@ -33,8 +33,10 @@
 //     v_mfma_f32_16x16x32_bf16, and reads the A operand (x, token = lane % 16)
 //     from LDS.  The matrix cores make the arithmetic per weight independent
 //     of M, which the vector path's is not.  Workgroups of 4 waves (two per
-//     CU) or, for large FP8 launches, 8 waves with all of the CU's LDS.  Its
-//     MoE form takes the units of each chosen expert's slice of routes.
+//     CU) or, for large FP8 launches, 8 waves with all of the CU's LDS in an
+//     exact-fit layout (swizzled instead of padded) that holds x of six
+//     tokens of K = 8192 whole.  Its MoE form takes the units of each chosen
+//     expert's slice of routes.
 //
 //   x windows are copied from global memory straight into LDS (no
 //   registers) while a unit's first weights load.  A linear cut into
@@ -263,6 +265,30 @@ __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr
       __builtin_amdgcn_global_load_lds(
           L.x + (size_t)src * xcpr + xw0 + c0 + lane,
           (__attribute__((address_space(3))) void*)(dst + m * stride + c0), 16, 0, 0);
+  }
+}
+
+// The exact-fit form of stage_x_direct: window slot s of token m holds chunk
+// s ^ (m % 8), so lane l of a 64-slot piece copies chunk c0 + (l ^ (m % 8));
+// slots whose chunk lies past the window's data (wlen) are zeroed by the lane
+// that owns them, so no slot is written twice.  win is a multiple of 8.
+template <int THREADS>
+__device__ __forceinline__ void stage_x_fit(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
+                                            int win, u32x4* dst) {
+  const int lane = threadIdx.x & 63;
+  const int pieces = (win + 63) / 64;
+  for (int p = threadIdx.x >> 6; p < M * pieces; p += THREADS / 64) {
+    const int m = p / pieces;
+    const int c0 = (p - m * pieces) * 64;
+    const int c = c0 + (lane ^ (m & 7));
+    if (c0 + lane < win) {
+      if (c < wlen)
+        __builtin_amdgcn_global_load_lds(
+            L.x + (size_t)m * xcpr + xw0 + c,
+            (__attribute__((address_space(3))) void*)(dst + m * win + c0), 16, 0, 0);
+      else
+        dst[m * win + c0 + lane] = zero4();
+    }
   }
 }
 
@@ -971,6 +997,15 @@ constexpr int tiles_lds(int wpb) { return wpb == kTilesWavesLarge ? 160 * 1024 :
 constexpr int tiles_w_bytes(int wpb) { return wpb * kTileRows * kRowStrideT; }
 constexpr int tiles_x_budget(int wpb) { return tiles_lds(wpb) - tiles_w_bytes(wpb); }
 constexpr int kTilesXBudget = tiles_x_budget(kTilesWavesSmall);
+// Exact-fit layout (FIT): W tiles of 512-byte rows and x rows without the pad
+// chunk or the zero row, both XOR-swizzled in 16-byte slots instead of padded
+// (slot c of W tile row r at c ^ (r % 16), chunk c of x token m at c ^ (m % 8),
+// so the operand reads still hit distinct bank groups), and absent tokens
+// read token 0 (their outputs are never written).  The 8-wave workgroup then
+// holds x of six tokens of K = 8192 whole: 6 x 16 KB + 8 x 8 KB is all of the
+// CU's 160 KB of LDS.
+constexpr int tiles_w_bytes_fit(int wpb) { return wpb * kTileRows * kSegBytesT; }
+constexpr int tiles_x_budget_fit(int wpb) { return tiles_lds(wpb) - tiles_w_bytes_fit(wpb); }
 // The K-split form keeps its waves' partial tiles, two halves of WPB x 64
 // lanes x 16 bytes, between the W tiles and the end of its LDS.
 constexpr int tiles_red_bytes(int wpb) { return 2 * wpb * 64 * 16; }
@@ -1001,8 +1036,10 @@ struct TileUnit {
 // where a row has only a few segments.  A window may then hold no segment
 // for some waves.  The waves' partial tiles are added in LDS in wave order
 // at the end of the unit (deterministic).
-template <int DT, int WPB, bool MOE, bool KS = false>
+template <int DT, int WPB, bool MOE, bool KS = false, bool FIT = false>
 __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
+  static_assert(!FIT || (!MOE && !KS), "the exact-fit layout is for dense launches");
+  constexpr int kStride = FIT ? kSegBytesT : kRowStrideT;   // W tile bytes per row
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = KS ? kTileRows : kTileRows * WPB;
   constexpr int kSegStep = KS ? WPB : 1;               // between a wave's segments
@@ -1013,9 +1050,11 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   const int wv = threadIdx.x >> 6;
   const int seg_off = KS ? wv : 0;                     // this wave's first segment of a window
   const int wrow = KS ? 0 : wv * kTileRows;            // this wave's first row of the group
-  unsigned char* wt = lds + a.x_lds_bytes + wv * (kTileRows * kRowStrideT);
+  unsigned char* wt = lds + a.x_lds_bytes + wv * (kTileRows * kStride);
   // KS: partial tiles [2][WPB][64 lanes], alternate halves on alternate units.
-  f32x4* red = reinterpret_cast<f32x4*>(lds + a.x_lds_bytes + WPB * kTileRows * kRowStrideT);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + a.x_lds_bytes + WPB * kTileRows * kStride);
+  // W tile slot of chunk c in tile row r (FIT: swizzled).
+  auto wslot = [](int c, int r) { return FIT ? (c ^ (r & 15)) : c; };
   int red_half = 0;
   const int n = lane & 15;                             // operand row: token (A) / W row (B)
   const int g = lane >> 4;                             // operand k-group
@@ -1110,19 +1149,20 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int xw0 = 0, xstride = 1;                            // x window of the current unit
   const u32x4* xrow = xs;
+  int xsw = 0;                                         // FIT: this lane's token's swizzle
   auto consume = [&](const TileSeg<DT>& s, const TileUnit& t, int j) {
     const LinDesc& L = a.lin[t.l];
 #pragma unroll
     for (int q = 0; q < kLoadsT; ++q)
-      *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kRowStrideT + lchunk * 16) =
-          s.w[q];
+      *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kStride +
+                                wslot(lchunk, kRowsPerLoadT * q + lrow) * 16) = s.w[q];
     if ((j + 1) * kSegChunksT > L.cpr && j * kSegChunksT + lchunk >= L.cpr) {
       // The row's ragged end: zero the chunks past it (written after the
       // clamped data, so these writes win).
 #pragma unroll
       for (int q = 0; q < kLoadsT; ++q)
-        *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kRowStrideT + lchunk * 16) =
-            zero4();
+        *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kStride +
+                                  wslot(lchunk, kRowsPerLoadT * q + lrow) * 16) = zero4();
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1130,13 +1170,14 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int st = 0; st < kStepsT; ++st) {
-      const u32x4 b = *reinterpret_cast<const u32x4*>(wt + n * kRowStrideT + (4 * st + g) * 16);
+      const u32x4 b =
+          *reinterpret_cast<const u32x4*>(wt + n * kStride + wslot(4 * st + g, n) * 16);
       const int xc = (j * kSegChunksT + 4 * st + g) * XC - xw0;  // x chunk in the window
       if (DT == SKINNY_BF16) {
-        acc = mfma_bf16(xrow[xc], b, acc);
+        acc = mfma_bf16(xrow[xc ^ xsw], b, acc);
       } else {
-        const u32x4 x0 = xrow[xc];
-        const u32x4 x1 = xrow[xc + 1];
+        const u32x4 x0 = xrow[xc ^ xsw];
+        const u32x4 x1 = xrow[(xc + 1) ^ xsw];
         u32x4 b0, b1;
         e4m3x16_to_bf16(b, b0, b1);
         p = mfma_bf16(x0, b0, p);
@@ -1161,9 +1202,15 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   auto stage = [&](const TileUnit& t) {
     const LinDesc& L = a.lin[t.l];
     const int win = t.spc * kSegChunksT * XC;                    // x chunks per token in LDS
-    xstride = win + 1;
+    xstride = FIT ? win : win + 1;
     xw0 = t.j0 * kSegChunksT * XC;
-    xrow = xs + (n < t.m ? n : t.m) * xstride;
+    if (FIT) {
+      const int tok = n < t.m ? n : 0;
+      xrow = xs + tok * xstride;
+      xsw = tok & 7;
+    } else {
+      xrow = xs + (n < t.m ? n : t.m) * xstride;
+    }
     if (t.slice == staged_l && t.chunk == staged_c && t.sub == staged_s) return;
     staged_l = t.slice;
     staged_c = t.chunk;
@@ -1173,17 +1220,23 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     // Token rows 0..M-1, zeros past K, then a zero row that lanes of absent
     // tokens read.
     const int wlen = min(win, xcpr - xw0);
-    const unsigned char* rows = MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr;
-    if (L.act == kActNone)
-      stage_x_direct<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
-    else
-      stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
-    const int pad = win - wlen;
-    for (int i = threadIdx.x; i < t.m * pad; i += kThreads) {
-      const int m = i / pad;
-      xs[m * xstride + wlen + (i - m * pad)] = zero4();
+    if constexpr (FIT) {
+      // Token rows 0..M-1 only, swizzled, zeros past K (plain x: the host
+      // takes this form only for linears without an activation).
+      stage_x_fit<kThreads>(L, t.m, xcpr, xw0, wlen, win, xs);
+    } else {
+      const unsigned char* rows = MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr;
+      if (L.act == kActNone)
+        stage_x_direct<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
+      else
+        stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
+      const int pad = win - wlen;
+      for (int i = threadIdx.x; i < t.m * pad; i += kThreads) {
+        const int m = i / pad;
+        xs[m * xstride + wlen + (i - m * pad)] = zero4();
+      }
+      for (int c = threadIdx.x; c < win; c += kThreads) xs[t.m * xstride + c] = zero4();
     }
-    for (int c = threadIdx.x; c < win; c += kThreads) xs[t.m * xstride + c] = zero4();
     __builtin_amdgcn_s_waitcnt(0);                               // direct loads landed
     __syncthreads();
   };
@@ -1959,15 +2012,17 @@ bool rows_supported(const skinny_linear& L, int M) {
 // budget (token rows padded by one chunk), or -1 if not even one segment fits.
 constexpr int kTilesMinSegs = 4;          // segments per chunk when splitting for parallelism
 // Most segments an x window of M tokens may span within the budget.
-int tiles_max_spc(int dtype, int M, int budget) {
+// fit: the exact-fit layout (M token rows, no pad chunk).
+int tiles_max_spc(int dtype, int M, int budget, bool fit = false) {
   const int xc = dtype == SKINNY_BF16 ? 1 : 2;
+  if (fit) return budget / (16 * M) / (kSegChunksT * xc);
   return (budget / (16 * (M + 1)) - 1) / (kSegChunksT * xc);
 }
 
-int tiles_lds_chunks(int dtype, int M, int K, int budget = kTilesXBudget) {
+int tiles_lds_chunks(int dtype, int M, int K, int budget = kTilesXBudget, bool fit = false) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  const int max_spc = tiles_max_spc(dtype, M, budget);
+  const int max_spc = tiles_max_spc(dtype, M, budget, fit);
   if (max_spc < 1) return -1;
   return (spt + max_spc - 1) / max_spc;
 }
@@ -1989,10 +2044,10 @@ int tiles_chunks(int dtype, int M, int K, long long par, int budget = kTilesXBud
 // wins at large M: MoE launches always walk, dense launches from
 // kTilesWalkMinM* tokens on (below).
 void tiles_split(int dtype, int M, int K, long long par, int budget, bool windows, int* chunks,
-                 int* sub) {
+                 int* sub, bool fit = false) {
   const int cpr = K / (dtype == SKINNY_BF16 ? 8 : 16);
   const int spt = (cpr + kSegChunksT - 1) / kSegChunksT;
-  const int c_lds = tiles_lds_chunks(dtype, M, K, budget);
+  const int c_lds = tiles_lds_chunks(dtype, M, K, budget, fit);
   *chunks = chunk_count(spt, c_lds, par, kTilesMinSegs);
   *sub = 1;
   if (windows && c_lds > 1 && chunk_count(spt, 1, par, kTilesMinSegs) == 1) {
@@ -2059,6 +2114,7 @@ struct KernelChoice {
   int wpb = 0;                 // waves per workgroup
   bool tiles = false;          // skinny_tiles (else skinny_rows)
   bool flat = false;           // skinny_rows_flat
+  bool fit = false;            // skinny_tiles in the exact-fit layout
   int waves_per_cu = kTargetRowsWavesPerCU;   // cap on the persistent grid
   int id = SKINNY_KERNEL_NONE; // enum skinny_kernel
 };
@@ -2073,6 +2129,15 @@ KernelChoice tiles_kernel() {
   k.wpb = WPB;
   k.tiles = true;
   k.id = WPB == kTilesWavesSmall ? SKINNY_KERNEL_TILES : SKINNY_KERNEL_TILES_WIDE;
+  return k;
+}
+
+// The 8-wave shape in the exact-fit layout (FP8 launches of plain linears).
+template <int DT>
+KernelChoice tiles_kernel_fit() {
+  KernelChoice k = tiles_kernel<DT, kTilesWavesLarge>();
+  k.fn = skinny_tiles<DT, kTilesWavesLarge, false, false, true>;
+  k.fit = true;
   return k;
 }
 
@@ -2360,6 +2425,23 @@ bool tiles_large(const skinny_linear* const* lin, int count, int M, int cus) {
   return groups >= (long long)kTilesLargeGroupsPerCU * cus;
 }
 
+// The 8-wave kernel of a large launch: for FP8 linears without an
+// activation in the exact-fit layout, whose larger x window leaves K = 8192
+// unsplit up to M = 6 (no partial sums, no second pass for those linears).
+// Writes that reach memory in the middle of the weight stream cost about ten
+// times their bytes in read rate (measured on MI355X with the read probe:
+// 0.8% of the bytes written as fp32 stores, 6.88 -> 6.25 TB/s; the same
+// stores into a cache-resident region, no loss), and the split's partial
+// sums were most of this kernel's writes.  Measured against the padded
+// layout, same process, 16-layer FP8 TP=1 launches: +0.3-0.7% at M = 6,
+// +0.3% at M = 5 and 8, even at M = 2 and 16.
+KernelChoice tiles_large_kernel(const skinny_linear* const* lin, int count) {
+  if (lin[0]->dtype == SKINNY_BF16) return tiles_kernel<SKINNY_BF16, kTilesWavesLarge>();
+  for (int i = 0; i < count; ++i)
+    if (lin[i]->reserved != kActNone) return tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
+  return tiles_kernel_fit<SKINNY_FP8_BS128>();
+}
+
 // Dense tile launches walk their x windows instead of splitting K for them
 // from these token counts on.  Measured on MI355X (8-layer TP=1 stack
 // launches, walk vs split): bf16 +0.8 / +2.8 / +1.7 / +5.7 / +10.5% at M = 5 /
@@ -2372,7 +2454,7 @@ constexpr int kTilesWalkMinMFp8 = 9;
 // budget and, when the launch is too small to give every workgroup the
 // kernel's units per worker, more - but never fewer segments per chunk than
 // a wave keeps in flight.  Assigns the partial slots of the split linears.
-void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
+void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles, bool fit = false) {
   const int rows = a.band_rows;
   long long groups = 0;
   for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
@@ -2383,7 +2465,7 @@ void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles) {
     LinDesc& d = a.lin[i];
     int c, w = 1;
     const bool walk = a.M >= (dtype == SKINNY_BF16 ? kTilesWalkMinMBf16 : kTilesWalkMinMFp8);
-    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, walk, &c, &w);
+    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, walk, &c, &w, fit);
     else c = rows_chunks(dtype, a.M, d.K, par);
     d.chunks = c;
     d.sub = w;
@@ -2410,9 +2492,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   if (!k.fn) return SKINNY_ERR_UNSUPPORTED;
   if (!k.tiles && rows_lean(lin, count, M)) k = pick_lean(M);
   if (const int fw = use_flat(lin, count, M, requested, dev.cus)) k = pick_flat(dtype, M, fw);
-  if (k.tiles && tiles_large(lin, count, M, dev.cus))
-    k = dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
-                             : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
+  if (k.tiles && tiles_large(lin, count, M, dev.cus)) k = tiles_large_kernel(lin, count);
   LaunchArgs a;
   memset(&a, 0, sizeof a);
   a.nlin = count;
@@ -2423,7 +2503,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
     if (!(k.tiles ? tiles_supported(*lin[i], M) : rows_supported(*lin[i], M)))
       return SKINNY_ERR_UNSUPPORTED;
   const int lds = kernel_lds(k, dtype);
-  a.x_lds_bytes = k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
+  a.x_lds_bytes = k.fit ? tiles_x_budget_fit(k.wpb) : k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
   skinny_status st = ensure_lds((const void*)k.fn, lds);
   if (st != SKINNY_OK) return st;
   for (int i = 0; i < count; ++i) {
@@ -2450,7 +2530,7 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   } else {
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
-  plan_chunks(a, count, G, dtype, k.tiles);
+  plan_chunks(a, count, G, dtype, k.tiles, k.fit);
   if (k.flat)
     for (int i = 0; i < count; ++i)
       if (a.lin[i].chunks != 1) return SKINNY_ERR_UNSUPPORTED;   // x fits: never split
@@ -3073,9 +3153,7 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
     out->variant = SKINNY_VARIANT_VECTOR;
     k = pick_flat(linears[0].dtype, M, fw);
   }
-  if (k.tiles && tiles_large(group, n, M, d.cus))
-    k = linears[0].dtype == SKINNY_BF16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
-                                        : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>();
+  if (k.tiles && tiles_large(group, n, M, d.cus)) k = tiles_large_kernel(group, n);
   out->kernel = k.id;
   const int lds = kernel_lds(k, linears[0].dtype);
   st = ensure_lds((const void*)k.fn, lds);

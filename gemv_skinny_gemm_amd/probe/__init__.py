@@ -30,8 +30,48 @@ def lib():
                                                      ctypes.c_longlong, ctypes.c_int,
                                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                      ctypes.c_void_p, ctypes.c_void_p]
+        L.skinny_probe_tiles_writes.restype = ctypes.c_int
+        L.skinny_probe_tiles_writes.argtypes = [ctypes.c_void_p, ctypes.c_longlong,
+                                                ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong,
+                                                ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
+
+
+WRITE_MODES = {0: "no stores", 1: "4 fp32 stores per lane per unit (0.8% of the bytes)",
+               2: "1 fp32 store per lane per unit (0.2%)", 3: "the 4 as nontemporal stores",
+               4: "the 4 into a 64 KB region (cache-resident)",
+               5: "the 4 hidden from the compiler's wait analysis"}
+
+
+def measure_tiles_writes(buf, row_bytes: int, mode: int, workgroups: int, lds_bytes: int,
+                         reps: int = 5) -> float:
+    """GB/s read by the tile pattern with writes added at the end of each unit
+    of 128 rows (mode: WRITE_MODES)."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    nbytes -= nbytes % (128 * row_bytes)
+    units = nbytes // row_bytes // 128
+    out = torch.empty(max(2048 * units, 16384), dtype=torch.float32, device=buf.device)
+    sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
+    stream = torch.cuda.current_stream()
+
+    def go():
+        rc = lib().skinny_probe_tiles_writes(buf.data_ptr(), nbytes, row_bytes, workgroups, mode,
+                                             lds_bytes, out.data_ptr(), out.numel(),
+                                             sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"skinny_probe_tiles_writes failed ({rc})")
+    for _ in range(2):
+        go()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        go()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def measure_tiles(buf, row_bytes: int, wpb: int, ksplit: bool, workgroups_per_cu: int,

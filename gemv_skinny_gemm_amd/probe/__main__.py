@@ -6,6 +6,8 @@
     python -m gemv_skinny_gemm_amd.probe tiles    the matrix-core kernel's read pattern
     python -m gemv_skinny_gemm_amd.probe nt       plain against nontemporal loads, the fastest
                                                   patterns of the sweeps above and the tiles one
+    python -m gemv_skinny_gemm_amd.probe writes   the tiles pattern with stores added at the end
+                                                  of every unit (writes in the read stream)
 
 Every figure is GB/s read from an 8 GiB buffer (GiB = 2^30 bytes), best of
 three measurements of five passes each.  Measurement only.
@@ -90,12 +92,28 @@ def nontemporal(buf):
                   f"{g[0]:.0f} | {g[1]:.0f} |", flush=True)
 
 
+def writes(buf):
+    """The tile pattern (8 KB rows, nontemporal loads, 252 workgroups of 8
+    waves with 160 KB of LDS each, as the 8-wave tile kernel's grid) with
+    writes added at the end of every 128-row unit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = cus - cus % 12     # 252 on 256 CUs: that kernel's grid when it splits K in 2 and 6
+    print("| stores at the end of each 1 MB unit | GB/s read |")
+    print("|---|---|")
+    for mode, name in probe.WRITE_MODES.items():
+        g = best(lambda: probe.measure_tiles_writes(buf, 8192, mode, wg, 160 * 1024))
+        print(f"| {name} | {g:.0f} |", flush=True)
+    g = best(lambda: probe.measure_tiles_writes(buf, 8192, 0, cus, 160 * 1024))
+    print(f"| no stores, {cus} workgroups | {g:.0f} |", flush=True)
+
+
 def main():
     what = sys.argv[1] if len(sys.argv) > 1 else "depth"
     buf = torch.ones(8 * GIB // 8, dtype=torch.int64, device="cuda")
     torch.cuda.synchronize()
     print(f"# {what} sweep, {torch.cuda.get_device_name(0)}", flush=True)
-    {"depth": depth, "stride": stride, "tiles": tiles, "nt": nontemporal}[what](buf)
+    {"depth": depth, "stride": stride, "tiles": tiles, "nt": nontemporal,
+     "writes": writes}[what](buf)
 
 
 if __name__ == "__main__":

@@ -140,6 +140,71 @@ __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, 
   if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
 }
 
+
+// The matrix-core kernel's pattern with writes added (stream_read_tiles,
+// KSPLIT = false, nontemporal loads, 8 waves): at the end of every unit
+// (128 rows of the whole row) each lane stores floats, as a kernel that
+// writes its outputs in the middle of its weight stream does.  MODE 0 no
+// stores; 1 four stores per lane, each wave writing 256 contiguous bytes per
+// store; 2 one such store; 3 the four as nontemporal stores; 4 the four into
+// the first 64 KB of out (a region that stays in the cache); 5 the four as
+// stores the compiler's wait analysis does not see (inline asm), so they
+// change none of its waits.
+template <int MODE>
+__global__ __launch_bounds__(512) void stream_read_tiles_writes(const u32x4* buf, long long rows,
+                                                               int row_chunks, float* out,
+                                                               unsigned* sink) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  constexpr int kUnitRows = 128;
+  const int segs = row_chunks / 32;
+  const long long units = rows / kUnitRows;
+  const int lrow = lane >> 5, lchunk = lane & 31;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    const u32x4* base = buf + (u * kUnitRows + 16 * wv + lrow) * (long long)row_chunks + lchunk;
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = ld<true>(base + 2 * q * (long long)row_chunks);
+    int s = 0;
+    for (; s + 1 < segs; s += 2) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) b[q] = ld<true>(base + 2 * q * (long long)row_chunks + (s + 1) * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= a[q];
+      if (s + 2 < segs) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = ld<true>(base + 2 * q * (long long)row_chunks + (s + 2) * 32);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= b[q];
+    }
+    if (s < segs) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc ^= a[q];
+    }
+    if (MODE != 0) {
+      const float v = (float)(acc.x & 0xFFFF);
+      constexpr int kStores = MODE == 2 ? 1 : 4;
+#pragma unroll
+      for (int i = 0; i < kStores; ++i) {
+        long long idx = ((u * 4 + i) * 8 + wv) * 64 + lane;
+        if (MODE == 4) idx &= 16383;
+        if (MODE == 3) {
+          __builtin_nontemporal_store(v, out + idx);
+        } else if (MODE == 5) {
+          asm volatile("global_store_dword %0, %1, off" : : "v"(out + idx), "v"(v));
+        } else {
+          out[idx] = v;
+        }
+      }
+    }
+  }
+  const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+typedef void (*writes_fn)(const u32x4*, long long, int, float*, unsigned*);
+
 typedef void (*probe_fn)(const u32x4*, long long, int, int, unsigned*);
 typedef void (*tiles_fn)(const u32x4*, long long, int, unsigned*);
 
@@ -218,4 +283,37 @@ int skinny_probe_stream_read_tiles(const void* buf, long long bytes, long long r
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
+
+// The tile pattern with writes (stream_read_tiles_writes): mode 0-5 as
+// there; `workgroups` workgroups of 8 waves, each asking for lds_bytes of
+// LDS (0 - 160 KB; more per workgroup means fewer per CU); out: device
+// floats, out_floats >= 2048 * (bytes / row_bytes / 128) (16384 for mode 4).
+// Requirements and returns as skinny_probe_stream_read_tiles; -2 also when
+// the LDS size cannot be set.
+int skinny_probe_tiles_writes(const void* buf, long long bytes, long long row_bytes,
+                              int workgroups, int mode, int lds_bytes, float* out,
+                              long long out_floats, unsigned* sink, void* stream) {
+  if (!buf || !out || !sink || bytes <= 0 || row_bytes <= 0 || workgroups < 1) return -1;
+  if (((uintptr_t)buf & 15) != 0 || row_bytes % 512 != 0) return -1;
+  if (bytes % (128LL * row_bytes) != 0 || row_bytes / 16 > (1LL << 30)) return -1;
+  if (lds_bytes < 0 || lds_bytes > 160 * 1024) return -1;
+  const long long units = bytes / row_bytes / 128;
+  if (out_floats < (mode == 4 ? 16384 : 2048 * units)) return -1;
+  writes_fn fn = nullptr;
+  switch (mode) {
+    case 0: fn = stream_read_tiles_writes<0>; break;
+    case 1: fn = stream_read_tiles_writes<1>; break;
+    case 2: fn = stream_read_tiles_writes<2>; break;
+    case 3: fn = stream_read_tiles_writes<3>; break;
+    case 4: fn = stream_read_tiles_writes<4>; break;
+    case 5: fn = stream_read_tiles_writes<5>; break;
+    default: return -1;
+  }
+  if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lds_bytes) != hipSuccess)
+    return -2;
+  hipLaunchKernelGGL(fn, dim3(workgroups), dim3(512), lds_bytes, (hipStream_t)stream,
+                     (const u32x4*)buf, bytes / row_bytes, (int)(row_bytes / 16), out, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 }  // extern "C"
