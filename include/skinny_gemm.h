@@ -133,11 +133,28 @@ size_t skinny_workspace_bytes(int dtype, int M, int N, int K);
 /* Bytes of workspace decode_linear_stack needs for these linears at this M. */
 size_t skinny_stack_workspace_bytes(const skinny_linear* linears, int count, int M);
 
-/* y = x . W^T with bf16 W. */
+/* y = x . W^T with bf16 W: one linear layer of the decode step, x the
+ * [M][K] activations of M tokens, W the layer's [N][K] weights ("Multi-GPU
+ * Inference and Serving at Scale", Example 2: a linear's product, worked on
+ * a small matrix; "Developing a custom Qwen2.5 72B inference engine from
+ * scratch - what is the real bottleneck?", section 6.1: the decode GEMV).
+ *   x, y       device, [M][K] and [M][N] bf16 row-major, 16-byte aligned
+ *   w          device, [N][K] bf16 row-major (the nn.Linear layout)
+ *   workspace  device, >= skinny_workspace_bytes(SKINNY_BF16, M, N, K)
+ * Argument errors are returned before anything is enqueued; the call is
+ * asynchronous on `stream`. */
 skinny_status skinny_gemm_bf16(const void* x, const void* w, void* y, int M, int N, int K,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* y = x . (e4m3(W) * block scale)^T, weight-only FP8 with 128 x 128 fp32 block scales. */
+/* y = x . (e4m3(W) * block scale)^T: weight-only FP8, each weight an OCP
+ * E4M3FN byte times the fp32 scale of its 128 x 128 block, activations and
+ * outputs bf16 ("9% faster GLM-5.3-Flash prefill with GPU-to-GPU IPC (and why
+ * TileLang didn't help)", section "TileLang: twice as fast, and no faster":
+ * FP8 weights with 128 x 128 block scales against 16-bit activations).
+ *   w_fp8      device, [N][K] bytes row-major
+ *   w_scale    device, [ceil(N/128)][ceil(K/128)] fp32 row-major; the scale
+ *              of W[n][k] is w_scale[n / 128][k / 128]
+ *   x, y, workspace as skinny_gemm_bf16 (workspace for SKINNY_FP8_BS128) */
 skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const float* w_scale,
                                     void* y, int M, int N, int K, void* workspace,
                                     size_t workspace_bytes, void* stream);
