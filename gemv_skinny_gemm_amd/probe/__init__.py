@@ -42,7 +42,9 @@ def lib():
 WRITE_MODES = {0: "no stores", 1: "4 fp32 stores per lane per unit (0.8% of the bytes)",
                2: "1 fp32 store per lane per unit (0.2%)", 3: "the 4 as nontemporal stores",
                4: "the 4 into a 64 KB region (cache-resident)",
-               5: "the 4 hidden from the compiler's wait analysis"}
+               5: "the 4 hidden from the compiler's wait analysis",
+               6: "the 4 every 4th unit only (mode 2's bytes in rarer bursts)",
+               7: "16 every 16th unit (mode 1's bytes in rarer bursts)"}
 
 
 def measure_tiles_writes(buf, row_bytes: int, mode: int, workgroups: int, lds_bytes: int,
@@ -53,7 +55,7 @@ def measure_tiles_writes(buf, row_bytes: int, mode: int, workgroups: int, lds_by
     nbytes = buf.numel() * buf.element_size()
     nbytes -= nbytes % (128 * row_bytes)
     units = nbytes // row_bytes // 128
-    out = torch.empty(max(2048 * units, 16384), dtype=torch.float32, device=buf.device)
+    out = torch.empty(max(8192 * units, 16384), dtype=torch.float32, device=buf.device)
     sink = torch.zeros(workgroups, dtype=torch.int32, device=buf.device)
     stream = torch.cuda.current_stream()
 

@@ -149,7 +149,9 @@ __global__ __launch_bounds__(64 * WPB) void stream_read_tiles(const u32x4* buf, 
 // store; 2 one such store; 3 the four as nontemporal stores; 4 the four into
 // the first 64 KB of out (a region that stays in the cache); 5 the four as
 // stores the compiler's wait analysis does not see (inline asm), so they
-// change none of its waits.
+// change none of its waits; 6 the four every fourth unit only (the bytes of
+// mode 2 in rarer, larger bursts); 7 sixteen every sixteenth unit (the bytes
+// of mode 1).
 template <int MODE>
 __global__ __launch_bounds__(512) void stream_read_tiles_writes(const u32x4* buf, long long rows,
                                                                int row_chunks, float* out,
@@ -183,12 +185,14 @@ __global__ __launch_bounds__(512) void stream_read_tiles_writes(const u32x4* buf
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc ^= a[q];
     }
+    if (MODE == 6 && (u / gridDim.x) % 4 != 3) continue;
+    if (MODE == 7 && (u / gridDim.x) % 16 != 15) continue;
     if (MODE != 0) {
       const float v = (float)(acc.x & 0xFFFF);
-      constexpr int kStores = MODE == 2 ? 1 : 4;
+      constexpr int kStores = MODE == 2 ? 1 : MODE == 7 ? 16 : 4;
 #pragma unroll
       for (int i = 0; i < kStores; ++i) {
-        long long idx = ((u * 4 + i) * 8 + wv) * 64 + lane;
+        long long idx = ((u * 16 + i) * 8 + wv) * 64 + lane;
         if (MODE == 4) idx &= 16383;
         if (MODE == 3) {
           __builtin_nontemporal_store(v, out + idx);
@@ -284,10 +288,10 @@ int skinny_probe_stream_read_tiles(const void* buf, long long bytes, long long r
 }
 
 
-// The tile pattern with writes (stream_read_tiles_writes): mode 0-5 as
+// The tile pattern with writes (stream_read_tiles_writes): mode 0-7 as
 // there; `workgroups` workgroups of 8 waves, each asking for lds_bytes of
 // LDS (0 - 160 KB; more per workgroup means fewer per CU); out: device
-// floats, out_floats >= 2048 * (bytes / row_bytes / 128) (16384 for mode 4).
+// floats, out_floats >= 8192 * (bytes / row_bytes / 128) (16384 for mode 4).
 // Requirements and returns as skinny_probe_stream_read_tiles; -2 also when
 // the LDS size cannot be set.
 int skinny_probe_tiles_writes(const void* buf, long long bytes, long long row_bytes,
@@ -298,7 +302,7 @@ int skinny_probe_tiles_writes(const void* buf, long long bytes, long long row_by
   if (bytes % (128LL * row_bytes) != 0 || row_bytes / 16 > (1LL << 30)) return -1;
   if (lds_bytes < 0 || lds_bytes > 160 * 1024) return -1;
   const long long units = bytes / row_bytes / 128;
-  if (out_floats < (mode == 4 ? 16384 : 2048 * units)) return -1;
+  if (out_floats < (mode == 4 ? 16384 : 8192 * units)) return -1;
   writes_fn fn = nullptr;
   switch (mode) {
     case 0: fn = stream_read_tiles_writes<0>; break;
@@ -307,6 +311,8 @@ int skinny_probe_tiles_writes(const void* buf, long long bytes, long long row_by
     case 3: fn = stream_read_tiles_writes<3>; break;
     case 4: fn = stream_read_tiles_writes<4>; break;
     case 5: fn = stream_read_tiles_writes<5>; break;
+    case 6: fn = stream_read_tiles_writes<6>; break;
+    case 7: fn = stream_read_tiles_writes<7>; break;
     default: return -1;
   }
   if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
