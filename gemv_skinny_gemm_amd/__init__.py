@@ -30,7 +30,7 @@ VARIANT_AUTO = 0
 VARIANT_VECTOR = 1
 VARIANT_MFMA = 2
 MAX_M = 16
-MAX_LINEARS_PER_LAUNCH = 32
+MAX_LINEARS_PER_LAUNCH = 32    # descriptors in a launch's arguments; more go in a table
 MAX_TOPK = 16
 MOE_X_PER_ROUTE = 1
 MOE_SWIGLU = 2

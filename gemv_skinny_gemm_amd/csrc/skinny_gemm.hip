@@ -51,6 +51,7 @@
 #include <atomic>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "skinny_gemm.h"
 
@@ -146,7 +147,21 @@ struct LaunchArgs {
   ArgmaxPair* pairs;     // skinny_rows, one unsplit linear: [M][G] greedy pairs, or NULL
   MoeArgs moe;
   LinDesc lin[SKINNY_MAX_LINEARS_PER_LAUNCH];
+  const LinDesc* table;  // the nlin descriptors in device memory, or NULL: lin[] above
 };
+
+// The kernels read descriptors through a constant-address-space pointer, so
+// every read is a scalar load (its own counter, never a wait on the weight
+// stream's vector loads): the kernel arguments' own array, or for launches of
+// more linears than it holds a table in the workspace, copied there ahead of
+// the launch on its stream and not written while the launch runs.
+typedef __attribute__((address_space(4))) const LinDesc KLinDesc;
+
+__device__ __forceinline__ KLinDesc* launch_lins(const LaunchArgs& a) {
+  return a.table ? (KLinDesc*)a.table : (KLinDesc*)a.lin;
+}
+// Mixture-of-experts launches describe one expert in lin[0] and never take a table.
+__device__ __forceinline__ const LinDesc* moe_lins(const LaunchArgs& a) { return a.lin; }
 
 // Weight loads are nontemporal: every weight byte is read once per call and
 // never again soon, and on MI355X the streaming-read probe reads 7.2 TB/s
@@ -210,10 +225,11 @@ __device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
 // up] per token (2 xcpr chunks) and the staged value is swiglu8(gate, up).
 // GATHER: staged row m is x's row rows[m].
 template <int THREADS, bool GATHER>
-__device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
-                                        u32x4* dst, int stride, const unsigned char* rows) {
+__device__ __forceinline__ void stage_x(const u32x4* X, int act, int M, int xcpr, int xw0,
+                                        int wlen, u32x4* dst, int stride,
+                                        const unsigned char* rows) {
   const int n = M * wlen;
-  if (L.act == kActNone) {
+  if (act == kActNone) {
     for (int b = threadIdx.x; b < n; b += 8 * THREADS) {
       u32x4 v[8];
 #pragma unroll
@@ -221,7 +237,7 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
         const int i = min(b + q * THREADS, n - 1);
         const int m = i / wlen;
         const int src = GATHER ? rows[m] : m;
-        v[q] = L.x[(size_t)src * xcpr + xw0 + (i - m * wlen)];
+        v[q] = X[(size_t)src * xcpr + xw0 + (i - m * wlen)];
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -238,7 +254,7 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
         const int i = min(b + q * THREADS, n - 1);
         const int m = i / wlen;
         const int src = GATHER ? rows[m] : m;
-        const u32x4* row = L.x + (size_t)src * 2 * xcpr + xw0 + (i - m * wlen);
+        const u32x4* row = X + (size_t)src * 2 * xcpr + xw0 + (i - m * wlen);
         g[q] = row[0];
         u[q] = row[xcpr];
       }
@@ -253,7 +269,7 @@ __device__ __forceinline__ void stage_x(const LinDesc& L, int M, int xcpr, int x
 }
 
 template <int THREADS, bool GATHER>
-__device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
+__device__ __forceinline__ void stage_x_direct(const u32x4* X, int M, int xcpr, int xw0, int wlen,
                                                u32x4* dst, int stride, const unsigned char* rows) {
   const int lane = threadIdx.x & 63;
   const int pieces = (wlen + 63) / 64;
@@ -263,7 +279,7 @@ __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr
     const int src = GATHER ? rows[m] : m;
     if (c0 + lane < wlen)
       __builtin_amdgcn_global_load_lds(
-          L.x + (size_t)src * xcpr + xw0 + c0 + lane,
+          X + (size_t)src * xcpr + xw0 + c0 + lane,
           (__attribute__((address_space(3))) void*)(dst + m * stride + c0), 16, 0, 0);
   }
 }
@@ -273,7 +289,7 @@ __device__ __forceinline__ void stage_x_direct(const LinDesc& L, int M, int xcpr
 // slots whose chunk lies past the window's data (wlen) are zeroed by the lane
 // that owns them, so no slot is written twice.  win is a multiple of 8.
 template <int THREADS>
-__device__ __forceinline__ void stage_x_fit(const LinDesc& L, int M, int xcpr, int xw0, int wlen,
+__device__ __forceinline__ void stage_x_fit(const u32x4* X, int M, int xcpr, int xw0, int wlen,
                                             int win, u32x4* dst) {
   const int lane = threadIdx.x & 63;
   const int pieces = (win + 63) / 64;
@@ -284,7 +300,7 @@ __device__ __forceinline__ void stage_x_fit(const LinDesc& L, int M, int xcpr, i
     if (c0 + lane < win) {
       if (c < wlen)
         __builtin_amdgcn_global_load_lds(
-            L.x + (size_t)m * xcpr + xw0 + c,
+            X + (size_t)m * xcpr + xw0 + c,
             (__attribute__((address_space(3))) void*)(dst + m * win + c0), 16, 0, 0);
       else
         dst[m * win + c0 + lane] = zero4();
@@ -414,6 +430,9 @@ template <int DT, int MT, int U, int R, int WPB, bool MOE = false>
 __global__ __launch_bounds__(64 * WPB)
 __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) void skinny_rows(
     const LaunchArgs a) {
+  const auto lins = [&] {
+    if constexpr (MOE) return moe_lins(a); else return launch_lins(a);
+  }();
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = WPB * R;
   constexpr int XC = DT == SKINNY_BF16 ? 1 : 2;        // x chunks per W chunk
@@ -429,7 +448,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
     // The slice table (built in the x region, free until the first staging),
     // then this workgroup's share of the zero rows.
     const MoeArgs& mo = a.moe;
-    const LinDesc& L = a.lin[0];
+    const auto& L = lins[0];
     tb = moe_table(lds + mo.table_lds, mo.max_slices);
     moe_setup<kThreads>(mo, tb, reinterpret_cast<int*>(lds));
     const long long zeros = (long long)tb.head[1] * L.N;
@@ -448,11 +467,11 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
       local = u - (long long)l * a.moe.units_per_slice;
       e = __builtin_amdgcn_readfirstlane(tb.expert[l]);
     } else {
-      while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
-      local = u - a.lin[l].unit_base;
+      while (l + 1 < a.nlin && lins[l + 1].unit_base <= u) ++l;
+      local = u - lins[l].unit_base;
       e = 0;
     }
-    const LinDesc& L = a.lin[MOE ? 0 : l];
+    const auto& L = lins[MOE ? 0 : l];
     grp = (int)(local / L.chunks);
     chunk = (int)(local - (long long)grp * L.chunks);
   };
@@ -460,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
     if (DT == SKINNY_FP8_BS128 && u < S) {
       int grp, chunk, e;
       unit_of(u, l, grp, chunk, e);
-      const LinDesc& L = a.lin[MOE ? 0 : l];
+      const auto& L = lins[MOE ? 0 : l];
       // The row group lies in one 128-row scale block (kGroupRows divides 128).
       const float* scale = MOE ? L.scale + (size_t)e * a.moe.s_stride : L.scale;
       const float* src = scale + (size_t)((grp * kGroupRows) / kScaleBlock) * L.kblocks;
@@ -488,14 +507,14 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     gbv[m] = -__builtin_inff();
-    gbi[m] = a.lin[0].N;
+    gbi[m] = lins[0].N;
   }
   prefetch_scales(u, 0);
   store_scales();
   for (; u < S; u += a.G) {
     int grp, chunk, e;
     unit_of(u, l, grp, chunk, e);
-    const LinDesc& L = a.lin[MOE ? 0 : l];
+    const auto& L = lins[MOE ? 0 : l];
     const int mt = MOE ? __builtin_amdgcn_readfirstlane(tb.rows[l]) : MT;   // tokens of the unit
     // Chunk c holds segments [c spt / chunks, (c + 1) spt / chunks).
     const int spc = (L.spt + L.chunks - 1) / L.chunks;          // window, in segments
@@ -573,10 +592,10 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
       const unsigned char* rows = MOE ? tb.xrow + l * kMoeMaxCap : nullptr;
       if (L.act == kActNone) {
         // Straight into LDS, no registers; the wait also covers the batch.
-        stage_x_direct<kThreads, MOE>(L, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
+        stage_x_direct<kThreads, MOE>(L.x, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
         __builtin_amdgcn_s_waitcnt(0);
       } else {
-        stage_x<kThreads, MOE>(L, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
+        stage_x<kThreads, MOE>(L.x, L.act, mt, xcpr, xw0, min(win, xcpr - xw0), xs, win, rows);
       }
       __syncthreads();
       staged_l = l;
@@ -651,7 +670,7 @@ __attribute__((amdgpu_waves_per_eu((DT == SKINNY_BF16 && MT <= 2) ? 4 : 1))) voi
     if (threadIdx.x < MT) {
       const int m = threadIdx.x;
       float bv = -__builtin_inff();
-      int bi = a.lin[0].N;
+      int bi = lins[0].N;
       for (int w = 0; w < WPB; ++w) argmax_take(red[w * MT + m].v, red[w * MT + m].i, bv, bi);
       a.pairs[(size_t)m * a.G + blockIdx.x] = ArgmaxPair{bv, bi};
     }
@@ -715,6 +734,7 @@ struct FlatSlot {
 
 template <int DT, int MT, int P, int U>
 __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(const LaunchArgs a) {
+  const auto lins = launch_lins(a);
   constexpr int WPB = kRowsWavesPerBlock;
   constexpr int kThreads = 64 * WPB;
   constexpr bool kFp8 = DT == SKINNY_FP8_BS128;
@@ -727,11 +747,11 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   const long long S = a.S;
   if ((long long)blockIdx.x >= S) {
     if (a.pairs && threadIdx.x < MT)
-      a.pairs[(size_t)threadIdx.x * a.G + blockIdx.x] = ArgmaxPair{-__builtin_inff(), a.lin[0].N};
+      a.pairs[(size_t)threadIdx.x * a.G + blockIdx.x] = ArgmaxPair{-__builtin_inff(), lins[0].N};
     return;
   }
   auto linear_of = [&](long long u, int l) {
-    while (l + 1 < a.nlin && a.lin[l + 1].unit_base <= u) ++l;
+    while (l + 1 < a.nlin && lins[l + 1].unit_base <= u) ++l;
     return l;
   };
   // Load cursor: unit lu of linear ll, next segment lj of the wave's row.
@@ -742,7 +762,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   const float* ls = nullptr;
   int lspt = 0, lcpr = 0;
   auto enter_load = [&]() {
-    const LinDesc& L = a.lin[ll];
+    const auto& L = lins[ll];
     const int row = min((int)(lu - L.unit_base) * WPB + wv, L.N - 1);
     lw = L.w + (size_t)row * L.cpr;
     if (kFp8) ls = L.scale + (size_t)(row / kScaleBlock) * L.kblocks;
@@ -782,10 +802,10 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   for (int m = 0; m < MT; ++m) {
     acc[m] = 0.0f;
     gbv[m] = -__builtin_inff();
-    gbi[m] = a.lin[0].N;
+    gbi[m] = lins[0].N;
   }
   auto enter_consume = [&]() {
-    const LinDesc& L = a.lin[cl];
+    const auto& L = lins[cl];
     crow = (int)(cu - L.unit_base) * WPB + wv;
     cspt = (L.spt + U - 1) / U;
     ccpr = L.cpr;
@@ -797,7 +817,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   // before ybuf is reused.
   auto flush_y = [&]() {
     __syncthreads();
-    const LinDesc& L = a.lin[cl];
+    const auto& L = lins[cl];
     const bool vec = (reinterpret_cast<size_t>(L.y) & 15) == 0 && L.N % 8 == 0;
     for (int i = threadIdx.x; i < ny * MT; i += kThreads) {
       const int t = i / MT, m = i - t * MT;
@@ -814,9 +834,9 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
   };
   auto stage = [&]() {
     __syncthreads();                                       // all done with the old x
-    const LinDesc& L = a.lin[cl];
+    const auto& L = lins[cl];
     const int xcpr = L.K >> 3;
-    stage_x_direct<kThreads, false>(L, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
+    stage_x_direct<kThreads, false>(L.x, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -872,7 +892,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
       if (lane == 0) {
         const __bf16 yv = (__bf16)acc[m];
         ybuf[(ny * MT + m) * WPB + wv] = yv;
-        if (a.pairs && crow < a.lin[cl].N) argmax_take((float)yv, crow, gbv[m], gbi[m]);
+        if (a.pairs && crow < lins[cl].N) argmax_take((float)yv, crow, gbv[m], gbi[m]);
       }
       acc[m] = 0.0f;
     }
@@ -905,9 +925,9 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
     // The first x goes out ahead of the first P - 1 slots, so one wait that
     // leaves those slots' loads in flight (loads complete in issue order)
     // covers it: the start does not drain the stream.
-    const LinDesc& L = a.lin[cl];
+    const auto& L = lins[cl];
     const int xcpr = L.K >> 3;
-    stage_x_direct<kThreads, false>(L, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
+    stage_x_direct<kThreads, false>(L.x, MT, xcpr, 0, xcpr, xs, xcpr, nullptr);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < P - 1; ++s) load_next(q[s]);
@@ -946,7 +966,7 @@ __global__ __launch_bounds__(64 * kRowsWavesPerBlock) void skinny_rows_flat(cons
     if (threadIdx.x < MT) {
       const int m = threadIdx.x;
       float bv = -__builtin_inff();
-      int bi = a.lin[0].N;
+      int bi = lins[0].N;
       for (int w = 0; w < WPB; ++w) argmax_take(red[w * MT + m].v, red[w * MT + m].i, bv, bi);
       a.pairs[(size_t)m * a.G + blockIdx.x] = ArgmaxPair{bv, bi};
     }
@@ -1039,6 +1059,9 @@ struct TileUnit {
 template <int DT, int WPB, bool MOE, bool KS = false, bool FIT = false>
 __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   static_assert(!FIT || (!MOE && !KS), "the exact-fit layout is for dense launches");
+  const auto lins = [&] {
+    if constexpr (MOE) return moe_lins(a); else return launch_lins(a);
+  }();
   constexpr int kStride = FIT ? kSegBytesT : kRowStrideT;   // W tile bytes per row
   constexpr int kThreads = 64 * WPB;
   constexpr int kGroupRows = KS ? kTileRows : kTileRows * WPB;
@@ -1067,7 +1090,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     // The slice table, then this workgroup's share of the zero rows; the
     // first workgroup also leaves the table for the second pass.
     const MoeArgs& mo = a.moe;
-    const LinDesc& L = a.lin[0];
+    const auto& L = lins[0];
     tb = moe_table(lds + mo.table_lds, mo.max_slices);
     moe_setup<kThreads>(mo, tb, reinterpret_cast<int*>(lds + a.x_lds_bytes));
     const int slices = tb.head[0];
@@ -1102,14 +1125,14 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
       t.e = __builtin_amdgcn_readfirstlane(tb.expert[sl]);
       t.m = __builtin_amdgcn_readfirstlane(tb.rows[sl]);
     } else {
-      while (ldec + 1 < a.nlin && a.lin[ldec + 1].unit_base <= u) ++ldec;
-      local = u - a.lin[ldec].unit_base;
+      while (ldec + 1 < a.nlin && lins[ldec + 1].unit_base <= u) ++ldec;
+      local = u - lins[ldec].unit_base;
       t.l = ldec;
       t.slice = ldec;
       t.e = 0;
       t.m = a.M;
     }
-    const LinDesc& L = a.lin[t.l];
+    const auto& L = lins[t.l];
     t.grp = (int)(local / L.chunks);
     t.chunk = (int)(local - (long long)t.grp * L.chunks);
     // Window `sub` of chunk c: [c0 + sub len / L.sub, c0 + (sub + 1) len / L.sub)
@@ -1127,7 +1150,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   // end read its last chunk (zeroed in LDS before use), so every load is
   // unconditional and in bounds and the compiler's waits stay exact.
   auto load = [&](TileSeg<DT>& s, const TileUnit& t, int j) {
-    const LinDesc& L = a.lin[t.l];
+    const auto& L = lins[t.l];
     const int row0 = t.grp * kGroupRows + wrow;
     const int c = min(j * kSegChunksT + lchunk, L.cpr - 1);
     const u32x4* w = MOE ? L.w + (size_t)t.e * a.moe.w_stride : L.w;
@@ -1151,7 +1174,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   const u32x4* xrow = xs;
   int xsw = 0;                                         // FIT: this lane's token's swizzle
   auto consume = [&](const TileSeg<DT>& s, const TileUnit& t, int j) {
-    const LinDesc& L = a.lin[t.l];
+    const auto& L = lins[t.l];
 #pragma unroll
     for (int q = 0; q < kLoadsT; ++q)
       *reinterpret_cast<u32x4*>(wt + (kRowsPerLoadT * q + lrow) * kStride +
@@ -1200,7 +1223,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   // there already (the same decision in every wave).
   int staged_l = -1, staged_c = -1, staged_s = -1;
   auto stage = [&](const TileUnit& t) {
-    const LinDesc& L = a.lin[t.l];
+    const auto& L = lins[t.l];
     const int win = t.spc * kSegChunksT * XC;                    // x chunks per token in LDS
     xstride = FIT ? win : win + 1;
     xw0 = t.j0 * kSegChunksT * XC;
@@ -1223,13 +1246,13 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
     if constexpr (FIT) {
       // Token rows 0..M-1 only, swizzled, zeros past K (plain x: the host
       // takes this form only for linears without an activation).
-      stage_x_fit<kThreads>(L, t.m, xcpr, xw0, wlen, win, xs);
+      stage_x_fit<kThreads>(L.x, t.m, xcpr, xw0, wlen, win, xs);
     } else {
       const unsigned char* rows = MOE ? tb.xrow + t.slice * kMoeMaxCap : nullptr;
       if (L.act == kActNone)
-        stage_x_direct<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
+        stage_x_direct<kThreads, MOE>(L.x, t.m, xcpr, xw0, wlen, xs, xstride, rows);
       else
-        stage_x<kThreads, MOE>(L, t.m, xcpr, xw0, wlen, xs, xstride, rows);
+        stage_x<kThreads, MOE>(L.x, L.act, t.m, xcpr, xw0, wlen, xs, xstride, rows);
       const int pad = win - wlen;
       for (int i = threadIdx.x; i < t.m * pad; i += kThreads) {
         const int m = i / pad;
@@ -1260,7 +1283,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
       acc = sum;
     }
     // Lane (n, g) holds D[4 g + i][n]: token 4 g + i, row row0 + n.
-    const LinDesc& L = a.lin[t.l];
+    const auto& L = lins[t.l];
     const int row = t.grp * kGroupRows + wrow + n;
     const long long slot = (MOE ? (long long)t.slice * a.moe.units_per_slice : L.slot_base) +
                            (long long)t.grp * L.chunks + t.chunk;
@@ -1317,7 +1340,7 @@ __global__ __launch_bounds__(64 * WPB) void skinny_tiles(const LaunchArgs a) {
   int in_b = 0;                                         // the current unit's first segment is in s1
   for (;;) {
     // A unit's x windows in turn (its sums stay in acc), then the next unit.
-    const bool last = cur.sub + 1 == a.lin[cur.l].sub;
+    const bool last = cur.sub + 1 == lins[cur.l].sub;
     const bool has_next = !last || u + a.G < S;
     const TileUnit nx = !last ? decode(u, cur.sub + 1) : has_next ? decode(u + a.G, 0) : cur;
     stage(cur);
@@ -1358,7 +1381,7 @@ __device__ __forceinline__ f32x4 sum_chunks(const f32x4* p, size_t stride, int n
   return sum;
 }
 __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchArgs a) {
-  const LinDesc& L = a.lin[blockIdx.y];
+  KLinDesc& L = launch_lins(a)[blockIdx.y];
   if (L.chunks == 1) return;
   const int R = a.band_rows;
   const int quads = (L.N + kCombineRows - 1) / kCombineRows;   // per token
@@ -1381,7 +1404,7 @@ __global__ __launch_bounds__(kCombineThreads) void skinny_combine(const LaunchAr
 // Second pass of a split MoE launch: grid row y is a slice, the table the
 // first workgroup of the main kernel left in the workspace names its routes.
 __global__ __launch_bounds__(kCombineThreads) void skinny_moe_combine(const LaunchArgs a) {
-  const LinDesc& L = a.lin[0];
+  const LinDesc& L = moe_lins(a)[0];
   const int* tb = a.moe.table;
   const int sl = blockIdx.y;
   if (sl >= tb[0]) return;
@@ -1982,10 +2005,10 @@ int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 // The persistent grid trimmed to a multiple of every K-chunk count of the
 // launch (3 x 2^k at most: at most a few percent of the workgroups), so each
 // workgroup keeps one chunk per linear; unchanged if no such multiple fits.
-int grid_for_chunks(int G, const LaunchArgs& a) {
+int grid_for_chunks(int G, const LinDesc* lin, int count) {
   int l = 1;
-  for (int i = 0; i < a.nlin; ++i) {
-    const int c = a.lin[i].chunks;
+  for (int i = 0; i < count; ++i) {
+    const int c = lin[i].chunks;
     l = l / gcd(l, c) * c;
     if (l > G) return G;
   }
@@ -2453,37 +2476,93 @@ constexpr int kTilesWalkMinMFp8 = 9;
 // K-chunks per linear (either kernel): enough for the x window to fit the LDS
 // budget and, when the launch is too small to give every workgroup the
 // kernel's units per worker, more - but never fewer segments per chunk than
-// a wave keeps in flight.  Assigns the partial slots of the split linears.
-void plan_chunks(LaunchArgs& a, int count, int G, int dtype, bool tiles, bool fit = false) {
-  const int rows = a.band_rows;
+// a wave keeps in flight.  Assigns the partial slots of the split linears and
+// returns how many the launch uses.  The chunk counts only grow with the grid.
+long long plan_chunks(LinDesc* lin, int count, int M, int rows, int x_lds_bytes, int G, int dtype,
+                      bool tiles, bool fit = false) {
   long long groups = 0;
-  for (int i = 0; i < count; ++i) groups += (a.lin[i].N + rows - 1) / rows;
+  for (int i = 0; i < count; ++i) groups += (lin[i].N + rows - 1) / rows;
   const long long want = (long long)(tiles ? kTilesUnitsPerWorker : kRowsUnitsPerWorker) * G;
   const long long par = (want + groups - 1) / groups;
   long long slots = 0;
   for (int i = 0; i < count; ++i) {
-    LinDesc& d = a.lin[i];
+    LinDesc& d = lin[i];
     int c, w = 1;
-    const bool walk = a.M >= (dtype == SKINNY_BF16 ? kTilesWalkMinMBf16 : kTilesWalkMinMFp8);
-    if (tiles) tiles_split(dtype, a.M, d.K, par, a.x_lds_bytes, walk, &c, &w, fit);
-    else c = rows_chunks(dtype, a.M, d.K, par);
+    const bool walk = M >= (dtype == SKINNY_BF16 ? kTilesWalkMinMBf16 : kTilesWalkMinMFp8);
+    if (tiles) tiles_split(dtype, M, d.K, par, x_lds_bytes, walk, &c, &w, fit);
+    else c = rows_chunks(dtype, M, d.K, par);
     d.chunks = c;
     d.sub = w;
     d.slot_base = slots;
     if (c > 1) slots += (long long)((d.N + rows - 1) / rows) * c;
   }
+  return slots;
 }
 
-// Enqueues one group of same-dtype linears (at most SKINNY_MAX_LINEARS_PER_LAUNCH).
-// workers = 0 sizes the persistent grid from occupancy; otherwise it is the
-// number of waves to run (rounded down to whole workgroups, at least one).
+constexpr size_t kWorkspaceAlign = 256;
+size_t align_ws(size_t b) { return (b + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign; }
+
+// Descriptor of linear L as kernel k reads it (chunks, windows and slots unplanned).
+LinDesc describe(const skinny_linear& L, const KernelChoice& k) {
+  LinDesc d;
+  memset(&d, 0, sizeof d);
+  d.w = (const u32x4*)L.w;
+  d.scale = L.w_scale;
+  d.x = (const u32x4*)L.x;
+  d.y = (__bf16*)L.y;
+  d.N = L.N;
+  d.K = L.K;
+  d.cpr = L.K / (L.dtype == SKINNY_BF16 ? 8 : 16);
+  d.spt = k.tiles ? (d.cpr + kSegChunksT - 1) / kSegChunksT : (d.cpr + kSegChunks - 1) / kSegChunks;
+  d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
+  d.chunks = 1;
+  d.sub = 1;
+  d.act = L.reserved;
+  return d;
+}
+
+int x_lds_budget(const KernelChoice& k) {
+  return k.fit ? tiles_x_budget_fit(k.wpb) : k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
+}
+
+// Partial-sum bytes one launch of all these linears may use: every kernel
+// shape the launch can take, planned at the largest grid any launch runs
+// (kMaxWaves waves), which bounds the plan at every smaller grid.
+size_t launch_slots_bound(const skinny_linear* const* lin, int count, int M) {
+  const int dtype = lin[0]->dtype;
+  const bool bf16 = dtype == SKINNY_BF16;
+  const KernelChoice shapes[] = {
+      pick(dtype, SKINNY_VARIANT_VECTOR, M), pick(dtype, SKINNY_VARIANT_MFMA, M),
+      bf16 ? pick_lean(M) : KernelChoice{},
+      bf16 ? tiles_kernel<SKINNY_BF16, kTilesWavesLarge>()
+           : tiles_kernel<SKINNY_FP8_BS128, kTilesWavesLarge>(),
+      bf16 ? KernelChoice{} : tiles_kernel_fit<SKINNY_FP8_BS128>()};
+  std::vector<LinDesc> d(count);
+  size_t most = 0;
+  for (const KernelChoice& k : shapes) {
+    if (!k.fn) continue;
+    for (int i = 0; i < count; ++i) d[i] = describe(*lin[i], k);
+    const long long slots = plan_chunks(d.data(), count, M, k.band_rows, x_lds_budget(k),
+                                        kMaxWaves / k.wpb, dtype, k.tiles, k.fit);
+    const size_t b = (size_t)slots * M * k.band_rows * sizeof(float);
+    if (b > most) most = b;
+  }
+  return most;
+}
+
+// Enqueues one launch over a group of same-dtype linears.  workers = 0 sizes
+// the persistent grid from occupancy; otherwise it is the number of waves to
+// run (rounded down to whole workgroups, at least one).  The partial sums
+// start at ws.  A group of more than SKINNY_MAX_LINEARS_PER_LAUNCH linears
+// passes its descriptors in a table placed in the workspace after the partial
+// sums, copied there on the stream ahead of the launch.
 //
 // pairs (optional): for a launch of one linear on the row kernel with K
 // unsplit, the kernel also writes each workgroup's greedy pair per token to
 // pairs[M][grid] and *pairs_grid is set to the grid; otherwise 0.
 skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* lin, int count,
-                           int M, int variant, int workers, float* slots, hipStream_t stream,
-                           hipEvent_t ev_before, hipEvent_t ev_after,
+                           int M, int variant, int workers, void* ws, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after,
                            ArgmaxPair* pairs = nullptr, int* pairs_grid = nullptr) {
   const int dtype = lin[0]->dtype;
   const int requested = variant;
@@ -2497,32 +2576,19 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   memset(&a, 0, sizeof a);
   a.nlin = count;
   a.M = M;
-  a.slots = slots;
+  a.slots = (float*)ws;
   a.band_rows = k.band_rows;
   for (int i = 0; i < count; ++i)
     if (!(k.tiles ? tiles_supported(*lin[i], M) : rows_supported(*lin[i], M)))
       return SKINNY_ERR_UNSUPPORTED;
   const int lds = kernel_lds(k, dtype);
-  a.x_lds_bytes = k.fit ? tiles_x_budget_fit(k.wpb) : k.tiles ? tiles_x_budget(k.wpb) : kRowsXBudget;
+  a.x_lds_bytes = x_lds_budget(k);
   skinny_status st = ensure_lds((const void*)k.fn, lds);
   if (st != SKINNY_OK) return st;
-  for (int i = 0; i < count; ++i) {
-    const skinny_linear& L = *lin[i];
-    LinDesc& d = a.lin[i];
-    d.w = (const u32x4*)L.w;
-    d.scale = L.w_scale;
-    d.x = (const u32x4*)L.x;
-    d.y = (__bf16*)L.y;
-    d.N = L.N;
-    d.K = L.K;
-    d.cpr = L.K / (dtype == SKINNY_BF16 ? 8 : 16);
-    d.spt = k.tiles ? (d.cpr + kSegChunksT - 1) / kSegChunksT
-                    : (d.cpr + kSegChunks - 1) / kSegChunks;
-    d.kblocks = (L.K + kScaleBlock - 1) / kScaleBlock;
-    d.chunks = 1;
-    d.sub = 1;
-    d.act = L.reserved;
-  }
+  const bool table = count > SKINNY_MAX_LINEARS_PER_LAUNCH;
+  std::vector<LinDesc> big(table ? count : 0);
+  LinDesc* D = table ? big.data() : a.lin;
+  for (int i = 0; i < count; ++i) D[i] = describe(*lin[i], k);
   int G = workers;
   if (G == 0) {
     st = auto_workers(dev, k, lds, &G);
@@ -2530,14 +2596,16 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   } else {
     G = G / k.wpb > 0 ? G / k.wpb : 1;
   }
-  plan_chunks(a, count, G, dtype, k.tiles, k.fit);
+  if (G > kMaxWaves / k.wpb) G = kMaxWaves / k.wpb;       // the grid the slot bound assumes
+  const long long slots = plan_chunks(D, count, M, k.band_rows, a.x_lds_bytes, G, dtype, k.tiles,
+                                      k.fit);
   if (k.flat)
     for (int i = 0; i < count; ++i)
-      if (a.lin[i].chunks != 1) return SKINNY_ERR_UNSUPPORTED;   // x fits: never split
-  G = grid_for_chunks(G, a);
+      if (D[i].chunks != 1) return SKINNY_ERR_UNSUPPORTED;   // x fits: never split
+  G = grid_for_chunks(G, D, count);
   long long S = 0;
   for (int i = 0; i < count; ++i) {
-    LinDesc& d = a.lin[i];
+    LinDesc& d = D[i];
     d.unit_base = S;
     S += (long long)((d.N + a.band_rows - 1) / a.band_rows) * d.chunks;
   }
@@ -2546,9 +2614,20 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   if (G < 1) G = 1;
   a.G = G;
   if (pairs_grid) *pairs_grid = 0;
-  if (pairs && !k.tiles && count == 1 && a.lin[0].chunks == 1) {
+  if (pairs && !k.tiles && count == 1 && D[0].chunks == 1) {
     a.pairs = pairs;
     if (pairs_grid) *pairs_grid = G;
+  }
+  if (table) {
+    // The table after the partial sums this plan uses (within the bound the
+    // workspace size was checked against; checked again here).
+    const size_t off = align_ws((size_t)slots * M * k.band_rows * sizeof(float));
+    const size_t bytes = (size_t)count * sizeof(LinDesc);
+    if (off + bytes > ws_bytes) return SKINNY_ERR_WORKSPACE;
+    LinDesc* t = (LinDesc*)((char*)ws + off);
+    if (hipMemcpyAsync(t, D, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return SKINNY_ERR_HIP;
+    a.table = t;
   }
   if (ev_before && hipEventRecord(ev_before, stream) != hipSuccess) return SKINNY_ERR_HIP;
   hipLaunchKernelGGL(k.fn, dim3(G), dim3(64 * k.wpb), lds, stream, a);
@@ -2557,8 +2636,8 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   // Second pass over the split linears (grid row y = linear; unsplit ones return).
   long long most = 0;
   for (int i = 0; i < count; ++i) {
-    const long long quads = (long long)M * ((a.lin[i].N + kCombineRows - 1) / kCombineRows);
-    if (a.lin[i].chunks > 1 && quads > most) most = quads;
+    const long long quads = (long long)M * ((D[i].N + kCombineRows - 1) / kCombineRows);
+    if (D[i].chunks > 1 && quads > most) most = quads;
   }
   if (most > 0) {
     const long long cblocks = (most + kCombineThreads - 1) / kCombineThreads;
@@ -2569,51 +2648,74 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
   return SKINNY_OK;
 }
 
-int launch_count(const skinny_linear* lin, int count) {
+// Launch groups: the linears of each dtype, in call order, make one launch
+// (their descriptors in a table in the workspace when there are more than
+// SKINNY_MAX_LINEARS_PER_LAUNCH), or, with max_group = that number, launches
+// of at most that many (descriptors in the kernel arguments only: the form
+// for streams under graph capture and for the static-buffer entry point).
+// Measured on MI355X (16 TP=1 layers, one process, interleaved, 2 to 16
+// launches): every launch costs ~9.5 us of ramp and tail (bf16 and FP8 at
+// M = 1) to ~16 us (FP8 at M = 6, with its second pass); copying a 5 KB
+// table ahead of a launch costs 0-10 us.
+constexpr int kGroupsUncapped = 1 << 30;
+
+int launch_count(const skinny_linear* lin, int count, int max_group) {
   int launches = 0;
   for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
     int n = 0;
     for (int i = 0; i < count; ++i) n += lin[i].dtype == dt;
-    launches += (n + SKINNY_MAX_LINEARS_PER_LAUNCH - 1) / SKINNY_MAX_LINEARS_PER_LAUNCH;
+    launches += (n + max_group - 1) / max_group;
   }
   return launches;
 }
 
-// Calls fn(group, n) for each launch group: in call order, by dtype, at most
-// SKINNY_MAX_LINEARS_PER_LAUNCH linears per group.  Stops at the first error.
+// Calls fn(group, n) for each launch group (above).  Stops at the first error.
 template <typename Fn>
-skinny_status for_each_group(const skinny_linear* lin, int count, Fn&& fn) {
-  const skinny_linear* group[SKINNY_MAX_LINEARS_PER_LAUNCH];
+skinny_status for_each_group(const skinny_linear* lin, int count, int max_group, Fn&& fn) {
+  std::vector<const skinny_linear*> group;
+  group.reserve(count < max_group ? count : max_group);
   for (int dt = SKINNY_BF16; dt <= SKINNY_FP8_BS128; ++dt) {
-    int n = 0;
+    group.clear();
     for (int i = 0; i < count; ++i) {
       if (lin[i].dtype != dt) continue;
-      group[n++] = &lin[i];
-      if (n == SKINNY_MAX_LINEARS_PER_LAUNCH) {
-        skinny_status st = fn(group, n);
+      group.push_back(&lin[i]);
+      if ((int)group.size() == max_group) {
+        skinny_status st = fn(group.data(), (int)group.size());
         if (st != SKINNY_OK) return st;
-        n = 0;
+        group.clear();
       }
     }
-    if (n > 0) {
-      skinny_status st = fn(group, n);
+    if (!group.empty()) {
+      skinny_status st = fn(group.data(), (int)group.size());
       if (st != SKINNY_OK) return st;
     }
   }
   return SKINNY_OK;
 }
 
-// Workspace a call over these linears needs (pure host arithmetic): the
-// largest launch group's partial slots under either variant, and never less
-// than SKINNY_MIN_WORKSPACE_BYTES.
-size_t required_workspace(const skinny_linear* lin, int count, int M) {
+// Workspace a call over these linears needs (pure host arithmetic), never less
+// than SKINNY_MIN_WORKSPACE_BYTES: for launches of at most
+// SKINNY_MAX_LINEARS_PER_LAUNCH linears (always possible), the largest
+// group's partial slots under either variant at the most K-chunks the planner
+// may give each linear; unless max_group caps the groups there, also each
+// larger group's partial sums (bounded at the largest grid) plus its table.
+size_t required_workspace(const skinny_linear* lin, int count, int M,
+                          int max_group = kGroupsUncapped) {
   size_t need = SKINNY_MIN_WORKSPACE_BYTES;
-  for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
+  for_each_group(lin, count, SKINNY_MAX_LINEARS_PER_LAUNCH,
+                 [&](const skinny_linear* const* g, int n) {
     for (int v = SKINNY_VARIANT_VECTOR; v <= SKINNY_VARIANT_MFMA; ++v) {
       const size_t b = group_slots_bytes(g, n, M, v);
       if (b > need) need = b;
     }
     const size_t b = group_slots_bytes(g, n, M, SKINNY_VARIANT_MFMA, kTilesWavesLarge);
+    if (b > need) need = b;
+    return SKINNY_OK;
+  });
+  if (max_group <= SKINNY_MAX_LINEARS_PER_LAUNCH) return need;
+  for_each_group(lin, count, max_group, [&](const skinny_linear* const* g, int n) {
+    if (n <= SKINNY_MAX_LINEARS_PER_LAUNCH) return SKINNY_OK;
+    const size_t b = align_ws(launch_slots_bound(g, n, M)) + (size_t)n * sizeof(LinDesc);
     if (b > need) need = b;
     return SKINNY_OK;
   });
@@ -2623,7 +2725,7 @@ size_t required_workspace(const skinny_linear* lin, int count, int M) {
 skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan* plan,
                   void* ws, size_t ws_bytes, void* stream, void* const* events = nullptr,
                   int event_count = 0, bool allow_act = false, ArgmaxPair* pairs = nullptr,
-                  int* pairs_grid = nullptr) {
+                  int* pairs_grid = nullptr, int max_group = kGroupsUncapped) {
   if (!lin || count < 1) return SKINNY_ERR_INVALID_ARG;
   if (M < 1 || M > SKINNY_MAX_M) return SKINNY_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {
@@ -2642,11 +2744,19 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   }
   if (variant == SKINNY_VARIANT_VECTOR && M > kRowsMaxM) return SKINNY_ERR_UNSUPPORTED;
   if (!ws) return SKINNY_ERR_WORKSPACE;
-  if (ws_bytes < required_workspace(lin, count, M)) return SKINNY_ERR_WORKSPACE;
+  if (max_group > SKINNY_MAX_LINEARS_PER_LAUNCH) {
+    // A table copy recorded into a graph would read this call's host memory
+    // at every replay: under capture, launches of kernel-argument size only.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess ||
+        cs != hipStreamCaptureStatusNone)
+      max_group = SKINNY_MAX_LINEARS_PER_LAUNCH;
+  }
+  if (ws_bytes < required_workspace(lin, count, M, max_group)) return SKINNY_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return SKINNY_ERR_UNSUPPORTED;
   skinny_status st = check_outputs(lin, count, M, ws, ws_bytes);
   if (st != SKINNY_OK) return st;
-  if (events && event_count < 2 * launch_count(lin, count)) return SKINNY_ERR_INVALID_ARG;
+  if (events && event_count < 2 * launch_count(lin, count, max_group)) return SKINNY_ERR_INVALID_ARG;
   // A plan the chosen kernel cannot run is rejected before anything is enqueued
   // (AUTO falls back to the matrix-core kernel where the row kernel cannot run).
   for (int i = 0; i < count; ++i) {
@@ -2660,11 +2770,11 @@ skinny_status run(const skinny_linear* lin, int count, int M, const skinny_plan*
   if (st != SKINNY_OK) return st;
   if (!d.gfx950) return SKINNY_ERR_UNSUPPORTED;
   int launch = 0;
-  return for_each_group(lin, count, [&](const skinny_linear* const* g, int n) {
+  return for_each_group(lin, count, max_group, [&](const skinny_linear* const* g, int n) {
     hipEvent_t before = events ? (hipEvent_t)events[2 * launch] : nullptr;
     hipEvent_t after = events ? (hipEvent_t)events[2 * launch + 1] : nullptr;
     ++launch;
-    return launch_group(d, g, n, M, variant, waves, (float*)ws, (hipStream_t)stream, before,
+    return launch_group(d, g, n, M, variant, waves, ws, ws_bytes, (hipStream_t)stream, before,
                         after, pairs, pairs_grid);
   });
 }
@@ -2713,7 +2823,6 @@ skinny_status check_argmax(const void* y, int M, int N, const int* idx, const vo
 
 // The two linears of a gated MLP: gate_up writes [gate | up] into the
 // intermediate buffer `gu`, down reads it through the fused activation.
-constexpr size_t kWorkspaceAlign = 256;
 size_t mlp_gu_bytes(const skinny_mlp& P, int M) {
   const size_t b = (size_t)M * 2 * P.I * 2;
   return (b + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
@@ -2977,7 +3086,7 @@ skinny_status moe_run(const skinny_experts* ex, const void* x, const int* ids, i
                         : p.x_budget + tiles_w_bytes(p.wpb) + (p.ks ? tiles_red_bytes(p.wpb) : 0);
   a.slots = (float*)((char*)ws + p.table_bytes);
   a.S = (long long)p.max_slices * mo.units_per_slice;
-  G = grid_for_chunks(G, a);
+  G = grid_for_chunks(G, a.lin, a.nlin);
   if (G > a.S) G = (int)a.S;
   a.G = G;
   hipStream_t s = (hipStream_t)stream;
@@ -3098,7 +3207,9 @@ skinny_status decode_linear_stack_noalloc(const skinny_linear* linears, int coun
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st != SKINNY_OK) return st;
-  return run(linears, count, M, nullptr, ws, SKINNY_STATIC_SCRATCH_BYTES, stream);
+  // Launches of kernel-argument size only: nothing to copy into the buffer.
+  return run(linears, count, M, nullptr, ws, SKINNY_STATIC_SCRATCH_BYTES, stream, nullptr, 0,
+             false, nullptr, nullptr, SKINNY_MAX_LINEARS_PER_LAUNCH);
 }
 
 skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
@@ -3118,7 +3229,7 @@ int skinny_launch_count(const skinny_linear* linears, int count) {
   if (!linears || count < 1) return 0;
   for (int i = 0; i < count; ++i)
     if (linears[i].dtype != SKINNY_BF16 && linears[i].dtype != SKINNY_FP8_BS128) return 0;
-  return launch_count(linears, count);
+  return launch_count(linears, count, kGroupsUncapped);
 }
 
 skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, int M,
@@ -3136,11 +3247,12 @@ skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
     skinny_status st = check_linear(linears[i], M);
     if (st != SKINNY_OK) return st;
   }
-  // The plan of the first launch group.
-  const skinny_linear* group[SKINNY_MAX_LINEARS_PER_LAUNCH];
-  int n = 0;
-  for (int i = 0; i < count && n < SKINNY_MAX_LINEARS_PER_LAUNCH; ++i)
-    if (linears[i].dtype == linears[0].dtype) group[n++] = &linears[i];
+  // The plan of the first launch group: every linear of the first one's dtype.
+  std::vector<const skinny_linear*> lins;
+  for (int i = 0; i < count; ++i)
+    if (linears[i].dtype == linears[0].dtype) lins.push_back(&linears[i]);
+  const skinny_linear* const* group = lins.data();
+  const int n = (int)lins.size();
   DeviceInfo d;
   skinny_status st = device_info(&d);
   if (st != SKINNY_OK) return st;

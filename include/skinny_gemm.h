@@ -59,7 +59,8 @@ extern "C" {
 
 #define SKINNY_ABI_VERSION 2
 #define SKINNY_MAX_M 16
-/* Linears one main-kernel launch carries; longer stacks use several launches. */
+/* Linears whose descriptors travel in a main-kernel launch's arguments; a
+ * launch over more linears reads them from a table in the workspace. */
 #define SKINNY_MAX_LINEARS_PER_LAUNCH 32
 /* Smallest workspace any call asks for (bytes). */
 #define SKINNY_MIN_WORKSPACE_BYTES 256
@@ -130,7 +131,10 @@ typedef struct skinny_plan {
  * Serving at Scale", Example 3, the row-split second linear). */
 size_t skinny_workspace_bytes(int dtype, int M, int N, int K);
 
-/* Bytes of workspace decode_linear_stack needs for these linears at this M. */
+/* Bytes of workspace decode_linear_stack needs for these linears at this M:
+ * the partial sums of its launches (for a launch of more than
+ * SKINNY_MAX_LINEARS_PER_LAUNCH linears, bounded at the largest grid any
+ * launch runs) plus that launch's descriptor table. */
 size_t skinny_stack_workspace_bytes(const skinny_linear* linears, int count, int M);
 
 /* y = x . W^T with bf16 W: one linear layer of the decode step, x the
@@ -170,11 +174,16 @@ skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const floa
  *   workspace  device, 16-byte aligned, >= skinny_stack_workspace_bytes(linears,
  *              count, M); contents undefined afterwards
  * Each linear reads its own x and writes its own y; no y may overlap any x,
- * W, w_scale, other y or the workspace (checked).  Linears are grouped by
- * dtype in call order and streamed by one persistent launch per
- * SKINNY_MAX_LINEARS_PER_LAUNCH group; each group's split-K partial sums are
- * combined by a second, deterministic pass.  Errors (any linear failing the
- * checks of a single linear) are returned before anything is enqueued. */
+ * W, w_scale, other y or the workspace (checked).  The linears of each dtype,
+ * in call order, are streamed by one persistent launch; a launch of more than
+ * SKINNY_MAX_LINEARS_PER_LAUNCH linears reads their descriptors from a table
+ * that the call copies from host memory into the workspace on `stream` just
+ * before it.  On a stream under graph capture (where such a copy would read
+ * this call's host memory at every replay) the call instead makes launches of
+ * at most SKINNY_MAX_LINEARS_PER_LAUNCH linears.  Each launch's split-K
+ * partial sums are combined by a second, deterministic pass.  Errors (any
+ * linear failing the checks of a single linear) are returned before anything
+ * is enqueued. */
 skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
@@ -183,7 +192,9 @@ skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M
  * hipMalloc): no workspace argument; the split-K partial sums go to a static
  * device buffer of SKINNY_STATIC_SCRATCH_BYTES that the library holds on each
  * GPU it runs on until the process ends.  Nothing is allocated on the call
- * path (the first call on a device only looks up the buffer's address there).
+ * path (the first call on a device only looks up the buffer's address there),
+ * and nothing is copied: its launches hold at most
+ * SKINNY_MAX_LINEARS_PER_LAUNCH linears each, descriptors in the arguments.
  *   A call is accepted only if skinny_stack_workspace_bytes(linears, count, M)
  *   <= SKINNY_STATIC_SCRATCH_BYTES (a bound from the shapes alone, so the
  *   same call is accepted on every device); otherwise SKINNY_ERR_WORKSPACE,
@@ -202,8 +213,8 @@ skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
                                 const skinny_plan* plan, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
-/* Number of main-kernel launches a call over these linears makes (one per
- * dtype group of at most SKINNY_MAX_LINEARS_PER_LAUNCH linears); 0 if invalid. */
+/* Number of main-kernel launches a call over these linears makes on a stream
+ * not under graph capture: one per dtype present; 0 if invalid. */
 int skinny_launch_count(const skinny_linear* linears, int count);
 
 /* skinny_linear_run that also records events around each main-kernel launch,
@@ -225,10 +236,11 @@ skinny_status skinny_linear_run_timed(const skinny_linear* linears, int count, i
  * launch splits; linears in order, then row groups, then K-chunks in K order. */
 int skinny_band_rows(int dtype, int variant, int M);
 
-/* The automatic plan (fills *out) of the first launch of linears[0]'s dtype
- * on the current device: a call launches its linears grouped by dtype, at
- * most SKINNY_MAX_LINEARS_PER_LAUNCH per launch, and each launch chooses its
- * own variant (it can depend on the launch's size).  out->variant, ->waves
+/* The automatic plan (fills *out) of the launch of linears[0]'s dtype on
+ * the current device: a call launches its linears grouped by dtype (one
+ * launch per dtype, or launches of at most SKINNY_MAX_LINEARS_PER_LAUNCH under
+ * graph capture), and each launch chooses its own variant (it can depend on
+ * the launch's size).  out->variant, ->waves
  * (persistent waves of the main launch) and ->kernel (its form) are set. */
 skinny_status skinny_plan_query(const skinny_linear* linears, int count, int M,
                                 skinny_plan* out);

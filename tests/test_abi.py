@@ -76,6 +76,23 @@ def test_workspace_bytes_is_host_arithmetic():
     assert sg.workspace_bytes(7, 1, 1, 8) == 0
 
 
+def test_table_launch_workspace():
+    """A launch of more linears than the kernel arguments hold also needs
+    room for its descriptor table and for its partial sums at the largest
+    grid; it never needs less than its launches of 32 would."""
+    tiny = [sg.Linear(sg.BF16, 16, 64, 0, A, None, B, C)]
+    assert sg.stack_workspace_bytes(tiny * 32, 1) == MIN_WORKSPACE        # no split, no table
+    t33, t66 = sg.stack_workspace_bytes(tiny * 33, 1), sg.stack_workspace_bytes(tiny * 66, 1)
+    assert MIN_WORKSPACE < t33 < t66 and t66 - t33 == 33 * (t33 // 33)  # the table only
+    shapes = [(10240, 8192), (8192, 8192), (59136, 8192), (8192, 29568)]
+    for dt in (sg.BF16, sg.FP8_BS128):
+        scale = None if dt == sg.BF16 else 0x300000
+        stack = [sg.Linear(dt, N, K, 0, A, scale, B, C) for N, K in shapes] * 80
+        for M in (1, 2, 6, 8, 16):
+            full = sg.stack_workspace_bytes(stack, M)
+            assert full >= sg.stack_workspace_bytes(stack[:32], M) and full >= 320 * 64
+
+
 def bf16_call(x=B, w=A, y=C, M=1, N=64, K=64, ws=WS, wsb=None):
     wsb = sg.workspace_bytes(sg.BF16, max(M, 1), 64, 64) if wsb is None else wsb
     return sg.lib().skinny_gemm_bf16(x, w, y, M, N, K, ws, wsb, None)
@@ -170,9 +187,10 @@ def test_band_rows_and_launch_counts():
     lin = sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C)
     fp8 = sg.Linear(sg.FP8_BS128, 64, 64, 0, A, 0x300000, B, C)
     assert sg.launch_count([lin] * 32) == 1
-    assert sg.launch_count([lin] * 33) == 2
-    assert sg.launch_count([lin] * 320) == 10
+    assert sg.launch_count([lin] * 33) == 1          # one launch per dtype, table in the workspace
+    assert sg.launch_count([lin] * 320) == 1
     assert sg.launch_count([lin, fp8, lin]) == 2
+    assert sg.launch_count([lin, fp8] * 40) == 2
     assert sg.lib().skinny_launch_count(None, 1) == 0
 
 

@@ -6,9 +6,10 @@ checked linear (FP8: whole 128-row bands with their block scales) the host
 regenerates the data from the same counter-based stream and first checks it
 is byte-identical to what the GPU holds; the linear's weights are then copied
 back from the device and the oracle computes its outputs.  Checked against the
-oracle: every output of the first and the last main launch (32 linears each,
-layers 0-7 and 72-79), and in every other launch one whole layer plus one full
-128-row band of each of its other linears."""
+oracle: every output of the first and the last eight layers (32 linears each,
+layers 0-7 and 72-79), and in every other block of eight layers one whole
+layer plus one full 128-row band of each of its other linears.  The whole
+stack of each dtype runs as one launch."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +21,7 @@ from tests.gpu_util import host_codes, need_gpu
 
 pytestmark = pytest.mark.gpu
 
-PER_LAUNCH = sg.MAX_LINEARS_PER_LAUNCH
+BLOCK = 32                  # linears of eight layers
 
 
 @pytest.fixture(autouse=True)
@@ -42,13 +43,14 @@ def _run_stack(specs, M):
 
 def _plan(n_linears, rng):
     """(linear, rows) to check: None = every row, else the start of a 128-row
-    band.  All of the first and last launch; in each other launch one whole
-    layer (4 linears) and one band of each of its other linears."""
-    launches = (n_linears + PER_LAUNCH - 1) // PER_LAUNCH
+    band.  All of the first and last block of eight layers; in each other
+    block one whole layer (4 linears) and one band of each of its other
+    linears."""
+    blocks = (n_linears + BLOCK - 1) // BLOCK
     out = []
-    for g in range(launches):
-        lins = range(g * PER_LAUNCH, min((g + 1) * PER_LAUNCH, n_linears))
-        if g in (0, launches - 1):
+    for g in range(blocks):
+        lins = range(g * BLOCK, min((g + 1) * BLOCK, n_linears))
+        if g in (0, blocks - 1):
             out += [(i, None) for i in lins]
             continue
         layer = int(rng.choice(len(lins) // 4))

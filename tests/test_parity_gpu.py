@@ -245,8 +245,8 @@ def test_automatic_variant():
     least 2.5 GB of weights (two TP=1 layers); the tile kernel otherwise.  FP8
     takes the tile kernel but for one-token launches of at least 1 GB of
     weights.  Launches under 0.4 GB of up to 4 tokens (bf16) or 2 (FP8), and
-    one-token FP8 ones of at least 1 GB, run the flat row kernel.  The stack's
-    launches hold up to 32 linears."""
+    one-token FP8 ones of at least 1 GB, run the flat row kernel.  A call makes
+    one launch per dtype."""
     V, T = sg.VARIANT_VECTOR, sg.VARIANT_MFMA
 
     def variant(shapes, M, dt=sg.BF16):
