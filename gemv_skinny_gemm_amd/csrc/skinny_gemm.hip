@@ -3198,7 +3198,9 @@ skinny_status decode_linear_stack_noalloc(const skinny_linear* linears, int coun
     skinny_status st = check_linear(linears[i], M);
     if (st != SKINNY_OK) return st;
   }
-  if (required_workspace(linears, count, M) > (size_t)SKINNY_STATIC_SCRATCH_BYTES)
+  // Its launches hold at most SKINNY_MAX_LINEARS_PER_LAUNCH linears each.
+  if (required_workspace(linears, count, M, SKINNY_MAX_LINEARS_PER_LAUNCH) >
+      (size_t)SKINNY_STATIC_SCRATCH_BYTES)
     return SKINNY_ERR_WORKSPACE;
   DeviceInfo d;
   skinny_status st = device_info(&d);
@@ -3207,7 +3209,7 @@ skinny_status decode_linear_stack_noalloc(const skinny_linear* linears, int coun
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st != SKINNY_OK) return st;
-  // Launches of kernel-argument size only: nothing to copy into the buffer.
+  // Descriptors in the kernel arguments only: nothing to copy into the buffer.
   return run(linears, count, M, nullptr, ws, SKINNY_STATIC_SCRATCH_BYTES, stream, nullptr, 0,
              false, nullptr, nullptr, SKINNY_MAX_LINEARS_PER_LAUNCH);
 }

@@ -195,10 +195,11 @@ skinny_status decode_linear_stack(const skinny_linear* linears, int count, int M
  * path (the first call on a device only looks up the buffer's address there),
  * and nothing is copied: its launches hold at most
  * SKINNY_MAX_LINEARS_PER_LAUNCH linears each, descriptors in the arguments.
- *   A call is accepted only if skinny_stack_workspace_bytes(linears, count, M)
- *   <= SKINNY_STATIC_SCRATCH_BYTES (a bound from the shapes alone, so the
- *   same call is accepted on every device); otherwise SKINNY_ERR_WORKSPACE,
- *   returned before anything is enqueued.  Every other argument rule and
+ *   A call is accepted only if skinny_stack_workspace_bytes of each of its
+ *   launches (every SKINNY_MAX_LINEARS_PER_LAUNCH consecutive linears of one
+ *   dtype, in call order) is <= SKINNY_STATIC_SCRATCH_BYTES (a bound from the
+ *   shapes alone, so the same call is accepted on every device); otherwise
+ *   SKINNY_ERR_WORKSPACE, returned before anything is enqueued.  Every other argument rule and
  *   error is that of decode_linear_stack.
  *   All calls on one GPU share its buffer, which keeps the last call's
  *   contents: calls on one stream are ordered and safe, but calls that may

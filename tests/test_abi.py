@@ -168,6 +168,13 @@ def test_noalloc_stack_rejects_before_any_device_call():
     assert L.decode_linear_stack_noalloc(arr, len(big), 16, None) == WORKSPACE
     with pytest.raises(sg.SkinnyError, match="WORKSPACE"):
         sg.decode_linear_stack_noalloc(big, 16, stream=0)
+    # Its launches keep to 32 linears, so the bound is that of each 32 (the
+    # whole call's bound adds a table launch's partial sums and table).
+    stack = big * 10
+    assert sg.stack_workspace_bytes(stack, 2) > sg.STATIC_SCRATCH_BYTES
+    assert sg.stack_workspace_bytes(stack[:32], 2) <= sg.STATIC_SCRATCH_BYTES
+    arr = (sg.Linear * len(stack))(*stack)
+    assert L.decode_linear_stack_noalloc(arr, len(stack), 17, None) == INVALID
     one = (sg.Linear * 1)(sg.Linear(sg.BF16, 64, 64, 0, A, None, B, C))
     assert L.decode_linear_stack_noalloc(one, 1, 0, None) == INVALID
     assert L.decode_linear_stack_noalloc(one, 0, 1, None) == INVALID
