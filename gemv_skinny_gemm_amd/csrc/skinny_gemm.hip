@@ -2656,8 +2656,11 @@ skinny_status launch_group(const DeviceInfo& dev, const skinny_linear* const* li
 // Measured on MI355X (16 TP=1 layers, one process, interleaved, 2 to 16
 // launches): every launch costs ~9.5 us of ramp and tail (bf16 and FP8 at
 // M = 1) to ~16 us (FP8 at M = 6, with its second pass); copying a 5 KB
-// table ahead of a launch costs 0-10 us.
-constexpr int kGroupsUncapped = 1 << 30;
+// table ahead of a launch costs 0-10 us.  A table holds at most
+// kTableLinearsMax descriptors (320 KB; the second pass's grid has a row per
+// linear), so a call of more linears of one dtype makes more launches.
+constexpr int kTableLinearsMax = 4096;
+constexpr int kGroupsUncapped = kTableLinearsMax;
 
 int launch_count(const skinny_linear* lin, int count, int max_group) {
   int launches = 0;

@@ -175,7 +175,8 @@ skinny_status skinny_gemm_fp8_bs128(const void* x, const void* w_fp8, const floa
  *              count, M); contents undefined afterwards
  * Each linear reads its own x and writes its own y; no y may overlap any x,
  * W, w_scale, other y or the workspace (checked).  The linears of each dtype,
- * in call order, are streamed by one persistent launch; a launch of more than
+ * in call order, are streamed by one persistent launch (one per 4096 linears
+ * of a dtype, should a call have more); a launch of more than
  * SKINNY_MAX_LINEARS_PER_LAUNCH linears reads their descriptors from a table
  * that the call copies from host memory into the workspace on `stream` just
  * before it.  On a stream under graph capture (where such a copy would read
@@ -215,7 +216,8 @@ skinny_status skinny_linear_run(const skinny_linear* linears, int count, int M,
                                 size_t workspace_bytes, void* stream);
 
 /* Number of main-kernel launches a call over these linears makes on a stream
- * not under graph capture: one per dtype present; 0 if invalid. */
+ * not under graph capture: one per dtype present (per 4096 linears of it);
+ * 0 if invalid. */
 int skinny_launch_count(const skinny_linear* linears, int count);
 
 /* skinny_linear_run that also records events around each main-kernel launch,

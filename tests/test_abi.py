@@ -198,6 +198,7 @@ def test_band_rows_and_launch_counts():
     assert sg.launch_count([lin] * 320) == 1
     assert sg.launch_count([lin, fp8, lin]) == 2
     assert sg.launch_count([lin, fp8] * 40) == 2
+    assert sg.launch_count([lin] * 4096) == 1 and sg.launch_count([lin] * 4097) == 2
     assert sg.lib().skinny_launch_count(None, 1) == 0
 
 
