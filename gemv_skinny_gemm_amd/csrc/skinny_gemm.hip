@@ -2472,6 +2472,14 @@ KernelChoice tiles_large_kernel(const skinny_linear* const* lin, int count) {
 // +2.4 / +10.4 / +7.0% at 10 / 12 / 16 (the walk costs 1.8% at M = 1).
 constexpr int kTilesWalkMinMBf16 = 5;
 constexpr int kTilesWalkMinMFp8 = 9;
+// The 8-wave FP8 shape walks from 4 tokens: its launches are the large ones
+// (a whole stack in one launch), whose split would write partial sums for
+// every split linear before one second pass reads them back.  Measured on
+// MI355X, 80-layer FP8 TP=1 stack in one launch, walk vs split (same
+// process, interleaved; with the exact-fit layout only down walks up to six
+// tokens): -0.3 / -0.1 / +0.7 / +1.4 / +2.3 / +6.7 / +10.4% at M = 2 / 3 / 4 /
+// 5 / 6 / 7 / 8.
+constexpr int kTilesWalkMinMFp8Large = 4;
 
 // K-chunks per linear (either kernel): enough for the x window to fit the LDS
 // budget and, when the launch is too small to give every workgroup the
@@ -2488,7 +2496,9 @@ long long plan_chunks(LinDesc* lin, int count, int M, int rows, int x_lds_bytes,
   for (int i = 0; i < count; ++i) {
     LinDesc& d = lin[i];
     int c, w = 1;
-    const bool walk = M >= (dtype == SKINNY_BF16 ? kTilesWalkMinMBf16 : kTilesWalkMinMFp8);
+    const bool walk = M >= (dtype == SKINNY_BF16                      ? kTilesWalkMinMBf16
+                            : rows == kTileRows * kTilesWavesLarge ? kTilesWalkMinMFp8Large
+                                                                   : kTilesWalkMinMFp8);
     if (tiles) tiles_split(dtype, M, d.K, par, x_lds_bytes, walk, &c, &w, fit);
     else c = rows_chunks(dtype, M, d.K, par);
     d.chunks = c;

@@ -167,9 +167,9 @@ def test_fp8_large_workgroup_sampled(M):
 def test_window_walk_sampled(dtype, M, K):
     """One linear of 524288 rows: its row groups alone give every tile
     workgroup 16 units (no K split for parallelism), and the x window of
-    M + 1 token rows holds half of K, so from M = 5 (bf16) or 9 (FP8) tokens
-    on each unit walks its two x windows with the sums in registers (no
-    partial sums, no second pass); FP8 on the 8-wave workgroup.  Sampled rows
+    M + 1 token rows holds half of K, so from M = 5 (bf16) or 4 (FP8, on the
+    8-wave workgroup) tokens on each unit walks its two x windows with the
+    sums in registers (no partial sums, no second pass).  Sampled rows
     against the oracle as above."""
     N = 524288
     tag = f"walk-{dtype}-{M}-{K}"
