@@ -2433,7 +2433,7 @@ int kernel_lds(const KernelChoice& k, int dtype) {
 }
 
 // The 8-wave tile workgroup (one per CU, twice the x window: fewer K-chunks,
-// one x copy per CU) for FP8 launches of M >= 2 tokens with at least 8 of its
+// one x copy per CU) for FP8 launches of M >= 2 tokens (bf16: M >= 5) with at least 8 of its
 // 128-row groups per CU.  Measured on MI355X against the 4-wave shape: FP8
 // TP=1 stack (8-layer launches) +3 / +2 / +6 / +7 / +7% at M = 2 / 4 / 6 / 8 /
 // 16 but -3% at M = 1; a single FP8 gate_up (462 groups) -11% at M = 6, the
@@ -2441,7 +2441,10 @@ int kernel_lds(const KernelChoice& k, int dtype) {
 // -4 to -6%.
 constexpr int kTilesLargeGroupsPerCU = 8;
 bool tiles_large(const skinny_linear* const* lin, int count, int M, int cus) {
-  if (lin[0]->dtype != SKINNY_FP8_BS128 || M < 2) return false;
+  // bf16 from M = 5 (its tile launches): with a whole stack in one launch
+  // the 8-wave shape gained +1.0 / +1.4 / +1.6% at M = 6 / 8 / 16 (80-layer
+  // bf16 stack, same process, outputs bitwise equal).
+  if (M < 2 || (lin[0]->dtype == SKINNY_BF16 && M < 5)) return false;
   long long groups = 0;
   for (int i = 0; i < count; ++i)
     groups += (lin[i]->N + kTileRows * kTilesWavesLarge - 1) / (kTileRows * kTilesWavesLarge);
